@@ -1,0 +1,241 @@
+"""fp64 reference for the top-k routed MoE feed-forward layer with MXFP4 expert weights.
+
+TEST INFRASTRUCTURE: imported only by tests/, the smoke check and the benchmark's CPU
+baseline. It shares no code, table or constant with the GPU library.
+
+What it computes, and where each step comes from:
+
+* Sources ("pages"):
+  - [walkthrough] the gpt-oss architecture walkthrough at pnsm.cn/news/1975454
+    (sections 1, 2.2 "MoE layer", 2.4 "comparison with GPT-2 / Qwen3", 4 "config.toml").
+  - [review] the review of the from-scratch PyTorch gpt-oss-20B at
+    pomoai.com/hubs/HamzaElshafie/gpt-oss-20B (sections 3.3 "SwiGLU", 3.4 "MoE", 5).
+  - [config] the config.json read-through at m.youleyou.com/wenzhang/3183859 (Part.01).
+  - [OCP-MX] OCP Microscaling Formats (MX) Specification v1.0 -- the public definition of
+    the MXFP4 element (E2M1) and scale (E8M0) encodings; the pages only name the format.
+* Every floating-point step runs in float64 on exact inputs (bf16 and fp32 inputs widen
+  exactly). The one place floating point decides an integer -- which experts a token
+  picks -- is decided on logits rounded to float32, the precision the GPU router works in.
+"""
+from __future__ import annotations
+
+import dataclasses
+from typing import Callable, Optional, Sequence, Tuple
+
+import numpy as np
+
+E2M1_BIAS = 1  # exponent bias of the FP4 E2M1 element [OCP-MX, FP4 element definition]
+E8M0_BIAS = 127  # exponent bias of the E8M0 shared scale [OCP-MX, scale definition]
+E8M0_NAN = 0xFF
+
+
+def e2m1_value(code: int) -> float:
+    """Value of one 4-bit E2M1 element [OCP-MX FP4 definition; walkthrough §1, §4 name MXFP4].
+
+    Bit 3 is the sign, bits 2..1 the exponent (bias 1), bit 0 the mantissa. Exponent
+    field 0 encodes subnormals (0 and 0.5); the format has no infinity and no NaN.
+    """
+    code = int(code) & 0xF
+    sign = (code >> 3) & 1
+    exp_field = (code >> 1) & 3
+    man = code & 1
+    if exp_field == 0:
+        mag = (man / 2.0) * 2.0 ** (1 - E2M1_BIAS)
+    else:
+        mag = (1.0 + man / 2.0) * 2.0 ** (exp_field - E2M1_BIAS)
+    return -mag if sign else mag
+
+
+def e8m0_value(byte: int) -> float:
+    """Value of one E8M0 scale byte: a bare power of two, 2^(byte-127); 0xFF is NaN [OCP-MX]."""
+    byte = int(byte) & 0xFF
+    if byte == E8M0_NAN:
+        return float("nan")
+    return 2.0 ** (byte - E8M0_BIAS)
+
+
+_E2M1_TABLE = np.array([e2m1_value(c) for c in range(16)], dtype=np.float64)
+_E8M0_TABLE = np.array([e8m0_value(b) for b in range(256)], dtype=np.float64)
+
+
+def mxfp4_decode(codes: np.ndarray, scales: np.ndarray) -> np.ndarray:
+    """Decode an MXFP4 tensor to float64 [walkthrough §1, §4: MoE weights in MXFP4, ~4.25 bit].
+
+    codes  uint8 [..., K/2]: element 2j is the low nibble of byte j, element 2j+1 the high one.
+    scales uint8 [..., K/32]: one E8M0 scale per 32 consecutive elements along the last axis.
+    4 bits per element plus 8 bits per 32 elements gives the pages' 4.25 bits per weight.
+    """
+    codes = np.asarray(codes, dtype=np.uint8)
+    scales = np.asarray(scales, dtype=np.uint8)
+    K = codes.shape[-1] * 2
+    if scales.shape[-1] * 32 != K or scales.shape[:-1] != codes.shape[:-1]:
+        raise ValueError("scales must hold one byte per 32 elements of each row")
+    elem = np.empty(codes.shape[:-1] + (K,), dtype=np.float64)
+    elem[..., 0::2] = _E2M1_TABLE[codes & 0xF]
+    elem[..., 1::2] = _E2M1_TABLE[codes >> 4]
+    blk = _E8M0_TABLE[scales]
+    elem = elem.reshape(codes.shape[:-1] + (K // 32, 32)) * blk[..., None]
+    return elem.reshape(codes.shape[:-1] + (K,))
+
+
+def bf16_to_f64(bits: np.ndarray) -> np.ndarray:
+    """bfloat16 bit patterns -> float64 (exact): the pattern is the top half of a float32."""
+    bits = np.asarray(bits, dtype=np.uint16)
+    return (bits.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+
+
+def router_logits(x: np.ndarray, w: np.ndarray, b: Optional[np.ndarray]) -> np.ndarray:
+    """One score per (token, expert) from a linear projection of the token [review §3.4].
+
+    x float64 [T][H]; w fp32 [E][H]; b fp32 [E] or None. Returns float64 [T][E].
+    """
+    logits = np.asarray(x, np.float64) @ np.asarray(w, np.float64).T
+    if b is not None:
+        logits = logits + np.asarray(b, np.float64)[None, :]
+    return logits
+
+
+def topk_select(logits: np.ndarray, k: int) -> np.ndarray:
+    """The k highest-scoring experts per token, highest first [review §3.4; walkthrough §2.2, §4;
+    config Part.01 experts_per_token = 4].
+
+    The pages do not say how ties break or in which order the k experts are listed. Reading
+    taken: ties go to the lower expert id, and the list is in descending score order. The
+    choice is made on the scores rounded to float32 (the GPU router's precision).
+    """
+    l32 = np.asarray(logits).astype(np.float32)
+    order = np.argsort(-l32, axis=-1, kind="stable")  # stable: equal scores keep id order
+    return order[..., :k].astype(np.int32)
+
+
+def softmax_selected(sel_logits: np.ndarray) -> np.ndarray:
+    """Mixing weights: softmax over the k selected experts' scores only [walkthrough §2.2;
+    review §3.4]. They sum to one for every token."""
+    sel = np.asarray(sel_logits, np.float64)
+    z = np.exp(sel - sel.max(axis=-1, keepdims=True))
+    return z / z.sum(axis=-1, keepdims=True)
+
+
+def route(x_bits: np.ndarray, w: np.ndarray, b: Optional[np.ndarray], k: int,
+          forced_idx: Optional[np.ndarray] = None) -> Tuple[np.ndarray, np.ndarray, np.ndarray]:
+    """Router: logits, top-k ids, softmax weights. ``forced_idx`` replaces the selection
+    (used to grade tokens whose k-th and (k+1)-th scores nearly tie)."""
+    logits = router_logits(bf16_to_f64(x_bits), w, b)
+    idx = topk_select(logits, k) if forced_idx is None else np.asarray(forced_idx, np.int32)
+    sel = np.take_along_axis(logits, idx.astype(np.int64), axis=-1)
+    return logits, idx, softmax_selected(sel)
+
+
+def permute(topk_idx: np.ndarray, E: int) -> Tuple[np.ndarray, np.ndarray, np.ndarray, np.ndarray]:
+    """Group the T*k (token, rank) slots by expert [review §3.4: only the picked experts run;
+    retrospective "当时发生了什么": all expert weights stay resident].
+
+    Slot s = t*k + j. Returns counts[E], offsets[E+1] (exclusive prefix sum of counts),
+    sorted_slot[T*k] (slots ordered by expert, then by slot id) and slot_row[T*k], the
+    position of each slot in that order (the inverse permutation).
+    """
+    flat = np.asarray(topk_idx, np.int64).reshape(-1)
+    counts = np.bincount(flat, minlength=E).astype(np.int32)
+    offsets = np.zeros(E + 1, np.int32)
+    offsets[1:] = np.cumsum(counts)
+    sorted_slot = np.argsort(flat, kind="stable").astype(np.int32)
+    slot_row = np.empty_like(sorted_slot)
+    slot_row[sorted_slot] = np.arange(flat.size, dtype=np.int32)
+    return counts, offsets, sorted_slot, slot_row
+
+
+def swiglu_clamped(h: np.ndarray, limit: float = 7.0, alpha: float = 1.0) -> np.ndarray:
+    """Clamped gated SwiGLU with the +1 on the linear branch [walkthrough §1, §2.2;
+    review §3.3].
+
+    h [..., 2I] holds the fused projection with gate and linear interleaved (2i = gate,
+    2i+1 = linear; the pages leave the order open). Both halves are clamped to
+    [-limit, limit] (the pages give +-7.0 without saying which half or side), then
+    a = g * sigmoid(alpha*g) * (l + 1). alpha = 1 is plain SiLU, the only slope the pages
+    imply; other values are accepted for parity runs.
+    """
+    h = np.asarray(h, np.float64)
+    g = np.clip(h[..., 0::2], -limit, limit)
+    lin = np.clip(h[..., 1::2], -limit, limit)
+    sig = 1.0 / (1.0 + np.exp(-alpha * g))
+    return g * sig * (lin + 1.0)
+
+
+def expert_ffn(x: np.ndarray, w1: np.ndarray, b1: Optional[np.ndarray], w2: np.ndarray,
+               b2: Optional[np.ndarray], limit: float = 7.0, alpha: float = 1.0
+               ) -> Tuple[np.ndarray, np.ndarray, np.ndarray]:
+    """One expert on rows x [n][H]: h = x W1^T + b1 (2I outputs), a = swiglu(h), y = a W2^T + b2
+    [walkthrough §2.4: embedding and expert projection widths are both 2880]. Returns (h, a, y)."""
+    h = np.asarray(x, np.float64) @ np.asarray(w1, np.float64).T
+    if b1 is not None:
+        h = h + b1[None, :]
+    a = swiglu_clamped(h, limit, alpha)
+    y = a @ np.asarray(w2, np.float64).T
+    if b2 is not None:
+        y = y + b2[None, :]
+    return h, a, y
+
+
+ExpertTensors = Tuple[np.ndarray, np.ndarray, Optional[np.ndarray],
+                      np.ndarray, np.ndarray, Optional[np.ndarray]]
+
+
+def experts_from_arrays(w1_codes, w1_scales, w1_bias, w2_codes, w2_scales, w2_bias
+                        ) -> Callable[[int], ExpertTensors]:
+    """Adapter: stacked [E][...] arrays -> per-expert tuple getter (bias arrays may be None)."""
+    def get(e: int) -> ExpertTensors:
+        return (w1_codes[e], w1_scales[e], None if w1_bias is None else w1_bias[e],
+                w2_codes[e], w2_scales[e], None if w2_bias is None else w2_bias[e])
+    return get
+
+
+@dataclasses.dataclass
+class MoEResult:
+    out: np.ndarray          # float64 [n_tok][H]
+    tokens: np.ndarray       # int64 [n_tok], which rows of x these are
+    logits: np.ndarray       # float64 [n_tok][E]
+    idx: np.ndarray          # int32 [n_tok][k]
+    w: np.ndarray            # float64 [n_tok][k]
+    h: Optional[np.ndarray] = None    # float64 [n_tok][k][2I]
+    act: Optional[np.ndarray] = None  # float64 [n_tok][k][I]
+    y: Optional[np.ndarray] = None    # float64 [n_tok][k][H]
+
+
+def moe_layer(x_bits: np.ndarray, router_w: np.ndarray, router_b: Optional[np.ndarray],
+              get_expert: Callable[[int], ExpertTensors], k: int,
+              limit: float = 7.0, alpha: float = 1.0,
+              tokens: Optional[Sequence[int]] = None,
+              forced_idx: Optional[np.ndarray] = None,
+              keep_intermediates: bool = False) -> MoEResult:
+    """The whole layer for the rows ``tokens`` of x (all rows if None).
+
+    Route each token to its top-k experts with softmax weights over the selected scores,
+    run only the selected experts, and sum their outputs weighted by those weights
+    [review §3.4; walkthrough §2.2]. Tokens are independent, so any subset can be computed.
+    """
+    x_bits = np.asarray(x_bits, np.uint16)
+    tok = np.arange(x_bits.shape[0]) if tokens is None else np.asarray(tokens, np.int64)
+    x = bf16_to_f64(x_bits[tok])
+    logits, idx, w = route(x_bits[tok], router_w, router_b, k, forced_idx)
+    n, H = x.shape
+    y_slots = np.zeros((n, k, H), np.float64)
+    h_slots = a_slots = None
+    for e in np.unique(idx):
+        rows, ranks = np.nonzero(idx == e)
+        w1c, w1s, b1, w2c, w2s, b2 = get_expert(int(e))
+        W1 = mxfp4_decode(w1c, w1s)
+        W2 = mxfp4_decode(w2c, w2s)
+        h, a, y = expert_ffn(x[rows], W1, None if b1 is None else bf16_to_f64(b1),
+                             W2, None if b2 is None else bf16_to_f64(b2), limit, alpha)
+        y_slots[rows, ranks] = y
+        if keep_intermediates:
+            if h_slots is None:
+                h_slots = np.zeros((n, k, h.shape[1]), np.float64)
+                a_slots = np.zeros((n, k, a.shape[1]), np.float64)
+            h_slots[rows, ranks] = h
+            a_slots[rows, ranks] = a
+    out = np.zeros((n, H), np.float64)
+    for j in range(k):  # weighted sum over the k picks, rank order
+        out += w[:, j:j + 1] * y_slots[:, j, :]
+    return MoEResult(out, tok, logits, idx, w, h_slots, a_slots,
+                     y_slots if keep_intermediates else None)

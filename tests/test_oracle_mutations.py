@@ -1,0 +1,169 @@
+"""Plant plausible mistakes in the oracle (CPU only) and check that some pin catches each.
+
+A pin set that lets one of these through would let the same mistake through in the oracle
+itself, so this is the evidence that the pins constrain every step of the oracle.
+"""
+import numpy as np
+import pytest
+
+import oracle.moe_oracle as om
+import pins
+
+_orig_decode = om.mxfp4_decode
+_orig_swiglu = om.swiglu_clamped
+_orig_topk = om.topk_select
+_orig_softmax = om.softmax_selected
+_orig_logits = om.router_logits
+_orig_ffn = om.expert_ffn
+_orig_permute = om.permute
+_orig_route = om.route
+_orig_e2m1 = om.e2m1_value
+_orig_e8m0 = om.e8m0_value
+
+
+def _decode_nibbles_swapped(codes, scales):
+    c = np.asarray(codes, np.uint8)
+    swapped = ((c & 0xF) << 4) | (c >> 4)
+    return _orig_decode(swapped.astype(np.uint8), scales)
+
+
+def _decode_block16(codes, scales):
+    """Mistake: scale index taken as element // 16 (clamped), i.e. 16-element blocks."""
+    c = np.asarray(codes, np.uint8)
+    K = c.shape[-1] * 2
+    table = np.array([om.e2m1_value(v) for v in range(16)])
+    el = np.empty(c.shape[:-1] + (K,))
+    el[..., 0::2] = table[c & 0xF]
+    el[..., 1::2] = table[c >> 4]
+    s = np.array([om.e8m0_value(b) for b in range(256)])[np.asarray(scales)]
+    sidx = np.minimum(np.arange(K) // 16, K // 32 - 1)
+    return el * s[..., sidx]
+
+
+def _decode_scale_bias128(codes, scales):
+    return _orig_decode(codes, scales) * 0.5
+
+
+def _swiglu_swapped(h, limit=7.0, alpha=1.0):
+    h = np.asarray(h, float).copy()
+    g = h[..., 0::2].copy()
+    h[..., 0::2] = h[..., 1::2]
+    h[..., 1::2] = g
+    return _orig_swiglu(h, limit, alpha)
+
+
+def _swiglu_no_plus1(h, limit=7.0, alpha=1.0):
+    h = np.asarray(h, float)
+    g = np.clip(h[..., 0::2], -limit, limit)
+    lin = np.clip(h[..., 1::2], -limit, limit)
+    return g / (1 + np.exp(-alpha * g)) * lin
+
+
+def _swiglu_sig_sign(h, limit=7.0, alpha=1.0):
+    h = np.asarray(h, float)
+    g = np.clip(h[..., 0::2], -limit, limit)
+    lin = np.clip(h[..., 1::2], -limit, limit)
+    return g / (1 + np.exp(alpha * g)) * (lin + 1)
+
+
+def _swiglu_gate_clamp_only(h, limit=7.0, alpha=1.0):
+    h = np.asarray(h, float)
+    g = np.clip(h[..., 0::2], -limit, limit)
+    lin = h[..., 1::2]
+    return g / (1 + np.exp(-alpha * g)) * (lin + 1)
+
+
+def _swiglu_no_clamp(h, limit=7.0, alpha=1.0):
+    h = np.asarray(h, float)
+    g = h[..., 0::2]
+    lin = h[..., 1::2]
+    return g / (1 + np.exp(-alpha * g)) * (lin + 1)
+
+
+def _swiglu_alpha_ignored(h, limit=7.0, alpha=1.0):
+    return _orig_swiglu(h, limit, 1.0)
+
+
+def _topk_ascending(logits, k):
+    l32 = np.asarray(logits).astype(np.float32)
+    return np.argsort(l32, axis=-1, kind="stable")[..., :k].astype(np.int32)
+
+
+def _topk_high_id_ties(logits, k):
+    l32 = np.asarray(logits).astype(np.float32)
+    E = l32.shape[-1]
+    order = np.argsort(-l32[..., ::-1], axis=-1, kind="stable")
+    return (E - 1 - order[..., :k]).astype(np.int32)
+
+
+def _topk_unsorted(logits, k):
+    return np.sort(_orig_topk(logits, k), axis=-1).astype(np.int32)
+
+
+def _softmax_not_renormalised(sel):
+    sel = np.asarray(sel, float)
+    return np.exp(sel) / (np.exp(sel).sum(-1, keepdims=True) + 1.0)
+
+
+def _logits_no_bias(x, w, b):
+    return _orig_logits(x, w, None)
+
+
+def _ffn_no_b1(x, w1, b1, w2, b2, limit=7.0, alpha=1.0):
+    return _orig_ffn(x, w1, None, w2, b2, limit, alpha)
+
+
+def _ffn_no_b2(x, w1, b1, w2, b2, limit=7.0, alpha=1.0):
+    return _orig_ffn(x, w1, b1, w2, None, limit, alpha)
+
+
+def _permute_unstable(topk_idx, E):
+    counts, offsets, sorted_slot, slot_row = _orig_permute(topk_idx, E)
+    ss = sorted_slot.copy()
+    for e in range(E):
+        ss[offsets[e]:offsets[e + 1]] = ss[offsets[e]:offsets[e + 1]][::-1]
+    sr = np.empty_like(ss)
+    sr[ss] = np.arange(ss.size, dtype=ss.dtype)
+    return counts, offsets, ss, sr
+
+
+def _route_weights_reversed(x_bits, w, b, k, forced_idx=None):
+    logits, idx, wt = _orig_route(x_bits, w, b, k, forced_idx)
+    return logits, idx, wt[..., ::-1].copy()
+
+
+MUTATIONS = {
+    "decode_nibbles_swapped": ("mxfp4_decode", _decode_nibbles_swapped),
+    "decode_scale_per_16": ("mxfp4_decode", _decode_block16),
+    "decode_scale_bias_128": ("mxfp4_decode", _decode_scale_bias128),
+    "e2m1_bias_0": ("e2m1_value", lambda c: 2.0 * _orig_e2m1(c)),
+    "e8m0_bias_126": ("e8m0_value", lambda b: 2.0 * _orig_e8m0(b)),
+    "swiglu_gate_linear_swapped": ("swiglu_clamped", _swiglu_swapped),
+    "swiglu_no_plus_one": ("swiglu_clamped", _swiglu_no_plus1),
+    "swiglu_sigmoid_sign": ("swiglu_clamped", _swiglu_sig_sign),
+    "swiglu_clamp_gate_only": ("swiglu_clamped", _swiglu_gate_clamp_only),
+    "swiglu_no_clamp": ("swiglu_clamped", _swiglu_no_clamp),
+    "swiglu_alpha_ignored": ("swiglu_clamped", _swiglu_alpha_ignored),
+    "topk_ascending": ("topk_select", _topk_ascending),
+    "topk_ties_to_high_id": ("topk_select", _topk_high_id_ties),
+    "topk_not_in_score_order": ("topk_select", _topk_unsorted),
+    "softmax_not_renormalised": ("softmax_selected", _softmax_not_renormalised),
+    "router_bias_dropped": ("router_logits", _logits_no_bias),
+    "ffn_gate_up_bias_dropped": ("expert_ffn", _ffn_no_b1),
+    "ffn_down_bias_dropped": ("expert_ffn", _ffn_no_b2),
+    "permute_unstable": ("permute", _permute_unstable),
+    "combine_weights_reversed": ("route", _route_weights_reversed),
+}
+
+
+@pytest.mark.parametrize("name", sorted(MUTATIONS))
+def test_some_pin_catches(name, monkeypatch):
+    attr, bad = MUTATIONS[name]
+    monkeypatch.setattr(om, attr, bad)
+    caught = []
+    for pin in pins.ALL_PINS:
+        try:
+            pin()
+        except Exception as exc:  # an assertion, or the mistake breaking a shape
+            caught.append((pin.__name__, type(exc).__name__))
+    assert caught, f"planted mistake {name!r} passed every pin"

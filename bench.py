@@ -1,0 +1,240 @@
+"""Benchmark of the MXFP4 top-k MoE layer on one MI355X; prints one JSON line.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload decode20b] [--T 64]
+
+A step is one call of the whole layer (router, top-k/softmax, permutation, expert
+gate_up + SwiGLU, down, weighted combine) over one batch of T tokens, with inputs
+resident in HBM. Steps rotate over L distinct copies of the layer's weights (24 for the
+20b-shaped layer, 36 for the 120b-shaped one, like the models' depth) so the 256 MB
+last-level cache cannot hold the weights between steps.
+
+The roofline object covers the dominant step, the expert FFN (moe_mxfp4_ffn: the gate_up
+and down kernels), timed with HIP events on the stream it runs on. cpu_baseline times
+the fp64 oracle on a bounded sample of the same workload on the host cores.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "MoE layer tokens/s; % HBM BW at T≤64, % MXFP4 MFMA peak at T=4096"
+HBM_PEAK_GBS = 8000.0
+BF16_PEAK_TFLOPS = 2500.0
+MXFP4_PEAK_TFLOPS = 10100.0
+
+EXPERT_BYTES_PER_ROW = lambda K: K // 2 + K // 32 + 2  # codes + scales + bf16 bias
+
+
+def parse():
+    p = argparse.ArgumentParser()
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=200)
+    p.add_argument("--warmup", type=int, default=20)
+    p.add_argument("--workload", default="decode20b",
+                   choices=["decode20b", "prefill20b", "prefill120b", "decode120b_zipf"])
+    p.add_argument("--T", type=int, default=0, help="batch size (default: the workload's largest)")
+    p.add_argument("--layers", type=int, default=0, help="rotated weight copies (default 24 / 36)")
+    p.add_argument("--path", type=int, default=0, help="0 auto, 1 stream, 2 gemm")
+    p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--no-sweep", action="store_true")
+    return p.parse_args()
+
+
+def main():
+    args = parse()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1"}), flush=True)
+        sys.exit(2)
+
+    import torch
+    import synth
+    import sparse_moe_transformer_router_amd as moe
+
+    torch.cuda.init()
+    dev = torch.device("cuda:0")
+    cfg = synth.get_config(args.workload)
+    T = args.T or cfg.T_list[-1]
+    L = args.layers or (24 if cfg.E <= 32 else 36)
+    H, I, E, k = cfg.H, cfg.I, cfg.E, cfg.k
+
+    def log(msg):
+        print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+    t0 = time.time()
+    inp = synth.make_inputs(cfg, T)
+    log(f"generated {cfg.name} T={T} in {time.time() - t0:.1f}s")
+
+    def u8(a):
+        return torch.from_numpy(np.ascontiguousarray(a)).to(dev)
+
+    def bf16(a):
+        return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).to(dev).view(torch.bfloat16)
+
+    base_w1 = moe.MXFP4Weight(u8(inp.w1_codes), u8(inp.w1_scales), bf16(inp.w1_bias))
+    base_w2 = moe.MXFP4Weight(u8(inp.w2_codes), u8(inp.w2_scales), bf16(inp.w2_bias))
+    base_rt = moe.Router(torch.from_numpy(inp.router_w).to(dev), torch.from_numpy(inp.router_b).to(dev))
+    layers = [(base_rt, base_w1, base_w2)]
+    for _ in range(L - 1):  # device-side copies at distinct addresses
+        layers.append((moe.Router(base_rt.weight.clone(), base_rt.bias.clone()),
+                       moe.MXFP4Weight(base_w1.codes.clone(), base_w1.scales.clone(), base_w1.bias.clone()),
+                       moe.MXFP4Weight(base_w2.codes.clone(), base_w2.scales.clone(), base_w2.bias.clone())))
+    x = bf16(inp.x)
+    opts = moe.Options(path=args.path)
+    ws = moe.workspace(T, E, k, H, I, args.path, device=dev)
+    out = torch.empty((T, H), dtype=torch.bfloat16, device=dev)
+    torch.cuda.synchronize()
+    log(f"{L} layer copies resident ({L * (base_w1.codes.numel() + base_w1.scales.numel() + base_w2.codes.numel() + base_w2.scales.numel()) / 1e9:.1f} GB)")
+
+    # realised routing of this batch (same for every copy)
+    idx, _ = moe.moe_route(x, base_rt, k)
+    counts = np.bincount(idx.cpu().numpy().ravel(), minlength=E)
+    touched = int((counts > 0).sum())
+
+    def step(i):
+        rt, w1, w2 = layers[i % L]
+        moe.moe_forward_ex(x, rt, w1, w2, k, opts, out=out, ws=ws)
+
+    def timed_steps(n, warm):
+        for i in range(warm):
+            step(i)
+        torch.cuda.synchronize()
+        ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        ev0.record()
+        for i in range(n):
+            step(i)
+        ev1.record()
+        torch.cuda.synchronize()
+        return ev0.elapsed_time(ev1) / n  # ms per step
+
+    ms = timed_steps(args.steps, args.warmup)
+    tok_s = T / (ms * 1e-3)
+    log(f"T={T}: {ms * 1e3:.1f} us/step, {tok_s:.0f} tok/s, touched {touched}/{E}")
+
+    # ---- dominant step: the expert FFN (gate_up + down), timed with events on its stream
+    offsets = torch.empty(E + 1, dtype=torch.int32, device=dev)
+    sorted_slot = torch.empty(T * k, dtype=torch.int32, device=dev)
+    slot_row = torch.empty(T * k, dtype=torch.int32, device=dev)
+    y = torch.empty((T * k, H), dtype=torch.float32, device=dev)
+    tw = torch.empty((T, k), dtype=torch.float32, device=dev)
+    ti = torch.empty((T, k), dtype=torch.int32, device=dev)
+    n_ffn = max(20, min(args.steps, 200))
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n_ffn)]
+    for rep in range(2):  # first pass warms up
+        for i in range(n_ffn):
+            rt, w1, w2 = layers[i % L]
+            moe.moe_route(x, rt, k, topk_idx=ti, topk_w=tw, ws=ws)
+            moe.moe_permute(ti, E, out=(offsets, sorted_slot, slot_row))
+            if rep:
+                evs[i][0].record()
+            moe.moe_mxfp4_ffn(x, k, E, offsets, sorted_slot, w1, w2, opts, y=y, ws=ws)
+            if rep:
+                evs[i][1].record()
+            moe.moe_combine(y, slot_row, tw, out=out)
+        torch.cuda.synchronize()
+    ffn_ms = float(np.mean([a.elapsed_time(b) for a, b in evs]))
+
+    expert_bytes = 2 * I * EXPERT_BYTES_PER_ROW(H) + H * EXPERT_BYTES_PER_ROW(I)
+    ffn_bytes = touched * expert_bytes + T * H * 2
+    ffn_flops = 2.0 * T * k * (2 * I * H + H * I)
+    decode_like = cfg.name.startswith("decode")
+    if decode_like:
+        achieved = ffn_bytes / (ffn_ms * 1e-3) / 1e9
+        roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                    "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None}
+    else:
+        achieved = ffn_flops / (ffn_ms * 1e-3) / 1e12
+        roofline = {"bound": "mfma", "achieved": round(achieved, 1), "peak": BF16_PEAK_TFLOPS,
+                    "unit": "TFLOP/s", "frac": round(achieved / BF16_PEAK_TFLOPS, 4), "traffic": None,
+                    "frac_of_mxfp4_peak": round(achieved / MXFP4_PEAK_TFLOPS, 4)}
+    roofline.update({"kernel": "moe_mxfp4_ffn (gate_up + down)", "ms_per_launch": round(ffn_ms, 5),
+                     "algorithmic_bytes": int(ffn_bytes), "algorithmic_flops": ffn_flops})
+    log(f"ffn: {ffn_ms * 1e3:.1f} us, {roofline['achieved']} {roofline['unit']} ({roofline['frac']:.1%})")
+
+    sweep = []
+    if not args.no_sweep and decode_like:
+        for Ts in cfg.T_list:
+            if Ts == T:
+                continue
+            xs = bf16(synth.make_x(cfg, Ts))
+            wss = moe.workspace(Ts, E, k, H, I, args.path, device=dev)
+            outs = torch.empty((Ts, H), dtype=torch.bfloat16, device=dev)
+            ids, _ = moe.moe_route(xs, base_rt, k)
+            tch = int((np.bincount(ids.cpu().numpy().ravel(), minlength=E) > 0).sum())
+
+            def step_s(i):
+                rt, w1, w2 = layers[i % L]
+                moe.moe_forward_ex(xs, rt, w1, w2, k, opts, out=outs, ws=wss)
+            for i in range(args.warmup):
+                step_s(i)
+            torch.cuda.synchronize()
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record()
+            for i in range(args.steps):
+                step_s(i)
+            b.record()
+            torch.cuda.synchronize()
+            ms_s = a.elapsed_time(b) / args.steps
+            layer_bytes = tch * expert_bytes + E * H * 4 + E * 4 + Ts * H * 4 + Ts * k * 8
+            sweep.append({"T": Ts, "ms_per_step": round(ms_s, 5), "tokens_per_s": round(Ts / (ms_s * 1e-3), 1),
+                          "touched_experts": tch, "layer_GBps": round(layer_bytes / (ms_s * 1e-3) / 1e9, 1)})
+            log(f"sweep T={Ts}: {ms_s * 1e3:.1f} us/step, touched {tch}")
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline(cfg, inp, T, log)
+
+    layer_bytes = touched * expert_bytes + E * H * 4 + E * 4 + T * H * 4 + T * k * 8
+    line = {
+        "metric": METRIC,
+        "value": round(tok_s, 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": cfg.name, "T": T, "E": E, "k": k, "hidden": H, "expert_width": I,
+                   "weights": "MXFP4 (E2M1 + E8M0 per 32)", "layers_rotated": L, "path": args.path,
+                   "touched_experts": touched, "per_expert_slots_min_max": [int(counts.min()), int(counts.max())],
+                   "layer_GBps": round(layer_bytes / (ms * 1e-3) / 1e9, 1)},
+        "roofline": roofline,
+        "cpu_baseline": cpu,
+    }
+    if sweep:
+        line["sweep"] = sweep
+    print(json.dumps(line), flush=True)
+
+
+def cpu_baseline(cfg, inp, T, log):
+    """The fp64 oracle as it stands, on a bounded token sample of the same batch."""
+    import oracle
+    n = min(T, 64 if cfg.E <= 32 else 16)
+    tokens = np.arange(n)
+    get = oracle.experts_from_arrays(inp.w1_codes, inp.w1_scales, inp.w1_bias, inp.w2_codes,
+                                     inp.w2_scales, inp.w2_bias)
+    threads = len(os.sched_getaffinity(0)) if hasattr(os, "sched_getaffinity") else (os.cpu_count() or 1)
+    t0 = time.perf_counter()
+    oracle.moe_layer(inp.x, inp.router_w, inp.router_b, get, cfg.k, tokens=tokens)
+    dt = time.perf_counter() - t0
+    log(f"oracle: {n} tokens in {dt:.1f}s on {threads} threads")
+    return {"value": round(n / dt, 3), "unit": "tokens/s", "cores": threads, "kind": "oracle",
+            "sample": f"first {n} of the {T} tokens, full layer in fp64 numpy (router, top-{cfg.k}, "
+                      f"per-expert MXFP4 decode, FFN, combine); {dt:.1f} s"}
+
+
+if __name__ == "__main__":
+    main()

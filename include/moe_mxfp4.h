@@ -1,0 +1,201 @@
+/*
+ * moe_mxfp4.h -- C ABI of a top-k routed mixture-of-experts feed-forward layer with
+ * MXFP4 expert weights, written for AMD Instinct MI355X (gfx950).
+ *
+ * The layer (gpt-oss pages: architecture walkthrough at pnsm.cn/news/1975454, sections 1,
+ * 2.2 and 2.4; review of the from-scratch gpt-oss-20B at pomoai.com, sections 3.3-3.4):
+ *   logits = x W_r^T + b_r                  linear router, one score per expert
+ *   idx    = the k best experts per token   (k = 4 in both gpt-oss sizes)
+ *   w      = softmax over those k scores
+ *   h      = W1_e x + b1_e                  fused gate/linear projection, 2I outputs
+ *   a      = clamp(g) * sigmoid(alpha * clamp(g)) * (clamp(l) + 1)   clamped SwiGLU, +1 residual
+ *   y      = W2_e a + b2_e
+ *   out    = sum_j w_j y_{idx_j}
+ * Expert weights are MXFP4: 4-bit E2M1 elements with one E8M0 power-of-two scale per 32
+ * consecutive input features (4.25 bits per weight; walkthrough sections 1 and 4).
+ *
+ * Conventions for every entry point:
+ *  - Every pointer argument is DEVICE memory owned by the caller, except the descriptor
+ *    structs (moe_router_t, moe_mxfp4_weight_t, moe_options_t), which are HOST structs
+ *    read during the call and not retained. Nothing is freed or retained by the library
+ *    except moe_forward's internal workspace (see there).
+ *  - bf16 tensors are passed as uint16_t bit patterns. All tensors are dense row-major.
+ *  - `stream` is a hipStream_t passed as void*; NULL means the default (null) stream.
+ *    Calls are asynchronous with respect to the host; device faults surface at the
+ *    caller's next synchronisation, as for any HIP kernel.
+ *  - All argument checks happen before the first HIP call, so an error return leaves no
+ *    partial work queued. T == 0 returns MOE_OK without launching anything.
+ *  - NaN/Inf inputs are not checked; results for them are unspecified.
+ *  - Return value: MOE_OK (0) or one of the negative MOE_ERR_* codes below.
+ *  - Limits: 1 <= k <= 8, k <= E <= 256, H and I multiples of 32 and at most 16384,
+ *    T * k < 2^31. x and code pointers must be 16-byte aligned, fp32 outputs 16-byte aligned.
+ */
+#ifndef MOE_MXFP4_H_
+#define MOE_MXFP4_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define MOE_ABI_VERSION 1
+
+/* status codes */
+#define MOE_OK 0
+#define MOE_ERR_INVALID_ARG (-1)  /* NULL pointer, negative size, misaligned pointer, bad enum */
+#define MOE_ERR_UNSUPPORTED (-2)  /* shape outside the limits above */
+#define MOE_ERR_WORKSPACE (-3)    /* caller workspace smaller than moe_workspace_size() */
+#define MOE_ERR_HIP (-4)          /* a HIP runtime call or kernel launch failed */
+
+/* output element types */
+#define MOE_DTYPE_BF16 0
+#define MOE_DTYPE_F32 1
+
+/* expert-FFN kernel family */
+#define MOE_PATH_AUTO 0    /* chosen from T*k and E on the host */
+#define MOE_PATH_STREAM 1  /* weight-streaming kernels for decode-sized batches */
+#define MOE_PATH_GEMM 2    /* LDS-tiled grouped GEMM for prefill-sized batches */
+
+/* moe_options_t.flags: test hooks for per-step checks of the expert FFN */
+#define MOE_FLAG_EMIT_PREACT 1u /* stop after gate_up: y <- h = W1 x + b1, fp32 [T*k][2I] */
+#define MOE_FLAG_EMIT_ACT 2u    /* stop after the SwiGLU: y <- a (bf16-rounded, as fp32) [T*k][I] */
+
+typedef void *moe_stream_t; /* a hipStream_t */
+
+/* Linear router [review section 3.4]. */
+typedef struct moe_router {
+  const float *weight; /* fp32 [E][H] */
+  const float *bias;   /* fp32 [E], or NULL for zero */
+} moe_router_t;
+
+/*
+ * One MXFP4 weight matrix for all E experts [walkthrough sections 1 and 4].
+ * Expert e's matrix has `n` rows (output features) of `k` elements (input features).
+ * codes:  uint8 [E][n][k/2]; byte j of a row holds element 2j in its low nibble and
+ *         element 2j+1 in its high nibble; a nibble is an E2M1 code (sign, 2 exponent
+ *         bits with bias 1, 1 mantissa bit; OCP MX v1.0).
+ * scales: uint8 [E][n][k/32]; byte b is the E8M0 scale 2^(byte-127) of elements
+ *         32b..32b+31 of the row (0xFF is NaN).
+ * bias:   bf16 [E][n], or NULL for zero.
+ * For the gate_up matrix n = 2I with rows interleaved: row 2i is unit i's gate, row
+ * 2i+1 its linear branch; k = H. For the down matrix n = H, k = I.
+ */
+typedef struct moe_mxfp4_weight {
+  const uint8_t *codes;
+  const uint8_t *scales;
+  const uint16_t *bias;
+  int32_t n;
+  int32_t k;
+} moe_mxfp4_weight_t;
+
+/* Options for the _ex entry points; NULL selects the defaults shown. */
+typedef struct moe_options {
+  float swiglu_limit; /* 7.0: clamp bound of both halves [review section 3.3] */
+  float swiglu_alpha; /* 1.0: sigmoid slope; 1 is plain SiLU */
+  int32_t out_dtype;  /* MOE_DTYPE_BF16 */
+  int32_t path;       /* MOE_PATH_AUTO */
+  uint32_t flags;     /* 0; see MOE_FLAG_* (moe_mxfp4_ffn only) */
+} moe_options_t;
+
+/* ABI version of the loaded library (MOE_ABI_VERSION of its build). */
+int moe_abi_version(void);
+
+/* Static, never-NULL description of a status code. */
+const char *moe_status_string(int status);
+
+/*
+ * Bytes of caller workspace that moe_route, moe_permute, moe_mxfp4_ffn and moe_forward_ex
+ * need for these sizes and this path (one size serves them all). Returns 0 for invalid
+ * sizes.
+ * A workspace passed to those calls must be 256-byte aligned.
+ */
+size_t moe_workspace_size(int64_t T, int32_t E, int32_t k, int32_t H, int32_t I, int32_t path);
+
+/*
+ * Decode n MXFP4 elements to fp32 (an exported test of the decode step; the layer never
+ * writes decoded weights to memory). codes: uint8 [n/2], scales: uint8 [n/32],
+ * out: fp32 [n]. n must be a multiple of 32. Exact: E2M1 value times 2^(scale-127),
+ * with fp32 overflow giving +-inf, fp32 subnormals kept, and scale 0xFF giving NaN.
+ */
+int moe_mxfp4_dequant(const uint8_t *codes, const uint8_t *scales, int64_t n, float *out,
+                      moe_stream_t stream);
+
+/*
+ * Router [review section 3.4; walkthrough sections 2.2 and 4; config.json read-through at
+ * m.youleyou.com, Part.01: experts_per_token = 4].
+ * x: bf16 [T][H]. router->weight fp32 [E][H], router->bias fp32 [E] or NULL.
+ * Outputs topk_idx int32 [T][k] (the k largest fp32 logits, largest first, ties to the
+ * lower expert id) and topk_w fp32 [T][k] (softmax over those k logits).
+ * Logits are accumulated in fp32. ws: at least moe_workspace_size(T, E, k, H, H, 0)
+ * bytes (the fp32 logits are staged there).
+ */
+int moe_route(const uint16_t *x, int64_t T, int32_t H, const moe_router_t *router, int32_t E,
+              int32_t k, int32_t *topk_idx, float *topk_w, void *ws, size_t ws_bytes,
+              moe_stream_t stream);
+
+/*
+ * Group the T*k slots (slot s = t*k + j) by expert [review section 3.4: only the picked
+ * experts run]. topk_idx int32 [T][k] with values in [0, E).
+ * Outputs: expert_offsets int32 [E+1] (exclusive prefix sum of per-expert slot counts,
+ * expert_offsets[E] = T*k), sorted_slot int32 [T*k] (slots ordered by expert, then by
+ * slot id), slot_row int32 [T*k] (position of slot s in that order).
+ * ws/ws_bytes: unused by this version (may be NULL/0). Deterministic.
+ */
+int moe_permute(const int32_t *topk_idx, int64_t T, int32_t E, int32_t k, int32_t *expert_offsets,
+                int32_t *sorted_slot, int32_t *slot_row, void *ws, size_t ws_bytes,
+                moe_stream_t stream);
+
+/*
+ * Expert FFNs of all slots [walkthrough sections 2.2 and 2.4; review section 3.3].
+ * For sorted row r (slot s = sorted_slot[r], token t = s / k, expert e with
+ * expert_offsets[e] <= r < expert_offsets[e+1]):
+ *   y[r] = W2_e (swiglu(W1_e x[t] + b1_e)) + b2_e,      y fp32 [T*k][H]
+ * The activation a is rounded to bf16 between the two products; accumulation is fp32.
+ * x bf16 [T][H]; gate_up->n = 2 * down->k, gate_up->k = down->n = H.
+ * opts->flags may stop early (MOE_FLAG_EMIT_PREACT: y is [T*k][2I]; MOE_FLAG_EMIT_ACT:
+ * y is [T*k][I]). ws: at least moe_workspace_size(T, E, k, H, I, opts->path) bytes.
+ */
+int moe_mxfp4_ffn(const uint16_t *x, int64_t T, int32_t k, int32_t E, const int32_t *expert_offsets,
+                  const int32_t *sorted_slot, const moe_mxfp4_weight_t *gate_up,
+                  const moe_mxfp4_weight_t *down, const moe_options_t *opts, float *y, void *ws,
+                  size_t ws_bytes, moe_stream_t stream);
+
+/*
+ * Weighted combine [review section 3.4]: out[t] = sum over j = 0..k-1, in that order, of
+ * topk_w[t][j] * y[slot_row[t*k + j]], accumulated in fp32, then rounded to nearest-even
+ * bf16 (out_dtype MOE_DTYPE_BF16, out is uint16 [T][H]) or stored as fp32 (MOE_DTYPE_F32).
+ */
+int moe_combine(const float *y, const int32_t *slot_row, const float *topk_w, int64_t T, int32_t k,
+                int32_t H, void *out, int32_t out_dtype, moe_stream_t stream);
+
+/*
+ * The whole layer: route, permute, expert FFNs, combine; out bf16 [T][H].
+ * Uses a workspace owned by the library, one per device, grown on demand and kept until
+ * moe_release_workspace() or process exit; growing it synchronises `stream` and calls
+ * hipMalloc. Calls that share a device and run concurrently from several host threads
+ * must use moe_forward_ex with their own workspaces instead.
+ */
+int moe_forward(const uint16_t *x, const moe_router_t *router, const moe_mxfp4_weight_t *w_gate_up,
+                const moe_mxfp4_weight_t *w_down, int64_t T, int32_t E, int32_t k, uint16_t *out,
+                moe_stream_t stream);
+
+/*
+ * moe_forward with options and a caller workspace of at least
+ * moe_workspace_size(T, E, k, H, I, opts->path) bytes (256-byte aligned). out is bf16
+ * [T][H] or fp32 [T][H] per opts->out_dtype. opts->flags must be 0.
+ */
+int moe_forward_ex(const uint16_t *x, const moe_router_t *router,
+                   const moe_mxfp4_weight_t *w_gate_up, const moe_mxfp4_weight_t *w_down,
+                   int64_t T, int32_t E, int32_t k, const moe_options_t *opts, void *out, void *ws,
+                   size_t ws_bytes, moe_stream_t stream);
+
+/* Free moe_forward's workspace on the current device (synchronises the device). */
+int moe_release_workspace(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MOE_MXFP4_H_ */

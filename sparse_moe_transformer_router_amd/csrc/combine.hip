@@ -1,0 +1,51 @@
+// Weighted combine: out[t] = sum_j w[t][j] * y[slot_row[t*k + j]], the routing-weighted sum
+// of the picked experts' outputs (review of the from-scratch gpt-oss-20B at pomoai.com,
+// section 3.4). A gather in rank order with fp32 accumulation, so no atomics and a
+// deterministic result; the output is rounded to nearest-even bf16 or kept in fp32.
+#include "common.h"
+#include "kernels.h"
+
+namespace moe {
+
+__global__ __launch_bounds__(256) void combine_kernel(const float *__restrict__ y,
+                                                      const int32_t *__restrict__ slot_row,
+                                                      const float *__restrict__ topk_w, int64_t T,
+                                                      int k, int H, void *__restrict__ out,
+                                                      int out_f32) {
+  const int chunks = (H / 4 + blockDim.x - 1) / blockDim.x;
+  const int64_t t = blockIdx.x / chunks;
+  const int h = ((blockIdx.x % chunks) * blockDim.x + threadIdx.x) * 4;
+  if (h >= H) return;
+  const int64_t S = T * k;
+  f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
+  for (int j = 0; j < k; ++j) {
+    const int32_t r = slot_row[t * k + j];
+    const float w = topk_w[t * k + j];
+    if ((uint32_t)r < (uint64_t)S) {
+      const f32x4_t v = *reinterpret_cast<const f32x4_t *>(y + (int64_t)r * H + h);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) acc[i] = fmaf(w, v[i], acc[i]);
+    }
+  }
+  if (out_f32) {
+    *reinterpret_cast<f32x4_t *>(reinterpret_cast<float *>(out) + t * H + h) = acc;
+  } else {
+    const uint32_t lo = (uint32_t)f32_to_bf16_rne(acc[0]) | ((uint32_t)f32_to_bf16_rne(acc[1]) << 16);
+    const uint32_t hi = (uint32_t)f32_to_bf16_rne(acc[2]) | ((uint32_t)f32_to_bf16_rne(acc[3]) << 16);
+    uint32_t *o = reinterpret_cast<uint32_t *>(reinterpret_cast<uint16_t *>(out) + t * H + h);
+    o[0] = lo;
+    o[1] = hi;
+  }
+}
+
+hipError_t launch_combine(const float *y, const int32_t *slot_row, const float *topk_w, int64_t T,
+                          int k, int H, void *out, bool out_f32, hipStream_t stream) {
+  const int threads = 256;
+  const int64_t chunks = (H / 4 + threads - 1) / threads;
+  dim3 grid((unsigned)(T * chunks));
+  hipLaunchKernelGGL(combine_kernel, grid, dim3(threads), 0, stream, y, slot_row, topk_w, T, k, H,
+                     out, out_f32 ? 1 : 0);
+  return hipGetLastError();
+}
+
+}  // namespace moe

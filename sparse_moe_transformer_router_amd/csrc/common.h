@@ -1,0 +1,80 @@
+// Device-side helpers shared by the layer's HIP kernels (gfx950 / CDNA4, wave64).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace moe {
+
+typedef __attribute__((__vector_size__(2 * sizeof(__bf16)))) __bf16 bf16x2_t;
+typedef __attribute__((__vector_size__(8 * sizeof(__bf16)))) __bf16 bf16x8_t;
+typedef __attribute__((__vector_size__(4 * sizeof(float)))) float f32x4_t;
+typedef __attribute__((__vector_size__(16 * sizeof(float)))) float f32x16_t;
+typedef __attribute__((__vector_size__(4 * sizeof(uint32_t)))) uint32_t u32x4_t;
+
+constexpr int kWave = 64;
+
+// fp32 -> bf16 bits, round to nearest even; NaN stays a quiet NaN.
+__device__ __forceinline__ uint16_t f32_to_bf16_rne(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7fffffffu) > 0x7f800000u) return (uint16_t)((u >> 16) | 0x40u);
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return (uint16_t)(u >> 16);
+}
+
+__device__ __forceinline__ float bf16_to_f32(uint16_t b) { return __uint_as_float((uint32_t)b << 16); }
+
+// The E8M0 scale byte as an fp32 multiplier 2^(s-127): exponent field s for 1..254,
+// the fp32 subnormal 2^-127 for s = 0, NaN for s = 255.
+__device__ __forceinline__ float e8m0_to_f32(uint32_t s) {
+  uint32_t bits = s << 23;
+  bits = (s == 0u) ? 0x00400000u : bits;
+  bits = (s == 255u) ? 0x7fc00000u : bits;
+  return __uint_as_float(bits);
+}
+
+// Eight MXFP4 elements (one dword of codes: byte j = elements 2j (low nibble), 2j+1 (high))
+// -> eight bf16 in element order, each multiplied by `scale`. Uses gfx950's scaled FP4
+// convert, one instruction per byte; E2M1 times a power of two is exact in bf16.
+__device__ __forceinline__ bf16x8_t fp4x8_to_bf16x8(uint32_t codes, float scale) {
+  bf16x2_t p0 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(codes, scale, 0);
+  bf16x2_t p1 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(codes, scale, 1);
+  bf16x2_t p2 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(codes, scale, 2);
+  bf16x2_t p3 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(codes, scale, 3);
+  u32x4_t u;
+  u[0] = __builtin_bit_cast(uint32_t, p0);
+  u[1] = __builtin_bit_cast(uint32_t, p1);
+  u[2] = __builtin_bit_cast(uint32_t, p2);
+  u[3] = __builtin_bit_cast(uint32_t, p3);
+  return __builtin_bit_cast(bf16x8_t, u);
+}
+
+__device__ __forceinline__ bf16x8_t as_bf16x8(u32x4_t v) { return __builtin_bit_cast(bf16x8_t, v); }
+
+// Clamped gated SwiGLU with the +1 on the linear branch, for one (gate, linear) pair.
+__device__ __forceinline__ float swiglu_unit(float g, float l, float limit, float alpha) {
+  g = fminf(fmaxf(g, -limit), limit);
+  l = fminf(fmaxf(l, -limit), limit);
+  return g / (1.0f + expf(-alpha * g)) * (l + 1.0f);
+}
+
+// Wave-wide helpers.
+__device__ __forceinline__ int lane_id() { return __lane_id(); }
+
+__device__ __forceinline__ int wave_inclusive_scan(int v) {
+  const int lane = __lane_id();
+#pragma unroll
+  for (int d = 1; d < kWave; d <<= 1) {
+    int o = __shfl_up(v, d, kWave);
+    if (lane >= d) v += o;
+  }
+  return v;
+}
+
+__device__ __forceinline__ int wave_sum(int v) {
+#pragma unroll
+  for (int d = kWave / 2; d >= 1; d >>= 1) v += __shfl_xor(v, d, kWave);
+  return v;
+}
+
+}  // namespace moe

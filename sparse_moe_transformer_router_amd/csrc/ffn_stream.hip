@@ -1,0 +1,194 @@
+// Expert FFN projections for decode-sized batches: a weight-streaming grouped GEMM.
+//
+// Each expert's projection y = W x (+ b) runs only on the slots routed to it (review of the
+// from-scratch gpt-oss-20B at pomoai.com, section 3.4), with W in MXFP4 (gpt-oss
+// walkthrough at pnsm.cn, sections 1 and 4) and the clamped SwiGLU with +1 on the linear
+// branch fused into the gate_up epilogue (walkthrough section 2.2; review section 3.3).
+//
+// With few slots per expert the product is bound by streaming the 4.25-bit weights from
+// HBM, so the weights take the MFMA's 16-row A operand straight from global memory:
+//   * a workgroup owns 64 weight rows (four 16-row groups) of one expert and up to 16 of
+//     that expert's slots (one "m-tile"); its four waves split the input dimension in
+//     128-wide chunks, round robin;
+//   * lane l reads 16 code bytes = one 32-element MX block of row (l % 16) in each row
+//     group and converts them with the block's scale into bf16 in registers (gfx950's
+//     scaled FP4 convert; E2M1 times a power of two is exact in bf16), lanes l / 16 = q
+//     taking consecutive blocks;
+//   * the slot activations (bf16) come from global memory through L1/L2, 64 bytes per lane
+//     per chunk, matching the k-range of the lane's weight block;
+//   * v_mfma_f32_16x16x32_bf16 accumulates in fp32; the four waves' partial sums are added
+//     in LDS in a fixed order, so results are deterministic.
+// The m-tile -> (expert, first slot) map is recomputed by every wave from expert_offsets
+// (a wave-wide scan over experts), so no tile list is materialised and the grid is sized
+// from host-known bounds only; surplus workgroups exit at once.
+#include "common.h"
+#include "kernels.h"
+
+namespace moe {
+
+constexpr int kSRows = 64;   // weight rows per workgroup
+constexpr int kSCols = 16;   // slots per m-tile
+constexpr int kSWaves = 4;
+
+template <int EPI>
+__global__ __launch_bounds__(kSWaves *kWave) void ffn_stream_kernel(
+    const uint16_t *__restrict__ a_src, int a_by_token, const int32_t *__restrict__ sorted_slot, int k,
+    const int32_t *__restrict__ offsets, int E, const uint8_t *__restrict__ codes,
+    const uint8_t *__restrict__ scales, const uint16_t *__restrict__ bias, int N, int K,
+    void *__restrict__ out, float limit, float alpha) {
+  __shared__ float red[kSWaves][kSRows][kSCols + 1];
+  const int wave = threadIdx.x / kWave, lane = threadIdx.x % kWave;
+  const int n0 = blockIdx.y * kSRows;
+  const int mt = blockIdx.x;
+
+  // ---- which expert and which 16 of its slots this m-tile covers
+  int e = -1, m0 = 0, rbase = 0, mcount = 0;
+  {
+    int carry = 0;
+    for (int eb = 0; eb < E; eb += kWave) {
+      const int ex = eb + lane;
+      const int cnt = (ex < E) ? offsets[ex + 1] - offsets[ex] : 0;
+      const int tiles = (cnt + kSCols - 1) / kSCols;
+      const int inc = wave_inclusive_scan(tiles);
+      const int excl = inc - tiles + carry;
+      const uint64_t hit = __ballot(tiles > 0 && mt >= excl && mt < excl + tiles);
+      if (hit) {
+        const int src = __ffsll((unsigned long long)hit) - 1;
+        const int sel_excl = __shfl(excl, src, kWave);
+        e = eb + src;
+        m0 = (mt - sel_excl) * kSCols;
+        rbase = offsets[e];
+        const int cnt_e = offsets[e + 1] - rbase;
+        mcount = (cnt_e - m0 < kSCols) ? cnt_e - m0 : kSCols;
+        break;
+      }
+      carry += __shfl(inc, kWave - 1, kWave);
+    }
+  }
+  if (e < 0) return;  // same decision in every wave: the whole workgroup leaves
+
+  const int rl = lane % 16, q = lane / 16;
+  const bool col_ok = rl < mcount;
+  const uint16_t *arow = a_src;
+  if (col_ok) {
+    const int r = rbase + m0 + rl;
+    const int64_t src_row = a_by_token ? (int64_t)(sorted_slot[r] / k) : (int64_t)r;
+    arow = a_src + src_row * K;
+  }
+
+  const int KB = K / 32;
+  const int nchunk = (KB + 3) / 4;
+  const int64_t row_bytes = K / 2;
+  const uint8_t *cexp = codes + (int64_t)e * N * row_bytes;
+  const uint8_t *sexp = scales + (int64_t)e * N * KB;
+
+  f32x4_t acc[4];
+#pragma unroll
+  for (int g = 0; g < 4; ++g) acc[g] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+
+  for (int c = wave; c < nchunk; c += kSWaves) {
+    const int b = c * 4 + q;  // this lane's MX block along K
+    const bool bvalid = b < KB;
+    u32x4_t cw[4];
+    uint32_t sw[4];
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+      const int row = n0 + 16 * g + rl;
+      if (bvalid && row < N) {
+        cw[g] = *reinterpret_cast<const u32x4_t *>(cexp + row * row_bytes + b * 16);
+        sw[g] = sexp[(int64_t)row * KB + b];
+      } else {
+        cw[g] = u32x4_t{0u, 0u, 0u, 0u};
+        sw[g] = 127u;
+      }
+    }
+    u32x4_t av[4];
+    if (bvalid && col_ok) {
+      const u32x4_t *ap = reinterpret_cast<const u32x4_t *>(arow + b * 32);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) av[j] = ap[j];
+    } else {
+#pragma unroll
+      for (int j = 0; j < 4; ++j) av[j] = u32x4_t{0u, 0u, 0u, 0u};
+    }
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+      const float sc = e8m0_to_f32(sw[g]);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const bf16x8_t wa = fp4x8_to_bf16x8(cw[g][j], sc);
+        acc[g] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wa, as_bf16x8(av[j]), acc[g], 0, 0, 0);
+      }
+    }
+  }
+
+  // ---- cross-wave reduction (fixed order) and epilogue
+  // mfma 16x16 output: lane l holds rows 4*(l/16) + i, column l % 16
+#pragma unroll
+  for (int g = 0; g < 4; ++g)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) red[wave][16 * g + 4 * q + i][rl] = acc[g][i];
+  __syncthreads();
+
+  const int col = threadIdx.x % kSCols;
+  const int r0 = (threadIdx.x / kSCols) * 4;  // 4 consecutive rows of the 64
+  if (col >= mcount) return;
+  float h[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    float s = red[0][r0 + i][col];
+#pragma unroll
+    for (int w = 1; w < kSWaves; ++w) s += red[w][r0 + i][col];
+    const int n = n0 + r0 + i;
+    if (bias != nullptr && n < N) s += bf16_to_f32(bias[(int64_t)e * N + n]);
+    h[i] = s;
+  }
+  const int64_t r = rbase + m0 + col;  // sorted row of this slot
+  if (EPI == kEpiSwigluBf16 || EPI == kEpiActF32) {
+    const int half = N / 2;
+#pragma unroll
+    for (int p = 0; p < 2; ++p) {
+      const int n = n0 + r0 + 2 * p;
+      if (n < N) {
+        const uint16_t ab = f32_to_bf16_rne(swiglu_unit(h[2 * p], h[2 * p + 1], limit, alpha));
+        if (EPI == kEpiSwigluBf16)
+          reinterpret_cast<uint16_t *>(out)[r * half + n / 2] = ab;
+        else
+          reinterpret_cast<float *>(out)[r * half + n / 2] = bf16_to_f32(ab);
+      }
+    }
+  } else {
+    float *o = reinterpret_cast<float *>(out) + r * N + n0 + r0;
+    if (n0 + r0 + 3 < N) {
+      *reinterpret_cast<f32x4_t *>(o) = f32x4_t{h[0], h[1], h[2], h[3]};
+    } else {
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        if (n0 + r0 + i < N) o[i] = h[i];
+    }
+  }
+}
+
+hipError_t launch_ffn_stream(const uint16_t *a_src, bool a_by_token, const int32_t *sorted_slot,
+                             int k, const int32_t *offsets, int E, int64_t S, const MxWeight &w,
+                             int epilogue, void *out, float limit, float alpha, hipStream_t stream) {
+  const int64_t busy = (S < E) ? S : E;  // experts with at least one slot, at most
+  const int64_t mtiles = (S + kSCols - 1) / kSCols + busy;
+  // m-tiles along x (unbounded), weight-row tiles along y (at most 512)
+  dim3 grid((unsigned)mtiles, (unsigned)((w.N + kSRows - 1) / kSRows));
+  dim3 block(kSWaves * kWave);
+#define MOE_LAUNCH_STREAM(EPI)                                                                   \
+  hipLaunchKernelGGL(ffn_stream_kernel<EPI>, grid, block, 0, stream, a_src, a_by_token ? 1 : 0,    \
+                     sorted_slot, k, offsets, E, w.codes, w.scales, w.bias, w.N, w.K, out, limit, \
+                     alpha)
+  switch (epilogue) {
+    case kEpiSwigluBf16: MOE_LAUNCH_STREAM(kEpiSwigluBf16); break;
+    case kEpiPreactF32: MOE_LAUNCH_STREAM(kEpiPreactF32); break;
+    case kEpiActF32: MOE_LAUNCH_STREAM(kEpiActF32); break;
+    default: MOE_LAUNCH_STREAM(kEpiLinearF32); break;
+  }
+#undef MOE_LAUNCH_STREAM
+  return hipGetLastError();
+}
+
+}  // namespace moe

@@ -1,0 +1,46 @@
+// Host-side launchers of the layer's HIP kernels (internal to the library).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace moe {
+
+// Output modes of the expert-FFN kernels' epilogues.
+enum FfnEpilogue : int {
+  kEpiSwigluBf16 = 0,  // gate_up: SwiGLU(h) -> bf16 act [S][N/2]
+  kEpiPreactF32 = 1,   // gate_up: h -> fp32 [S][N]
+  kEpiActF32 = 2,      // gate_up: bf16-rounded SwiGLU(h) widened to fp32 [S][N/2]
+  kEpiLinearF32 = 3,   // down: W a + b -> fp32 [S][N]
+};
+
+struct MxWeight {
+  const uint8_t *codes;   // [E][N][K/2]
+  const uint8_t *scales;  // [E][N][K/32]
+  const uint16_t *bias;   // [E][N] bf16 or nullptr
+  int N, K;
+};
+
+hipError_t launch_dequant(const uint8_t *codes, const uint8_t *scales, int64_t n, float *out,
+                          hipStream_t stream);
+
+hipError_t launch_router_logits(const uint16_t *x, int64_t T, int H, const float *w, const float *b,
+                                int E, float *logits, hipStream_t stream);
+
+hipError_t launch_router_topk(const float *logits, int64_t T, int E, int k, int32_t *topk_idx,
+                              float *topk_w, hipStream_t stream);
+
+hipError_t launch_permute(const int32_t *topk_idx, int64_t S, int E, int32_t *offsets,
+                          int32_t *sorted_slot, int32_t *slot_row, hipStream_t stream);
+
+// One expert GEMM over all sorted rows, weight-streaming kernel family.
+// a_src: bf16 rows; if a_by_token, sorted row r reads a_src[(sorted_slot[r] / k) * K], else
+// a_src[r * K]. Output rows are sorted rows.
+hipError_t launch_ffn_stream(const uint16_t *a_src, bool a_by_token, const int32_t *sorted_slot,
+                             int k, const int32_t *offsets, int E, int64_t S, const MxWeight &w,
+                             int epilogue, void *out, float limit, float alpha, hipStream_t stream);
+
+hipError_t launch_combine(const float *y, const int32_t *slot_row, const float *topk_w, int64_t T,
+                          int k, int H, void *out, bool out_f32, hipStream_t stream);
+
+}  // namespace moe

@@ -1,0 +1,364 @@
+// extern "C" entry points of the MXFP4 top-k MoE layer: argument checks (all before the first
+// HIP call), workspace layout, kernel-family choice, and launches on the caller's stream.
+#include <hip/hip_runtime.h>
+
+#include <mutex>
+#include <new>
+#include <unordered_map>
+
+#include "kernels.h"
+#include "moe_mxfp4.h"
+
+namespace {
+
+constexpr int kMaxTopK = 8;
+constexpr int kMaxExperts = 256;
+constexpr int kMaxDim = 16384;
+constexpr size_t kWsAlign = 256;
+
+bool aligned(const void *p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+size_t align_up(size_t v) { return (v + kWsAlign - 1) / kWsAlign * kWsAlign; }
+
+// One workspace layout serves every entry point (each uses a subset of the regions).
+struct WsLayout {
+  size_t logits, topk_idx, topk_w, offsets, sorted_slot, slot_row, act, y, total;
+};
+
+bool ws_layout(int64_t T, int E, int k, int H, int I, WsLayout *L) {
+  if (T < 0 || E < 1 || k < 1 || H < 1 || I < 1) return false;
+  const size_t S = (size_t)T * (size_t)k;
+  size_t off = 0;
+  L->logits = off;      off = align_up(off + (size_t)T * E * sizeof(float));
+  L->topk_idx = off;    off = align_up(off + S * sizeof(int32_t));
+  L->topk_w = off;      off = align_up(off + S * sizeof(float));
+  L->offsets = off;     off = align_up(off + (size_t)(E + 1) * sizeof(int32_t));
+  L->sorted_slot = off; off = align_up(off + S * sizeof(int32_t));
+  L->slot_row = off;    off = align_up(off + S * sizeof(int32_t));
+  L->act = off;         off = align_up(off + S * (size_t)I * sizeof(uint16_t));
+  L->y = off;           off = align_up(off + S * (size_t)H * sizeof(float));
+  L->total = off;
+  return true;
+}
+
+template <typename P>
+P *at(void *base, size_t off) {
+  return reinterpret_cast<P *>(static_cast<char *>(base) + off);
+}
+
+int check_common(int64_t T, int E, int k) {
+  if (T < 0) return MOE_ERR_INVALID_ARG;
+  if (k < 1 || k > kMaxTopK || E < k || E > kMaxExperts) return MOE_ERR_UNSUPPORTED;
+  if (T > 0 && (T * (int64_t)k >= ((int64_t)1 << 31))) return MOE_ERR_UNSUPPORTED;
+  return MOE_OK;
+}
+
+int check_dim(int64_t d) { return (d >= 32 && d <= kMaxDim && d % 32 == 0) ? MOE_OK : MOE_ERR_UNSUPPORTED; }
+
+int check_weight(const moe_mxfp4_weight_t *w) {
+  if (w == nullptr || w->codes == nullptr || w->scales == nullptr) return MOE_ERR_INVALID_ARG;
+  if (!aligned(w->codes, 16) || !aligned(w->bias, 2)) return MOE_ERR_INVALID_ARG;
+  if (check_dim(w->k) != MOE_OK || w->n < 1 || w->n > 2 * kMaxDim) return MOE_ERR_UNSUPPORTED;
+  return MOE_OK;
+}
+
+moe_options_t default_options() {
+  moe_options_t o;
+  o.swiglu_limit = 7.0f;
+  o.swiglu_alpha = 1.0f;
+  o.out_dtype = MOE_DTYPE_BF16;
+  o.path = MOE_PATH_AUTO;
+  o.flags = 0;
+  return o;
+}
+
+int check_options(const moe_options_t &o) {
+  if (o.out_dtype != MOE_DTYPE_BF16 && o.out_dtype != MOE_DTYPE_F32) return MOE_ERR_INVALID_ARG;
+  if (o.path < MOE_PATH_AUTO || o.path > MOE_PATH_GEMM) return MOE_ERR_INVALID_ARG;
+  if (!(o.swiglu_limit > 0.0f) || !(o.swiglu_alpha == o.swiglu_alpha)) return MOE_ERR_INVALID_ARG;
+  if (o.flags & ~(MOE_FLAG_EMIT_PREACT | MOE_FLAG_EMIT_ACT)) return MOE_ERR_INVALID_ARG;
+  if ((o.flags & MOE_FLAG_EMIT_PREACT) && (o.flags & MOE_FLAG_EMIT_ACT)) return MOE_ERR_INVALID_ARG;
+  return MOE_OK;
+}
+
+// The expert GEMMs that follow the permutation. Arguments already validated.
+int run_ffn(const uint16_t *x, int64_t T, int k, int E, const int32_t *offsets, const int32_t *sorted_slot,
+            const moe_mxfp4_weight_t &gu, const moe_mxfp4_weight_t &dn, const moe_options_t &o, float *y,
+            uint16_t *act, hipStream_t stream) {
+  const int64_t S = T * k;
+  const moe::MxWeight w1{gu.codes, gu.scales, gu.bias, gu.n, gu.k};
+  const moe::MxWeight w2{dn.codes, dn.scales, dn.bias, dn.n, dn.k};
+  hipError_t err;
+  if (o.flags & MOE_FLAG_EMIT_PREACT) {
+    err = moe::launch_ffn_stream(x, true, sorted_slot, k, offsets, E, S, w1, moe::kEpiPreactF32, y,
+                                 o.swiglu_limit, o.swiglu_alpha, stream);
+    return err == hipSuccess ? MOE_OK : MOE_ERR_HIP;
+  }
+  if (o.flags & MOE_FLAG_EMIT_ACT) {
+    err = moe::launch_ffn_stream(x, true, sorted_slot, k, offsets, E, S, w1, moe::kEpiActF32, y,
+                                 o.swiglu_limit, o.swiglu_alpha, stream);
+    return err == hipSuccess ? MOE_OK : MOE_ERR_HIP;
+  }
+  err = moe::launch_ffn_stream(x, true, sorted_slot, k, offsets, E, S, w1, moe::kEpiSwigluBf16, act,
+                               o.swiglu_limit, o.swiglu_alpha, stream);
+  if (err != hipSuccess) return MOE_ERR_HIP;
+  err = moe::launch_ffn_stream(act, false, sorted_slot, k, offsets, E, S, w2, moe::kEpiLinearF32, y,
+                               o.swiglu_limit, o.swiglu_alpha, stream);
+  return err == hipSuccess ? MOE_OK : MOE_ERR_HIP;
+}
+
+int check_layer(const uint16_t *x, const moe_router_t *router, const moe_mxfp4_weight_t *gu,
+                const moe_mxfp4_weight_t *dn, int64_t T, int E, int k, const void *out) {
+  int st = check_common(T, E, k);
+  if (st != MOE_OK) return st;
+  if (router == nullptr || gu == nullptr || dn == nullptr) return MOE_ERR_INVALID_ARG;
+  if ((st = check_weight(gu)) != MOE_OK || (st = check_weight(dn)) != MOE_OK) return st;
+  const int H = gu->k, I = dn->k;
+  if (gu->n != 2 * I || dn->n != H) return MOE_ERR_UNSUPPORTED;
+  if ((st = check_dim(H)) != MOE_OK || (st = check_dim(I)) != MOE_OK) return st;
+  if (T > 0) {
+    if (x == nullptr || out == nullptr || router->weight == nullptr) return MOE_ERR_INVALID_ARG;
+    if (!aligned(x, 16) || !aligned(out, 16) || !aligned(router->weight, 16))
+      return MOE_ERR_INVALID_ARG;
+  }
+  return MOE_OK;
+}
+
+int forward_impl(const uint16_t *x, const moe_router_t *router, const moe_mxfp4_weight_t *gu,
+                 const moe_mxfp4_weight_t *dn, int64_t T, int E, int k, const moe_options_t &o, void *out,
+                 void *ws, size_t ws_bytes, hipStream_t stream) {
+  const int H = gu->k, I = dn->k;
+  WsLayout L;
+  ws_layout(T, E, k, H, I, &L);
+  if (ws == nullptr || ws_bytes < L.total) return MOE_ERR_WORKSPACE;
+  if (!aligned(ws, kWsAlign)) return MOE_ERR_INVALID_ARG;
+  const int64_t S = T * k;
+  float *logits = at<float>(ws, L.logits);
+  int32_t *idx = at<int32_t>(ws, L.topk_idx);
+  float *wts = at<float>(ws, L.topk_w);
+  int32_t *offsets = at<int32_t>(ws, L.offsets);
+  int32_t *sorted_slot = at<int32_t>(ws, L.sorted_slot);
+  int32_t *slot_row = at<int32_t>(ws, L.slot_row);
+  uint16_t *act = at<uint16_t>(ws, L.act);
+  float *y = at<float>(ws, L.y);
+  if (moe::launch_router_logits(x, T, H, router->weight, router->bias, E, logits, stream) != hipSuccess)
+    return MOE_ERR_HIP;
+  if (moe::launch_router_topk(logits, T, E, k, idx, wts, stream) != hipSuccess) return MOE_ERR_HIP;
+  if (moe::launch_permute(idx, S, E, offsets, sorted_slot, slot_row, stream) != hipSuccess)
+    return MOE_ERR_HIP;
+  int st = run_ffn(x, T, k, E, offsets, sorted_slot, *gu, *dn, o, y, act, stream);
+  if (st != MOE_OK) return st;
+  if (moe::launch_combine(y, slot_row, wts, T, k, H, out, o.out_dtype == MOE_DTYPE_F32, stream) !=
+      hipSuccess)
+    return MOE_ERR_HIP;
+  return MOE_OK;
+}
+
+struct OwnedWorkspace {
+  void *ptr = nullptr;
+  size_t bytes = 0;
+};
+std::mutex g_ws_mutex;
+std::unordered_map<int, OwnedWorkspace> g_ws;
+
+}  // namespace
+
+#define MOE_GUARD_BEGIN try {
+#define MOE_GUARD_END                   \
+  }                                     \
+  catch (const std::bad_alloc &) {      \
+    return MOE_ERR_HIP;                 \
+  }                                     \
+  catch (...) {                         \
+    return MOE_ERR_HIP;                 \
+  }
+
+extern "C" {
+
+int moe_abi_version(void) { return MOE_ABI_VERSION; }
+
+const char *moe_status_string(int status) {
+  switch (status) {
+    case MOE_OK: return "ok";
+    case MOE_ERR_INVALID_ARG: return "invalid argument (null, negative, misaligned or bad enum)";
+    case MOE_ERR_UNSUPPORTED: return "unsupported shape (k, E, H, I or T*k outside the limits)";
+    case MOE_ERR_WORKSPACE: return "workspace too small";
+    case MOE_ERR_HIP: return "HIP runtime or kernel launch error";
+    default: return "unknown status";
+  }
+}
+
+size_t moe_workspace_size(int64_t T, int32_t E, int32_t k, int32_t H, int32_t I, int32_t path) {
+  if (path < MOE_PATH_AUTO || path > MOE_PATH_GEMM) return 0;
+  if (check_common(T, E, k) != MOE_OK || check_dim(H) != MOE_OK || check_dim(I) != MOE_OK) return 0;
+  WsLayout L;
+  if (!ws_layout(T, E, k, H, I, &L)) return 0;
+  return L.total;
+}
+
+int moe_mxfp4_dequant(const uint8_t *codes, const uint8_t *scales, int64_t n, float *out,
+                      moe_stream_t stream) {
+  MOE_GUARD_BEGIN
+  if (n < 0 || n % 32 != 0) return MOE_ERR_INVALID_ARG;
+  if (n == 0) return MOE_OK;
+  if (codes == nullptr || scales == nullptr || out == nullptr) return MOE_ERR_INVALID_ARG;
+  if (!aligned(codes, 16) || !aligned(out, 16)) return MOE_ERR_INVALID_ARG;
+  return moe::launch_dequant(codes, scales, n, out, (hipStream_t)stream) == hipSuccess ? MOE_OK
+                                                                                        : MOE_ERR_HIP;
+  MOE_GUARD_END
+}
+
+int moe_route(const uint16_t *x, int64_t T, int32_t H, const moe_router_t *router, int32_t E,
+              int32_t k, int32_t *topk_idx, float *topk_w, void *ws, size_t ws_bytes,
+              moe_stream_t stream) {
+  MOE_GUARD_BEGIN
+  int st = check_common(T, E, k);
+  if (st != MOE_OK) return st;
+  if (router == nullptr) return MOE_ERR_INVALID_ARG;
+  if ((st = check_dim(H)) != MOE_OK) return st;
+  if (T == 0) return MOE_OK;
+  if (x == nullptr || router->weight == nullptr || topk_idx == nullptr || topk_w == nullptr)
+    return MOE_ERR_INVALID_ARG;
+  if (!aligned(x, 16) || !aligned(router->weight, 16)) return MOE_ERR_INVALID_ARG;
+  WsLayout L;
+  ws_layout(T, E, k, H, H, &L);
+  if (ws == nullptr || ws_bytes < L.total) return MOE_ERR_WORKSPACE;
+  if (!aligned(ws, kWsAlign)) return MOE_ERR_INVALID_ARG;
+  float *logits = at<float>(ws, L.logits);
+  hipStream_t s = (hipStream_t)stream;
+  if (moe::launch_router_logits(x, T, H, router->weight, router->bias, E, logits, s) != hipSuccess)
+    return MOE_ERR_HIP;
+  return moe::launch_router_topk(logits, T, E, k, topk_idx, topk_w, s) == hipSuccess ? MOE_OK
+                                                                                      : MOE_ERR_HIP;
+  MOE_GUARD_END
+}
+
+int moe_permute(const int32_t *topk_idx, int64_t T, int32_t E, int32_t k, int32_t *expert_offsets,
+                int32_t *sorted_slot, int32_t *slot_row, void *ws, size_t ws_bytes,
+                moe_stream_t stream) {
+  MOE_GUARD_BEGIN
+  (void)ws;
+  (void)ws_bytes;
+  int st = check_common(T, E, k);
+  if (st != MOE_OK) return st;
+  if (T == 0) return MOE_OK;
+  if (topk_idx == nullptr || expert_offsets == nullptr || sorted_slot == nullptr || slot_row == nullptr)
+    return MOE_ERR_INVALID_ARG;
+  return moe::launch_permute(topk_idx, T * k, E, expert_offsets, sorted_slot, slot_row,
+                             (hipStream_t)stream) == hipSuccess
+             ? MOE_OK
+             : MOE_ERR_HIP;
+  MOE_GUARD_END
+}
+
+int moe_mxfp4_ffn(const uint16_t *x, int64_t T, int32_t k, int32_t E, const int32_t *expert_offsets,
+                  const int32_t *sorted_slot, const moe_mxfp4_weight_t *gate_up,
+                  const moe_mxfp4_weight_t *down, const moe_options_t *opts, float *y, void *ws,
+                  size_t ws_bytes, moe_stream_t stream) {
+  MOE_GUARD_BEGIN
+  int st = check_common(T, E, k);
+  if (st != MOE_OK) return st;
+  if (gate_up == nullptr || down == nullptr) return MOE_ERR_INVALID_ARG;
+  if ((st = check_weight(gate_up)) != MOE_OK || (st = check_weight(down)) != MOE_OK) return st;
+  const int H = gate_up->k, I = down->k;
+  if (gate_up->n != 2 * I || down->n != H) return MOE_ERR_UNSUPPORTED;
+  if ((st = check_dim(H)) != MOE_OK || (st = check_dim(I)) != MOE_OK) return st;
+  const moe_options_t o = opts ? *opts : default_options();
+  if ((st = check_options(o)) != MOE_OK) return st;
+  if (T == 0) return MOE_OK;
+  if (x == nullptr || expert_offsets == nullptr || sorted_slot == nullptr || y == nullptr)
+    return MOE_ERR_INVALID_ARG;
+  if (!aligned(x, 16) || !aligned(y, 16)) return MOE_ERR_INVALID_ARG;
+  WsLayout L;
+  ws_layout(T, E, k, H, I, &L);
+  if (ws == nullptr || ws_bytes < L.total) return MOE_ERR_WORKSPACE;
+  if (!aligned(ws, kWsAlign)) return MOE_ERR_INVALID_ARG;
+  return run_ffn(x, T, k, E, expert_offsets, sorted_slot, *gate_up, *down, o, y, at<uint16_t>(ws, L.act),
+                 (hipStream_t)stream);
+  MOE_GUARD_END
+}
+
+int moe_combine(const float *y, const int32_t *slot_row, const float *topk_w, int64_t T, int32_t k,
+                int32_t H, void *out, int32_t out_dtype, moe_stream_t stream) {
+  MOE_GUARD_BEGIN
+  if (T < 0) return MOE_ERR_INVALID_ARG;
+  if (k < 1 || k > kMaxTopK) return MOE_ERR_UNSUPPORTED;
+  int st = check_dim(H);
+  if (st != MOE_OK) return st;
+  if (out_dtype != MOE_DTYPE_BF16 && out_dtype != MOE_DTYPE_F32) return MOE_ERR_INVALID_ARG;
+  if (T * (int64_t)k >= ((int64_t)1 << 31)) return MOE_ERR_UNSUPPORTED;
+  if (T == 0) return MOE_OK;
+  if (y == nullptr || slot_row == nullptr || topk_w == nullptr || out == nullptr) return MOE_ERR_INVALID_ARG;
+  if (!aligned(y, 16) || !aligned(out, 16)) return MOE_ERR_INVALID_ARG;
+  return moe::launch_combine(y, slot_row, topk_w, T, k, H, out, out_dtype == MOE_DTYPE_F32,
+                             (hipStream_t)stream) == hipSuccess
+             ? MOE_OK
+             : MOE_ERR_HIP;
+  MOE_GUARD_END
+}
+
+int moe_forward_ex(const uint16_t *x, const moe_router_t *router,
+                   const moe_mxfp4_weight_t *w_gate_up, const moe_mxfp4_weight_t *w_down,
+                   int64_t T, int32_t E, int32_t k, const moe_options_t *opts, void *out, void *ws,
+                   size_t ws_bytes, moe_stream_t stream) {
+  MOE_GUARD_BEGIN
+  int st = check_layer(x, router, w_gate_up, w_down, T, E, k, out);
+  if (st != MOE_OK) return st;
+  const moe_options_t o = opts ? *opts : default_options();
+  if ((st = check_options(o)) != MOE_OK) return st;
+  if (o.flags != 0) return MOE_ERR_INVALID_ARG;
+  if (T == 0) return MOE_OK;
+  return forward_impl(x, router, w_gate_up, w_down, T, E, k, o, out, ws, ws_bytes, (hipStream_t)stream);
+  MOE_GUARD_END
+}
+
+int moe_forward(const uint16_t *x, const moe_router_t *router, const moe_mxfp4_weight_t *w_gate_up,
+                const moe_mxfp4_weight_t *w_down, int64_t T, int32_t E, int32_t k, uint16_t *out,
+                moe_stream_t stream) {
+  MOE_GUARD_BEGIN
+  int st = check_layer(x, router, w_gate_up, w_down, T, E, k, out);
+  if (st != MOE_OK) return st;
+  if (T == 0) return MOE_OK;
+  WsLayout L;
+  ws_layout(T, E, k, w_gate_up->k, w_down->k, &L);
+  hipStream_t s = (hipStream_t)stream;
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return MOE_ERR_HIP;
+  void *ws = nullptr;
+  {
+    std::lock_guard<std::mutex> lock(g_ws_mutex);
+    OwnedWorkspace &w = g_ws[dev];
+    if (w.bytes < L.total) {
+      if (w.ptr != nullptr) {
+        if (hipStreamSynchronize(s) != hipSuccess) return MOE_ERR_HIP;
+        if (hipFree(w.ptr) != hipSuccess) return MOE_ERR_HIP;
+        w.ptr = nullptr;
+        w.bytes = 0;
+      }
+      if (hipMalloc(&w.ptr, L.total) != hipSuccess) {
+        w.ptr = nullptr;
+        return MOE_ERR_HIP;
+      }
+      w.bytes = L.total;
+    }
+    ws = w.ptr;
+  }
+  const moe_options_t o = default_options();
+  return forward_impl(x, router, w_gate_up, w_down, T, E, k, o, out, ws, L.total, s);
+  MOE_GUARD_END
+}
+
+int moe_release_workspace(void) {
+  MOE_GUARD_BEGIN
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return MOE_ERR_HIP;
+  std::lock_guard<std::mutex> lock(g_ws_mutex);
+  auto it = g_ws.find(dev);
+  if (it == g_ws.end() || it->second.ptr == nullptr) return MOE_OK;
+  if (hipDeviceSynchronize() != hipSuccess) return MOE_ERR_HIP;
+  const hipError_t err = hipFree(it->second.ptr);
+  g_ws.erase(it);
+  return err == hipSuccess ? MOE_OK : MOE_ERR_HIP;
+  MOE_GUARD_END
+}
+
+}  // extern "C"

@@ -1,0 +1,195 @@
+"""torch-tensor front end of the C ABI: one function per entry point, same names.
+
+Argument marshalling only (device pointers, sizes, the current HIP stream); every step of
+the layer runs in libmoe_mxfp4.so. Tensors must already live on the GPU; bf16 tensors are
+torch.bfloat16 (passed as their bit patterns).
+"""
+from __future__ import annotations
+
+import ctypes
+import dataclasses
+from typing import Optional, Tuple
+
+import torch
+
+from . import _lib as L
+
+
+@dataclasses.dataclass
+class MXFP4Weight:
+    """One MXFP4 matrix for all experts: codes uint8 [E][n][k/2], scales uint8 [E][n][k/32],
+    bias bf16 [E][n] or None."""
+    codes: torch.Tensor
+    scales: torch.Tensor
+    bias: Optional[torch.Tensor]
+
+    @property
+    def n(self) -> int:
+        return int(self.codes.shape[1])
+
+    @property
+    def k(self) -> int:
+        return int(self.codes.shape[2]) * 2
+
+    def desc(self) -> L.MoeMxfp4Weight:
+        return L.MoeMxfp4Weight(_ptr(self.codes), _ptr(self.scales), _ptr(self.bias), self.n, self.k)
+
+
+@dataclasses.dataclass
+class Router:
+    """Linear router: weight fp32 [E][H], bias fp32 [E] or None."""
+    weight: torch.Tensor
+    bias: Optional[torch.Tensor]
+
+    def desc(self) -> L.MoeRouter:
+        return L.MoeRouter(_ptr(self.weight), _ptr(self.bias))
+
+
+@dataclasses.dataclass
+class Options:
+    swiglu_limit: float = 7.0
+    swiglu_alpha: float = 1.0
+    out_dtype: int = L.MOE_DTYPE_BF16
+    path: int = L.MOE_PATH_AUTO
+    flags: int = 0
+
+    def desc(self) -> L.MoeOptions:
+        return L.MoeOptions(self.swiglu_limit, self.swiglu_alpha, self.out_dtype, self.path, self.flags)
+
+
+def _ptr(t: Optional[torch.Tensor]) -> Optional[int]:
+    if t is None:
+        return None
+    if not t.is_cuda:
+        raise ValueError("tensors passed to the MoE library must be on the GPU")
+    if not t.is_contiguous():
+        raise ValueError("tensors passed to the MoE library must be contiguous")
+    return t.data_ptr() or None
+
+
+def _stream(stream: Optional[torch.cuda.Stream]) -> int:
+    s = torch.cuda.current_stream() if stream is None else stream
+    return s.cuda_stream
+
+
+def abi_version() -> int:
+    return int(L.lib().moe_abi_version())
+
+
+def moe_workspace_size(T: int, E: int, k: int, H: int, I: int, path: int = L.MOE_PATH_AUTO) -> int:
+    return int(L.lib().moe_workspace_size(T, E, k, H, I, path))
+
+
+def workspace(T: int, E: int, k: int, H: int, I: int, path: int = L.MOE_PATH_AUTO,
+              device=None) -> torch.Tensor:
+    """A caller-owned workspace tensor of the size the library asks for (torch's allocator
+    returns 256-byte aligned blocks)."""
+    n = moe_workspace_size(T, E, k, H, I, path)
+    if n == 0:
+        raise ValueError("invalid sizes for a workspace")
+    return torch.empty(n, dtype=torch.uint8, device=device or "cuda")
+
+
+def moe_mxfp4_dequant(codes: torch.Tensor, scales: torch.Tensor, out: Optional[torch.Tensor] = None,
+                      stream=None) -> torch.Tensor:
+    n = codes.numel() * 2
+    if out is None:
+        out = torch.empty(n, dtype=torch.float32, device=codes.device)
+    L.check("moe_mxfp4_dequant", L.lib().moe_mxfp4_dequant(_ptr(codes), _ptr(scales), n, _ptr(out),
+                                                              _stream(stream)))
+    return out
+
+
+def moe_route(x: torch.Tensor, router: Router, k: int, topk_idx=None, topk_w=None, ws=None,
+              stream=None) -> Tuple[torch.Tensor, torch.Tensor]:
+    T, H = x.shape
+    E = int(router.weight.shape[0])
+    if topk_idx is None:
+        topk_idx = torch.empty((T, k), dtype=torch.int32, device=x.device)
+    if topk_w is None:
+        topk_w = torch.empty((T, k), dtype=torch.float32, device=x.device)
+    if ws is None:
+        ws = workspace(T, E, k, H, H, device=x.device)
+    r = router.desc()
+    L.check("moe_route", L.lib().moe_route(_ptr(x), T, H, ctypes.byref(r), E, k, _ptr(topk_idx),
+                                              _ptr(topk_w), _ptr(ws), ws.numel(), _stream(stream)))
+    return topk_idx, topk_w
+
+
+def moe_permute(topk_idx: torch.Tensor, E: int, out=None, stream=None
+                ) -> Tuple[torch.Tensor, torch.Tensor, torch.Tensor]:
+    T, k = topk_idx.shape
+    dev = topk_idx.device
+    if out is None:
+        out = (torch.empty(E + 1, dtype=torch.int32, device=dev),
+               torch.empty(T * k, dtype=torch.int32, device=dev),
+               torch.empty(T * k, dtype=torch.int32, device=dev))
+    offsets, sorted_slot, slot_row = out
+    L.check("moe_permute", L.lib().moe_permute(_ptr(topk_idx), T, E, k, _ptr(offsets), _ptr(sorted_slot),
+                                                  _ptr(slot_row), None, 0, _stream(stream)))
+    return offsets, sorted_slot, slot_row
+
+
+def moe_mxfp4_ffn(x: torch.Tensor, k: int, E: int, expert_offsets: torch.Tensor, sorted_slot: torch.Tensor,
+                  gate_up: MXFP4Weight, down: MXFP4Weight, opts: Optional[Options] = None,
+                  y: Optional[torch.Tensor] = None, ws=None, stream=None) -> torch.Tensor:
+    T, H = x.shape
+    I = down.k
+    o = opts or Options()
+    width = {L.MOE_FLAG_EMIT_PREACT: 2 * I, L.MOE_FLAG_EMIT_ACT: I}.get(o.flags, H)
+    if y is None:
+        y = torch.empty((T * k, width), dtype=torch.float32, device=x.device)
+    if ws is None:
+        ws = workspace(T, E, k, H, I, o.path, device=x.device)
+    g, d, od = gate_up.desc(), down.desc(), o.desc()
+    L.check("moe_mxfp4_ffn", L.lib().moe_mxfp4_ffn(
+        _ptr(x), T, k, E, _ptr(expert_offsets), _ptr(sorted_slot), ctypes.byref(g), ctypes.byref(d),
+        ctypes.byref(od), _ptr(y), _ptr(ws), ws.numel(), _stream(stream)))
+    return y
+
+
+def moe_combine(y: torch.Tensor, slot_row: torch.Tensor, topk_w: torch.Tensor,
+                out_dtype: int = L.MOE_DTYPE_BF16, out: Optional[torch.Tensor] = None,
+                stream=None) -> torch.Tensor:
+    T, k = topk_w.shape
+    H = int(y.shape[1])
+    if out is None:
+        dt = torch.bfloat16 if out_dtype == L.MOE_DTYPE_BF16 else torch.float32
+        out = torch.empty((T, H), dtype=dt, device=y.device)
+    L.check("moe_combine", L.lib().moe_combine(_ptr(y), _ptr(slot_row), _ptr(topk_w), T, k, H, _ptr(out),
+                                                  out_dtype, _stream(stream)))
+    return out
+
+
+def moe_forward(x: torch.Tensor, router: Router, w_gate_up: MXFP4Weight, w_down: MXFP4Weight, k: int,
+                out: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    T, H = x.shape
+    E = int(router.weight.shape[0])
+    if out is None:
+        out = torch.empty((T, H), dtype=torch.bfloat16, device=x.device)
+    r, g, d = router.desc(), w_gate_up.desc(), w_down.desc()
+    L.check("moe_forward", L.lib().moe_forward(_ptr(x), ctypes.byref(r), ctypes.byref(g), ctypes.byref(d),
+                                                  T, E, k, _ptr(out), _stream(stream)))
+    return out
+
+
+def moe_forward_ex(x: torch.Tensor, router: Router, w_gate_up: MXFP4Weight, w_down: MXFP4Weight, k: int,
+                   opts: Optional[Options] = None, out: Optional[torch.Tensor] = None, ws=None,
+                   stream=None) -> torch.Tensor:
+    T, H = x.shape
+    E = int(router.weight.shape[0])
+    o = opts or Options()
+    if out is None:
+        dt = torch.bfloat16 if o.out_dtype == L.MOE_DTYPE_BF16 else torch.float32
+        out = torch.empty((T, H), dtype=dt, device=x.device)
+    if ws is None:
+        ws = workspace(T, E, k, H, w_down.k, o.path, device=x.device)
+    r, g, d, od = router.desc(), w_gate_up.desc(), w_down.desc(), o.desc()
+    L.check("moe_forward_ex", L.lib().moe_forward_ex(
+        _ptr(x), ctypes.byref(r), ctypes.byref(g), ctypes.byref(d), T, E, k, ctypes.byref(od), _ptr(out),
+        _ptr(ws), ws.numel(), _stream(stream)))
+    return out
+
+
+def moe_release_workspace() -> None:
+    L.check("moe_release_workspace", L.lib().moe_release_workspace())

@@ -1,0 +1,128 @@
+"""The C-ABI library on the CPU: it loads, exports what include/moe_mxfp4.h declares, and
+rejects bad arguments before any HIP call (so nothing here launches a kernel)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "moe_mxfp4.h")
+
+L = pytest.importorskip("sparse_moe_transformer_router_amd._lib")
+
+if not os.path.exists(L.LIB_PATH):  # pragma: no cover
+    pytest.skip("library not built (run python -m sparse_moe_transformer_router_amd.build)",
+                allow_module_level=True)
+
+FAKE = 0x10000  # a host address that validation must reject or never dereference
+
+
+def header_functions():
+    text = open(HEADER, encoding="utf-8").read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\s*\*?\s*(moe_\w+)\s*\(", text, flags=re.M)))
+
+
+def test_exports_every_declared_symbol():
+    lib = L.lib()
+    names = header_functions()
+    assert len(names) >= 11, names
+    for n in names:
+        assert hasattr(lib, n), f"{n} declared in the header but not exported"
+    assert set(names) == set(L.SIGNATURES), "binding signatures and header disagree"
+
+
+def test_version_and_status_strings():
+    lib = L.lib()
+    assert lib.moe_abi_version() == 1
+    for st in (0, -1, -2, -3, -4, 7):
+        assert lib.moe_status_string(st)
+
+
+def test_workspace_size():
+    lib = L.lib()
+    n = lib.moe_workspace_size(64, 32, 4, 2880, 2880, 0)
+    assert n > 64 * 4 * 2880 * (4 + 2) and n % 256 == 0
+    assert lib.moe_workspace_size(64, 32, 9, 2880, 2880, 0) == 0     # k > 8
+    assert lib.moe_workspace_size(64, 3, 4, 2880, 2880, 0) == 0      # k > E
+    assert lib.moe_workspace_size(64, 32, 4, 2880 + 16, 2880, 0) == 0  # H % 32
+    assert lib.moe_workspace_size(-1, 32, 4, 2880, 2880, 0) == 0
+    assert lib.moe_workspace_size(64, 32, 4, 2880, 2880, 5) == 0     # bad path
+    assert lib.moe_workspace_size(0, 32, 4, 2880, 2880, 0) > 0
+
+
+def _weight(n, k, codes=FAKE, scales=FAKE):
+    return L.MoeMxfp4Weight(codes, scales, None, n, k)
+
+
+def _router():
+    return L.MoeRouter(FAKE, None)
+
+
+def test_route_errors():
+    lib = L.lib()
+    r = _router()
+    big = 1 << 40
+    assert lib.moe_route(FAKE, 4, 64, ctypes.byref(r), 8, 0, FAKE, FAKE, FAKE, big, None) == L.MOE_ERR_UNSUPPORTED
+    assert lib.moe_route(FAKE, 4, 64, ctypes.byref(r), 8, 9, FAKE, FAKE, FAKE, big, None) == L.MOE_ERR_UNSUPPORTED
+    assert lib.moe_route(FAKE, 4, 64, ctypes.byref(r), 300, 4, FAKE, FAKE, FAKE, big, None) == L.MOE_ERR_UNSUPPORTED
+    assert lib.moe_route(FAKE, 4, 48, ctypes.byref(r), 8, 4, FAKE, FAKE, FAKE, big, None) == L.MOE_ERR_UNSUPPORTED
+    assert lib.moe_route(FAKE, -1, 64, ctypes.byref(r), 8, 4, FAKE, FAKE, FAKE, big, None) == L.MOE_ERR_INVALID_ARG
+    assert lib.moe_route(FAKE, 4, 64, None, 8, 4, FAKE, FAKE, FAKE, big, None) == L.MOE_ERR_INVALID_ARG
+    assert lib.moe_route(None, 4, 64, ctypes.byref(r), 8, 4, FAKE, FAKE, FAKE, big, None) == L.MOE_ERR_INVALID_ARG
+    assert lib.moe_route(FAKE + 2, 4, 64, ctypes.byref(r), 8, 4, FAKE, FAKE, FAKE, big, None) == L.MOE_ERR_INVALID_ARG
+    assert lib.moe_route(FAKE, 4, 64, ctypes.byref(r), 8, 4, FAKE, FAKE, FAKE, 16, None) == L.MOE_ERR_WORKSPACE
+    assert lib.moe_route(FAKE, 4, 64, ctypes.byref(r), 8, 4, FAKE, FAKE, FAKE + 8, big, None) == L.MOE_ERR_INVALID_ARG
+    assert lib.moe_route(None, 0, 64, ctypes.byref(r), 8, 4, None, None, None, 0, None) == L.MOE_OK  # T = 0
+
+
+def test_permute_and_combine_errors():
+    lib = L.lib()
+    assert lib.moe_permute(FAKE, 4, 8, 0, FAKE, FAKE, FAKE, None, 0, None) == L.MOE_ERR_UNSUPPORTED
+    assert lib.moe_permute(None, 4, 8, 4, FAKE, FAKE, FAKE, None, 0, None) == L.MOE_ERR_INVALID_ARG
+    assert lib.moe_permute(None, 0, 8, 4, None, None, None, None, 0, None) == L.MOE_OK
+    assert lib.moe_combine(FAKE, FAKE, FAKE, 4, 4, 48, FAKE, 0, None) == L.MOE_ERR_UNSUPPORTED
+    assert lib.moe_combine(FAKE, FAKE, FAKE, 4, 4, 64, FAKE, 7, None) == L.MOE_ERR_INVALID_ARG
+    assert lib.moe_combine(FAKE, FAKE, FAKE, 4, 4, 64, FAKE + 4, 0, None) == L.MOE_ERR_INVALID_ARG
+    assert lib.moe_combine(None, None, None, 0, 4, 64, None, 0, None) == L.MOE_OK
+
+
+def test_ffn_and_forward_errors():
+    lib = L.lib()
+    H, I, E, k = 64, 96, 8, 4
+    g, d = _weight(2 * I, H), _weight(H, I)
+    big = 1 << 40
+    o = L.MoeOptions(7.0, 1.0, 0, 0, 0)
+    args = lambda g_, d_, o_, ws=FAKE, wsb=big: (FAKE, 4, k, E, FAKE, FAKE, ctypes.byref(g_), ctypes.byref(d_),
+                                                  ctypes.byref(o_), FAKE, ws, wsb, None)
+    assert lib.moe_mxfp4_ffn(*args(_weight(2 * I + 2, H), d, o)) == L.MOE_ERR_UNSUPPORTED  # n != 2I
+    assert lib.moe_mxfp4_ffn(*args(g, _weight(H + 32, I), o)) == L.MOE_ERR_UNSUPPORTED     # down.n != H
+    assert lib.moe_mxfp4_ffn(*args(_weight(2 * I, H, codes=FAKE + 1), d, o)) == L.MOE_ERR_INVALID_ARG
+    assert lib.moe_mxfp4_ffn(*args(_weight(2 * I, H, scales=0), d, o)) == L.MOE_ERR_INVALID_ARG
+    assert lib.moe_mxfp4_ffn(*args(g, d, L.MoeOptions(7.0, 1.0, 3, 0, 0))) == L.MOE_ERR_INVALID_ARG
+    assert lib.moe_mxfp4_ffn(*args(g, d, L.MoeOptions(7.0, 1.0, 0, 9, 0))) == L.MOE_ERR_INVALID_ARG
+    assert lib.moe_mxfp4_ffn(*args(g, d, L.MoeOptions(-1.0, 1.0, 0, 0, 0))) == L.MOE_ERR_INVALID_ARG
+    assert lib.moe_mxfp4_ffn(*args(g, d, L.MoeOptions(7.0, 1.0, 0, 0, 3))) == L.MOE_ERR_INVALID_ARG
+    assert lib.moe_mxfp4_ffn(*args(g, d, o, wsb=64)) == L.MOE_ERR_WORKSPACE
+    assert lib.moe_mxfp4_ffn(*args(g, d, o, ws=None)) == L.MOE_ERR_WORKSPACE
+    r = _router()
+    assert lib.moe_forward(FAKE, ctypes.byref(r), ctypes.byref(g), ctypes.byref(d), 4, 8, 9, FAKE, None) \
+        == L.MOE_ERR_UNSUPPORTED
+    assert lib.moe_forward(FAKE, ctypes.byref(r), ctypes.byref(g), ctypes.byref(d), 4, 2, 4, FAKE, None) \
+        == L.MOE_ERR_UNSUPPORTED
+    assert lib.moe_forward(FAKE, None, ctypes.byref(g), ctypes.byref(d), 4, 8, 4, FAKE, None) == L.MOE_ERR_INVALID_ARG
+    assert lib.moe_forward(FAKE, ctypes.byref(r), ctypes.byref(g), ctypes.byref(d), 0, 8, 4, FAKE, None) == L.MOE_OK
+    assert lib.moe_forward_ex(FAKE, ctypes.byref(r), ctypes.byref(g), ctypes.byref(d), 4, 8, 4,
+                              ctypes.byref(o), FAKE, FAKE, 64, None) == L.MOE_ERR_WORKSPACE
+    flagged = L.MoeOptions(7.0, 1.0, 0, 0, 1)
+    assert lib.moe_forward_ex(FAKE, ctypes.byref(r), ctypes.byref(g), ctypes.byref(d), 4, 8, 4,
+                              ctypes.byref(flagged), FAKE, FAKE, big, None) == L.MOE_ERR_INVALID_ARG
+
+
+def test_dequant_errors():
+    lib = L.lib()
+    assert lib.moe_mxfp4_dequant(FAKE, FAKE, 33, FAKE, None) == L.MOE_ERR_INVALID_ARG
+    assert lib.moe_mxfp4_dequant(FAKE + 4, FAKE, 64, FAKE, None) == L.MOE_ERR_INVALID_ARG
+    assert lib.moe_mxfp4_dequant(None, FAKE, 64, FAKE, None) == L.MOE_ERR_INVALID_ARG
+    assert lib.moe_mxfp4_dequant(None, None, 0, None, None) == L.MOE_OK

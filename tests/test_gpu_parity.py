@@ -1,0 +1,268 @@
+"""GPU parity: the HIP library, called through its C ABI, against the fp64 oracle.
+
+Bars: bit-exact MXFP4 decode and permutation; top-k indices bit-exact except tokens whose
+k-th and (k+1)-th fp64 logits differ by < 1e-3 (those must still be a valid choice);
+routing weights within 1e-5; layer outputs within 2e-2 x RMS of the oracle output (plus half
+a bf16 ulp of the oracle value when the output is bf16).
+"""
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import gpu_util as gu
+import oracle
+import synth
+
+pytestmark = pytest.mark.gpu
+
+moe = pytest.importorskip("sparse_moe_transformer_router_amd")
+
+
+@pytest.fixture(autouse=True)
+def _announce(request):
+    sys.__stderr__.write(f"\n[gpu case] {request.node.nodeid}\n")
+    sys.__stderr__.flush()
+    yield
+    torch.cuda.synchronize()
+
+
+# ------------------------------------------------------------------ a0: MXFP4 decode
+def test_dequant_all_codes_all_scales():
+    # block b (32 elements) uses scale byte b and holds codes 0..15 twice
+    byte_row = np.array([(2 * j % 16) | (((2 * j + 1) % 16) << 4) for j in range(16)], np.uint8)
+    codes = np.tile(byte_row, (256, 1))
+    scales = np.arange(256, dtype=np.uint8).reshape(256, 1)
+    got = moe.moe_mxfp4_dequant(gu.to_dev_u8(codes), gu.to_dev_u8(scales)).cpu().numpy()
+    with np.errstate(over="ignore"):
+        ref = oracle.mxfp4_decode(codes, scales).reshape(-1).astype(np.float32)
+    nan_g, nan_r = np.isnan(got), np.isnan(ref)
+    assert np.array_equal(nan_g, nan_r)
+    assert np.array_equal(got[~nan_g].view(np.uint32), ref[~nan_r].view(np.uint32))
+
+
+# ------------------------------------------------------------------ a1/a2: router
+@pytest.mark.parametrize("name,T", [("tiny", 16), ("decode20b", 1), ("decode20b", 64),
+                                    ("decode120b_zipf", 256), ("prefill20b", 4096),
+                                    ("prefill120b", 8192)])
+def test_route(name, T):
+    cfg = synth.get_config(name)
+    x = synth.make_x(cfg, T)
+    rw, rb = synth.make_router(cfg)
+    router = moe.Router(gu.to_dev_f32(rw), gu.to_dev_f32(rb))
+    idx, w = moe.moe_route(gu.to_dev_bf16(x), router, cfg.k)
+    logits = oracle.router_logits(oracle.bf16_to_f64(x), rw, rb)
+    gu.check_routing(idx.cpu().numpy(), w.cpu().numpy(), logits, cfg.k)
+
+
+def test_route_ties_and_k_range():
+    rng = np.random.default_rng(7)
+    T, H = 37, 64
+    for E, k in [(8, 1), (8, 8), (16, 8), (256, 4), (5, 3), (130, 2)]:
+        x = synth.bf16_bits_from_f32(rng.standard_normal((T, H)).astype(np.float32))
+        rw = (rng.standard_normal((E, H)) * 0.05).astype(np.float32)
+        rb = rng.standard_normal(E).astype(np.float32)
+        rw[E // 2] = rw[0]  # exact duplicate experts: equal logits, the lower id must win
+        rb[E // 2] = rb[0]
+        router = moe.Router(gu.to_dev_f32(rw), gu.to_dev_f32(rb))
+        idx, w = moe.moe_route(gu.to_dev_bf16(x), router, k)
+        idx = idx.cpu().numpy()
+        logits = oracle.router_logits(oracle.bf16_to_f64(x), rw, rb)
+        gu.check_routing(idx, w.cpu().numpy(), logits, k)
+        # the duplicate of expert 0 is never picked ahead of it
+        for t in range(T):
+            row = idx[t].tolist()
+            if E // 2 in row:
+                assert 0 in row and row.index(0) < row.index(E // 2)
+
+
+# ------------------------------------------------------------------ a3: permutation
+@pytest.mark.parametrize("T,E,k,mode", [(1, 8, 4, "rand"), (16, 8, 4, "rand"), (4096, 32, 4, "rand"),
+                                        (8192, 128, 4, "rand"), (1000, 256, 8, "rand"),
+                                        (300, 128, 4, "hot"), (77, 16, 1, "rand"), (50, 4, 4, "rand")])
+def test_permute(T, E, k, mode):
+    rng = np.random.default_rng(T * 131 + E)
+    if mode == "hot":  # every token picks experts 0..k-1: most experts empty
+        idx = np.tile(np.arange(k, dtype=np.int32), (T, 1))
+    else:
+        idx = np.argsort(rng.random((T, E)), axis=1)[:, :k].astype(np.int32)
+    off, ss, sr = moe.moe_permute(torch.from_numpy(idx).cuda(), E)
+    counts, r_off, r_ss, r_sr = oracle.permute(idx, E)
+    assert np.array_equal(off.cpu().numpy(), r_off)
+    assert np.array_equal(ss.cpu().numpy(), r_ss)
+    assert np.array_equal(sr.cpu().numpy(), r_sr)
+
+
+# ------------------------------------------------------------------ a4: in-kernel decode
+def _ffn_inputs(E, H, I, scale_lo, scale_hi, seed):
+    rng = np.random.default_rng(seed)
+    w1c = rng.integers(0, 256, (E, 2 * I, H // 2), dtype=np.uint8)
+    w1s = rng.integers(scale_lo, scale_hi + 1, (E, 2 * I, H // 32), dtype=np.uint8)
+    w2c = rng.integers(0, 256, (E, H, I // 2), dtype=np.uint8)
+    w2s = rng.integers(scale_lo, scale_hi + 1, (E, H, I // 32), dtype=np.uint8)
+    return w1c, w1s, w2c, w2s
+
+
+@pytest.mark.parametrize("scale_lo,scale_hi", [(4, 252), (123, 127)])
+def test_ffn_preact_identity_decode(scale_lo, scale_hi):
+    """One-hot activations and no bias: h = W1 x is one decoded weight column, exactly."""
+    E, H, I, k = 3, 128, 96, 1
+    w1c, w1s, w2c, w2s = _ffn_inputs(E, H, I, scale_lo, scale_hi, 11)
+    T = H  # token t is e_t, routed to expert t % E
+    x = np.zeros((T, H), np.uint16)
+    x[np.arange(T), np.arange(T)] = 0x3F80
+    idx = (np.arange(T) % E).astype(np.int32).reshape(T, 1)
+    _, off, ss, sr = oracle.permute(idx, E)
+    w1 = moe.MXFP4Weight(gu.to_dev_u8(w1c), gu.to_dev_u8(w1s), None)
+    w2 = moe.MXFP4Weight(gu.to_dev_u8(w2c), gu.to_dev_u8(w2s), None)
+    y = moe.moe_mxfp4_ffn(gu.to_dev_bf16(x), k, E, torch.from_numpy(off).cuda(), torch.from_numpy(ss).cuda(),
+                          w1, w2, moe.Options(flags=moe.MOE_FLAG_EMIT_PREACT)).cpu().numpy()
+    for e in range(E):
+        W1 = oracle.mxfp4_decode(w1c[e], w1s[e]).astype(np.float32)
+        for r in range(off[e], off[e + 1]):
+            t = ss[r]  # k = 1: slot id = token id
+            assert np.array_equal(y[r].view(np.uint32), W1[:, t].view(np.uint32)), (e, t)
+
+
+def test_ffn_activation_step():
+    """Stop after the SwiGLU: the bf16-rounded activation of every slot."""
+    cfg = synth.get_config("tiny").with_(scale_bytes=(118, 122))
+    inp = synth.make_inputs(cfg)
+    dev = gu.device_layer(inp)
+    res = gu.oracle_forward(inp, None, keep_intermediates=True)
+    idx = res.idx
+    _, off, ss, sr = oracle.permute(idx, cfg.E)
+    act = moe.moe_mxfp4_ffn(dev.x, cfg.k, cfg.E, torch.from_numpy(off).cuda(), torch.from_numpy(ss).cuda(),
+                            dev.w1, dev.w2, moe.Options(flags=moe.MOE_FLAG_EMIT_ACT)).cpu().numpy()
+    ref = res.act.reshape(-1, cfg.I)[ss]  # slot order -> sorted rows
+    rms = np.sqrt(np.mean(ref ** 2))
+    err = np.abs(act - ref)
+    assert (err <= 1e-2 * rms + gu.bf16_half_ulp(ref)).all(), err.max() / rms
+    assert np.abs(act).max() <= 7.0 / (1 + np.exp(-7.0)) * 8.0 + 1e-3  # clamp bound holds on the GPU
+
+
+# ------------------------------------------------------------------ whole layer
+def _run_forward(dev, out_dtype, path=0):
+    return moe.moe_forward_ex(dev.x, dev.router, dev.w1, dev.w2, dev.k,
+                              moe.Options(out_dtype=out_dtype, path=path))
+
+
+def _gpu_idx(dev):
+    idx, _ = moe.moe_route(dev.x, dev.router, dev.k)
+    return idx.cpu().numpy()
+
+
+def _check_layer(inp, tokens=None, path=0):
+    dev = gu.device_layer(inp)
+    gidx = _gpu_idx(dev)
+    ref = gu.oracle_forward(inp, gidx, tokens=tokens)
+    tok = ref.tokens
+    out32 = _run_forward(dev, moe.MOE_DTYPE_F32, path).cpu().numpy()
+    assert np.isfinite(out32).all()
+    rel32 = gu.check_output(out32[tok], ref.out, bf16=False)
+    out16 = gu.bf16_bits(_run_forward(dev, moe.MOE_DTYPE_BF16, path))
+    o16 = synth.f32_from_bf16_bits(out16)
+    rel16 = gu.check_output(o16[tok], ref.out, bf16=True)
+    # moe_forward (library-owned workspace) gives the same bits as moe_forward_ex
+    out_fw = gu.bf16_bits(moe.moe_forward(dev.x, dev.router, dev.w1, dev.w2, dev.k))
+    assert np.array_equal(out_fw, out16)
+    return rel32, rel16
+
+
+def test_layer_tiny():
+    _check_layer(synth.make_inputs(synth.get_config("tiny")))
+
+
+@pytest.mark.parametrize("scales", [(123, 127), (118, 121), (121, 124)])
+def test_layer_tiny_scale_ranges(scales):
+    """The default weight law clamps ~93% of pre-activations; smaller scales exercise the
+    smooth SiLU region (about 0% and about 50% clamped)."""
+    _check_layer(synth.make_inputs(synth.get_config("tiny").with_(scale_bytes=scales)))
+
+
+def test_layer_tiny_alpha_limit():
+    cfg = synth.get_config("tiny").with_(scale_bytes=(119, 123))
+    inp = synth.make_inputs(cfg)
+    dev = gu.device_layer(inp)
+    for alpha, limit in [(1.702, 7.0), (1.0, 3.5)]:
+        ref = gu.oracle_forward(inp, _gpu_idx(dev), limit=limit, alpha=alpha)
+        out = moe.moe_forward_ex(dev.x, dev.router, dev.w1, dev.w2, dev.k,
+                                 moe.Options(out_dtype=moe.MOE_DTYPE_F32, swiglu_alpha=alpha,
+                                             swiglu_limit=limit)).cpu().numpy()
+        gu.check_output(out, ref.out, bf16=False)
+
+
+@pytest.mark.parametrize("T", [1, 8, 32, 64])
+def test_layer_decode20b(T):
+    cfg = synth.get_config("decode20b")
+    _check_layer(synth.make_inputs(cfg, T))
+
+
+@pytest.mark.parametrize("T", [1, 16, 64, 256])
+def test_layer_decode120b_zipf(T):
+    cfg = synth.get_config("decode120b_zipf")
+    _check_layer(synth.make_inputs(cfg, T))
+
+
+def test_layer_prefill20b_sampled():
+    cfg = synth.get_config("prefill20b")
+    inp = synth.make_inputs(cfg)
+    tokens = np.sort(np.random.default_rng(20).choice(cfg.T_list[-1], 48, replace=False))
+    _check_layer(inp, tokens)
+
+
+def test_layer_prefill120b_sampled():
+    cfg = synth.get_config("prefill120b")
+    inp = synth.make_inputs(cfg)
+    tokens = np.sort(np.random.default_rng(120).choice(cfg.T_list[-1], 20, replace=False))
+    _check_layer(inp, tokens)
+
+
+# ------------------------------------------------------------------ edge cases
+def _small_cfg(E, k, H=128, I=96, T=24, seed=31, scales=(119, 123)):
+    return synth.LayerConfig("edge", (T,), H, I, E, k, seed, scale_bytes=scales)
+
+
+@pytest.mark.parametrize("E,k,H,I,T", [(4, 4, 128, 96, 9), (16, 1, 64, 64, 33), (16, 8, 96, 160, 21),
+                                       (256, 4, 64, 32, 40), (8, 2, 32, 32, 1), (2, 1, 160, 96, 70)])
+def test_layer_shapes(E, k, H, I, T):
+    _check_layer(synth.make_inputs(_small_cfg(E, k, H, I, T)))
+
+
+def test_layer_all_tokens_one_group():
+    """A router bias that sends every token to experts 0..3: most experts are empty and the
+    four busy experts hold many m-tiles each."""
+    cfg = _small_cfg(32, 4, T=100)
+    bias = np.zeros(32, np.float32)
+    bias[:4] = 50.0
+    _check_layer(synth.make_inputs(cfg, router_bias=bias))
+
+
+def test_layer_no_bias_and_empty_batch():
+    cfg = _small_cfg(8, 4)
+    inp = synth.make_inputs(cfg)
+    dev = gu.device_layer(inp, with_bias=False)
+    ref = gu.oracle_forward(inp, _gpu_idx(dev), with_bias=False)
+    out = moe.moe_forward_ex(dev.x, dev.router, dev.w1, dev.w2, dev.k,
+                             moe.Options(out_dtype=moe.MOE_DTYPE_F32)).cpu().numpy()
+    gu.check_output(out, ref.out, bf16=False)
+    empty = dev.x[:0]
+    out0 = moe.moe_forward(empty, dev.router, dev.w1, dev.w2, dev.k)
+    assert out0.shape == (0, cfg.H)
+
+
+def test_determinism_and_guard_regions():
+    cfg = synth.get_config("decode20b")
+    inp = synth.make_inputs(cfg, 64)
+    dev = gu.device_layer(inp)
+    T, H = 64, cfg.H
+    pad = 4096
+    buf = torch.full((T * H + 2 * pad,), 12345, dtype=torch.int16, device="cuda")
+    out = buf[pad:pad + T * H].view(torch.bfloat16).view(T, H)
+    moe.moe_forward(dev.x, dev.router, dev.w1, dev.w2, cfg.k, out=out)
+    first = gu.bf16_bits(out).copy()
+    moe.moe_forward(dev.x, dev.router, dev.w1, dev.w2, cfg.k, out=out)
+    assert np.array_equal(first, gu.bf16_bits(out)), "two runs differ"
+    b = buf.cpu().numpy()
+    assert (b[:pad] == 12345).all() and (b[pad + T * H:] == 12345).all(), "write outside the output"

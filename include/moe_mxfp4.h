@@ -58,6 +58,10 @@ extern "C" {
 #define MOE_PATH_STREAM 1  /* weight-streaming kernels for decode-sized batches */
 #define MOE_PATH_GEMM 2    /* LDS-tiled grouped GEMM for prefill-sized batches */
 
+/* moe_mxfp4_weight_t.layout */
+#define MOE_LAYOUT_ROWMAJOR 0 /* codes [E][n][k/2], scales [E][n][k/32] as described below */
+#define MOE_LAYOUT_TILED 1    /* the kernel layout written by moe_mxfp4_pack */
+
 /* moe_options_t.flags: test hooks for per-step checks of the expert FFN */
 #define MOE_FLAG_EMIT_PREACT 1u /* stop after gate_up: y <- h = W1 x + b1, fp32 [T*k][2I] */
 #define MOE_FLAG_EMIT_ACT 2u    /* stop after the SwiGLU: y <- a (bf16-rounded, as fp32) [T*k][I] */
@@ -81,6 +85,8 @@ typedef struct moe_router {
  * bias:   bf16 [E][n], or NULL for zero.
  * For the gate_up matrix n = 2I with rows interleaved: row 2i is unit i's gate, row
  * 2i+1 its linear branch; k = H. For the down matrix n = H, k = I.
+ * layout MOE_LAYOUT_TILED: codes and scales hold the same values re-ordered by
+ * moe_mxfp4_pack into 16-row x 128-element tiles (see there); bias is unchanged.
  */
 typedef struct moe_mxfp4_weight {
   const uint8_t *codes;
@@ -88,6 +94,7 @@ typedef struct moe_mxfp4_weight {
   const uint16_t *bias;
   int32_t n;
   int32_t k;
+  int32_t layout; /* MOE_LAYOUT_ROWMAJOR or MOE_LAYOUT_TILED */
 } moe_mxfp4_weight_t;
 
 /* Options for the _ex entry points; NULL selects the defaults shown. */
@@ -121,6 +128,27 @@ size_t moe_workspace_size(int64_t T, int32_t E, int32_t k, int32_t H, int32_t I,
  */
 int moe_mxfp4_dequant(const uint8_t *codes, const uint8_t *scales, int64_t n, float *out,
                       moe_stream_t stream);
+
+/*
+ * Bytes of the tiled copies of one MXFP4 matrix (E experts, n x k each) that
+ * moe_mxfp4_pack writes: *codes_bytes = E * (n/16) * ceil(k/128) * 1024 and
+ * *scales_bytes = E * (n/16) * ceil(k/128) * 64. Returns MOE_ERR_UNSUPPORTED unless
+ * n is a positive multiple of 16 and k a positive multiple of 32.
+ */
+int moe_mxfp4_tiled_bytes(int32_t E, int32_t n, int32_t k, size_t *codes_bytes, size_t *scales_bytes);
+
+/*
+ * Re-order a row-major MXFP4 matrix (src->layout must be MOE_LAYOUT_ROWMAJOR) into the
+ * tiled kernel layout, on the device. A one-time, load-time conversion: the values and
+ * their MX blocks are unchanged, only their order in memory. Tile (g, c) of expert e covers
+ * rows 16g..16g+15 and elements 128c..128c+127 and is stored as 64 lanes x 16 bytes
+ * (lane l = r + 16q: for j = 0..3 its bytes 4j..4j+3 are bytes 16j+4q..16j+4q+3 of row
+ * 16g+r's 64-byte run of chunk c), followed in the scales array by 16 rows x 4 scale bytes
+ * (blocks 4c..4c+3). Elements past k are zero codes with scale 127.
+ * codes_out / scales_out: device buffers of moe_mxfp4_tiled_bytes() bytes, 16-byte aligned.
+ */
+int moe_mxfp4_pack(const moe_mxfp4_weight_t *src, int32_t E, uint8_t *codes_out, uint8_t *scales_out,
+                   moe_stream_t stream);
 
 /*
  * Router [review section 3.4; walkthrough sections 2.2 and 4; config.json read-through at

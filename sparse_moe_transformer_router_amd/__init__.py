@@ -9,6 +9,8 @@ from ._lib import (  # noqa: F401
     MOE_DTYPE_F32,
     MOE_FLAG_EMIT_ACT,
     MOE_FLAG_EMIT_PREACT,
+    MOE_LAYOUT_ROWMAJOR,
+    MOE_LAYOUT_TILED,
     MOE_PATH_AUTO,
     MOE_PATH_GEMM,
     MOE_PATH_STREAM,
@@ -25,6 +27,8 @@ from .ops import (  # noqa: F401
     moe_forward_ex,
     moe_mxfp4_dequant,
     moe_mxfp4_ffn,
+    moe_mxfp4_pack,
+    moe_mxfp4_tiled_bytes,
     moe_permute,
     moe_release_workspace,
     moe_route,

@@ -28,6 +28,9 @@ MOE_PATH_AUTO = 0
 MOE_PATH_STREAM = 1
 MOE_PATH_GEMM = 2
 
+MOE_LAYOUT_ROWMAJOR = 0
+MOE_LAYOUT_TILED = 1
+
 MOE_FLAG_EMIT_PREACT = 1
 MOE_FLAG_EMIT_ACT = 2
 
@@ -43,7 +46,7 @@ class MoeRouter(ctypes.Structure):
 
 class MoeMxfp4Weight(ctypes.Structure):
     _fields_ = [("codes", c_void_p), ("scales", c_void_p), ("bias", c_void_p),
-                ("n", c_int32), ("k", c_int32)]
+                ("n", c_int32), ("k", c_int32), ("layout", c_int32)]
 
 
 class MoeOptions(ctypes.Structure):
@@ -57,6 +60,9 @@ SIGNATURES = {
     "moe_status_string": (ctypes.c_char_p, [c_int32]),
     "moe_workspace_size": (c_size_t, [c_int64, c_int32, c_int32, c_int32, c_int32, c_int32]),
     "moe_mxfp4_dequant": (c_int32, [c_void_p, c_void_p, c_int64, c_void_p, c_void_p]),
+    "moe_mxfp4_tiled_bytes": (c_int32, [c_int32, c_int32, c_int32, ctypes.POINTER(c_size_t),
+                                        ctypes.POINTER(c_size_t)]),
+    "moe_mxfp4_pack": (c_int32, [ctypes.POINTER(MoeMxfp4Weight), c_int32, c_void_p, c_void_p, c_void_p]),
     "moe_route": (c_int32, [c_void_p, c_int64, c_int32, ctypes.POINTER(MoeRouter), c_int32, c_int32,
                             c_void_p, c_void_p, c_void_p, c_size_t, c_void_p]),
     "moe_permute": (c_int32, [c_void_p, c_int64, c_int32, c_int32, c_void_p, c_void_p, c_void_p,

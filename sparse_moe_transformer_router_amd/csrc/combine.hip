@@ -17,14 +17,25 @@ __global__ __launch_bounds__(256) void combine_kernel(const float *__restrict__ 
   const int h = ((blockIdx.x % chunks) * blockDim.x + threadIdx.x) * 4;
   if (h >= H) return;
   const int64_t S = T * k;
-  f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
-  for (int j = 0; j < k; ++j) {
-    const int32_t r = slot_row[t * k + j];
-    const float w = topk_w[t * k + j];
-    if ((uint32_t)r < (uint64_t)S) {
-      const f32x4_t v = *reinterpret_cast<const f32x4_t *>(y + (int64_t)r * H + h);
+  // all index/weight loads first, then all row loads, then the sum in rank order
+  int32_t r[8];
+  float w[8];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) acc[i] = fmaf(w, v[i], acc[i]);
+  for (int j = 0; j < 8; ++j) {
+    r[j] = (j < k) ? slot_row[t * k + j] : -1;
+    w[j] = (j < k) ? topk_w[t * k + j] : 0.f;
+  }
+  f32x4_t v[8];
+#pragma unroll
+  for (int j = 0; j < 8; ++j)
+    v[j] = ((uint32_t)r[j] < (uint64_t)S) ? *reinterpret_cast<const f32x4_t *>(y + (int64_t)r[j] * H + h)
+                                          : f32x4_t{0.f, 0.f, 0.f, 0.f};
+  f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    if (j < k && (uint32_t)r[j] < (uint64_t)S) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) acc[i] = fmaf(w[j], v[j][i], acc[i]);
     }
   }
   if (out_f32) {

@@ -169,6 +169,151 @@ __global__ __launch_bounds__(kSWaves *kWave) void ffn_stream_kernel(
   }
 }
 
+// ---------------------------------------------------------------------------------------
+// Same product on the tiled weight layout (moe_mxfp4_pack): every weight load is one
+// contiguous 1 KB tile per wave, one MFMA step is one MX block, and a lane's activation
+// loads for a step cover 64 contiguous bytes of one token. Workgroup tiles are numbered
+// m-tile-major along a 1-D grid, so consecutive workgroups stream consecutive row tiles of
+// the same expert. PF = chunks of register prefetch per wave.
+template <int EPI, int PF>
+__global__ __launch_bounds__(kSWaves *kWave) void ffn_stream_tiled_kernel(
+    const uint16_t *__restrict__ a_src, int a_by_token, const int32_t *__restrict__ sorted_slot, int k,
+    const int32_t *__restrict__ offsets, int E, const uint8_t *__restrict__ pcodes,
+    const uint8_t *__restrict__ pscales, const uint16_t *__restrict__ bias, int N, int K, int ntiles_n,
+    void *__restrict__ out, float limit, float alpha) {
+  constexpr int RG = kSRows / 16;
+  __shared__ float red[kSWaves][kSRows][kSCols + 1];
+  const int wave = threadIdx.x / kWave, lane = threadIdx.x % kWave;
+  const int mt = blockIdx.x / ntiles_n, nt = blockIdx.x % ntiles_n;
+  const int g0 = nt * RG;
+  const int n0 = nt * kSRows;
+
+  int e = -1, m0 = 0, rbase = 0, mcount = 0;
+  {
+    int carry = 0;
+    for (int eb = 0; eb < E; eb += kWave) {
+      const int ex = eb + lane;
+      const int cnt = (ex < E) ? offsets[ex + 1] - offsets[ex] : 0;
+      const int tiles = (cnt + kSCols - 1) / kSCols;
+      const int inc = wave_inclusive_scan(tiles);
+      const int excl = inc - tiles + carry;
+      const uint64_t hit = __ballot(tiles > 0 && mt >= excl && mt < excl + tiles);
+      if (hit) {
+        const int src = __ffsll((unsigned long long)hit) - 1;
+        const int sel_excl = __shfl(excl, src, kWave);
+        e = eb + src;
+        m0 = (mt - sel_excl) * kSCols;
+        rbase = offsets[e];
+        const int cnt_e = offsets[e + 1] - rbase;
+        mcount = (cnt_e - m0 < kSCols) ? cnt_e - m0 : kSCols;
+        break;
+      }
+      carry += __shfl(inc, kWave - 1, kWave);
+    }
+  }
+  if (e < 0) return;
+
+  const int rl = lane % 16, q = lane / 16;
+  const bool col_ok = rl < mcount;
+  const uint16_t *arow = a_src;
+  if (col_ok) {
+    const int r = rbase + m0 + rl;
+    arow = a_src + (a_by_token ? (int64_t)(sorted_slot[r] / k) : (int64_t)r) * K;
+  }
+  const int KB = K / 32;
+  const int nchunk = (KB + 3) / 4;
+  const int NG = N / 16;
+  const uint8_t *cbase = pcodes + (int64_t)e * NG * nchunk * 1024 + lane * 16;
+  const uint8_t *sbase = pscales + (int64_t)e * NG * nchunk * 64 + rl * 4;
+  const uint16_t *ap = arow + q * 8;
+
+  f32x4_t acc[RG];
+#pragma unroll
+  for (int g = 0; g < RG; ++g) acc[g] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  u32x4_t cw[PF][RG];
+  uint32_t sw[PF][RG];
+  u32x4_t av[PF][4];
+  auto load = [&](int c, int s) {
+    const bool cvalid = c < nchunk;
+#pragma unroll
+    for (int g = 0; g < RG; ++g) {
+      const bool ok = cvalid && (g0 + g) < NG;
+      const int64_t t = (int64_t)(g0 + g) * nchunk + c;
+      cw[s][g] = ok ? *reinterpret_cast<const u32x4_t *>(cbase + t * 1024) : u32x4_t{0u, 0u, 0u, 0u};
+      sw[s][g] = ok ? *reinterpret_cast<const uint32_t *>(sbase + t * 64) : 0x7f7f7f7fu;
+    }
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+      av[s][j] = (cvalid && col_ok && (4 * c + j) < KB)
+                     ? *reinterpret_cast<const u32x4_t *>(ap + c * 128 + j * 32)
+                     : u32x4_t{0u, 0u, 0u, 0u};
+  };
+#pragma unroll
+  for (int s = 0; s < PF; ++s) load(wave + s * kSWaves, s);
+  for (int c = wave; c < nchunk; c += PF * kSWaves) {
+#pragma unroll
+    for (int s = 0; s < PF; ++s) {
+      const int cc = c + s * kSWaves;
+      if (cc < nchunk) {
+#pragma unroll
+        for (int g = 0; g < RG; ++g) {
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            const float sc = e8m0_to_f32((sw[s][g] >> (8 * j)) & 0xffu);
+            const bf16x8_t wa = fp4x8_to_bf16x8(cw[s][g][j], sc);
+            acc[g] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wa, as_bf16x8(av[s][j]), acc[g], 0, 0, 0);
+          }
+        }
+        load(cc + PF * kSWaves, s);
+      }
+    }
+  }
+
+#pragma unroll
+  for (int g = 0; g < RG; ++g)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) red[wave][16 * g + 4 * q + i][rl] = acc[g][i];
+  __syncthreads();
+
+  const int col = threadIdx.x % kSCols;
+  const int r0 = (threadIdx.x / kSCols) * 4;
+  if (col >= mcount) return;
+  float h[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    float sum = red[0][r0 + i][col];
+#pragma unroll
+    for (int w = 1; w < kSWaves; ++w) sum += red[w][r0 + i][col];
+    const int n = n0 + r0 + i;
+    if (bias != nullptr && n < N) sum += bf16_to_f32(bias[(int64_t)e * N + n]);
+    h[i] = sum;
+  }
+  const int64_t r = rbase + m0 + col;
+  if (EPI == kEpiSwigluBf16 || EPI == kEpiActF32) {
+    const int half = N / 2;
+#pragma unroll
+    for (int p = 0; p < 2; ++p) {
+      const int n = n0 + r0 + 2 * p;
+      if (n < N) {
+        const uint16_t ab = f32_to_bf16_rne(swiglu_unit(h[2 * p], h[2 * p + 1], limit, alpha));
+        if (EPI == kEpiSwigluBf16)
+          reinterpret_cast<uint16_t *>(out)[r * half + n / 2] = ab;
+        else
+          reinterpret_cast<float *>(out)[r * half + n / 2] = bf16_to_f32(ab);
+      }
+    }
+  } else {
+    float *o = reinterpret_cast<float *>(out) + r * N + n0 + r0;
+    if (n0 + r0 + 3 < N) {
+      *reinterpret_cast<f32x4_t *>(o) = f32x4_t{h[0], h[1], h[2], h[3]};
+    } else {
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        if (n0 + r0 + i < N) o[i] = h[i];
+    }
+  }
+}
+
 hipError_t launch_ffn_stream(const uint16_t *a_src, bool a_by_token, const int32_t *sorted_slot,
                              int k, const int32_t *offsets, int E, int64_t S, const MxWeight &w,
                              int epilogue, void *out, float limit, float alpha, hipStream_t stream) {
@@ -181,6 +326,31 @@ hipError_t launch_ffn_stream(const uint16_t *a_src, bool a_by_token, const int32
   hipLaunchKernelGGL(ffn_stream_kernel<EPI>, grid, block, 0, stream, a_src, a_by_token ? 1 : 0,    \
                      sorted_slot, k, offsets, E, w.codes, w.scales, w.bias, w.N, w.K, out, limit, \
                      alpha)
+  if (w.tiled) {
+    // m-tile-major 1-D grid; a deeper register prefetch when few slots make few workgroups
+    const int ntn = (w.N + kSRows - 1) / kSRows;
+    dim3 g1((unsigned)(mtiles * ntn));
+    const bool deep = S <= 64;
+#define MOE_LAUNCH_TILED(EPI)                                                                        \
+  do {                                                                                               \
+    if (deep)                                                                                        \
+      hipLaunchKernelGGL((ffn_stream_tiled_kernel<EPI, 2>), g1, block, 0, stream, a_src,            \
+                         a_by_token ? 1 : 0, sorted_slot, k, offsets, E, w.codes, w.scales, w.bias, \
+                         w.N, w.K, ntn, out, limit, alpha);                                         \
+    else                                                                                             \
+      hipLaunchKernelGGL((ffn_stream_tiled_kernel<EPI, 1>), g1, block, 0, stream, a_src,            \
+                         a_by_token ? 1 : 0, sorted_slot, k, offsets, E, w.codes, w.scales, w.bias, \
+                         w.N, w.K, ntn, out, limit, alpha);                                         \
+  } while (0)
+    switch (epilogue) {
+      case kEpiSwigluBf16: MOE_LAUNCH_TILED(kEpiSwigluBf16); break;
+      case kEpiPreactF32: MOE_LAUNCH_TILED(kEpiPreactF32); break;
+      case kEpiActF32: MOE_LAUNCH_TILED(kEpiActF32); break;
+      default: MOE_LAUNCH_TILED(kEpiLinearF32); break;
+    }
+#undef MOE_LAUNCH_TILED
+    return hipGetLastError();
+  }
   switch (epilogue) {
     case kEpiSwigluBf16: MOE_LAUNCH_STREAM(kEpiSwigluBf16); break;
     case kEpiPreactF32: MOE_LAUNCH_STREAM(kEpiPreactF32); break;

@@ -15,20 +15,23 @@ enum FfnEpilogue : int {
 };
 
 struct MxWeight {
-  const uint8_t *codes;   // [E][N][K/2]
-  const uint8_t *scales;  // [E][N][K/32]
+  const uint8_t *codes;   // row-major [E][N][K/2], or tiled (moe_mxfp4_pack)
+  const uint8_t *scales;  // row-major [E][N][K/32], or tiled
   const uint16_t *bias;   // [E][N] bf16 or nullptr
   int N, K;
+  bool tiled;
 };
+
+hipError_t launch_pack(const uint8_t *codes, const uint8_t *scales, int E, int N, int K, uint8_t *pcodes,
+                       uint8_t *pscales, hipStream_t stream);
 
 hipError_t launch_dequant(const uint8_t *codes, const uint8_t *scales, int64_t n, float *out,
                           hipStream_t stream);
 
-hipError_t launch_router_logits(const uint16_t *x, int64_t T, int H, const float *w, const float *b,
-                                int E, float *logits, hipStream_t stream);
-
-hipError_t launch_router_topk(const float *logits, int64_t T, int E, int k, int32_t *topk_idx,
-                              float *topk_w, hipStream_t stream);
+// Router: split-K partial logits into `partial` (router_partial_floats() floats), then top-k.
+size_t router_partial_floats(int64_t T, int E, int H);
+hipError_t launch_router(const uint16_t *x, int64_t T, int H, const float *w, const float *b, int E, int k,
+                         float *partial, int32_t *topk_idx, float *topk_w, hipStream_t stream);
 
 hipError_t launch_permute(const int32_t *topk_idx, int64_t S, int E, int32_t *offsets,
                           int32_t *sorted_slot, int32_t *slot_row, hipStream_t stream);

@@ -28,7 +28,7 @@ bool ws_layout(int64_t T, int E, int k, int H, int I, WsLayout *L) {
   if (T < 0 || E < 1 || k < 1 || H < 1 || I < 1) return false;
   const size_t S = (size_t)T * (size_t)k;
   size_t off = 0;
-  L->logits = off;      off = align_up(off + (size_t)T * E * sizeof(float));
+  L->logits = off;      off = align_up(off + moe::router_partial_floats(T, E, H) * sizeof(float));
   L->topk_idx = off;    off = align_up(off + S * sizeof(int32_t));
   L->topk_w = off;      off = align_up(off + S * sizeof(float));
   L->offsets = off;     off = align_up(off + (size_t)(E + 1) * sizeof(int32_t));
@@ -56,9 +56,16 @@ int check_dim(int64_t d) { return (d >= 32 && d <= kMaxDim && d % 32 == 0) ? MOE
 
 int check_weight(const moe_mxfp4_weight_t *w) {
   if (w == nullptr || w->codes == nullptr || w->scales == nullptr) return MOE_ERR_INVALID_ARG;
+  if (w->layout != MOE_LAYOUT_ROWMAJOR && w->layout != MOE_LAYOUT_TILED) return MOE_ERR_INVALID_ARG;
   if (!aligned(w->codes, 16) || !aligned(w->bias, 2)) return MOE_ERR_INVALID_ARG;
+  if (w->layout == MOE_LAYOUT_TILED && !aligned(w->scales, 4)) return MOE_ERR_INVALID_ARG;
   if (check_dim(w->k) != MOE_OK || w->n < 1 || w->n > 2 * kMaxDim) return MOE_ERR_UNSUPPORTED;
+  if (w->layout == MOE_LAYOUT_TILED && w->n % 16 != 0) return MOE_ERR_UNSUPPORTED;
   return MOE_OK;
+}
+
+moe::MxWeight mx(const moe_mxfp4_weight_t &w) {
+  return moe::MxWeight{w.codes, w.scales, w.bias, w.n, w.k, w.layout == MOE_LAYOUT_TILED};
 }
 
 moe_options_t default_options() {
@@ -85,8 +92,8 @@ int run_ffn(const uint16_t *x, int64_t T, int k, int E, const int32_t *offsets, 
             const moe_mxfp4_weight_t &gu, const moe_mxfp4_weight_t &dn, const moe_options_t &o, float *y,
             uint16_t *act, hipStream_t stream) {
   const int64_t S = T * k;
-  const moe::MxWeight w1{gu.codes, gu.scales, gu.bias, gu.n, gu.k};
-  const moe::MxWeight w2{dn.codes, dn.scales, dn.bias, dn.n, dn.k};
+  const moe::MxWeight w1 = mx(gu);
+  const moe::MxWeight w2 = mx(dn);
   hipError_t err;
   if (o.flags & MOE_FLAG_EMIT_PREACT) {
     err = moe::launch_ffn_stream(x, true, sorted_slot, k, offsets, E, S, w1, moe::kEpiPreactF32, y,
@@ -140,9 +147,8 @@ int forward_impl(const uint16_t *x, const moe_router_t *router, const moe_mxfp4_
   int32_t *slot_row = at<int32_t>(ws, L.slot_row);
   uint16_t *act = at<uint16_t>(ws, L.act);
   float *y = at<float>(ws, L.y);
-  if (moe::launch_router_logits(x, T, H, router->weight, router->bias, E, logits, stream) != hipSuccess)
+  if (moe::launch_router(x, T, H, router->weight, router->bias, E, k, logits, idx, wts, stream) != hipSuccess)
     return MOE_ERR_HIP;
-  if (moe::launch_router_topk(logits, T, E, k, idx, wts, stream) != hipSuccess) return MOE_ERR_HIP;
   if (moe::launch_permute(idx, S, E, offsets, sorted_slot, slot_row, stream) != hipSuccess)
     return MOE_ERR_HIP;
   int st = run_ffn(x, T, k, E, offsets, sorted_slot, *gu, *dn, o, y, act, stream);
@@ -195,6 +201,34 @@ size_t moe_workspace_size(int64_t T, int32_t E, int32_t k, int32_t H, int32_t I,
   return L.total;
 }
 
+int moe_mxfp4_tiled_bytes(int32_t E, int32_t n, int32_t k, size_t *codes_bytes, size_t *scales_bytes) {
+  MOE_GUARD_BEGIN
+  if (E < 1 || E > kMaxExperts || n < 16 || n % 16 != 0 || n > 2 * kMaxDim || check_dim(k) != MOE_OK)
+    return MOE_ERR_UNSUPPORTED;
+  const size_t tiles = (size_t)E * (size_t)(n / 16) * (size_t)((k / 32 + 3) / 4);
+  if (codes_bytes) *codes_bytes = tiles * 1024;
+  if (scales_bytes) *scales_bytes = tiles * 64;
+  return MOE_OK;
+  MOE_GUARD_END
+}
+
+int moe_mxfp4_pack(const moe_mxfp4_weight_t *src, int32_t E, uint8_t *codes_out, uint8_t *scales_out,
+                   moe_stream_t stream) {
+  MOE_GUARD_BEGIN
+  if (src == nullptr || codes_out == nullptr || scales_out == nullptr) return MOE_ERR_INVALID_ARG;
+  if (src->layout != MOE_LAYOUT_ROWMAJOR) return MOE_ERR_INVALID_ARG;
+  int st = check_weight(src);
+  if (st != MOE_OK) return st;
+  size_t cb = 0, sb = 0;
+  if ((st = moe_mxfp4_tiled_bytes(E, src->n, src->k, &cb, &sb)) != MOE_OK) return st;
+  if (!aligned(codes_out, 16) || !aligned(scales_out, 16)) return MOE_ERR_INVALID_ARG;
+  return moe::launch_pack(src->codes, src->scales, E, src->n, src->k, codes_out, scales_out,
+                          (hipStream_t)stream) == hipSuccess
+             ? MOE_OK
+             : MOE_ERR_HIP;
+  MOE_GUARD_END
+}
+
 int moe_mxfp4_dequant(const uint8_t *codes, const uint8_t *scales, int64_t n, float *out,
                       moe_stream_t stream) {
   MOE_GUARD_BEGIN
@@ -224,11 +258,10 @@ int moe_route(const uint16_t *x, int64_t T, int32_t H, const moe_router_t *route
   if (ws == nullptr || ws_bytes < L.total) return MOE_ERR_WORKSPACE;
   if (!aligned(ws, kWsAlign)) return MOE_ERR_INVALID_ARG;
   float *logits = at<float>(ws, L.logits);
-  hipStream_t s = (hipStream_t)stream;
-  if (moe::launch_router_logits(x, T, H, router->weight, router->bias, E, logits, s) != hipSuccess)
-    return MOE_ERR_HIP;
-  return moe::launch_router_topk(logits, T, E, k, topk_idx, topk_w, s) == hipSuccess ? MOE_OK
-                                                                                      : MOE_ERR_HIP;
+  return moe::launch_router(x, T, H, router->weight, router->bias, E, k, logits, topk_idx, topk_w,
+                            (hipStream_t)stream) == hipSuccess
+             ? MOE_OK
+             : MOE_ERR_HIP;
   MOE_GUARD_END
 }
 

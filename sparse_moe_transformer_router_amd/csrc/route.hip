@@ -2,62 +2,87 @@
 // over their logits (review of the from-scratch gpt-oss-20B at pomoai.com, section 3.4: a
 // linear projection plus top-k, outputs weighted by softmax-normalised scores; gpt-oss
 // walkthrough at pnsm.cn, section 2.2: top-4 with softmax weighting of the picked experts).
+//
+// Logits on the matrix cores: x is bf16, and each fp32 router weight w is split exactly into
+// three bf16 terms (hi = w with its low 16 bits cleared, mid = the same of w - hi, lo = the
+// rest, which has at most 8 significant bits), so every product x * term is exact and
+// v_mfma_f32_16x16x32_bf16 accumulates them in fp32. The input dimension is split across
+// waves (split-K) when there are few tokens, so decode batches still spread over the chip;
+// the partial sums are added in a fixed order by the top-k kernel.
 #include "common.h"
 #include "kernels.h"
 
 namespace moe {
 
-constexpr int kRouteTok = 4;  // tokens per wave in the logits kernel
+__device__ __forceinline__ void split3(const f32x4_t &a, const f32x4_t &b, bf16x8_t &hi, bf16x8_t &mid,
+                                       bf16x8_t &lo) {
+  u32x4_t h, m, l;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const float w0 = (i < 2) ? a[2 * i] : b[2 * i - 4];
+    const float w1 = (i < 2) ? a[2 * i + 1] : b[2 * i - 3];
+    const uint32_t h0 = __float_as_uint(w0) & 0xffff0000u, h1 = __float_as_uint(w1) & 0xffff0000u;
+    const float r0 = w0 - __uint_as_float(h0), r1 = w1 - __uint_as_float(h1);  // exact
+    const uint32_t m0 = __float_as_uint(r0) & 0xffff0000u, m1 = __float_as_uint(r1) & 0xffff0000u;
+    const float s0 = r0 - __uint_as_float(m0), s1 = r1 - __uint_as_float(m1);  // exact, <= 8 bits
+    h[i] = (h0 >> 16) | h1;
+    m[i] = (m0 >> 16) | m1;
+    l[i] = (__float_as_uint(s0) >> 16) | (__float_as_uint(s1) & 0xffff0000u);
+  }
+  hi = as_bf16x8(h);
+  mid = as_bf16x8(m);
+  lo = as_bf16x8(l);
+}
 
-// One wave computes the logits of kRouteTok consecutive tokens for one expert. Lane l
-// accumulates 8 consecutive features at a time; the wave then reduces its lanes.
-__global__ __launch_bounds__(256) void router_logits_kernel(const uint16_t *__restrict__ x, int64_t T,
-                                                            int H, const float *__restrict__ w,
-                                                            const float *__restrict__ b, int E,
-                                                            float *__restrict__ logits) {
-  const int wave = threadIdx.x / kWave, lane = threadIdx.x % kWave;
-  const int e = blockIdx.y * 4 + wave;
-  const int64_t t0 = (int64_t)blockIdx.x * kRouteTok;
-  if (e >= E) return;
-  const float *wr = w + (int64_t)e * H;
-  float acc[kRouteTok];
-#pragma unroll
-  for (int i = 0; i < kRouteTok; ++i) acc[i] = 0.f;
-  for (int h = lane * 8; h < H; h += kWave * 8) {
-    const f32x4_t w0 = *reinterpret_cast<const f32x4_t *>(wr + h);
-    const f32x4_t w1 = *reinterpret_cast<const f32x4_t *>(wr + h + 4);
-#pragma unroll
-    for (int i = 0; i < kRouteTok; ++i) {
-      if (t0 + i < T) {
-        const u32x4_t xv = *reinterpret_cast<const u32x4_t *>(x + (t0 + i) * H + h);
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          const float lo = __uint_as_float(xv[q] << 16);
-          const float hi = __uint_as_float(xv[q] & 0xffff0000u);
-          const float wl = (q < 2) ? w0[2 * q] : w1[2 * q - 4];
-          const float wh = (q < 2) ? w0[2 * q + 1] : w1[2 * q - 3];
-          acc[i] = fmaf(lo, wl, acc[i]);
-          acc[i] = fmaf(hi, wh, acc[i]);
-        }
-      }
+constexpr int kMaxSplitVec = 12;  // at most 48 splits, read as 12 float4 per logit
+
+// One wave: 16 tokens x 16 experts over the MX-block range of split blockIdx.z.
+// Writes partial[(t * E + e) * nsp + split] (nsp = split count rounded up to 4).
+__global__ __launch_bounds__(kWave) void router_partial_kernel(const uint16_t *__restrict__ x, int64_t T,
+                                                               int H, const float *__restrict__ w, int E,
+                                                               int blocks_per_split, int nsp,
+                                                               float *__restrict__ partial) {
+  const int lane = threadIdx.x;
+  const int64_t t0 = (int64_t)blockIdx.x * 16;
+  const int e0 = blockIdx.y * 16;
+  const int split = blockIdx.z;
+  const int KB = H / 32;
+  const int b0 = split * blocks_per_split;
+  const int b1 = (b0 + blocks_per_split < KB) ? b0 + blocks_per_split : KB;
+  const int r = lane % 16, q = lane / 16;
+  const bool t_ok = t0 + r < T, e_ok = e0 + r < E;
+  const uint16_t *xp = x + (t_ok ? (t0 + r) : 0) * H + 8 * q;
+  const float *wp = w + (int64_t)(e_ok ? (e0 + r) : 0) * H + 8 * q;
+  f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
+  for (int b = b0; b < b1; ++b) {
+    const u32x4_t xa = t_ok ? *reinterpret_cast<const u32x4_t *>(xp + 32 * b) : u32x4_t{0u, 0u, 0u, 0u};
+    f32x4_t wa = {0.f, 0.f, 0.f, 0.f}, wb = {0.f, 0.f, 0.f, 0.f};
+    if (e_ok) {
+      wa = *reinterpret_cast<const f32x4_t *>(wp + 32 * b);
+      wb = *reinterpret_cast<const f32x4_t *>(wp + 32 * b + 4);
     }
+    bf16x8_t hi, mid, lo;
+    split3(wa, wb, hi, mid, lo);
+    const bf16x8_t xb = as_bf16x8(xa);
+    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xb, lo, acc, 0, 0, 0);
+    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xb, mid, acc, 0, 0, 0);
+    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xb, hi, acc, 0, 0, 0);
   }
+  // lane holds tokens t0 + 4q + i, expert e0 + r
+  if (e_ok) {
 #pragma unroll
-  for (int i = 0; i < kRouteTok; ++i) {
-#pragma unroll
-    for (int d = kWave / 2; d >= 1; d >>= 1) acc[i] += __shfl_xor(acc[i], d, kWave);
-  }
-  if (lane == 0) {
-    const float be = b ? b[e] : 0.f;
-#pragma unroll
-    for (int i = 0; i < kRouteTok; ++i)
-      if (t0 + i < T) logits[(t0 + i) * E + e] = acc[i] + be;
+    for (int i = 0; i < 4; ++i) {
+      const int64_t t = t0 + 4 * q + i;
+      if (t < T) partial[(t * E + e0 + r) * nsp + split] = acc[i];
+    }
   }
 }
 
-// One wave per token: k rounds of a wave-wide argmax (larger logit wins, equal logits go to
-// the lower expert id), then softmax over the k picked logits.
-__global__ __launch_bounds__(256) void router_topk_kernel(const float *__restrict__ logits, int64_t T,
+// One wave per token: sum the split partials in order and add the bias, then k rounds of a
+// wave-wide argmax (larger logit wins, equal logits go to the lower expert id), then softmax
+// over the k picked logits.
+__global__ __launch_bounds__(256) void router_topk_kernel(const float *__restrict__ partial, int nsplit,
+                                                          int nsp, const float *__restrict__ bias, int64_t T,
                                                           int E, int k, int32_t *__restrict__ topk_idx,
                                                           float *__restrict__ topk_w) {
   const int lane = threadIdx.x % kWave;
@@ -68,64 +93,103 @@ __global__ __launch_bounds__(256) void router_topk_kernel(const float *__restric
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     const int e = lane + i * kWave;
-    v[i] = (e < E) ? logits[t * E + e] : 0.f;
-    if (e >= E) taken |= 1 << i;
+    float s = 0.f;
+    if (e < E) {
+      // every split's partial of this logit is contiguous: issue all loads, then add in order
+      const f32x4_t *p = reinterpret_cast<const f32x4_t *>(partial + (t * E + e) * nsp);
+      f32x4_t pv[kMaxSplitVec];
+#pragma unroll
+      for (int c = 0; c < kMaxSplitVec; ++c) pv[c] = (4 * c < nsplit) ? p[c] : f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int c = 0; c < kMaxSplitVec; ++c)
+#pragma unroll
+        for (int u = 0; u < 4; ++u)
+          if (4 * c + u < nsplit) s += pv[c][u];
+      if (bias) s += bias[e];
+    } else {
+      taken |= 1 << i;
+    }
+    v[i] = s;
   }
   float sel_v[8];
   int sel_e[8];
-  for (int j = 0; j < k; ++j) {
-    float bv = 0.f;
-    int be = 0x7fffffff;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {  // lane-local best; ids ascend with i, so '>' keeps the lower id
-      const int e = lane + i * kWave;
-      if (!(taken & (1 << i)) && (be == 0x7fffffff || v[i] > bv)) {
-        bv = v[i];
-        be = e;
-      }
-    }
+  for (int j = 0; j < 8; ++j) {
+    sel_v[j] = 0.f;
+    sel_e[j] = 0;
+    if (j < k) {
+      float bv = 0.f;
+      int be = 0x7fffffff;
 #pragma unroll
-    for (int d = kWave / 2; d >= 1; d >>= 1) {
-      const float ov = __shfl_xor(bv, d, kWave);
-      const int oe = __shfl_xor(be, d, kWave);
-      const bool other = (oe != 0x7fffffff) &&
-                         (be == 0x7fffffff || ov > bv || (ov == bv && oe < be));
-      if (other) {
-        bv = ov;
-        be = oe;
+      for (int i = 0; i < 4; ++i) {  // ids ascend with i, so '>' keeps the lower id on ties
+        if (!(taken & (1 << i)) && (be == 0x7fffffff || v[i] > bv)) {
+          bv = v[i];
+          be = lane + i * kWave;
+        }
       }
+#pragma unroll
+      for (int d = kWave / 2; d >= 1; d >>= 1) {
+        const float ov = __shfl_xor(bv, d, kWave);
+        const int oe = __shfl_xor(be, d, kWave);
+        if (oe != 0x7fffffff && (be == 0x7fffffff || ov > bv || (ov == bv && oe < be))) {
+          bv = ov;
+          be = oe;
+        }
+      }
+      sel_v[j] = bv;
+      sel_e[j] = be;
+      if ((be % kWave) == lane) taken |= 1 << (be / kWave);
     }
-    sel_v[j] = bv;
-    sel_e[j] = be;
-    if ((be % kWave) == lane) taken |= 1 << (be / kWave);
   }
   if (lane == 0) {
-    const float m = sel_v[0];
     float z[8], sum = 0.f;
-    for (int j = 0; j < k; ++j) {
-      z[j] = expf(sel_v[j] - m);
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      z[j] = (j < k) ? expf(sel_v[j] - sel_v[0]) : 0.f;
       sum += z[j];
     }
     const float inv = 1.0f / sum;
-    for (int j = 0; j < k; ++j) {
-      topk_idx[t * k + j] = sel_e[j];
-      topk_w[t * k + j] = z[j] * inv;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      if (j < k) {
+        topk_idx[t * k + j] = sel_e[j];
+        topk_w[t * k + j] = z[j] * inv;
+      }
     }
   }
 }
 
-hipError_t launch_router_logits(const uint16_t *x, int64_t T, int H, const float *w, const float *b,
-                                int E, float *logits, hipStream_t stream) {
-  dim3 grid((unsigned)((T + kRouteTok - 1) / kRouteTok), (unsigned)((E + 3) / 4));
-  hipLaunchKernelGGL(router_logits_kernel, grid, dim3(256), 0, stream, x, T, H, w, b, E, logits);
-  return hipGetLastError();
+// Split count for the router's input dimension: enough waves to spread a decode batch over
+// the chip (a few hundred), at most 4 * kMaxSplitVec, at least 2 MX blocks per split.
+int router_splits(int64_t T, int E, int H) {
+  const int64_t tiles = ((T + 15) / 16) * ((E + 15) / 16);
+  const int KB = H / 32;
+  if (tiles <= 0 || KB < 2) return 1;
+  int64_t s = (512 + tiles - 1) / tiles;
+  if (s > KB / 2) s = KB / 2;
+  if (s > 4 * kMaxSplitVec) s = 4 * kMaxSplitVec;
+  if (s < 1) s = 1;
+  const int bps = (KB + (int)s - 1) / (int)s;
+  return (KB + bps - 1) / bps;
 }
 
-hipError_t launch_router_topk(const float *logits, int64_t T, int E, int k, int32_t *topk_idx,
-                              float *topk_w, hipStream_t stream) {
-  dim3 grid((unsigned)((T + 3) / 4));
-  hipLaunchKernelGGL(router_topk_kernel, grid, dim3(256), 0, stream, logits, T, E, k, topk_idx,
-                     topk_w);
+size_t router_partial_floats(int64_t T, int E, int H) {
+  const int nsp = (router_splits(T, E, H) + 3) / 4 * 4;
+  return (size_t)nsp * T * E;
+}
+
+hipError_t launch_router(const uint16_t *x, int64_t T, int H, const float *w, const float *b, int E, int k,
+                         float *partial, int32_t *topk_idx, float *topk_w, hipStream_t stream) {
+  const int KB = H / 32;
+  const int ns = router_splits(T, E, H);
+  const int bps = (KB + ns - 1) / ns;
+  const int nsp = (ns + 3) / 4 * 4;
+  dim3 grid((unsigned)((T + 15) / 16), (unsigned)((E + 15) / 16), (unsigned)ns);
+  hipLaunchKernelGGL(router_partial_kernel, grid, dim3(kWave), 0, stream, x, T, H, w, E, bps, nsp, partial);
+  hipError_t err = hipGetLastError();
+  if (err != hipSuccess) return err;
+  hipLaunchKernelGGL(router_topk_kernel, dim3((unsigned)((T + 3) / 4)), dim3(256), 0, stream, partial, ns, nsp, b,
+                     T, E, k, topk_idx, topk_w);
   return hipGetLastError();
 }
 

@@ -17,22 +17,26 @@ from . import _lib as L
 
 @dataclasses.dataclass
 class MXFP4Weight:
-    """One MXFP4 matrix for all experts: codes uint8 [E][n][k/2], scales uint8 [E][n][k/32],
+    """One MXFP4 matrix for all experts. Row-major: codes uint8 [E][n][k/2], scales uint8
+    [E][n][k/32]; tiled (from moe_mxfp4_pack): flat uint8 buffers, with n and k given.
     bias bf16 [E][n] or None."""
     codes: torch.Tensor
     scales: torch.Tensor
     bias: Optional[torch.Tensor]
+    layout: int = L.MOE_LAYOUT_ROWMAJOR
+    shape_nk: Optional[Tuple[int, int]] = None  # (n, k) for the tiled layout
 
     @property
     def n(self) -> int:
-        return int(self.codes.shape[1])
+        return self.shape_nk[0] if self.shape_nk else int(self.codes.shape[1])
 
     @property
     def k(self) -> int:
-        return int(self.codes.shape[2]) * 2
+        return self.shape_nk[1] if self.shape_nk else int(self.codes.shape[2]) * 2
 
     def desc(self) -> L.MoeMxfp4Weight:
-        return L.MoeMxfp4Weight(_ptr(self.codes), _ptr(self.scales), _ptr(self.bias), self.n, self.k)
+        return L.MoeMxfp4Weight(_ptr(self.codes), _ptr(self.scales), _ptr(self.bias), self.n, self.k,
+                                self.layout)
 
 
 @dataclasses.dataclass
@@ -88,6 +92,24 @@ def workspace(T: int, E: int, k: int, H: int, I: int, path: int = L.MOE_PATH_AUT
     if n == 0:
         raise ValueError("invalid sizes for a workspace")
     return torch.empty(n, dtype=torch.uint8, device=device or "cuda")
+
+
+def moe_mxfp4_tiled_bytes(E: int, n: int, k: int) -> Tuple[int, int]:
+    cb, sb = ctypes.c_size_t(0), ctypes.c_size_t(0)
+    L.check("moe_mxfp4_tiled_bytes", L.lib().moe_mxfp4_tiled_bytes(E, n, k, ctypes.byref(cb), ctypes.byref(sb)))
+    return cb.value, sb.value
+
+
+def moe_mxfp4_pack(w: MXFP4Weight, stream=None) -> MXFP4Weight:
+    """A tiled copy of a row-major weight (new device buffers; the bias tensor is shared)."""
+    E = int(w.codes.shape[0])
+    cb, sb = moe_mxfp4_tiled_bytes(E, w.n, w.k)
+    codes = torch.empty(cb, dtype=torch.uint8, device=w.codes.device)
+    scales = torch.empty(sb, dtype=torch.uint8, device=w.codes.device)
+    d = w.desc()
+    L.check("moe_mxfp4_pack", L.lib().moe_mxfp4_pack(ctypes.byref(d), E, _ptr(codes), _ptr(scales),
+                                                        _stream(stream)))
+    return MXFP4Weight(codes, scales, w.bias, L.MOE_LAYOUT_TILED, (w.n, w.k))
 
 
 def moe_mxfp4_dequant(codes: torch.Tensor, scales: torch.Tensor, out: Optional[torch.Tensor] = None,

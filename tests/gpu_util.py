@@ -55,14 +55,31 @@ class DevLayer:
         return self.inp.cfg.E
 
 
-def device_layer(inp: synth.MoEInputs, with_bias: bool = True) -> DevLayer:
+def device_layer(inp: synth.MoEInputs, with_bias: bool = True, tiled: bool = False) -> DevLayer:
     x = to_dev_bf16(inp.x)
     router = moe.Router(to_dev_f32(inp.router_w), to_dev_f32(inp.router_b))
     w1 = moe.MXFP4Weight(to_dev_u8(inp.w1_codes), to_dev_u8(inp.w1_scales),
                          to_dev_bf16(inp.w1_bias) if with_bias else None)
     w2 = moe.MXFP4Weight(to_dev_u8(inp.w2_codes), to_dev_u8(inp.w2_scales),
                          to_dev_bf16(inp.w2_bias) if with_bias else None)
+    if tiled:
+        w1, w2 = moe.moe_mxfp4_pack(w1), moe.moe_mxfp4_pack(w2)
     return DevLayer(inp, x, router, w1, w2)
+
+
+def tiled_reference(codes: np.ndarray, scales: np.ndarray):
+    """The tiled layout re-derived with numpy reshapes, independently of the library."""
+    E, N, KH = codes.shape
+    KB = scales.shape[2]
+    nchunk = (KB + 3) // 4
+    c = np.zeros((E, N, nchunk * 64), np.uint8)
+    c[:, :, :KH] = codes
+    sc = np.full((E, N, nchunk * 4), 127, np.uint8)
+    sc[:, :, :KB] = scales
+    # row bytes of a chunk: 16 j + 4 q + b; tile order: e, g, c, lane (q, r), j, b
+    c = c.reshape(E, N // 16, 16, nchunk, 4, 4, 4).transpose(0, 1, 3, 5, 2, 4, 6)
+    sc = sc.reshape(E, N // 16, 16, nchunk, 4).transpose(0, 1, 3, 2, 4)
+    return np.ascontiguousarray(c).reshape(-1), np.ascontiguousarray(sc).reshape(-1)
 
 
 def oracle_experts(inp: synth.MoEInputs, with_bias: bool = True):

@@ -94,6 +94,18 @@ def test_permute(T, E, k, mode):
     assert np.array_equal(sr.cpu().numpy(), r_sr)
 
 
+@pytest.mark.parametrize("E,N,K", [(2, 64, 256), (3, 5760, 2880), (1, 48, 96), (2, 16, 32)])
+def test_pack_tiled_layout(E, N, K):
+    rng = np.random.default_rng(E * N + K)
+    codes = rng.integers(0, 256, (E, N, K // 2), dtype=np.uint8)
+    scales = rng.integers(0, 256, (E, N, K // 32), dtype=np.uint8)
+    w = moe.MXFP4Weight(gu.to_dev_u8(codes), gu.to_dev_u8(scales), None)
+    t = moe.moe_mxfp4_pack(w)
+    rc, rs = gu.tiled_reference(codes, scales)
+    assert np.array_equal(t.codes.cpu().numpy(), rc)
+    assert np.array_equal(t.scales.cpu().numpy(), rs)
+
+
 # ------------------------------------------------------------------ a4: in-kernel decode
 def _ffn_inputs(E, H, I, scale_lo, scale_hi, seed):
     rng = np.random.default_rng(seed)
@@ -104,8 +116,9 @@ def _ffn_inputs(E, H, I, scale_lo, scale_hi, seed):
     return w1c, w1s, w2c, w2s
 
 
+@pytest.mark.parametrize("tiled", [False, True])
 @pytest.mark.parametrize("scale_lo,scale_hi", [(4, 252), (123, 127)])
-def test_ffn_preact_identity_decode(scale_lo, scale_hi):
+def test_ffn_preact_identity_decode(scale_lo, scale_hi, tiled):
     """One-hot activations and no bias: h = W1 x is one decoded weight column, exactly."""
     E, H, I, k = 3, 128, 96, 1
     w1c, w1s, w2c, w2s = _ffn_inputs(E, H, I, scale_lo, scale_hi, 11)
@@ -116,6 +129,8 @@ def test_ffn_preact_identity_decode(scale_lo, scale_hi):
     _, off, ss, sr = oracle.permute(idx, E)
     w1 = moe.MXFP4Weight(gu.to_dev_u8(w1c), gu.to_dev_u8(w1s), None)
     w2 = moe.MXFP4Weight(gu.to_dev_u8(w2c), gu.to_dev_u8(w2s), None)
+    if tiled:
+        w1, w2 = moe.moe_mxfp4_pack(w1), moe.moe_mxfp4_pack(w2)
     y = moe.moe_mxfp4_ffn(gu.to_dev_bf16(x), k, E, torch.from_numpy(off).cuda(), torch.from_numpy(ss).cuda(),
                           w1, w2, moe.Options(flags=moe.MOE_FLAG_EMIT_PREACT)).cpu().numpy()
     for e in range(E):
@@ -126,11 +141,12 @@ def test_ffn_preact_identity_decode(scale_lo, scale_hi):
             assert np.array_equal(y[r], W1[:, t]), (e, t)
 
 
-def test_ffn_activation_step():
+@pytest.mark.parametrize("tiled", [False, True])
+def test_ffn_activation_step(tiled):
     """Stop after the SwiGLU: the bf16-rounded activation of every slot."""
     cfg = synth.get_config("tiny").with_(scale_bytes=(118, 122))
     inp = synth.make_inputs(cfg)
-    dev = gu.device_layer(inp)
+    dev = gu.device_layer(inp, tiled=tiled)
     res = gu.oracle_forward(inp, None, keep_intermediates=True)
     idx = res.idx
     _, off, ss, sr = oracle.permute(idx, cfg.E)
@@ -154,8 +170,8 @@ def _gpu_idx(dev):
     return idx.cpu().numpy()
 
 
-def _check_layer(inp, tokens=None, path=0):
-    dev = gu.device_layer(inp)
+def _check_layer(inp, tokens=None, path=0, tiled=True):
+    dev = gu.device_layer(inp, tiled=tiled)
     gidx = _gpu_idx(dev)
     ref = gu.oracle_forward(inp, gidx, tokens=tokens)
     tok = ref.tokens
@@ -171,8 +187,9 @@ def _check_layer(inp, tokens=None, path=0):
     return rel32, rel16
 
 
-def test_layer_tiny():
-    _check_layer(synth.make_inputs(synth.get_config("tiny")))
+@pytest.mark.parametrize("tiled", [False, True])
+def test_layer_tiny(tiled):
+    _check_layer(synth.make_inputs(synth.get_config("tiny")), tiled=tiled)
 
 
 @pytest.mark.parametrize("scales", [(123, 127), (118, 121), (121, 124)])
@@ -194,10 +211,11 @@ def test_layer_tiny_alpha_limit():
         gu.check_output(out, ref.out, bf16=False)
 
 
+@pytest.mark.parametrize("tiled", [False, True])
 @pytest.mark.parametrize("T", [1, 8, 32, 64])
-def test_layer_decode20b(T):
+def test_layer_decode20b(T, tiled):
     cfg = synth.get_config("decode20b")
-    _check_layer(synth.make_inputs(cfg, T))
+    _check_layer(synth.make_inputs(cfg, T), tiled=tiled)
 
 
 @pytest.mark.parametrize("T", [1, 16, 64, 256])
@@ -225,10 +243,11 @@ def _small_cfg(E, k, H=128, I=96, T=24, seed=31, scales=(119, 123)):
     return synth.LayerConfig("edge", (T,), H, I, E, k, seed, scale_bytes=scales)
 
 
+@pytest.mark.parametrize("tiled", [False, True])
 @pytest.mark.parametrize("E,k,H,I,T", [(4, 4, 128, 96, 9), (16, 1, 64, 64, 33), (16, 8, 96, 160, 21),
                                        (256, 4, 64, 32, 40), (8, 2, 32, 32, 1), (2, 1, 160, 96, 70)])
-def test_layer_shapes(E, k, H, I, T):
-    _check_layer(synth.make_inputs(_small_cfg(E, k, H, I, T)))
+def test_layer_shapes(E, k, H, I, T, tiled):
+    _check_layer(synth.make_inputs(_small_cfg(E, k, H, I, T)), tiled=tiled)
 
 
 def test_layer_all_tokens_one_group():

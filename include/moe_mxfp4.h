@@ -56,7 +56,9 @@ extern "C" {
 /* expert-FFN kernel family */
 #define MOE_PATH_AUTO 0    /* chosen from T*k and E on the host */
 #define MOE_PATH_STREAM 1  /* weight-streaming kernels for decode-sized batches */
-#define MOE_PATH_GEMM 2    /* LDS-tiled grouped GEMM for prefill-sized batches */
+#define MOE_PATH_GEMM 2    /* LDS-tiled grouped GEMM for prefill-sized batches; needs
+                              MOE_LAYOUT_TILED weights (else MOE_ERR_UNSUPPORTED). AUTO picks it
+                              for tiled weights when T*k >= 48*E. */
 
 /* moe_mxfp4_weight_t.layout */
 #define MOE_LAYOUT_ROWMAJOR 0 /* codes [E][n][k/2], scales [E][n][k/32] as described below */
@@ -86,7 +88,7 @@ typedef struct moe_router {
  * For the gate_up matrix n = 2I with rows interleaved: row 2i is unit i's gate, row
  * 2i+1 its linear branch; k = H. For the down matrix n = H, k = I.
  * layout MOE_LAYOUT_TILED: codes and scales hold the same values re-ordered by
- * moe_mxfp4_pack into 16-row x 128-element tiles (see there); bias is unchanged.
+ * moe_mxfp4_pack into 32-row x 128-element tiles (see there); bias is unchanged.
  */
 typedef struct moe_mxfp4_weight {
   const uint8_t *codes;
@@ -131,20 +133,20 @@ int moe_mxfp4_dequant(const uint8_t *codes, const uint8_t *scales, int64_t n, fl
 
 /*
  * Bytes of the tiled copies of one MXFP4 matrix (E experts, n x k each) that
- * moe_mxfp4_pack writes: *codes_bytes = E * (n/16) * ceil(k/128) * 1024 and
- * *scales_bytes = E * (n/16) * ceil(k/128) * 64. Returns MOE_ERR_UNSUPPORTED unless
- * n is a positive multiple of 16 and k a positive multiple of 32.
+ * moe_mxfp4_pack writes: *codes_bytes = E * (n/32) * ceil(k/128) * 2048 and
+ * *scales_bytes = E * (n/32) * ceil(k/128) * 128. Returns MOE_ERR_UNSUPPORTED unless
+ * n is a positive multiple of 32 and k a positive multiple of 32.
  */
 int moe_mxfp4_tiled_bytes(int32_t E, int32_t n, int32_t k, size_t *codes_bytes, size_t *scales_bytes);
 
 /*
  * Re-order a row-major MXFP4 matrix (src->layout must be MOE_LAYOUT_ROWMAJOR) into the
  * tiled kernel layout, on the device. A one-time, load-time conversion: the values and
- * their MX blocks are unchanged, only their order in memory. Tile (g, c) of expert e covers
- * rows 16g..16g+15 and elements 128c..128c+127 and is stored as 64 lanes x 16 bytes
- * (lane l = r + 16q: for j = 0..3 its bytes 4j..4j+3 are bytes 16j+4q..16j+4q+3 of row
- * 16g+r's 64-byte run of chunk c), followed in the scales array by 16 rows x 4 scale bytes
- * (blocks 4c..4c+3). Elements past k are zero codes with scale 127.
+ * their MX blocks are unchanged, only their order in memory. Tile (G, c) of expert e covers
+ * rows 32G..32G+31 and elements 128c..128c+127 (MX blocks 4c..4c+3) and is stored as two
+ * 1 KB halves p = 0, 1 of 64 lanes x 16 bytes, lane l holding the 16 code bytes of block
+ * 4c + 2p + l/32 of row 32G + l%32; the scales array holds 32 rows x 4 scale bytes (blocks
+ * 4c..4c+3) per tile. Elements past k are zero codes with scale 127. Requires n % 32 == 0.
  * codes_out / scales_out: device buffers of moe_mxfp4_tiled_bytes() bytes, 16-byte aligned.
  */
 int moe_mxfp4_pack(const moe_mxfp4_weight_t *src, int32_t E, uint8_t *codes_out, uint8_t *scales_out,

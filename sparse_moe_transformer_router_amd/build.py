@@ -29,6 +29,7 @@ SOURCES = [
     "route.hip",
     "permute.hip",
     "ffn_stream.hip",
+    "ffn_gemm.hip",
     "pack.hip",
     "combine.hip",
 ]

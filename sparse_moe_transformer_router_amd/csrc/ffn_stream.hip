@@ -170,23 +170,28 @@ __global__ __launch_bounds__(kSWaves *kWave) void ffn_stream_kernel(
 }
 
 // ---------------------------------------------------------------------------------------
-// Same product on the tiled weight layout (moe_mxfp4_pack): every weight load is one
-// contiguous 1 KB tile per wave, one MFMA step is one MX block, and a lane's activation
-// loads for a step cover 64 contiguous bytes of one token. Workgroup tiles are numbered
-// m-tile-major along a 1-D grid, so consecutive workgroups stream consecutive row tiles of
-// the same expert. PF = chunks of register prefetch per wave.
+// Same product on the tiled weight layout (moe_mxfp4_pack), on v_mfma_f32_32x32x16_bf16 (which
+// issues at twice the rate of the 16x16x32 form on gfx950): a workgroup owns 64 weight rows
+// (two 32-row tiles) of one expert and up to 32 of its slots; four waves split the chunks.
+// Every weight load is one contiguous 1 KB per wave; a lane's two 16-byte loads per tile and
+// chunk are MX blocks 4c + 2p + lane/32 (p = 0, 1) of row lane%32, each split into four
+// 8-element MFMA k-steps; the slot activations for a step are read with the same
+// k-assignment (64 contiguous bytes per lane and block). PF = chunks of register prefetch.
+constexpr int kTRows = 64;   // weight rows per workgroup (two 32-row tiles)
+constexpr int kTCols = 32;   // slots per m-tile
+
 template <int EPI, int PF>
 __global__ __launch_bounds__(kSWaves *kWave) void ffn_stream_tiled_kernel(
     const uint16_t *__restrict__ a_src, int a_by_token, const int32_t *__restrict__ sorted_slot, int k,
     const int32_t *__restrict__ offsets, int E, const uint8_t *__restrict__ pcodes,
     const uint8_t *__restrict__ pscales, const uint16_t *__restrict__ bias, int N, int K, int ntiles_n,
     void *__restrict__ out, float limit, float alpha) {
-  constexpr int RG = kSRows / 16;
-  __shared__ float red[kSWaves][kSRows][kSCols + 1];
+  constexpr int RG = kTRows / 32;
+  __shared__ float red[kSWaves][kTRows][kTCols + 1];
   const int wave = threadIdx.x / kWave, lane = threadIdx.x % kWave;
   const int mt = blockIdx.x / ntiles_n, nt = blockIdx.x % ntiles_n;
   const int g0 = nt * RG;
-  const int n0 = nt * kSRows;
+  const int n0 = nt * kTRows;
 
   int e = -1, m0 = 0, rbase = 0, mcount = 0;
   {
@@ -194,7 +199,7 @@ __global__ __launch_bounds__(kSWaves *kWave) void ffn_stream_tiled_kernel(
     for (int eb = 0; eb < E; eb += kWave) {
       const int ex = eb + lane;
       const int cnt = (ex < E) ? offsets[ex + 1] - offsets[ex] : 0;
-      const int tiles = (cnt + kSCols - 1) / kSCols;
+      const int tiles = (cnt + kTCols - 1) / kTCols;
       const int inc = wave_inclusive_scan(tiles);
       const int excl = inc - tiles + carry;
       const uint64_t hit = __ballot(tiles > 0 && mt >= excl && mt < excl + tiles);
@@ -202,10 +207,10 @@ __global__ __launch_bounds__(kSWaves *kWave) void ffn_stream_tiled_kernel(
         const int src = __ffsll((unsigned long long)hit) - 1;
         const int sel_excl = __shfl(excl, src, kWave);
         e = eb + src;
-        m0 = (mt - sel_excl) * kSCols;
+        m0 = (mt - sel_excl) * kTCols;
         rbase = offsets[e];
         const int cnt_e = offsets[e + 1] - rbase;
-        mcount = (cnt_e - m0 < kSCols) ? cnt_e - m0 : kSCols;
+        mcount = (cnt_e - m0 < kTCols) ? cnt_e - m0 : kTCols;
         break;
       }
       carry += __shfl(inc, kWave - 1, kWave);
@@ -213,40 +218,46 @@ __global__ __launch_bounds__(kSWaves *kWave) void ffn_stream_tiled_kernel(
   }
   if (e < 0) return;
 
-  const int rl = lane % 16, q = lane / 16;
-  const bool col_ok = rl < mcount;
+  const int r32 = lane % 32, kh = lane / 32;
+  const bool col_ok = r32 < mcount;
   const uint16_t *arow = a_src;
   if (col_ok) {
-    const int r = rbase + m0 + rl;
+    const int r = rbase + m0 + r32;
     arow = a_src + (a_by_token ? (int64_t)(sorted_slot[r] / k) : (int64_t)r) * K;
   }
   const int KB = K / 32;
   const int nchunk = (KB + 3) / 4;
-  const int NG = N / 16;
-  const uint8_t *cbase = pcodes + (int64_t)e * NG * nchunk * 1024 + lane * 16;
-  const uint8_t *sbase = pscales + (int64_t)e * NG * nchunk * 64 + rl * 4;
-  const uint16_t *ap = arow + q * 8;
+  const int NG = N / 32;
+  const uint8_t *cbase = pcodes + (int64_t)e * NG * nchunk * 2048 + lane * 16;
+  const uint8_t *sbase = pscales + (int64_t)e * NG * nchunk * 128 + r32 * 4;
+  const uint16_t *ap = arow + kh * 32;  // + (4c + 2p) * 32 elements: this lane's block
 
-  f32x4_t acc[RG];
+  f32x16_t acc[RG];
 #pragma unroll
-  for (int g = 0; g < RG; ++g) acc[g] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-  u32x4_t cw[PF][RG];
+  for (int g = 0; g < RG; ++g)
+#pragma unroll
+    for (int i = 0; i < 16; ++i) acc[g][i] = 0.f;
+  u32x4_t cw[PF][RG][2];
   uint32_t sw[PF][RG];
-  u32x4_t av[PF][4];
+  u32x4_t av[PF][2][4];
   auto load = [&](int c, int s) {
     const bool cvalid = c < nchunk;
 #pragma unroll
     for (int g = 0; g < RG; ++g) {
       const bool ok = cvalid && (g0 + g) < NG;
       const int64_t t = (int64_t)(g0 + g) * nchunk + c;
-      cw[s][g] = ok ? *reinterpret_cast<const u32x4_t *>(cbase + t * 1024) : u32x4_t{0u, 0u, 0u, 0u};
-      sw[s][g] = ok ? *reinterpret_cast<const uint32_t *>(sbase + t * 64) : 0x7f7f7f7fu;
+#pragma unroll
+      for (int p = 0; p < 2; ++p)
+        cw[s][g][p] = ok ? *reinterpret_cast<const u32x4_t *>(cbase + t * 2048 + p * 1024) : u32x4_t{0u, 0u, 0u, 0u};
+      sw[s][g] = ok ? *reinterpret_cast<const uint32_t *>(sbase + t * 128) : 0x7f7f7f7fu;
     }
 #pragma unroll
-    for (int j = 0; j < 4; ++j)
-      av[s][j] = (cvalid && col_ok && (4 * c + j) < KB)
-                     ? *reinterpret_cast<const u32x4_t *>(ap + c * 128 + j * 32)
-                     : u32x4_t{0u, 0u, 0u, 0u};
+    for (int p = 0; p < 2; ++p) {
+      const bool ok = cvalid && col_ok && (4 * c + 2 * p + kh) < KB;
+      const u32x4_t *a4 = reinterpret_cast<const u32x4_t *>(ap + (4 * c + 2 * p) * 32);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) av[s][p][j] = ok ? a4[j] : u32x4_t{0u, 0u, 0u, 0u};
+    }
   };
 #pragma unroll
   for (int s = 0; s < PF; ++s) load(wave + s * kSWaves, s);
@@ -258,10 +269,13 @@ __global__ __launch_bounds__(kSWaves *kWave) void ffn_stream_tiled_kernel(
 #pragma unroll
         for (int g = 0; g < RG; ++g) {
 #pragma unroll
-          for (int j = 0; j < 4; ++j) {
-            const float sc = e8m0_to_f32((sw[s][g] >> (8 * j)) & 0xffu);
-            const bf16x8_t wa = fp4x8_to_bf16x8(cw[s][g][j], sc);
-            acc[g] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wa, as_bf16x8(av[s][j]), acc[g], 0, 0, 0);
+          for (int p = 0; p < 2; ++p) {
+            const float sc = e8m0_to_f32((sw[s][g] >> (8 * (2 * p + kh))) & 0xffu);
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+              const bf16x8_t wa = fp4x8_to_bf16x8(cw[s][g][p][j], sc);
+              acc[g] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wa, as_bf16x8(av[s][p][j]), acc[g], 0, 0, 0);
+            }
           }
         }
         load(cc + PF * kSWaves, s);
@@ -269,47 +283,54 @@ __global__ __launch_bounds__(kSWaves *kWave) void ffn_stream_tiled_kernel(
     }
   }
 
+  // 32x32 output: lane holds slot column lane%32, rows 8i + 4*(lane/32) + j (i, j = 0..3)
 #pragma unroll
   for (int g = 0; g < RG; ++g)
 #pragma unroll
-    for (int i = 0; i < 4; ++i) red[wave][16 * g + 4 * q + i][rl] = acc[g][i];
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) red[wave][32 * g + 8 * i + 4 * kh + j][r32] = acc[g][4 * i + j];
   __syncthreads();
 
-  const int col = threadIdx.x % kSCols;
-  const int r0 = (threadIdx.x / kSCols) * 4;
+  const int col = threadIdx.x % kTCols;
+  const int rq = (threadIdx.x / kTCols) * 8;  // 8 consecutive rows of the 64
   if (col >= mcount) return;
-  float h[4];
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    float sum = red[0][r0 + i][col];
-#pragma unroll
-    for (int w = 1; w < kSWaves; ++w) sum += red[w][r0 + i][col];
-    const int n = n0 + r0 + i;
-    if (bias != nullptr && n < N) sum += bf16_to_f32(bias[(int64_t)e * N + n]);
-    h[i] = sum;
-  }
   const int64_t r = rbase + m0 + col;
-  if (EPI == kEpiSwigluBf16 || EPI == kEpiActF32) {
-    const int half = N / 2;
 #pragma unroll
-    for (int p = 0; p < 2; ++p) {
-      const int n = n0 + r0 + 2 * p;
-      if (n < N) {
-        const uint16_t ab = f32_to_bf16_rne(swiglu_unit(h[2 * p], h[2 * p + 1], limit, alpha));
-        if (EPI == kEpiSwigluBf16)
-          reinterpret_cast<uint16_t *>(out)[r * half + n / 2] = ab;
-        else
-          reinterpret_cast<float *>(out)[r * half + n / 2] = bf16_to_f32(ab);
-      }
+  for (int h4 = 0; h4 < 2; ++h4) {
+    const int r0 = rq + 4 * h4;
+    float h[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      float sum = red[0][r0 + i][col];
+#pragma unroll
+      for (int w = 1; w < kSWaves; ++w) sum += red[w][r0 + i][col];
+      const int n = n0 + r0 + i;
+      if (bias != nullptr && n < N) sum += bf16_to_f32(bias[(int64_t)e * N + n]);
+      h[i] = sum;
     }
-  } else {
-    float *o = reinterpret_cast<float *>(out) + r * N + n0 + r0;
-    if (n0 + r0 + 3 < N) {
-      *reinterpret_cast<f32x4_t *>(o) = f32x4_t{h[0], h[1], h[2], h[3]};
-    } else {
+    if (EPI == kEpiSwigluBf16 || EPI == kEpiActF32) {
+      const int half = N / 2;
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
-        if (n0 + r0 + i < N) o[i] = h[i];
+      for (int p = 0; p < 2; ++p) {
+        const int n = n0 + r0 + 2 * p;
+        if (n < N) {
+          const uint16_t ab = f32_to_bf16_rne(swiglu_unit(h[2 * p], h[2 * p + 1], limit, alpha));
+          if (EPI == kEpiSwigluBf16)
+            reinterpret_cast<uint16_t *>(out)[r * half + n / 2] = ab;
+          else
+            reinterpret_cast<float *>(out)[r * half + n / 2] = bf16_to_f32(ab);
+        }
+      }
+    } else {
+      float *o = reinterpret_cast<float *>(out) + r * N + n0 + r0;
+      if (n0 + r0 + 3 < N) {
+        *reinterpret_cast<f32x4_t *>(o) = f32x4_t{h[0], h[1], h[2], h[3]};
+      } else {
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          if (n0 + r0 + i < N) o[i] = h[i];
+      }
     }
   }
 }
@@ -328,8 +349,9 @@ hipError_t launch_ffn_stream(const uint16_t *a_src, bool a_by_token, const int32
                      alpha)
   if (w.tiled) {
     // m-tile-major 1-D grid; a deeper register prefetch when few slots make few workgroups
-    const int ntn = (w.N + kSRows - 1) / kSRows;
-    dim3 g1((unsigned)(mtiles * ntn));
+    const int64_t mt32 = (S + kTCols - 1) / kTCols + busy;
+    const int ntn = (w.N + kTRows - 1) / kTRows;
+    dim3 g1((unsigned)(mt32 * ntn));
     const bool deep = S <= 64;
 #define MOE_LAUNCH_TILED(EPI)                                                                        \
   do {                                                                                               \

@@ -43,6 +43,11 @@ hipError_t launch_ffn_stream(const uint16_t *a_src, bool a_by_token, const int32
                              int k, const int32_t *offsets, int E, int64_t S, const MxWeight &w,
                              int epilogue, void *out, float limit, float alpha, hipStream_t stream);
 
+// One expert GEMM, LDS-tiled grouped-GEMM family (tiled weights only), same contract.
+hipError_t launch_ffn_gemm(const uint16_t *a_src, bool a_by_token, const int32_t *sorted_slot, int k,
+                           const int32_t *offsets, int E, int64_t S, const MxWeight &w, int epilogue, void *out,
+                           float limit, float alpha, hipStream_t stream);
+
 hipError_t launch_combine(const float *y, const int32_t *slot_row, const float *topk_w, int64_t T,
                           int k, int H, void *out, bool out_f32, hipStream_t stream);
 

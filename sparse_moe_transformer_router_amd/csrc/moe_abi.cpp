@@ -60,7 +60,7 @@ int check_weight(const moe_mxfp4_weight_t *w) {
   if (!aligned(w->codes, 16) || !aligned(w->bias, 2)) return MOE_ERR_INVALID_ARG;
   if (w->layout == MOE_LAYOUT_TILED && !aligned(w->scales, 4)) return MOE_ERR_INVALID_ARG;
   if (check_dim(w->k) != MOE_OK || w->n < 1 || w->n > 2 * kMaxDim) return MOE_ERR_UNSUPPORTED;
-  if (w->layout == MOE_LAYOUT_TILED && w->n % 16 != 0) return MOE_ERR_UNSUPPORTED;
+  if (w->layout == MOE_LAYOUT_TILED && w->n % 32 != 0) return MOE_ERR_UNSUPPORTED;
   return MOE_OK;
 }
 
@@ -87,6 +87,25 @@ int check_options(const moe_options_t &o) {
   return MOE_OK;
 }
 
+// Which expert-GEMM family runs: the grouped GEMM (tiled weights only) when asked for, or on
+// AUTO when the batch averages at least kGemmSlotsPerExpert slots per expert; otherwise the
+// weight-streaming kernels.
+constexpr int64_t kGemmSlotsPerExpert = 48;
+
+int check_path(const moe_options_t &o, const moe_mxfp4_weight_t &gu, const moe_mxfp4_weight_t &dn) {
+  if (o.path == MOE_PATH_GEMM && (gu.layout != MOE_LAYOUT_TILED || dn.layout != MOE_LAYOUT_TILED))
+    return MOE_ERR_UNSUPPORTED;
+  return MOE_OK;
+}
+
+bool use_gemm(const moe_options_t &o, const moe_mxfp4_weight_t &gu, const moe_mxfp4_weight_t &dn, int64_t S,
+              int E) {
+  const bool tiled = gu.layout == MOE_LAYOUT_TILED && dn.layout == MOE_LAYOUT_TILED;
+  if (o.path == MOE_PATH_GEMM) return true;
+  if (o.path == MOE_PATH_STREAM || !tiled) return false;
+  return S >= kGemmSlotsPerExpert * (int64_t)E;
+}
+
 // The expert GEMMs that follow the permutation. Arguments already validated.
 int run_ffn(const uint16_t *x, int64_t T, int k, int E, const int32_t *offsets, const int32_t *sorted_slot,
             const moe_mxfp4_weight_t &gu, const moe_mxfp4_weight_t &dn, const moe_options_t &o, float *y,
@@ -94,23 +113,19 @@ int run_ffn(const uint16_t *x, int64_t T, int k, int E, const int32_t *offsets, 
   const int64_t S = T * k;
   const moe::MxWeight w1 = mx(gu);
   const moe::MxWeight w2 = mx(dn);
-  hipError_t err;
-  if (o.flags & MOE_FLAG_EMIT_PREACT) {
-    err = moe::launch_ffn_stream(x, true, sorted_slot, k, offsets, E, S, w1, moe::kEpiPreactF32, y,
-                                 o.swiglu_limit, o.swiglu_alpha, stream);
-    return err == hipSuccess ? MOE_OK : MOE_ERR_HIP;
-  }
-  if (o.flags & MOE_FLAG_EMIT_ACT) {
-    err = moe::launch_ffn_stream(x, true, sorted_slot, k, offsets, E, S, w1, moe::kEpiActF32, y,
-                                 o.swiglu_limit, o.swiglu_alpha, stream);
-    return err == hipSuccess ? MOE_OK : MOE_ERR_HIP;
-  }
-  err = moe::launch_ffn_stream(x, true, sorted_slot, k, offsets, E, S, w1, moe::kEpiSwigluBf16, act,
-                               o.swiglu_limit, o.swiglu_alpha, stream);
-  if (err != hipSuccess) return MOE_ERR_HIP;
-  err = moe::launch_ffn_stream(act, false, sorted_slot, k, offsets, E, S, w2, moe::kEpiLinearF32, y,
-                               o.swiglu_limit, o.swiglu_alpha, stream);
-  return err == hipSuccess ? MOE_OK : MOE_ERR_HIP;
+  const bool gemm = use_gemm(o, gu, dn, S, E);
+  auto launch = [&](const uint16_t *a, bool by_token, const moe::MxWeight &w, int epi, void *out) {
+    return gemm ? moe::launch_ffn_gemm(a, by_token, sorted_slot, k, offsets, E, S, w, epi, out, o.swiglu_limit,
+                                       o.swiglu_alpha, stream)
+                : moe::launch_ffn_stream(a, by_token, sorted_slot, k, offsets, E, S, w, epi, out, o.swiglu_limit,
+                                         o.swiglu_alpha, stream);
+  };
+  if (o.flags & MOE_FLAG_EMIT_PREACT)
+    return launch(x, true, w1, moe::kEpiPreactF32, y) == hipSuccess ? MOE_OK : MOE_ERR_HIP;
+  if (o.flags & MOE_FLAG_EMIT_ACT)
+    return launch(x, true, w1, moe::kEpiActF32, y) == hipSuccess ? MOE_OK : MOE_ERR_HIP;
+  if (launch(x, true, w1, moe::kEpiSwigluBf16, act) != hipSuccess) return MOE_ERR_HIP;
+  return launch(act, false, w2, moe::kEpiLinearF32, y) == hipSuccess ? MOE_OK : MOE_ERR_HIP;
 }
 
 int check_layer(const uint16_t *x, const moe_router_t *router, const moe_mxfp4_weight_t *gu,
@@ -203,11 +218,11 @@ size_t moe_workspace_size(int64_t T, int32_t E, int32_t k, int32_t H, int32_t I,
 
 int moe_mxfp4_tiled_bytes(int32_t E, int32_t n, int32_t k, size_t *codes_bytes, size_t *scales_bytes) {
   MOE_GUARD_BEGIN
-  if (E < 1 || E > kMaxExperts || n < 16 || n % 16 != 0 || n > 2 * kMaxDim || check_dim(k) != MOE_OK)
+  if (E < 1 || E > kMaxExperts || n < 32 || n % 32 != 0 || n > 2 * kMaxDim || check_dim(k) != MOE_OK)
     return MOE_ERR_UNSUPPORTED;
-  const size_t tiles = (size_t)E * (size_t)(n / 16) * (size_t)((k / 32 + 3) / 4);
-  if (codes_bytes) *codes_bytes = tiles * 1024;
-  if (scales_bytes) *scales_bytes = tiles * 64;
+  const size_t tiles = (size_t)E * (size_t)(n / 32) * (size_t)((k / 32 + 3) / 4);
+  if (codes_bytes) *codes_bytes = tiles * 2048;
+  if (scales_bytes) *scales_bytes = tiles * 128;
   return MOE_OK;
   MOE_GUARD_END
 }
@@ -297,6 +312,7 @@ int moe_mxfp4_ffn(const uint16_t *x, int64_t T, int32_t k, int32_t E, const int3
   if ((st = check_dim(H)) != MOE_OK || (st = check_dim(I)) != MOE_OK) return st;
   const moe_options_t o = opts ? *opts : default_options();
   if ((st = check_options(o)) != MOE_OK) return st;
+  if ((st = check_path(o, *gate_up, *down)) != MOE_OK) return st;
   if (T == 0) return MOE_OK;
   if (x == nullptr || expert_offsets == nullptr || sorted_slot == nullptr || y == nullptr)
     return MOE_ERR_INVALID_ARG;
@@ -339,6 +355,7 @@ int moe_forward_ex(const uint16_t *x, const moe_router_t *router,
   const moe_options_t o = opts ? *opts : default_options();
   if ((st = check_options(o)) != MOE_OK) return st;
   if (o.flags != 0) return MOE_ERR_INVALID_ARG;
+  if ((st = check_path(o, *w_gate_up, *w_down)) != MOE_OK) return st;
   if (T == 0) return MOE_OK;
   return forward_impl(x, router, w_gate_up, w_down, T, E, k, o, out, ws, ws_bytes, (hipStream_t)stream);
   MOE_GUARD_END

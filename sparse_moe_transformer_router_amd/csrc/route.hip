@@ -54,19 +54,27 @@ __global__ __launch_bounds__(kWave) void router_partial_kernel(const uint16_t *_
   const uint16_t *xp = x + (t_ok ? (t0 + r) : 0) * H + 8 * q;
   const float *wp = w + (int64_t)(e_ok ? (e0 + r) : 0) * H + 8 * q;
   f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
-  for (int b = b0; b < b1; ++b) {
-    const u32x4_t xa = t_ok ? *reinterpret_cast<const u32x4_t *>(xp + 32 * b) : u32x4_t{0u, 0u, 0u, 0u};
-    f32x4_t wa = {0.f, 0.f, 0.f, 0.f}, wb = {0.f, 0.f, 0.f, 0.f};
-    if (e_ok) {
-      wa = *reinterpret_cast<const f32x4_t *>(wp + 32 * b);
-      wb = *reinterpret_cast<const f32x4_t *>(wp + 32 * b + 4);
+  constexpr int U = 4;  // MX blocks per round: all of a round's loads are issued before any math
+  for (int bb = b0; bb < b1; bb += U) {
+    u32x4_t xa[U];
+    f32x4_t wa[U], wb[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int b = bb + u;
+      const bool ok = b < b1;
+      xa[u] = (ok && t_ok) ? *reinterpret_cast<const u32x4_t *>(xp + 32 * b) : u32x4_t{0u, 0u, 0u, 0u};
+      wa[u] = (ok && e_ok) ? *reinterpret_cast<const f32x4_t *>(wp + 32 * b) : f32x4_t{0.f, 0.f, 0.f, 0.f};
+      wb[u] = (ok && e_ok) ? *reinterpret_cast<const f32x4_t *>(wp + 32 * b + 4) : f32x4_t{0.f, 0.f, 0.f, 0.f};
     }
-    bf16x8_t hi, mid, lo;
-    split3(wa, wb, hi, mid, lo);
-    const bf16x8_t xb = as_bf16x8(xa);
-    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xb, lo, acc, 0, 0, 0);
-    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xb, mid, acc, 0, 0, 0);
-    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xb, hi, acc, 0, 0, 0);
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      bf16x8_t hi, mid, lo;
+      split3(wa[u], wb[u], hi, mid, lo);
+      const bf16x8_t xb = as_bf16x8(xa[u]);
+      acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xb, lo, acc, 0, 0, 0);
+      acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xb, mid, acc, 0, 0, 0);
+      acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xb, hi, acc, 0, 0, 0);
+    }
   }
   // lane holds tokens t0 + 4q + i, expert e0 + r
   if (e_ok) {
@@ -159,13 +167,13 @@ __global__ __launch_bounds__(256) void router_topk_kernel(const float *__restric
   }
 }
 
-// Split count for the router's input dimension: enough waves to spread a decode batch over
-// the chip (a few hundred), at most 4 * kMaxSplitVec, at least 2 MX blocks per split.
+// Split count for the router's input dimension: enough waves (about 2048, eight per SIMD) to
+// spread any batch over the chip, at most 4 * kMaxSplitVec, at least 2 MX blocks per split.
 int router_splits(int64_t T, int E, int H) {
   const int64_t tiles = ((T + 15) / 16) * ((E + 15) / 16);
   const int KB = H / 32;
   if (tiles <= 0 || KB < 2) return 1;
-  int64_t s = (512 + tiles - 1) / tiles;
+  int64_t s = (2048 + tiles - 1) / tiles;
   if (s > KB / 2) s = KB / 2;
   if (s > 4 * kMaxSplitVec) s = 4 * kMaxSplitVec;
   if (s < 1) s = 1;

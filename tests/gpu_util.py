@@ -68,7 +68,9 @@ def device_layer(inp: synth.MoEInputs, with_bias: bool = True, tiled: bool = Fal
 
 
 def tiled_reference(codes: np.ndarray, scales: np.ndarray):
-    """The tiled layout re-derived with numpy reshapes, independently of the library."""
+    """The tiled layout re-derived with numpy reshapes, independently of the library:
+    tile (e, G, c) = half p, lane l -> block 4c + 2p + l//32 of row 32G + l%32; scales per
+    tile: 32 rows x 4 blocks."""
     E, N, KH = codes.shape
     KB = scales.shape[2]
     nchunk = (KB + 3) // 4
@@ -76,9 +78,9 @@ def tiled_reference(codes: np.ndarray, scales: np.ndarray):
     c[:, :, :KH] = codes
     sc = np.full((E, N, nchunk * 4), 127, np.uint8)
     sc[:, :, :KB] = scales
-    # row bytes of a chunk: 16 j + 4 q + b; tile order: e, g, c, lane (q, r), j, b
-    c = c.reshape(E, N // 16, 16, nchunk, 4, 4, 4).transpose(0, 1, 3, 5, 2, 4, 6)
-    sc = sc.reshape(E, N // 16, 16, nchunk, 4).transpose(0, 1, 3, 2, 4)
+    # row bytes of chunk c: block (2p + kh) * 16 + byte; tile order: e, G, c, p, lane (kh, r), byte
+    c = c.reshape(E, N // 32, 32, nchunk, 2, 2, 16).transpose(0, 1, 3, 4, 5, 2, 6)
+    sc = sc.reshape(E, N // 32, 32, nchunk, 4).transpose(0, 1, 3, 2, 4)
     return np.ascontiguousarray(c).reshape(-1), np.ascontiguousarray(sc).reshape(-1)
 
 

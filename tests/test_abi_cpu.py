@@ -124,8 +124,8 @@ def test_tiled_bytes_and_pack_errors():
     lib = L.lib()
     cb, sb = ctypes.c_size_t(0), ctypes.c_size_t(0)
     assert lib.moe_mxfp4_tiled_bytes(32, 5760, 2880, ctypes.byref(cb), ctypes.byref(sb)) == L.MOE_OK
-    assert cb.value == 32 * 360 * 23 * 1024 and sb.value == 32 * 360 * 23 * 64
-    assert lib.moe_mxfp4_tiled_bytes(32, 5768, 2880, ctypes.byref(cb), ctypes.byref(sb)) == L.MOE_ERR_UNSUPPORTED
+    assert cb.value == 32 * 180 * 23 * 2048 and sb.value == 32 * 180 * 23 * 128
+    assert lib.moe_mxfp4_tiled_bytes(32, 5776, 2880, ctypes.byref(cb), ctypes.byref(sb)) == L.MOE_ERR_UNSUPPORTED
     assert lib.moe_mxfp4_tiled_bytes(32, 5760, 2890, ctypes.byref(cb), ctypes.byref(sb)) == L.MOE_ERR_UNSUPPORTED
     w = _weight(64, 64)
     assert lib.moe_mxfp4_pack(None, 2, FAKE, FAKE, None) == L.MOE_ERR_INVALID_ARG
@@ -133,7 +133,7 @@ def test_tiled_bytes_and_pack_errors():
     assert lib.moe_mxfp4_pack(ctypes.byref(w), 2, FAKE + 8, FAKE, None) == L.MOE_ERR_INVALID_ARG
     wt = L.MoeMxfp4Weight(FAKE, FAKE, None, 64, 64, 1)
     assert lib.moe_mxfp4_pack(ctypes.byref(wt), 2, FAKE, FAKE, None) == L.MOE_ERR_INVALID_ARG  # already tiled
-    assert lib.moe_mxfp4_pack(ctypes.byref(_weight(40, 64)), 2, FAKE, FAKE, None) == L.MOE_ERR_UNSUPPORTED
+    assert lib.moe_mxfp4_pack(ctypes.byref(_weight(48, 64)), 2, FAKE, FAKE, None) == L.MOE_ERR_UNSUPPORTED
     bad = L.MoeMxfp4Weight(FAKE, FAKE, None, 64, 64, 7)
     assert lib.moe_mxfp4_pack(ctypes.byref(bad), 2, FAKE, FAKE, None) == L.MOE_ERR_INVALID_ARG
 

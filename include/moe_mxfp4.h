@@ -88,7 +88,9 @@ typedef struct moe_router {
  * For the gate_up matrix n = 2I with rows interleaved: row 2i is unit i's gate, row
  * 2i+1 its linear branch; k = H. For the down matrix n = H, k = I.
  * layout MOE_LAYOUT_TILED: codes and scales hold the same values re-ordered by
- * moe_mxfp4_pack into 32-row x 128-element tiles (see there); bias is unchanged.
+ * moe_mxfp4_pack into 32-row x 128-element tiles (see there); bias is unchanged but
+ * must be 8-byte aligned (codes 16-byte, scales 4-byte); row-major: codes 16-byte,
+ * bias 2-byte. Misaligned pointers are rejected with MOE_ERR_INVALID_ARG.
  */
 typedef struct moe_mxfp4_weight {
   const uint8_t *codes;

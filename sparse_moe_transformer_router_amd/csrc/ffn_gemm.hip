@@ -43,6 +43,7 @@ constexpr int kG2RowBytes = 256;        // one 128-element bf16 chunk of a slot
 constexpr int kG2StageBytes = kG2Cols * kG2RowBytes;
 constexpr int kG2RGW = 3;               // 32-row weight tiles per wave (wave owns 96 rows)
 constexpr int kG2Rows = 2 * 32 * kG2RGW;  // weight rows per workgroup
+constexpr int kG2Waves = 8;             // two per SIMD: 2 x 2 output quarters x 2 k-halves
 constexpr int kG2GroupM = 4;            // m-tiles per group of the XCD-local tile order
 constexpr int kXcds = 8;                // accelerator complex dies, one L2 each
 
@@ -54,7 +55,7 @@ __device__ __forceinline__ constexpr int vmcnt_imm(int n) {
 }
 
 template <int EPI>
-__global__ __launch_bounds__(256) void ffn_gemm2_kernel(const uint16_t *__restrict__ a_src, int a_by_token,
+__global__ __launch_bounds__(kG2Waves * 64) void ffn_gemm2_kernel(const uint16_t *__restrict__ a_src, int a_by_token,
                                                         const int32_t *__restrict__ sorted_slot, int k,
                                                         const int32_t *__restrict__ offsets, int E,
                                                         const uint8_t *__restrict__ pcodes,
@@ -65,7 +66,8 @@ __global__ __launch_bounds__(256) void ffn_gemm2_kernel(const uint16_t *__restri
   extern __shared__ __attribute__((aligned(16))) unsigned char lds[];
   const int tid = threadIdx.x, lane = tid % 64;
   const int wave = __builtin_amdgcn_readfirstlane(tid / 64);  // uniform: LDS targets stay scalar
-  const int wy = wave / 2, wx = wave % 2;  // weight-row half, slot half
+  const int wk = wave >> 2;                       // which half of every chunk's k-steps
+  const int wy = (wave >> 1) & 1, wx = wave & 1;  // weight-row half, slot half
   // Real m-tile count: the grid is sized for the worst case, the surplus blocks exit.
   int mt_total = 0;
   for (int eb = 0; eb < E; eb += 64) {
@@ -119,22 +121,24 @@ __global__ __launch_bounds__(256) void ffn_gemm2_kernel(const uint16_t *__restri
   const int NG = N / 32;
   const int r32 = lane % 32, kh = lane / 32;
 
-  // staging: wave stages slot rows 32 wave + 4 i + lane / 16 (i = 0..7), physical 16-byte
+  // staging: wave stages slot rows 16 wave + 4 i + lane / 16 (i = 0..3), physical 16-byte
   // column lane % 16
-  const uint16_t *aptr[8];
-  int lcol[8];
+  const uint16_t *aptr[4];
+  int lcol[4];
 #pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    const int row = 32 * wave + 4 * i + lane / 16;
+  for (int i = 0; i < 4; ++i) {
+    const int row = 16 * wave + 4 * i + lane / 16;
     const int srow = row < mcount ? row : 0;  // padding slots re-read slot 0 (results discarded)
     const int r = rbase + m0 + srow;
     lcol[i] = ((lane % 16) ^ (row & 15)) * 8;  // logical element offset within the chunk
     aptr[i] = a_src + (a_by_token ? (int64_t)(sorted_slot[r] / k) : (int64_t)r) * K;
   }
-  // One DMA of stage cc (a chunk index, always < nchunk) into ring slot `slot`:
-  //   i = 0..7: activation rows 4 i .. 4 i + 3 of this wave's 32;
-  //   i = 8..10: 1 KB of weight codes (tile m / 2, half m % 2 with m = 3 wave + i - 8);
-  //   i = 11: 256 bytes of the scale block.
+  // One DMA of stage cc (a chunk index, always < nchunk) into ring slot `slot`; a wave issues
+  // six per stage:
+  //   i = 0..3: activation rows 4 i .. 4 i + 3 of this wave's 16;
+  //   i = 4, 5: waves 0..5: 1 KB half i - 4 of weight tile `wave`; waves 6, 7: 256 bytes of
+  //             the stage's scale block (bytes 512 (wave - 6) + 256 (i - 4) ...; the block
+  //             holds 2 RGW x 128 bytes, the rest is padding).
   constexpr int kWStage = 2 * RGW * 2048;
   constexpr int kSStage = 1024;
   unsigned char *lds_w = lds + kG2Stages * kG2StageBytes;
@@ -143,23 +147,23 @@ __global__ __launch_bounds__(256) void ffn_gemm2_kernel(const uint16_t *__restri
   const uint8_t *cexp = pcodes + (int64_t)e * NG * nchunk * 2048 + lane * 16;
   const uint8_t *sexp = pscales + (int64_t)e * NG * nchunk * 128;
   auto dma = [&](int i, int cc, int slot) {
-    if (i < 8) {
+    if (i < 4) {
       int kk = cc * 128 + lcol[i];
       kk = kk < K ? kk : 0;  // past K: any in-bounds element (its weight is an exact zero)
       __builtin_amdgcn_global_load_lds(aptr[i] + kk,
-                                       lds + slot * kG2StageBytes + (32 * wave + 4 * i) * kG2RowBytes, 16, 0, 0);
-    } else if (i < 11) {
-      const int m = 3 * wave + i - 8;  // 0..11
-      const int g = gt0 + m / 2;
+                                       lds + slot * kG2StageBytes + (16 * wave + 4 * i) * kG2RowBytes, 16, 0, 0);
+    } else if (wave < 2 * RGW) {
+      const int g = gt0 + wave;
       const int64_t t = (g < NG) ? (int64_t)g * nchunk + cc : 0;
-      __builtin_amdgcn_global_load_lds(cexp + t * 2048 + (m % 2) * 1024,
-                                       lds_w + slot * kWStage + (m / 2) * 2048 + (m % 2) * 1024, 16, 0, 0);
+      __builtin_amdgcn_global_load_lds(cexp + t * 2048 + (i - 4) * 1024,
+                                       lds_w + slot * kWStage + wave * 2048 + (i - 4) * 1024, 16, 0, 0);
     } else {
-      const int o = 256 * wave + 4 * lane;  // byte of the stage's scale block
+      const int ob = 512 * (wave - 2 * RGW) + 256 * (i - 4);  // first byte of this DMA
+      const int o = ob + 4 * lane;
       const int ti = o / 128;
       const int g = gt0 + ti;
       const int64_t t = (ti < 2 * RGW && g < NG) ? (int64_t)g * nchunk + cc : 0;
-      __builtin_amdgcn_global_load_lds(sexp + t * 128 + (o % 128), lds_s + slot * kSStage + 256 * wave, 4, 0, 0);
+      __builtin_amdgcn_global_load_lds(sexp + t * 128 + (o % 128), lds_s + slot * kSStage + ob, 4, 0, 0);
     }
   };
 
@@ -171,65 +175,109 @@ __global__ __launch_bounds__(256) void ffn_gemm2_kernel(const uint16_t *__restri
 #pragma unroll
       for (int i = 0; i < 16; ++i) acc[g][b][i] = 0.f;
 
-  // Every chunk issues exactly 12 DMAs (past the last chunk they re-load the last chunk into
-  // the ring slot nobody reads), so before chunk c the younger loads are always chunk c+1's 12.
+  // Every chunk issues exactly 6 DMAs per wave (past the last chunk they re-load the last
+  // chunk into the ring slot nobody reads), so before chunk c the younger loads are always
+  // chunk c+1's 6.
 #pragma unroll
-  for (int i = 0; i < 12; ++i) dma(i, 0, 0);
+  for (int i = 0; i < 6; ++i) dma(i, 0, 0);
 #pragma unroll
-  for (int i = 0; i < 12; ++i) dma(i, nchunk > 1 ? 1 : 0, 1);
+  for (int i = 0; i < 6; ++i) dma(i, nchunk > 1 ? 1 : 0, 1);
+  const int p = wk;  // this wave's half of each chunk: MX blocks 4c + 2p + kh
   for (int c = 0; c < nchunk; ++c) {
-    __builtin_amdgcn_s_waitcnt(vmcnt_imm(12));
+    __builtin_amdgcn_s_waitcnt(vmcnt_imm(6));
     __builtin_amdgcn_s_barrier();
     const int cn = (c + 2 < nchunk) ? c + 2 : nchunk - 1;  // chunk staged during this one
     const int sn = (c + 2) % kG2Stages;                      // its ring slot (read by nobody now)
     const int sc_ = c % kG2Stages;
     const unsigned char *abuf = lds + sc_ * kG2StageBytes;
-    const unsigned char *wbuf = lds_w + sc_ * kWStage + (wy * RGW) * 2048 + lane * 16;
+    const unsigned char *wbuf = lds_w + sc_ * kWStage + (wy * RGW) * 2048 + p * 1024 + lane * 16;
     const unsigned char *sbuf = lds_s + sc_ * kSStage + (wy * RGW) * 128 + r32 * 4;
-    uint32_t swd[RGW];
+    u32x4_t cw[RGW];
+    float sc[RGW];
 #pragma unroll
-    for (int g = 0; g < RGW; ++g) swd[g] = *reinterpret_cast<const uint32_t *>(sbuf + g * 128);
-    auto bload = [&](int p, int j, bf16x8_t *bv) {
+    for (int g = 0; g < RGW; ++g) {
+      cw[g] = *reinterpret_cast<const u32x4_t *>(wbuf + g * 2048);
+      sc[g] = e8m0_to_f32((*reinterpret_cast<const uint32_t *>(sbuf + g * 128) >> (8 * (2 * p + kh))) & 0xffu);
+    }
+    auto bload = [&](int j, bf16x8_t *bv) {
 #pragma unroll
       for (int b = 0; b < 2; ++b)
         bv[b] = as_bf16x8(
             *reinterpret_cast<const u32x4_t *>(abuf + g2_off(wx * 64 + 32 * b + r32, 4 * (2 * p + kh) + j)));
     };
     bf16x8_t bcur[2], bnext[2];
-    bload(0, 0, bcur);
+    bload(0, bcur);
 #pragma unroll
-    for (int p = 0; p < 2; ++p) {
-      u32x4_t cw[RGW];
-      float sc[RGW];
+    for (int j = 0; j < 4; ++j) {
+      if (j < 3) bload(j + 1, bnext);
+      // this k-step's share of the next stage's DMAs, issued in the shadow of its MFMAs
+      if (j < 2) {
+        dma(2 * j, cn, sn);
+        dma(2 * j + 1, cn, sn);
+      } else {
+        dma(j + 2, cn, sn);
+      }
 #pragma unroll
       for (int g = 0; g < RGW; ++g) {
-        cw[g] = *reinterpret_cast<const u32x4_t *>(wbuf + g * 2048 + p * 1024);
-        sc[g] = e8m0_to_f32((swd[g] >> (8 * (2 * p + kh))) & 0xffu);
+        const bf16x8_t wa = fp4x8_to_bf16x8(cw[g][j], sc[g]);
+#pragma unroll
+        for (int b = 0; b < 2; ++b)
+          acc[g][b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wa, bcur[b], acc[g][b], 0, 0, 0);
       }
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int st = 4 * p + j;
-        const int nj = (j + 1) & 3, np = p + (j == 3 ? 1 : 0);
-        if (np < 2) bload(np, nj, bnext);
-        // this k-step's share of the next stage's DMAs, issued in the shadow of its MFMAs
-        dma(st, cn, sn);
-        if (st < 4) dma(8 + st, cn, sn);
-#pragma unroll
-        for (int g = 0; g < RGW; ++g) {
-          const bf16x8_t wa = fp4x8_to_bf16x8(cw[g][j], sc[g]);
-#pragma unroll
-          for (int b = 0; b < 2; ++b)
-            acc[g][b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wa, bcur[b], acc[g][b], 0, 0, 0);
-        }
-        bcur[0] = bnext[0];
-        bcur[1] = bnext[1];
-      }
+      bcur[0] = bnext[0];
+      bcur[1] = bnext[1];
     }
   }
-  __builtin_amdgcn_s_waitcnt(0);  // no DMA may still target this workgroup's LDS when it ends
+  __builtin_amdgcn_s_waitcnt(0);  // no DMA may still target this workgroup's LDS
+  __syncthreads();                // every wave is done reading the ring
 
-  // epilogue: lane holds slot column wx*64 + 32b + r32 and, per tile g, rows 8i + 4kh + jj
+  // The two halves of each output tile: the p = 1 waves hand their sums to the p = 0 waves
+  // through LDS (fixed order: p = 0 sum + p = 1 sum).
+  {
+    f32x4_t *red = reinterpret_cast<f32x4_t *>(lds) + (wave & 3) * (RGW * 2 * 4) * 64 + lane;
+    if (wk == 1) {
+#pragma unroll
+      for (int g = 0; g < RGW; ++g)
+#pragma unroll
+        for (int b = 0; b < 2; ++b)
+#pragma unroll
+          for (int q = 0; q < 4; ++q)
+            red[((g * 2 + b) * 4 + q) * 64] =
+                f32x4_t{acc[g][b][4 * q], acc[g][b][4 * q + 1], acc[g][b][4 * q + 2], acc[g][b][4 * q + 3]};
+    }
+    __syncthreads();
+    if (wk == 1) return;
+#pragma unroll
+    for (int g = 0; g < RGW; ++g)
+#pragma unroll
+      for (int b = 0; b < 2; ++b)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const f32x4_t o = red[((g * 2 + b) * 4 + q) * 64];
+#pragma unroll
+          for (int u = 0; u < 4; ++u) acc[g][b][4 * q + u] += o[u];
+        }
+  }
+
+  // epilogue: lane holds slot column wx*64 + 32b + r32 and, per tile g, rows 8i + 4kh + jj.
+  // The bias of a lane's rows is 4 consecutive bf16 per (g, i): twelve 8-byte loads, all
+  // issued before any is used (clamped rows past N read row 0 and are never stored).
   const int nbase = nt * kG2Rows + wy * 32 * RGW;
+  uint2 bq[RGW][4];
+#pragma unroll
+  for (int g = 0; g < RGW; ++g)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) bq[g][i] = uint2{0u, 0u};
+  if (bias != nullptr) {
+    const uint16_t *be = bias + (int64_t)e * N;
+#pragma unroll
+    for (int g = 0; g < RGW; ++g)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int n = nbase + 32 * g + 8 * i + 4 * kh;
+        bq[g][i] = *reinterpret_cast<const uint2 *>(be + (n < N ? n : 0));
+      }
+  }
 #pragma unroll
   for (int b = 0; b < 2; ++b) {
     const int col = wx * 64 + 32 * b + r32;
@@ -242,9 +290,10 @@ __global__ __launch_bounds__(256) void ffn_gemm2_kernel(const uint16_t *__restri
         const int n = nbase + 32 * g + 8 * i + 4 * kh;
         if (n >= N) continue;
         float h[4];
-#pragma unroll
-        for (int jj = 0; jj < 4; ++jj)
-          h[jj] = acc[g][b][4 * i + jj] + (bias ? bf16_to_f32(bias[(int64_t)e * N + n + jj]) : 0.f);
+        h[0] = acc[g][b][4 * i + 0] + __uint_as_float(bq[g][i].x << 16);
+        h[1] = acc[g][b][4 * i + 1] + __uint_as_float(bq[g][i].x & 0xffff0000u);
+        h[2] = acc[g][b][4 * i + 2] + __uint_as_float(bq[g][i].y << 16);
+        h[3] = acc[g][b][4 * i + 3] + __uint_as_float(bq[g][i].y & 0xffff0000u);
         if (EPI == kEpiSwigluBf16 || EPI == kEpiActF32) {
           const int half = N / 2;
           const uint16_t a0 = f32_to_bf16_rne(swiglu_unit(h[0], h[1], limit, alpha));
@@ -253,9 +302,8 @@ __global__ __launch_bounds__(256) void ffn_gemm2_kernel(const uint16_t *__restri
             *reinterpret_cast<uint32_t *>(reinterpret_cast<uint16_t *>(out) + r * half + n / 2) =
                 (uint32_t)a0 | ((uint32_t)a1 << 16);
           } else {
-            float *o = reinterpret_cast<float *>(out) + r * half + n / 2;
-            o[0] = bf16_to_f32(a0);
-            o[1] = bf16_to_f32(a1);
+            *reinterpret_cast<float2 *>(reinterpret_cast<float *>(out) + r * half + n / 2) =
+                float2{bf16_to_f32(a0), bf16_to_f32(a1)};
           }
         } else {
           *reinterpret_cast<f32x4_t *>(reinterpret_cast<float *>(out) + r * N + n) = f32x4_t{h[0], h[1], h[2], h[3]};
@@ -274,7 +322,7 @@ hipError_t launch_ffn_gemm(const uint16_t *a_src, bool a_by_token, const int32_t
   dim3 grid((unsigned)(mtiles * ntn));
   const size_t lds = (size_t)kG2Stages * (kG2StageBytes + 2 * kG2RGW * 2048 + 1024);
 #define MOE_LAUNCH_GEMM(EPI)                                                                          \
-  hipLaunchKernelGGL(ffn_gemm2_kernel<EPI>, grid, dim3(256), lds, stream, a_src, a_by_token ? 1 : 0, \
+  hipLaunchKernelGGL(ffn_gemm2_kernel<EPI>, grid, dim3(kG2Waves * 64), lds, stream, a_src, a_by_token ? 1 : 0, \
                      sorted_slot, k, offsets, E, w.codes, w.scales, w.bias, w.N, w.K, ntn, out, limit, alpha)
   switch (epilogue) {
     case kEpiSwigluBf16: MOE_LAUNCH_GEMM(kEpiSwigluBf16); break;

@@ -21,6 +21,8 @@
 // The m-tile -> (expert, first slot) map is recomputed by every wave from expert_offsets
 // (a wave-wide scan over experts), so no tile list is materialised and the grid is sized
 // from host-known bounds only; surplus workgroups exit at once.
+#include <type_traits>
+
 #include "common.h"
 #include "kernels.h"
 
@@ -296,18 +298,26 @@ __global__ __launch_bounds__(kSWaves *kWave) void ffn_stream_tiled_kernel(
   const int rq = (threadIdx.x / kTCols) * 8;  // 8 consecutive rows of the 64
   if (col >= mcount) return;
   const int64_t r = rbase + m0 + col;
+  uint2 bq[2] = {uint2{0u, 0u}, uint2{0u, 0u}};  // bias of the 8 rows (rows past N: row 0)
+  if (bias != nullptr) {
+#pragma unroll
+    for (int h4 = 0; h4 < 2; ++h4) {
+      const int n = n0 + rq + 4 * h4;
+      bq[h4] = *reinterpret_cast<const uint2 *>(bias + (int64_t)e * N + (n < N ? n : 0));
+    }
+  }
 #pragma unroll
   for (int h4 = 0; h4 < 2; ++h4) {
     const int r0 = rq + 4 * h4;
+    const float bv[4] = {__uint_as_float(bq[h4].x << 16), __uint_as_float(bq[h4].x & 0xffff0000u),
+                         __uint_as_float(bq[h4].y << 16), __uint_as_float(bq[h4].y & 0xffff0000u)};
     float h[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       float sum = red[0][r0 + i][col];
 #pragma unroll
       for (int w = 1; w < kSWaves; ++w) sum += red[w][r0 + i][col];
-      const int n = n0 + r0 + i;
-      if (bias != nullptr && n < N) sum += bf16_to_f32(bias[(int64_t)e * N + n]);
-      h[i] = sum;
+      h[i] = sum + bv[i];
     }
     if (EPI == kEpiSwigluBf16 || EPI == kEpiActF32) {
       const int half = N / 2;
@@ -335,6 +345,182 @@ __global__ __launch_bounds__(kSWaves *kWave) void ffn_stream_tiled_kernel(
   }
 }
 
+
+// ---------------------------------------------------------------------------------------
+// Row-split form for more than a handful of slots, tiled weights: the four waves of a
+// workgroup own four different 32-row tiles (128 rows) of one expert and walk the whole
+// input dimension together, so the 32-slot activation chunk is fetched once per workgroup
+// and shared through LDS, and no cross-wave reduction is needed. Each chunk's activations
+// go global -> registers (two 16-byte pieces per lane, loaded three chunks ahead) ->
+// ds_write into a 2-deep LDS ring (16-byte columns XOR-swizzled by slot); weights stream
+// into registers D chunks ahead. No LDS DMA here: the compiler's wait counting for the
+// register loads stays exact only without it. All loads are issued unconditionally from
+// clamped in-bounds addresses (values past K or of absent slots are zeroed after the
+// load), so no control path skips a load and the compiler's waits stay tight.
+constexpr int kRWaves = 4;
+constexpr int kRCols = 32;            // slots per m-tile
+constexpr int kRowSplitMinSlots = 16; // below this the K-split form keeps more waves busy
+
+template <int EPI, int D>
+__global__ __launch_bounds__(kRWaves *kWave) void ffn_stream_rows_kernel(
+    const uint16_t *__restrict__ a_src, int a_by_token, const int32_t *__restrict__ sorted_slot, int k,
+    const int32_t *__restrict__ offsets, int E, const uint8_t *__restrict__ pcodes,
+    const uint8_t *__restrict__ pscales, const uint16_t *__restrict__ bias, int N, int K, int ntiles_n,
+    void *__restrict__ out, float limit, float alpha) {
+  static_assert(D % 2 == 0, "the weight ring period must be even");
+  __shared__ __attribute__((aligned(16))) unsigned char lds[2 * kRCols * 256];
+  const int lane = threadIdx.x % kWave;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+  const int mt = blockIdx.x / ntiles_n, nt = blockIdx.x % ntiles_n;
+  int e = -1, m0 = 0, rbase = 0, mcount = 0;
+  {
+    int carry = 0;
+    for (int eb = 0; eb < E; eb += kWave) {
+      const int ex = eb + lane;
+      const int cnt = (ex < E) ? offsets[ex + 1] - offsets[ex] : 0;
+      const int tiles = (cnt + kRCols - 1) / kRCols;
+      const int inc = wave_inclusive_scan(tiles);
+      const int excl = inc - tiles + carry;
+      const uint64_t hit = __ballot(tiles > 0 && mt >= excl && mt < excl + tiles);
+      if (hit) {
+        const int src = __ffsll((unsigned long long)hit) - 1;
+        const int sel_excl = __shfl(excl, src, kWave);
+        e = eb + src;
+        m0 = (mt - sel_excl) * kRCols;
+        rbase = offsets[e];
+        const int cnt_e = offsets[e + 1] - rbase;
+        mcount = (cnt_e - m0 < kRCols) ? cnt_e - m0 : kRCols;
+        break;
+      }
+      carry += __shfl(inc, kWave - 1, kWave);
+    }
+  }
+  if (e < 0) return;
+  const int r32 = lane % 32, kh = lane / 32;
+  const int KB = K / 32;
+  const int nchunk = (KB + 3) / 4;
+  const int NG = N / 32;
+  const int g = nt * kRWaves + wave;
+  const int gc = g < NG ? g : 0;  // a wave past N streams tile 0 again and stores nothing
+
+  // activation staging: piece i of this wave is slot 8 wave + 4 i + lane / 16, logical
+  // 16-byte column lane % 16, stored at column (lane % 16) ^ (slot & 15)
+  const uint16_t *rowp[2];
+  int soff[2];
+  bool sok[2];
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    const int slot = 8 * wave + 4 * i + lane / 16;
+    sok[i] = slot < mcount;
+    const int r = rbase + m0 + (sok[i] ? slot : 0);
+    rowp[i] = a_src + (a_by_token ? (int64_t)(sorted_slot[r] / k) : (int64_t)r) * K;  // row start
+    soff[i] = slot * 256 + (((lane % 16) ^ (slot & 15)) << 4);
+  }
+  u32x4_t ar[2][2];
+  auto aload = [&](int c, int s) {
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      // in range: elements c*128 + 8 (lane % 16) .. +7 of the row; otherwise the row's first 8
+      const int off = c * 128 + (lane % 16) * 8;
+      const bool ok = sok[i] && c < nchunk && off < K;
+      const u32x4_t v = *reinterpret_cast<const u32x4_t *>(rowp[i] + (ok ? off : 0));
+      ar[s][i] = ok ? v : u32x4_t{0u, 0u, 0u, 0u};
+    }
+  };
+  auto awrite = [&](int c, int s) {
+#pragma unroll
+    for (int i = 0; i < 2; ++i) *reinterpret_cast<u32x4_t *>(lds + (c & 1) * 8192 + soff[i]) = ar[s][i];
+  };
+  const uint8_t *cb = pcodes + ((int64_t)e * NG + gc) * nchunk * 2048 + lane * 16;
+  const uint32_t *sb = reinterpret_cast<const uint32_t *>(pscales + ((int64_t)e * NG + gc) * nchunk * 128) + r32;
+  u32x4_t cw[D][2];
+  uint32_t sw[D];
+  auto wload = [&](int c, int s) {
+    const int cc = c < nchunk ? c : 0;
+    cw[s][0] = *reinterpret_cast<const u32x4_t *>(cb + (int64_t)cc * 2048);
+    cw[s][1] = *reinterpret_cast<const u32x4_t *>(cb + (int64_t)cc * 2048 + 1024);
+    sw[s] = sb[cc * 32];
+  };
+  f32x16_t acc;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) acc[i] = 0.f;
+
+  // prologue: chunk 0 into LDS, chunks 1 and 2 in register sets 1 and 0, weights 0..D-1
+  aload(0, 0);
+#pragma unroll
+  for (int s = 0; s < D; ++s) wload(s, s);
+  awrite(0, 0);
+  aload(1, 1);
+  aload(2, 0);
+  // chunk c: barrier; MFMAs on LDS stage c & 1 with weight set u; write chunk c + 1 (register
+  // set a) to stage (c + 1) & 1, reload set a with chunk c + 3, reload weight set u with c + D
+  auto body = [&](int c, auto U_, auto A_) {
+    constexpr int u = decltype(U_)::value;
+    constexpr int a = decltype(A_)::value;
+    __syncthreads();
+    const unsigned char *abuf = lds + (c & 1) * 8192;
+#pragma unroll
+    for (int p = 0; p < 2; ++p) {
+      const float sc = e8m0_to_f32((sw[u] >> (8 * (2 * p + kh))) & 0xffu);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int col16 = 4 * (2 * p + kh) + j;
+        const bf16x8_t bv =
+            as_bf16x8(*reinterpret_cast<const u32x4_t *>(abuf + r32 * 256 + ((col16 ^ (r32 & 15)) << 4)));
+        acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fp4x8_to_bf16x8(cw[u][p][j], sc), bv, acc, 0, 0, 0);
+      }
+    }
+    awrite(c + 1, a);
+    aload(c + 3, a);
+    wload(c + D, u);
+  };
+  using I0 = std::integral_constant<int, 0>;
+  using I1 = std::integral_constant<int, 1>;
+  using I2 = std::integral_constant<int, 2 % D>;
+  using I3 = std::integral_constant<int, 3 % D>;
+  int c = 0;
+  for (; c + D <= nchunk; c += D) {
+    body(c, I0{}, I1{});
+    body(c + 1, I1{}, I0{});
+    if constexpr (D > 2) {
+      body(c + 2, I2{}, I1{});
+      body(c + 3, I3{}, I0{});
+    }
+  }
+  if (c < nchunk) body(c, I0{}, I1{});
+  if (c + 1 < nchunk) body(c + 1, I1{}, I0{});
+  if constexpr (D > 2)
+    if (c + 2 < nchunk) body(c + 2, I2{}, I1{});
+
+  // epilogue: lane holds slot lane % 32 and rows 32 g + 8 i + 4 kh + jj of the output
+  if (g >= NG || r32 >= mcount) return;
+  const int64_t r = rbase + m0 + r32;
+  uint2 bq[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+    bq[i] = bias ? *reinterpret_cast<const uint2 *>(bias + (int64_t)e * N + 32 * g + 8 * i + 4 * kh) : uint2{0u, 0u};
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int n = 32 * g + 8 * i + 4 * kh;
+    const float h0 = acc[4 * i + 0] + __uint_as_float(bq[i].x << 16);
+    const float h1 = acc[4 * i + 1] + __uint_as_float(bq[i].x & 0xffff0000u);
+    const float h2 = acc[4 * i + 2] + __uint_as_float(bq[i].y << 16);
+    const float h3 = acc[4 * i + 3] + __uint_as_float(bq[i].y & 0xffff0000u);
+    if (EPI == kEpiSwigluBf16 || EPI == kEpiActF32) {
+      const uint16_t a0 = f32_to_bf16_rne(swiglu_unit(h0, h1, limit, alpha));
+      const uint16_t a1 = f32_to_bf16_rne(swiglu_unit(h2, h3, limit, alpha));
+      if (EPI == kEpiSwigluBf16)
+        *reinterpret_cast<uint32_t *>(reinterpret_cast<uint16_t *>(out) + r * (N / 2) + n / 2) =
+            (uint32_t)a0 | ((uint32_t)a1 << 16);
+      else
+        *reinterpret_cast<float2 *>(reinterpret_cast<float *>(out) + r * (N / 2) + n / 2) =
+            float2{bf16_to_f32(a0), bf16_to_f32(a1)};
+    } else {
+      *reinterpret_cast<f32x4_t *>(reinterpret_cast<float *>(out) + r * N + n) = f32x4_t{h0, h1, h2, h3};
+    }
+  }
+}
+
 hipError_t launch_ffn_stream(const uint16_t *a_src, bool a_by_token, const int32_t *sorted_slot,
                              int k, const int32_t *offsets, int E, int64_t S, const MxWeight &w,
                              int epilogue, void *out, float limit, float alpha, hipStream_t stream) {
@@ -347,6 +533,31 @@ hipError_t launch_ffn_stream(const uint16_t *a_src, bool a_by_token, const int32
   hipLaunchKernelGGL(ffn_stream_kernel<EPI>, grid, block, 0, stream, a_src, a_by_token ? 1 : 0,    \
                      sorted_slot, k, offsets, E, w.codes, w.scales, w.bias, w.N, w.K, out, limit, \
                      alpha)
+  if (w.tiled && S >= kRowSplitMinSlots) {
+    const int64_t mt32 = (S + kRCols - 1) / kRCols + busy;
+    const int ntn = (w.N / 32 + kRWaves - 1) / kRWaves;
+    dim3 g1((unsigned)(mt32 * ntn));
+    const bool deep = S >= 128;  // a 4-chunk weight ring once the grid is large
+#define MOE_LAUNCH_ROWS(EPI)                                                                           \
+  do {                                                                                                 \
+    if (deep)                                                                                          \
+      hipLaunchKernelGGL((ffn_stream_rows_kernel<EPI, 4>), g1, dim3(kRWaves * kWave), 0, stream, a_src, \
+                         a_by_token ? 1 : 0, sorted_slot, k, offsets, E, w.codes, w.scales, w.bias, w.N, \
+                         w.K, ntn, out, limit, alpha);                                                 \
+    else                                                                                               \
+      hipLaunchKernelGGL((ffn_stream_rows_kernel<EPI, 2>), g1, dim3(kRWaves * kWave), 0, stream, a_src, \
+                         a_by_token ? 1 : 0, sorted_slot, k, offsets, E, w.codes, w.scales, w.bias, w.N, \
+                         w.K, ntn, out, limit, alpha);                                                 \
+  } while (0)
+    switch (epilogue) {
+      case kEpiSwigluBf16: MOE_LAUNCH_ROWS(kEpiSwigluBf16); break;
+      case kEpiPreactF32: MOE_LAUNCH_ROWS(kEpiPreactF32); break;
+      case kEpiActF32: MOE_LAUNCH_ROWS(kEpiActF32); break;
+      default: MOE_LAUNCH_ROWS(kEpiLinearF32); break;
+    }
+#undef MOE_LAUNCH_ROWS
+    return hipGetLastError();
+  }
   if (w.tiled) {
     // m-tile-major 1-D grid; a deeper register prefetch when few slots make few workgroups
     const int64_t mt32 = (S + kTCols - 1) / kTCols + busy;

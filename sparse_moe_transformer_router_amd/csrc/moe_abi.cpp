@@ -58,7 +58,7 @@ int check_weight(const moe_mxfp4_weight_t *w) {
   if (w == nullptr || w->codes == nullptr || w->scales == nullptr) return MOE_ERR_INVALID_ARG;
   if (w->layout != MOE_LAYOUT_ROWMAJOR && w->layout != MOE_LAYOUT_TILED) return MOE_ERR_INVALID_ARG;
   if (!aligned(w->codes, 16) || !aligned(w->bias, 2)) return MOE_ERR_INVALID_ARG;
-  if (w->layout == MOE_LAYOUT_TILED && !aligned(w->scales, 4)) return MOE_ERR_INVALID_ARG;
+  if (w->layout == MOE_LAYOUT_TILED && (!aligned(w->scales, 4) || !aligned(w->bias, 8))) return MOE_ERR_INVALID_ARG;
   if (check_dim(w->k) != MOE_OK || w->n < 1 || w->n > 2 * kMaxDim) return MOE_ERR_UNSUPPORTED;
   if (w->layout == MOE_LAYOUT_TILED && w->n % 32 != 0) return MOE_ERR_UNSUPPORTED;
   return MOE_OK;

@@ -100,6 +100,11 @@ def test_ffn_and_forward_errors():
     assert lib.moe_mxfp4_ffn(*args(g, _weight(H + 32, I), o)) == L.MOE_ERR_UNSUPPORTED     # down.n != H
     assert lib.moe_mxfp4_ffn(*args(_weight(2 * I, H, codes=FAKE + 1), d, o)) == L.MOE_ERR_INVALID_ARG
     assert lib.moe_mxfp4_ffn(*args(_weight(2 * I, H, scales=0), d, o)) == L.MOE_ERR_INVALID_ARG
+    # bias alignment: 2 bytes for the row-major layout, 8 for the tiled one
+    gt, dt = (L.MoeMxfp4Weight(FAKE, FAKE, FAKE + 4, 2 * I, H, 1), L.MoeMxfp4Weight(FAKE, FAKE, None, H, I, 1))
+    assert lib.moe_mxfp4_ffn(*args(gt, dt, o)) == L.MOE_ERR_INVALID_ARG
+    gr = L.MoeMxfp4Weight(FAKE, FAKE, FAKE + 1, 2 * I, H, 0)
+    assert lib.moe_mxfp4_ffn(*args(gr, d, o)) == L.MOE_ERR_INVALID_ARG
     assert lib.moe_mxfp4_ffn(*args(g, d, L.MoeOptions(7.0, 1.0, 3, 0, 0))) == L.MOE_ERR_INVALID_ARG
     assert lib.moe_mxfp4_ffn(*args(g, d, L.MoeOptions(7.0, 1.0, 0, 9, 0))) == L.MOE_ERR_INVALID_ARG
     assert lib.moe_mxfp4_ffn(*args(g, d, L.MoeOptions(-1.0, 1.0, 0, 0, 0))) == L.MOE_ERR_INVALID_ARG

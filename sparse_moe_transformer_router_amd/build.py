@@ -30,6 +30,7 @@ SOURCES = [
     "permute.hip",
     "ffn_stream.hip",
     "ffn_gemm.hip",
+    "gather.hip",
     "pack.hip",
     "combine.hip",
 ]

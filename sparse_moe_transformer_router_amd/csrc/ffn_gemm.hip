@@ -1,329 +1,368 @@
-// Expert FFN projections for prefill-sized batches: a grouped GEMM on the matrix cores.
+// Expert FFN projections for prefill-sized batches: a persistent grouped GEMM on the matrix
+// cores.
 //
 // Each expert's slots (review of the from-scratch gpt-oss-20B at pomoai.com, section 3.4)
 // are multiplied by its MXFP4 weights (gpt-oss walkthrough at pnsm.cn, sections 1 and 4),
 // with the clamped SwiGLU (+1 on the linear branch) fused into the gate_up epilogue
-// (walkthrough section 2.2; review section 3.3). Weights must be in the tiled layout.
+// (walkthrough section 2.2; review section 3.3). Weights must be in the tiled layout; the
+// activations are expert-sorted rows (x gathered by launch_gather_rows, or the act rows).
 //
-// Workgroup tile: 192 weight rows x 128 slots of one expert (192 divides 5760 and 2880).
-// Four waves in a 2 x 2 arrangement; a wave owns 96 rows (three 32-row weight tiles) x 64
-// slots (two 32-slot column groups): six v_mfma_f32_32x32x16_bf16 accumulators (96 fp32 in
-// AGPRs). The 32x32x16 form issues at twice the rate of 16x16x32 on gfx950. Weights are the
+// Output tile: 192 weight rows x 128 slots of one expert (192 divides 5760 and 2880). Four
+// waves in a 2 x 2 arrangement; a wave owns 96 rows (three 32-row weight tiles) x 64 slots
+// (two 32-slot column groups): six v_mfma_f32_32x32x16_bf16 accumulators. Weights are the
 // cheap operand (0.53 B per element against 2 B for a bf16 activation), so the tile is wide
-// in weight rows. Per 128-element chunk of the input dimension (one "stage"):
-//   * the 128 slots' bf16 activations (gathered rows of x, or rows of act) go straight from
-//     global memory to LDS with gfx950's global_load_lds_dwordx4 (no staging registers),
-//     into a 3-deep ring of 32 KB stages; each 256-byte slot row has its 16-byte columns
-//     XOR-swizzled by the row index, so a wave's 16-row reads land on distinct banks (the
-//     swizzle is applied on the global side: lane l of a DMA writes LDS column l % 16);
-//   * the workgroup's six weight tiles (2 KB each) and their scale tiles go to LDS the same
-//     way, so no global load has a register destination (register reuse would otherwise
-//     force the compiler to drain every load in flight);
-//   * all of a stage's loads are issued two stages ahead (12 DMA instructions per wave),
-//     spread over the eight MFMA k-steps of the chunk before. A stage is consumed after an
-//     explicit s_waitcnt vmcnt(12) (the next stage's loads may stay in flight) and a bare
-//     s_barrier -- no fence, which would drain the prefetches. Every DMA is issued
-//     unconditionally from a clamped, in-bounds address (past the last chunk the last chunk
-//     is re-loaded into the ring slot nobody reads), so the count is exact; tiles past N
-//     read tile 0 and their rows are never stored;
-//   * the LDS reads of the next MFMA k-step's slot operands are issued before the current
-//     step's MFMAs;
-//   * lane l of a weight tile holds MX block 4c + 2p + l/32 of row l%32 (p = 0, 1), split into
-//     four 8-element k-steps; the B operand reads the same k-assignment from LDS.
-#include <type_traits>
-
+// in weight rows.
+//
+// Persistent: one workgroup per CU walks a list of tiles, and its load stream runs across
+// tile boundaries, so a tile's start-up (locating its expert, first loads) and its epilogue
+// hide behind the neighbouring tiles' matrix work. Per 128-element chunk of the input
+// dimension (one "stage"), everything the chunk needs goes from global memory to LDS with
+// gfx950's global_load_lds (no register destinations: with loads into registers in flight
+// beside LDS DMA the compiler can only wait for all of them):
+//   * 128 slot rows x 256 bytes of bf16 activations into a 3-deep ring; each row's 16-byte
+//     columns are XOR-swizzled by the row index so a wave's 16-row reads hit distinct banks
+//     (applied on the global side: lane l of a DMA writes LDS column l % 16);
+//   * the six 2 KB weight tiles, their 128-byte scale tiles and the tile's 192 bias values.
+// Each wave issues exactly 13 DMAs per stage, two stages ahead, spread over the eight MFMA
+// k-steps of the chunk before; a stage is consumed after an explicit s_waitcnt vmcnt(13)
+// and a bare s_barrier (a fence would drain the prefetches). Every DMA reads a clamped,
+// in-bounds address (past the end of the list the last chunk is re-loaded into the ring
+// slot nobody reads), so the count is exact. Rows past N read tile 0 and are never stored;
+// slots past an m-tile's count re-read its first slot and are never stored.
+//
+// Tile order: workgroups are dispatched round-robin over the 8 XCDs (block b to XCD b % 8),
+// each with its own L2. XCD x owns a contiguous range of the tile list, ordered in groups of
+// kGGroupM m-tiles x all n-tiles (n-major), and its workgroups sweep the range together, so
+// the ~32 tiles an XCD works on at a time share 4 slot tiles and 8 weight tiles.
+//
+// Lane l of a weight tile holds MX block 4c + 2p + l/32 of row l%32 (p = 0, 1), split into
+// four 8-element k-steps; the B operand reads the same k-assignment from LDS.
 #include "common.h"
 #include "kernels.h"
 
 namespace moe {
 
-constexpr int kG2Cols = 128;            // slots per tile
-constexpr int kG2Stages = 3;            // LDS ring depth
-constexpr int kG2RowBytes = 256;        // one 128-element bf16 chunk of a slot
-constexpr int kG2StageBytes = kG2Cols * kG2RowBytes;
-constexpr int kG2RGW = 3;               // 32-row weight tiles per wave (wave owns 96 rows)
-constexpr int kG2Rows = 2 * 32 * kG2RGW;  // weight rows per workgroup
-constexpr int kG2Waves = 8;             // two per SIMD: 2 x 2 output quarters x 2 k-halves
-constexpr int kG2GroupM = 4;            // m-tiles per group of the XCD-local tile order
-constexpr int kXcds = 8;                // accelerator complex dies, one L2 each
+constexpr int kGCols = 128;                 // slots per tile
+constexpr int kGStages = 3;                 // LDS ring depth
+constexpr int kGRowBytes = 256;             // one 128-element bf16 chunk of a slot row
+constexpr int kGRGW = 3;                    // 32-row weight tiles per wave (96 rows)
+constexpr int kGRows = 2 * 32 * kGRGW;      // weight rows per tile
+constexpr int kGActBytes = kGCols * kGRowBytes;
+constexpr int kGWBytes = 2 * kGRGW * 2048;  // codes of the six weight tiles
+constexpr int kGSBytes = 1024;              // their scales (768 bytes used)
+constexpr int kGBBytes = 1024;              // the tile's bias (384 bytes used)
+constexpr int kGStageBytes = kGActBytes + kGWBytes + kGSBytes + kGBBytes;
+constexpr int kGDma = 13;                   // DMAs per wave per stage
+constexpr int kGGroupM = 4;                 // m-tiles per group of the XCD-local tile order
+constexpr int kXcds = 8;
+constexpr int kGMaxExperts = 256;
+constexpr size_t kGLds = (size_t)kGStages * kGStageBytes + (kGMaxExperts + 4) * sizeof(int32_t);
 
-__device__ __forceinline__ int g2_off(int row, int col16) { return row * kG2RowBytes + ((col16 ^ (row & 15)) << 4); }
+__device__ __forceinline__ int g_off(int row, int col16) { return row * kGRowBytes + ((col16 ^ (row & 15)) << 4); }
 
 __device__ __forceinline__ constexpr int vmcnt_imm(int n) {
   // s_waitcnt immediate with vmcnt = n (split field) and expcnt / lgkmcnt left at their maxima
   return (n & 0xf) | ((n >> 4) << 14) | (0x7 << 4) | (0xf << 8);
 }
 
-template <int EPI>
-__global__ __launch_bounds__(kG2Waves * 64) void ffn_gemm2_kernel(const uint16_t *__restrict__ a_src, int a_by_token,
-                                                        const int32_t *__restrict__ sorted_slot, int k,
-                                                        const int32_t *__restrict__ offsets, int E,
-                                                        const uint8_t *__restrict__ pcodes,
-                                                        const uint8_t *__restrict__ pscales,
-                                                        const uint16_t *__restrict__ bias, int N, int K, int ntiles_n,
-                                                        void *__restrict__ out, float limit, float alpha) {
-  constexpr int RGW = kG2RGW;
-  extern __shared__ __attribute__((aligned(16))) unsigned char lds[];
-  const int tid = threadIdx.x, lane = tid % 64;
-  const int wave = __builtin_amdgcn_readfirstlane(tid / 64);  // uniform: LDS targets stay scalar
-  const int wk = wave >> 2;                       // which half of every chunk's k-steps
-  const int wy = (wave >> 1) & 1, wx = wave & 1;  // weight-row half, slot half
-  // Real m-tile count: the grid is sized for the worst case, the surplus blocks exit.
-  int mt_total = 0;
+// An 8-byte LDS read that waits for its own result (inside the asm block). The compiler
+// cannot see that it reads LDS the in-flight DMAs do not touch, and would otherwise wait
+// for every load in flight before it.
+__device__ __forceinline__ uint2 lds_read_b64_sync(const void *p) {
+  const uint32_t a = (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void *)p;
+  uint2 v;
+  asm volatile("ds_read_b64 %0, %1\n\ts_waitcnt lgkmcnt(0)" : "=v"(v) : "v"(a) : "memory");
+  return v;
+}
+
+struct GTile {
+  int e, nt, row0, mcount;  // expert, weight-row tile, first sorted row, slots (1..128)
+};
+
+// Tile L of the global list -> its expert and rows, from the expert offsets held in LDS.
+__device__ GTile g_tile(int L, const int32_t *off, int E, int mt_total, int ntn, int lane) {
+  const int grp = L / (kGGroupM * ntn);
+  const int gm = (mt_total - grp * kGGroupM < kGGroupM) ? mt_total - grp * kGGroupM : kGGroupM;
+  const int rem = L - grp * kGGroupM * ntn;
+  const int mt = grp * kGGroupM + rem % gm;
+  GTile t{0, rem / gm, 0, 1};
+  int carry = 0;
   for (int eb = 0; eb < E; eb += 64) {
     const int ex = eb + lane;
-    const int cnt = (ex < E) ? offsets[ex + 1] - offsets[ex] : 0;
-    mt_total += __shfl(wave_inclusive_scan((cnt + kG2Cols - 1) / kG2Cols), 63, 64);
-  }
-  const int nb = mt_total * ntiles_n;
-  if ((int)blockIdx.x >= nb) return;
-  int mt, nt;
-  {
-    // Workgroups are dispatched round-robin over the 8 XCDs (block b to XCD b % 8), each with
-    // its own L2. Give XCD x a contiguous range of the nb logical tiles, and order a range in
-    // groups of kG2GroupM m-tiles x all n-tiles, n-major: the ~32 workgroups an XCD runs at a
-    // time then share 4 slot tiles and 8 weight tiles.
-    const int b = blockIdx.x, x = b % kXcds, loc = b / kXcds;
-    const int q = nb / kXcds, rr = nb % kXcds;
-    const int L = (x < rr) ? x * (q + 1) + loc : rr * (q + 1) + (x - rr) * q + loc;
-    const int grp = L / (kG2GroupM * ntiles_n);
-    const int gm = (mt_total - grp * kG2GroupM < kG2GroupM) ? mt_total - grp * kG2GroupM : kG2GroupM;
-    const int rem = L - grp * kG2GroupM * ntiles_n;
-    nt = rem / gm;
-    mt = grp * kG2GroupM + rem % gm;
-  }
-  int e = -1, m0 = 0, rbase = 0, mcount = 0;
-  {
-    int carry = 0;
-    for (int eb = 0; eb < E; eb += 64) {
-      const int ex = eb + lane;
-      const int cnt = (ex < E) ? offsets[ex + 1] - offsets[ex] : 0;
-      const int tiles = (cnt + kG2Cols - 1) / kG2Cols;
-      const int inc = wave_inclusive_scan(tiles);
-      const int excl = inc - tiles + carry;
-      const uint64_t hit = __ballot(tiles > 0 && mt >= excl && mt < excl + tiles);
-      if (hit) {
-        const int src = __ffsll((unsigned long long)hit) - 1;
-        const int sel_excl = __shfl(excl, src, 64);
-        e = eb + src;
-        m0 = (mt - sel_excl) * kG2Cols;
-        rbase = offsets[e];
-        const int cnt_e = offsets[e + 1] - rbase;
-        mcount = (cnt_e - m0 < kG2Cols) ? cnt_e - m0 : kG2Cols;
-        break;
-      }
-      carry += __shfl(inc, 63, 64);
+    const int cnt = (ex < E) ? off[ex + 1] - off[ex] : 0;
+    const int tiles = (cnt + kGCols - 1) / kGCols;
+    const int inc = wave_inclusive_scan(tiles);
+    const int excl = inc - tiles + carry;
+    const uint64_t hit = __ballot(tiles > 0 && mt >= excl && mt < excl + tiles);
+    if (hit) {
+      const int src = __ffsll((unsigned long long)hit) - 1;
+      const int e = eb + src;
+      const int m0 = (mt - __shfl(excl, src, 64)) * kGCols;
+      const int cnt_e = off[e + 1] - off[e];
+      t.e = e;
+      t.row0 = off[e] + m0;
+      t.mcount = (cnt_e - m0 < kGCols) ? cnt_e - m0 : kGCols;
+      break;
     }
+    carry += __shfl(inc, 63, 64);
   }
-  if (e < 0) return;
+  // wave-uniform by construction; say so, so the fields live in scalar registers
+  t.e = __builtin_amdgcn_readfirstlane(t.e);
+  t.nt = __builtin_amdgcn_readfirstlane(t.nt);
+  t.row0 = __builtin_amdgcn_readfirstlane(t.row0);
+  t.mcount = __builtin_amdgcn_readfirstlane(t.mcount);
+  return t;
+}
+
+template <int EPI>
+__global__ __launch_bounds__(256) void ffn_gemm_kernel(const uint16_t *__restrict__ a, const int32_t *__restrict__ offsets,
+                                                       int E, const uint8_t *__restrict__ pcodes,
+                                                       const uint8_t *__restrict__ pscales,
+                                                       const uint16_t *__restrict__ bias, int N, int K, int ntn,
+                                                       void *__restrict__ out, float limit, float alpha) {
+  constexpr int RGW = kGRGW;
+  extern __shared__ __attribute__((aligned(16))) unsigned char lds[];
+  int32_t *off = reinterpret_cast<int32_t *>(lds + kGStages * kGStageBytes);
+  const int tid = threadIdx.x, lane = tid % 64;
+  const int wave = __builtin_amdgcn_readfirstlane(tid / 64);  // uniform: LDS targets stay scalar
+  const int wy = wave >> 1, wx = wave & 1;                      // weight-row half, slot half
+  const int r32 = lane % 32, kh = lane / 32;
+
+  for (int i = tid; i <= E; i += 256) off[i] = offsets[i];
+  __syncthreads();
+  int mt_total = 0;  // m-tiles over all experts (the list is sized from them, not from the grid)
+  for (int eb = 0; eb < E; eb += 64) {
+    const int ex = eb + lane;
+    const int cnt = (ex < E) ? off[ex + 1] - off[ex] : 0;
+    mt_total += __shfl(wave_inclusive_scan((cnt + kGCols - 1) / kGCols), 63, 64);
+  }
+  mt_total = __builtin_amdgcn_readfirstlane(mt_total);
+  const int nb = mt_total * ntn;
+  // nx contiguous ranges of the list, one per XCD (fewer when the grid is smaller, so every
+  // range has workgroups); range x belongs to the workgroups b with b % nx == x
+  const int nx = (int)gridDim.x < kXcds ? (int)gridDim.x : kXcds;
+  const int x = blockIdx.x % nx, q = blockIdx.x / nx;
+  const int nq = ((int)gridDim.x - x + nx - 1) / nx;  // workgroups on range x
+  const int lo = (int)((int64_t)nb * x / nx), hi = (int)((int64_t)nb * (x + 1) / nx);
+  const int first = lo + q;
+  if (first >= hi) return;
+  const int ntiles = (hi - first + nq - 1) / nq;  // this workgroup's tiles: first + nq j
   const int KB = K / 32;
   const int nchunk = (KB + 3) / 4;
   const int NG = N / 32;
-  const int r32 = lane % 32, kh = lane / 32;
 
-  // staging: wave stages slot rows 16 wave + 4 i + lane / 16 (i = 0..3), physical 16-byte
-  // column lane % 16
-  const uint16_t *aptr[4];
-  int lcol[4];
+  // ---- issue side: the tile and chunk whose stage is loaded next
+  int ji = 0, ci = 0;
+  GTile ti = g_tile(first, off, E, mt_total, ntn, lane);
+  const uint16_t *aptr[8];
+  int lcol[8];
+  auto set_rows = [&]() {
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int row = 16 * wave + 4 * i + lane / 16;
-    const int srow = row < mcount ? row : 0;  // padding slots re-read slot 0 (results discarded)
-    const int r = rbase + m0 + srow;
-    lcol[i] = ((lane % 16) ^ (row & 15)) * 8;  // logical element offset within the chunk
-    aptr[i] = a_src + (a_by_token ? (int64_t)(sorted_slot[r] / k) : (int64_t)r) * K;
-  }
-  // One DMA of stage cc (a chunk index, always < nchunk) into ring slot `slot`; a wave issues
-  // six per stage:
-  //   i = 0..3: activation rows 4 i .. 4 i + 3 of this wave's 16;
-  //   i = 4, 5: waves 0..5: 1 KB half i - 4 of weight tile `wave`; waves 6, 7: 256 bytes of
-  //             the stage's scale block (bytes 512 (wave - 6) + 256 (i - 4) ...; the block
-  //             holds 2 RGW x 128 bytes, the rest is padding).
-  constexpr int kWStage = 2 * RGW * 2048;
-  constexpr int kSStage = 1024;
-  unsigned char *lds_w = lds + kG2Stages * kG2StageBytes;
-  unsigned char *lds_s = lds_w + kG2Stages * kWStage;
-  const int gt0 = nt * 2 * RGW;  // first weight tile of the workgroup
-  const uint8_t *cexp = pcodes + (int64_t)e * NG * nchunk * 2048 + lane * 16;
-  const uint8_t *sexp = pscales + (int64_t)e * NG * nchunk * 128;
-  auto dma = [&](int i, int cc, int slot) {
-    if (i < 4) {
-      int kk = cc * 128 + lcol[i];
-      kk = kk < K ? kk : 0;  // past K: any in-bounds element (its weight is an exact zero)
-      __builtin_amdgcn_global_load_lds(aptr[i] + kk,
-                                       lds + slot * kG2StageBytes + (16 * wave + 4 * i) * kG2RowBytes, 16, 0, 0);
-    } else if (wave < 2 * RGW) {
-      const int g = gt0 + wave;
-      const int64_t t = (g < NG) ? (int64_t)g * nchunk + cc : 0;
-      __builtin_amdgcn_global_load_lds(cexp + t * 2048 + (i - 4) * 1024,
-                                       lds_w + slot * kWStage + wave * 2048 + (i - 4) * 1024, 16, 0, 0);
+    for (int i = 0; i < 8; ++i) {
+      const int row = 32 * wave + 4 * i + lane / 16;
+      aptr[i] = a + (int64_t)(ti.row0 + (row < ti.mcount ? row : 0)) * K;
+    }
+  };
+#pragma unroll
+  for (int i = 0; i < 8; ++i) lcol[i] = ((lane % 16) ^ ((32 * wave + 4 * i + lane / 16) & 15)) * 8;
+  set_rows();
+  auto advance_issue = [&]() {
+    if (++ci < nchunk) return;
+    if (ji + 1 < ntiles) {
+      ++ji;
+      ci = 0;
+      ti = g_tile(first + ji * nq, off, E, mt_total, ntn, lane);
+      set_rows();
     } else {
-      const int ob = 512 * (wave - 2 * RGW) + 256 * (i - 4);  // first byte of this DMA
-      const int o = ob + 4 * lane;
-      const int ti = o / 128;
-      const int g = gt0 + ti;
-      const int64_t t = (ti < 2 * RGW && g < NG) ? (int64_t)g * nchunk + cc : 0;
-      __builtin_amdgcn_global_load_lds(sexp + t * 128 + (o % 128), lds_s + slot * kSStage + ob, 4, 0, 0);
+      ci = nchunk - 1;  // past the end: keep re-loading the last chunk (into a free slot)
+    }
+  };
+  // DMA i (0..12) of the issue-side chunk into ring slot `slot`:
+  //   0..7  activation rows 32 wave + 4 i .. + 3;
+  //   8..10 1 KB of weight codes: tile m / 2, half m % 2, m = 3 wave + i - 8;
+  //   11    256 bytes of the scale block (2 RGW tiles x 128 bytes, then padding);
+  //   12    waves 0, 1: 256 bytes of the tile's 384-byte bias run; waves 2, 3: a dummy.
+  const uint8_t *ccode = pcodes + lane * 16;
+  auto dma = [&](int i, int slot) {
+    unsigned char *st = lds + slot * kGStageBytes;
+    const int gt0 = ti.nt * 2 * RGW;
+    const int64_t ebase = (int64_t)ti.e * NG * nchunk;
+    if (i < 8) {
+      int kk = ci * 128 + lcol[i];
+      kk = kk < K ? kk : 0;  // past K: any in-bounds element (its weight is an exact zero)
+      __builtin_amdgcn_global_load_lds(aptr[i] + kk, st + (32 * wave + 4 * i) * kGRowBytes, 16, 0, 0);
+    } else if (i < 11) {
+      const int m = 3 * wave + i - 8;
+      const int g = gt0 + m / 2;
+      const int64_t t = (g < NG) ? ebase + (int64_t)g * nchunk + ci : 0;
+      __builtin_amdgcn_global_load_lds(ccode + t * 2048 + (m % 2) * 1024, st + kGActBytes + m * 1024, 16, 0, 0);
+    } else if (i == 11) {
+      const int o = 256 * wave + 4 * lane;
+      const int tt = o / 128, g = gt0 + tt;
+      const int64_t t = (tt < 2 * RGW && g < NG) ? ebase + (int64_t)g * nchunk + ci : 0;
+      __builtin_amdgcn_global_load_lds(pscales + t * 128 + (o % 128), st + kGActBytes + kGWBytes + 256 * wave, 4, 0,
+                                       0);
+    } else {
+      const int o = 256 * wave + 4 * lane;  // byte of the tile's bias run
+      const int n = ti.nt * kGRows + o / 2;
+      const uint16_t *src = (bias != nullptr && o < 2 * kGRows && n < N) ? bias + (int64_t)ti.e * N + n
+                                                                         : reinterpret_cast<const uint16_t *>(pscales);
+      __builtin_amdgcn_global_load_lds(src, st + kGActBytes + kGWBytes + kGSBytes + 256 * wave, 4, 0, 0);
     }
   };
 
+  // ---- compute side
+  GTile tc = ti;
   f32x16_t acc[RGW][2];
+  auto zero = [&]() {
 #pragma unroll
-  for (int g = 0; g < RGW; ++g)
-#pragma unroll
-    for (int b = 0; b < 2; ++b)
-#pragma unroll
-      for (int i = 0; i < 16; ++i) acc[g][b][i] = 0.f;
-
-  // Every chunk issues exactly 6 DMAs per wave (past the last chunk they re-load the last
-  // chunk into the ring slot nobody reads), so before chunk c the younger loads are always
-  // chunk c+1's 6.
-#pragma unroll
-  for (int i = 0; i < 6; ++i) dma(i, 0, 0);
-#pragma unroll
-  for (int i = 0; i < 6; ++i) dma(i, nchunk > 1 ? 1 : 0, 1);
-  const int p = wk;  // this wave's half of each chunk: MX blocks 4c + 2p + kh
-  for (int c = 0; c < nchunk; ++c) {
-    __builtin_amdgcn_s_waitcnt(vmcnt_imm(6));
-    __builtin_amdgcn_s_barrier();
-    const int cn = (c + 2 < nchunk) ? c + 2 : nchunk - 1;  // chunk staged during this one
-    const int sn = (c + 2) % kG2Stages;                      // its ring slot (read by nobody now)
-    const int sc_ = c % kG2Stages;
-    const unsigned char *abuf = lds + sc_ * kG2StageBytes;
-    const unsigned char *wbuf = lds_w + sc_ * kWStage + (wy * RGW) * 2048 + p * 1024 + lane * 16;
-    const unsigned char *sbuf = lds_s + sc_ * kSStage + (wy * RGW) * 128 + r32 * 4;
-    u32x4_t cw[RGW];
-    float sc[RGW];
-#pragma unroll
-    for (int g = 0; g < RGW; ++g) {
-      cw[g] = *reinterpret_cast<const u32x4_t *>(wbuf + g * 2048);
-      sc[g] = e8m0_to_f32((*reinterpret_cast<const uint32_t *>(sbuf + g * 128) >> (8 * (2 * p + kh))) & 0xffu);
-    }
-    auto bload = [&](int j, bf16x8_t *bv) {
+    for (int g = 0; g < RGW; ++g)
 #pragma unroll
       for (int b = 0; b < 2; ++b)
-        bv[b] = as_bf16x8(
-            *reinterpret_cast<const u32x4_t *>(abuf + g2_off(wx * 64 + 32 * b + r32, 4 * (2 * p + kh) + j)));
-    };
-    bf16x8_t bcur[2], bnext[2];
-    bload(0, bcur);
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      if (j < 3) bload(j + 1, bnext);
-      // this k-step's share of the next stage's DMAs, issued in the shadow of its MFMAs
-      if (j < 2) {
-        dma(2 * j, cn, sn);
-        dma(2 * j + 1, cn, sn);
-      } else {
-        dma(j + 2, cn, sn);
+        for (int i = 0; i < 16; ++i) acc[g][b][i] = 0.f;
+  };
+  zero();
+
+  // epilogue of the compute-side tile from ring slot `slot` (its last chunk's stage holds the
+  // tile's bias): lane holds slot column wx*64 + 32b + r32 and rows 8i + 4kh + jj of tile g
+  auto epilogue = [&](int slot) {
+    const unsigned char *bb = lds + slot * kGStageBytes + kGActBytes + kGWBytes + kGSBytes;
+    const int nloc0 = wy * 32 * RGW;
+    const uint32_t bmask = bias != nullptr ? 0xffffffffu : 0u;  // without bias the run holds junk
+    uint2 bq[RGW][4];
+#pragma unroll
+    for (int g = 0; g < RGW; ++g)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const uint2 v = lds_read_b64_sync(bb + 2 * (nloc0 + 32 * g + 8 * i + 4 * kh));
+        bq[g][i] = uint2{v.x & bmask, v.y & bmask};
       }
+#pragma unroll
+    for (int b = 0; b < 2; ++b) {
+      const int col = wx * 64 + 32 * b + r32;
+      if (col >= tc.mcount) continue;
+      const int64_t r = tc.row0 + col;
 #pragma unroll
       for (int g = 0; g < RGW; ++g) {
-        const bf16x8_t wa = fp4x8_to_bf16x8(cw[g][j], sc[g]);
 #pragma unroll
-        for (int b = 0; b < 2; ++b)
-          acc[g][b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wa, bcur[b], acc[g][b], 0, 0, 0);
-      }
-      bcur[0] = bnext[0];
-      bcur[1] = bnext[1];
-    }
-  }
-  __builtin_amdgcn_s_waitcnt(0);  // no DMA may still target this workgroup's LDS
-  __syncthreads();                // every wave is done reading the ring
-
-  // The two halves of each output tile: the p = 1 waves hand their sums to the p = 0 waves
-  // through LDS (fixed order: p = 0 sum + p = 1 sum).
-  {
-    f32x4_t *red = reinterpret_cast<f32x4_t *>(lds) + (wave & 3) * (RGW * 2 * 4) * 64 + lane;
-    if (wk == 1) {
-#pragma unroll
-      for (int g = 0; g < RGW; ++g)
-#pragma unroll
-        for (int b = 0; b < 2; ++b)
-#pragma unroll
-          for (int q = 0; q < 4; ++q)
-            red[((g * 2 + b) * 4 + q) * 64] =
-                f32x4_t{acc[g][b][4 * q], acc[g][b][4 * q + 1], acc[g][b][4 * q + 2], acc[g][b][4 * q + 3]};
-    }
-    __syncthreads();
-    if (wk == 1) return;
-#pragma unroll
-    for (int g = 0; g < RGW; ++g)
-#pragma unroll
-      for (int b = 0; b < 2; ++b)
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          const f32x4_t o = red[((g * 2 + b) * 4 + q) * 64];
-#pragma unroll
-          for (int u = 0; u < 4; ++u) acc[g][b][4 * q + u] += o[u];
-        }
-  }
-
-  // epilogue: lane holds slot column wx*64 + 32b + r32 and, per tile g, rows 8i + 4kh + jj.
-  // The bias of a lane's rows is 4 consecutive bf16 per (g, i): twelve 8-byte loads, all
-  // issued before any is used (clamped rows past N read row 0 and are never stored).
-  const int nbase = nt * kG2Rows + wy * 32 * RGW;
-  uint2 bq[RGW][4];
-#pragma unroll
-  for (int g = 0; g < RGW; ++g)
-#pragma unroll
-    for (int i = 0; i < 4; ++i) bq[g][i] = uint2{0u, 0u};
-  if (bias != nullptr) {
-    const uint16_t *be = bias + (int64_t)e * N;
-#pragma unroll
-    for (int g = 0; g < RGW; ++g)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int n = nbase + 32 * g + 8 * i + 4 * kh;
-        bq[g][i] = *reinterpret_cast<const uint2 *>(be + (n < N ? n : 0));
-      }
-  }
-#pragma unroll
-  for (int b = 0; b < 2; ++b) {
-    const int col = wx * 64 + 32 * b + r32;
-    if (col >= mcount) continue;
-    const int64_t r = rbase + m0 + col;
-#pragma unroll
-    for (int g = 0; g < RGW; ++g) {
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int n = nbase + 32 * g + 8 * i + 4 * kh;
-        if (n >= N) continue;
-        float h[4];
-        h[0] = acc[g][b][4 * i + 0] + __uint_as_float(bq[g][i].x << 16);
-        h[1] = acc[g][b][4 * i + 1] + __uint_as_float(bq[g][i].x & 0xffff0000u);
-        h[2] = acc[g][b][4 * i + 2] + __uint_as_float(bq[g][i].y << 16);
-        h[3] = acc[g][b][4 * i + 3] + __uint_as_float(bq[g][i].y & 0xffff0000u);
-        if (EPI == kEpiSwigluBf16 || EPI == kEpiActF32) {
-          const int half = N / 2;
-          const uint16_t a0 = f32_to_bf16_rne(swiglu_unit(h[0], h[1], limit, alpha));
-          const uint16_t a1 = f32_to_bf16_rne(swiglu_unit(h[2], h[3], limit, alpha));
-          if (EPI == kEpiSwigluBf16) {
-            *reinterpret_cast<uint32_t *>(reinterpret_cast<uint16_t *>(out) + r * half + n / 2) =
-                (uint32_t)a0 | ((uint32_t)a1 << 16);
+        for (int i = 0; i < 4; ++i) {
+          const int n = tc.nt * kGRows + nloc0 + 32 * g + 8 * i + 4 * kh;
+          if (n >= N) continue;
+          float h[4];
+          h[0] = acc[g][b][4 * i + 0] + __uint_as_float(bq[g][i].x << 16);
+          h[1] = acc[g][b][4 * i + 1] + __uint_as_float(bq[g][i].x & 0xffff0000u);
+          h[2] = acc[g][b][4 * i + 2] + __uint_as_float(bq[g][i].y << 16);
+          h[3] = acc[g][b][4 * i + 3] + __uint_as_float(bq[g][i].y & 0xffff0000u);
+          if (EPI == kEpiSwigluBf16 || EPI == kEpiActF32) {
+            const int half = N / 2;
+            const uint16_t a0 = f32_to_bf16_rne(swiglu_unit(h[0], h[1], limit, alpha));
+            const uint16_t a1 = f32_to_bf16_rne(swiglu_unit(h[2], h[3], limit, alpha));
+            if (EPI == kEpiSwigluBf16) {
+              *reinterpret_cast<uint32_t *>(reinterpret_cast<uint16_t *>(out) + r * half + n / 2) =
+                  (uint32_t)a0 | ((uint32_t)a1 << 16);
+            } else {
+              *reinterpret_cast<float2 *>(reinterpret_cast<float *>(out) + r * half + n / 2) =
+                  float2{bf16_to_f32(a0), bf16_to_f32(a1)};
+            }
           } else {
-            *reinterpret_cast<float2 *>(reinterpret_cast<float *>(out) + r * half + n / 2) =
-                float2{bf16_to_f32(a0), bf16_to_f32(a1)};
+            *reinterpret_cast<f32x4_t *>(reinterpret_cast<float *>(out) + r * N + n) =
+                f32x4_t{h[0], h[1], h[2], h[3]};
           }
-        } else {
-          *reinterpret_cast<f32x4_t *>(reinterpret_cast<float *>(out) + r * N + n) = f32x4_t{h[0], h[1], h[2], h[3]};
         }
       }
     }
+  };
+
+  // prologue: stages 0 and 1
+#pragma unroll
+  for (int s = 0; s < 2; ++s) {
+#pragma unroll
+    for (int i = 0; i < kGDma; ++i) dma(i, s);
+    advance_issue();
   }
+  int G = 0;  // global chunk counter: ring slot G % 3
+  for (int jc = 0; jc < ntiles; ++jc) {
+    for (int cc = 0; cc < nchunk; ++cc, ++G) {
+      // this wave's 13 loads of stage G are the oldest outstanding but for stage G+1's 13
+      __builtin_amdgcn_s_waitcnt(vmcnt_imm(kGDma));
+      __builtin_amdgcn_s_barrier();
+      const int slot = G % kGStages, nslot = (G + 2) % kGStages;
+      const unsigned char *abuf = lds + slot * kGStageBytes;
+      const unsigned char *wbuf = abuf + kGActBytes + (wy * RGW) * 2048 + lane * 16;
+      const unsigned char *sbuf = abuf + kGActBytes + kGWBytes + (wy * RGW) * 128 + r32 * 4;
+      uint32_t swd[RGW];
+#pragma unroll
+      for (int g = 0; g < RGW; ++g) swd[g] = *reinterpret_cast<const uint32_t *>(sbuf + g * 128);
+      auto bload = [&](int p, int j, bf16x8_t *bv) {
+#pragma unroll
+        for (int b = 0; b < 2; ++b)
+          bv[b] = as_bf16x8(
+              *reinterpret_cast<const u32x4_t *>(abuf + g_off(wx * 64 + 32 * b + r32, 4 * (2 * p + kh) + j)));
+      };
+      bf16x8_t bcur[2], bnext[2];
+      bload(0, 0, bcur);
+#pragma unroll
+      for (int p = 0; p < 2; ++p) {
+        u32x4_t cw[RGW];
+        float sc[RGW];
+#pragma unroll
+        for (int g = 0; g < RGW; ++g) {
+          cw[g] = *reinterpret_cast<const u32x4_t *>(wbuf + g * 2048 + p * 1024);
+          sc[g] = e8m0_to_f32((swd[g] >> (8 * (2 * p + kh))) & 0xffu);
+        }
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const int s = 4 * p + j;
+          const int nj = (j + 1) & 3, np = p + (j == 3 ? 1 : 0);
+          if (np < 2) bload(np, nj, bnext);
+          // this k-step's share of the stage-after-next DMAs, in the shadow of its MFMAs
+          dma(s, nslot);
+          if (s < 5) dma(8 + s, nslot);
+#pragma unroll
+          for (int g = 0; g < RGW; ++g) {
+            const bf16x8_t wa = fp4x8_to_bf16x8(cw[g][j], sc[g]);
+#pragma unroll
+            for (int b = 0; b < 2; ++b)
+              acc[g][b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wa, bcur[b], acc[g][b], 0, 0, 0);
+          }
+          bcur[0] = bnext[0];
+          bcur[1] = bnext[1];
+        }
+      }
+      advance_issue();
+    }
+    epilogue((G - 1) % kGStages);  // the tile's last chunk is still in its ring slot
+    zero();
+    if (jc + 1 < ntiles) tc = g_tile(first + (jc + 1) * nq, off, E, mt_total, ntn, lane);
+  }
+  __builtin_amdgcn_s_waitcnt(0);  // no DMA may still target this workgroup's LDS when it ends
 }
 
-hipError_t launch_ffn_gemm(const uint16_t *a_src, bool a_by_token, const int32_t *sorted_slot, int k,
-                           const int32_t *offsets, int E, int64_t S, const MxWeight &w, int epilogue, void *out,
-                           float limit, float alpha, hipStream_t stream) {
+int gemm_grid_cap() {
+  static int cus[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  if (cus[dev] == 0) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
+    cus[dev] = n;
+  }
+  return cus[dev];
+}
+
+hipError_t launch_ffn_gemm(const uint16_t *a_sorted, const int32_t *offsets, int E, int64_t S, const MxWeight &w,
+                           int epilogue, void *out, float limit, float alpha, hipStream_t stream) {
+  if (E > kGMaxExperts) return hipErrorInvalidValue;
   const int64_t busy = (S < E) ? S : E;
-  const int64_t mtiles = (S + kG2Cols - 1) / kG2Cols + busy;
-  const int ntn = (w.N + kG2Rows - 1) / kG2Rows;
-  dim3 grid((unsigned)(mtiles * ntn));
-  const size_t lds = (size_t)kG2Stages * (kG2StageBytes + 2 * kG2RGW * 2048 + 1024);
-#define MOE_LAUNCH_GEMM(EPI)                                                                          \
-  hipLaunchKernelGGL(ffn_gemm2_kernel<EPI>, grid, dim3(kG2Waves * 64), lds, stream, a_src, a_by_token ? 1 : 0, \
-                     sorted_slot, k, offsets, E, w.codes, w.scales, w.bias, w.N, w.K, ntn, out, limit, alpha)
+  const int64_t mtiles = (S + kGCols - 1) / kGCols + busy;  // bound on the real m-tile count
+  const int ntn = (w.N + kGRows - 1) / kGRows;
+  const int64_t bound = mtiles * ntn;
+  const int cap = gemm_grid_cap();  // one workgroup per CU (the LDS ring takes most of a CU)
+  dim3 grid((unsigned)(bound < cap ? bound : cap));
+#define MOE_LAUNCH_GEMM(EPI)                                                                                 \
+  hipLaunchKernelGGL(ffn_gemm_kernel<EPI>, grid, dim3(256), kGLds, stream, a_sorted, offsets, E, w.codes, \
+                     w.scales, w.bias, w.N, w.K, ntn, out, limit, alpha)
   switch (epilogue) {
     case kEpiSwigluBf16: MOE_LAUNCH_GEMM(kEpiSwigluBf16); break;
     case kEpiPreactF32: MOE_LAUNCH_GEMM(kEpiPreactF32); break;

@@ -43,10 +43,15 @@ hipError_t launch_ffn_stream(const uint16_t *a_src, bool a_by_token, const int32
                              int k, const int32_t *offsets, int E, int64_t S, const MxWeight &w,
                              int epilogue, void *out, float limit, float alpha, hipStream_t stream);
 
-// One expert GEMM, LDS-tiled grouped-GEMM family (tiled weights only), same contract.
-hipError_t launch_ffn_gemm(const uint16_t *a_src, bool a_by_token, const int32_t *sorted_slot, int k,
-                           const int32_t *offsets, int E, int64_t S, const MxWeight &w, int epilogue, void *out,
-                           float limit, float alpha, hipStream_t stream);
+// One expert GEMM, persistent LDS-tiled grouped-GEMM family (tiled weights only): the
+// activations are expert-sorted rows a_sorted[r * K] (r = sorted row); output rows are
+// sorted rows. E at most 256.
+hipError_t launch_ffn_gemm(const uint16_t *a_sorted, const int32_t *offsets, int E, int64_t S, const MxWeight &w,
+                           int epilogue, void *out, float limit, float alpha, hipStream_t stream);
+
+// xs[r] = x[sorted_slot[r] / k] for every sorted row r (rows of H bf16).
+hipError_t launch_gather_rows(const uint16_t *x, const int32_t *sorted_slot, int k, int64_t S, int H,
+                              uint16_t *xs, hipStream_t stream);
 
 hipError_t launch_combine(const float *y, const int32_t *slot_row, const float *topk_w, int64_t T,
                           int k, int H, void *out, bool out_f32, hipStream_t stream);

@@ -21,7 +21,7 @@ size_t align_up(size_t v) { return (v + kWsAlign - 1) / kWsAlign * kWsAlign; }
 
 // One workspace layout serves every entry point (each uses a subset of the regions).
 struct WsLayout {
-  size_t logits, topk_idx, topk_w, offsets, sorted_slot, slot_row, act, y, total;
+  size_t logits, topk_idx, topk_w, offsets, sorted_slot, slot_row, act, y, xs, total;
 };
 
 bool ws_layout(int64_t T, int E, int k, int H, int I, WsLayout *L) {
@@ -36,6 +36,7 @@ bool ws_layout(int64_t T, int E, int k, int H, int I, WsLayout *L) {
   L->slot_row = off;    off = align_up(off + S * sizeof(int32_t));
   L->act = off;         off = align_up(off + S * (size_t)I * sizeof(uint16_t));
   L->y = off;           off = align_up(off + S * (size_t)H * sizeof(float));
+  L->xs = off;          off = align_up(off + S * (size_t)H * sizeof(uint16_t));  // sorted x (GEMM path)
   L->total = off;
   return true;
 }
@@ -106,16 +107,19 @@ bool use_gemm(const moe_options_t &o, const moe_mxfp4_weight_t &gu, const moe_mx
   return S >= kGemmSlotsPerExpert * (int64_t)E;
 }
 
-// The expert GEMMs that follow the permutation. Arguments already validated.
+// The expert GEMMs that follow the permutation. Arguments already validated. The GEMM
+// family reads its gate_up activations from an expert-sorted copy of x (xs, S x H bf16).
 int run_ffn(const uint16_t *x, int64_t T, int k, int E, const int32_t *offsets, const int32_t *sorted_slot,
             const moe_mxfp4_weight_t &gu, const moe_mxfp4_weight_t &dn, const moe_options_t &o, float *y,
-            uint16_t *act, hipStream_t stream) {
+            uint16_t *act, uint16_t *xs, hipStream_t stream) {
   const int64_t S = T * k;
   const moe::MxWeight w1 = mx(gu);
   const moe::MxWeight w2 = mx(dn);
   const bool gemm = use_gemm(o, gu, dn, S, E);
+  if (gemm && moe::launch_gather_rows(x, sorted_slot, k, S, gu.k, xs, stream) != hipSuccess) return MOE_ERR_HIP;
+  // a: x (first projection) or act (second); by_token says which
   auto launch = [&](const uint16_t *a, bool by_token, const moe::MxWeight &w, int epi, void *out) {
-    return gemm ? moe::launch_ffn_gemm(a, by_token, sorted_slot, k, offsets, E, S, w, epi, out, o.swiglu_limit,
+    return gemm ? moe::launch_ffn_gemm(by_token ? xs : a, offsets, E, S, w, epi, out, o.swiglu_limit,
                                        o.swiglu_alpha, stream)
                 : moe::launch_ffn_stream(a, by_token, sorted_slot, k, offsets, E, S, w, epi, out, o.swiglu_limit,
                                          o.swiglu_alpha, stream);
@@ -166,7 +170,7 @@ int forward_impl(const uint16_t *x, const moe_router_t *router, const moe_mxfp4_
     return MOE_ERR_HIP;
   if (moe::launch_permute(idx, S, E, offsets, sorted_slot, slot_row, stream) != hipSuccess)
     return MOE_ERR_HIP;
-  int st = run_ffn(x, T, k, E, offsets, sorted_slot, *gu, *dn, o, y, act, stream);
+  int st = run_ffn(x, T, k, E, offsets, sorted_slot, *gu, *dn, o, y, act, at<uint16_t>(ws, L.xs), stream);
   if (st != MOE_OK) return st;
   if (moe::launch_combine(y, slot_row, wts, T, k, H, out, o.out_dtype == MOE_DTYPE_F32, stream) !=
       hipSuccess)
@@ -322,7 +326,7 @@ int moe_mxfp4_ffn(const uint16_t *x, int64_t T, int32_t k, int32_t E, const int3
   if (ws == nullptr || ws_bytes < L.total) return MOE_ERR_WORKSPACE;
   if (!aligned(ws, kWsAlign)) return MOE_ERR_INVALID_ARG;
   return run_ffn(x, T, k, E, expert_offsets, sorted_slot, *gate_up, *down, o, y, at<uint16_t>(ws, L.act),
-                 (hipStream_t)stream);
+                 at<uint16_t>(ws, L.xs), (hipStream_t)stream);
   MOE_GUARD_END
 }
 

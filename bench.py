@@ -48,7 +48,80 @@ def parse():
                    help="weights prepacked once (untimed) into the kernel layout, or row-major")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--no-sweep", action="store_true")
+    p.add_argument("--pmc-summary", nargs=4, metavar=("COPY_FETCH", "COPY_WRITE", "FETCH", "WRITE"),
+                   help="only print the traffic line for --workload/--T from four rocprofv3 --pmc csv "
+                        "output folders (FETCH_SIZE and WRITE_SIZE of --copy-calibration 1024, then of "
+                        "this benchmark) and exit")
+    p.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
+                   help="only copy MIB MiB device-to-device 4 times and exit: the known-size copy "
+                        "that scales the FETCH_SIZE / WRITE_SIZE counters of a profiled run")
     return p.parse_args()
+
+
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "pmc_traffic.md")
+CALIBRATION_MIB = 1024
+FFN_KERNELS = ("ffn_", "gather_rows")  # kernels one moe_mxfp4_ffn call launches, once each
+
+
+def kernel_source_hash():
+    """Hash of the library's kernel sources: a stored traffic figure is valid for these only."""
+    import hashlib
+    csrc = os.path.join(ROOT, "sparse_moe_transformer_router_amd", "csrc")
+    h = hashlib.sha256()
+    for name in sorted(os.listdir(csrc)):
+        if name.endswith((".hip", ".h", ".cpp")):
+            with open(os.path.join(csrc, name), "rb") as f:
+                h.update(name.encode() + b"\0" + f.read())
+    return h.hexdigest()[:16]
+
+
+def pmc_means(folder, counter):
+    """Mean counter value per dispatch, per kernel name, from a rocprofv3 --pmc csv folder."""
+    import csv
+    import glob
+    sums = {}
+    for path in glob.glob(os.path.join(folder, "*counter_collection.csv")):
+        with open(path) as f:
+            for r in csv.DictReader(f):
+                if r["Counter_Name"] != counter:
+                    continue
+                name = r["Kernel_Name"].split("(")[0].replace("void ", "").strip()
+                tot, n = sums.get(name, (0.0, 0))
+                sums[name] = (tot + float(r["Counter_Value"]), n + 1)
+    return {k: t / n for k, (t, n) in sums.items()}
+
+
+def pmc_summary(args, T):
+    cal = CALIBRATION_MIB << 10  # KiB the copy moves each way
+    cf = pmc_means(args.pmc_summary[0], "FETCH_SIZE")
+    cw = pmc_means(args.pmc_summary[1], "WRITE_SIZE")
+    copy = [k for k in cf if "copyBuffer" in k]
+    fetch_scale = cal / cf[copy[0]]
+    write_scale = cal / cw[copy[0]]
+    f = pmc_means(args.pmc_summary[2], "FETCH_SIZE")
+    w = pmc_means(args.pmc_summary[3], "WRITE_SIZE")
+    names = sorted(k for k in f if any(t in k for t in FFN_KERNELS))
+    fk = sum(f[k] for k in names)
+    wk = sum(w.get(k, 0.0) for k in names)
+    nbytes = int(round((fk * fetch_scale + wk * write_scale) * 1024))
+    print(f"traffic workload={args.workload} T={T} src={kernel_source_hash()} bytes={nbytes} "
+          f"fetch_kib={fk:.0f} write_kib={wk:.0f} fetch_scale={fetch_scale:.4f} write_scale={write_scale:.4f} "
+          f"kernels={'+'.join(n.replace(' ', '') for n in names)}", flush=True)
+
+
+def stored_traffic(workload, T):
+    """HBM bytes per expert-FFN call measured by rocprofv3 for these exact kernel sources, or None."""
+    if not os.path.exists(TRAFFIC_FILE):
+        return None
+    src = kernel_source_hash()
+    with open(TRAFFIC_FILE) as f:
+        for line in f:
+            if not line.startswith("traffic "):
+                continue
+            kv = dict(t.split("=", 1) for t in line.split()[1:])
+            if kv.get("workload") == workload and kv.get("T") == str(T) and kv.get("src") == src:
+                return int(kv["bytes"])
+    return None
 
 
 def main():
@@ -62,8 +135,21 @@ def main():
     import synth
     import sparse_moe_transformer_router_amd as moe
 
+    if args.pmc_summary:
+        cfg = synth.get_config(args.workload)
+        pmc_summary(args, args.T or cfg.T_list[-1])
+        return
     torch.cuda.init()
     dev = torch.device("cuda:0")
+    if args.copy_calibration:
+        n = args.copy_calibration << 20
+        src = torch.ones(n, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(4):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_calibration_bytes": n, "copies": 4}), flush=True)
+        return
     cfg = synth.get_config(args.workload)
     T = args.T or cfg.T_list[-1]
     L = args.layers or (24 if cfg.E <= 32 else 36)
@@ -155,11 +241,12 @@ def main():
     if decode_like:
         achieved = ffn_bytes / (ffn_ms * 1e-3) / 1e9
         roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                    "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None}
+                    "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": stored_traffic(cfg.name, T)}
     else:
         achieved = ffn_flops / (ffn_ms * 1e-3) / 1e12
         roofline = {"bound": "mfma", "achieved": round(achieved, 1), "peak": BF16_PEAK_TFLOPS,
-                    "unit": "TFLOP/s", "frac": round(achieved / BF16_PEAK_TFLOPS, 4), "traffic": None,
+                    "unit": "TFLOP/s", "frac": round(achieved / BF16_PEAK_TFLOPS, 4),
+                    "traffic": stored_traffic(cfg.name, T),
                     "frac_of_mxfp4_peak": round(achieved / MXFP4_PEAK_TFLOPS, 4)}
     roofline.update({"kernel": "moe_mxfp4_ffn (gate_up + down)", "ms_per_launch": round(ffn_ms, 5),
                      "algorithmic_bytes": int(ffn_bytes), "algorithmic_flops": ffn_flops})

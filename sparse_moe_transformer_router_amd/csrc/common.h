@@ -71,6 +71,24 @@ __device__ __forceinline__ int wave_inclusive_scan(int v) {
   return v;
 }
 
+// Maximum over the wave's 64 lanes, for every lane. DPP moves (register speed, no LDS round
+// trip): swap neighbours, swap pairs, mirror within 8 and within 16 lanes (every row of 16
+// now holds its maximum), then broadcast lane 15 of a row into the next row and lane 31 into
+// the upper half, so lane 63 holds the maximum of all 64.
+__device__ __forceinline__ float wave_max_f32(float v) {
+  int x = __float_as_int(v);
+#define MOE_DPP_MAX(CTRL, ROWS) \
+  x = __float_as_int(fmaxf(__int_as_float(x), __int_as_float(__builtin_amdgcn_update_dpp(x, x, CTRL, ROWS, 0xF, false))))
+  MOE_DPP_MAX(0xB1, 0xF);   // quad_perm [1, 0, 3, 2]
+  MOE_DPP_MAX(0x4E, 0xF);   // quad_perm [2, 3, 0, 1]
+  MOE_DPP_MAX(0x141, 0xF);  // row_half_mirror
+  MOE_DPP_MAX(0x140, 0xF);  // row_mirror
+  MOE_DPP_MAX(0x142, 0xA);  // row_bcast15 into rows 1 and 3
+  MOE_DPP_MAX(0x143, 0xC);  // row_bcast31 into rows 2 and 3
+#undef MOE_DPP_MAX
+  return __int_as_float(__builtin_amdgcn_readlane(x, 63));
+}
+
 __device__ __forceinline__ int wave_sum(int v) {
 #pragma unroll
   for (int d = kWave / 2; d >= 1; d >>= 1) v += __shfl_xor(v, d, kWave);

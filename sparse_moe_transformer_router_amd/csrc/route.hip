@@ -86,9 +86,59 @@ __global__ __launch_bounds__(kWave) void router_partial_kernel(const uint16_t *_
   }
 }
 
-// One wave per token: sum the split partials in order and add the bias, then k rounds of a
-// wave-wide argmax (larger logit wins, equal logits go to the lower expert id), then softmax
-// over the k picked logits.
+// k rounds of a wave-wide argmax over a token's logits (lane holds experts lane + 64 i;
+// larger logit wins, equal logits go to the lower expert id): the maximum by DPP moves, then
+// the lowest id holding it by ballots. Then softmax over the k picked logits; lane 0 writes
+// the token's ids and weights.
+__device__ __forceinline__ void topk_softmax_wave(const float (&v)[4], int E, int k, int lane,
+                                                  int32_t *__restrict__ idx_out, float *__restrict__ w_out) {
+  int taken = 0;
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+    if (lane + i * kWave >= E) taken |= 1 << i;
+  float sel_v[8];
+  int sel_e[8];
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    sel_v[j] = 0.f;
+    sel_e[j] = 0;
+    if (j < k) {
+      float lm = -INFINITY;
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        if (!(taken & (1 << i))) lm = fmaxf(lm, v[i]);
+      const float m = wave_max_f32(lm);
+      int be = -1;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {  // ids ascend with i, then with the lane
+        const uint64_t hit = __ballot(!(taken & (1 << i)) && v[i] == m);
+        if (be < 0 && hit != 0) be = i * kWave + __ffsll((unsigned long long)hit) - 1;
+      }
+      sel_v[j] = m;
+      sel_e[j] = be;
+      if ((be % kWave) == lane) taken |= 1 << (be / kWave);
+    }
+  }
+  if (lane == 0) {
+    float z[8], sum = 0.f;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      z[j] = (j < k) ? expf(sel_v[j] - sel_v[0]) : 0.f;
+      sum += z[j];
+    }
+    const float inv = 1.0f / sum;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      if (j < k) {
+        idx_out[j] = sel_e[j];
+        w_out[j] = z[j] * inv;
+      }
+    }
+  }
+}
+
+// One wave per token: sum the split partials in order and add the bias, then the top k and
+// their softmax.
 __global__ __launch_bounds__(256) void router_topk_kernel(const float *__restrict__ partial, int nsplit,
                                                           int nsp, const float *__restrict__ bias, int64_t T,
                                                           int E, int k, int32_t *__restrict__ topk_idx,
@@ -97,7 +147,6 @@ __global__ __launch_bounds__(256) void router_topk_kernel(const float *__restric
   const int64_t t = (int64_t)blockIdx.x * (blockDim.x / kWave) + threadIdx.x / kWave;
   if (t >= T) return;
   float v[4];
-  int taken = 0;
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     const int e = lane + i * kWave;
@@ -114,57 +163,10 @@ __global__ __launch_bounds__(256) void router_topk_kernel(const float *__restric
         for (int u = 0; u < 4; ++u)
           if (4 * c + u < nsplit) s += pv[c][u];
       if (bias) s += bias[e];
-    } else {
-      taken |= 1 << i;
     }
     v[i] = s;
   }
-  float sel_v[8];
-  int sel_e[8];
-#pragma unroll
-  for (int j = 0; j < 8; ++j) {
-    sel_v[j] = 0.f;
-    sel_e[j] = 0;
-    if (j < k) {
-      float bv = 0.f;
-      int be = 0x7fffffff;
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {  // ids ascend with i, so '>' keeps the lower id on ties
-        if (!(taken & (1 << i)) && (be == 0x7fffffff || v[i] > bv)) {
-          bv = v[i];
-          be = lane + i * kWave;
-        }
-      }
-#pragma unroll
-      for (int d = kWave / 2; d >= 1; d >>= 1) {
-        const float ov = __shfl_xor(bv, d, kWave);
-        const int oe = __shfl_xor(be, d, kWave);
-        if (oe != 0x7fffffff && (be == 0x7fffffff || ov > bv || (ov == bv && oe < be))) {
-          bv = ov;
-          be = oe;
-        }
-      }
-      sel_v[j] = bv;
-      sel_e[j] = be;
-      if ((be % kWave) == lane) taken |= 1 << (be / kWave);
-    }
-  }
-  if (lane == 0) {
-    float z[8], sum = 0.f;
-#pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      z[j] = (j < k) ? expf(sel_v[j] - sel_v[0]) : 0.f;
-      sum += z[j];
-    }
-    const float inv = 1.0f / sum;
-#pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      if (j < k) {
-        topk_idx[t * k + j] = sel_e[j];
-        topk_w[t * k + j] = z[j] * inv;
-      }
-    }
-  }
+  topk_softmax_wave(v, E, k, lane, topk_idx + t * k, topk_w + t * k);
 }
 
 // Split count for the router's input dimension: enough waves (about 2048, eight per SIMD) to

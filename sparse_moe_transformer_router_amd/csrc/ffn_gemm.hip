@@ -7,11 +7,11 @@
 // (walkthrough section 2.2; review section 3.3). Weights must be in the tiled layout; the
 // activations are expert-sorted rows (x gathered by launch_gather_rows, or the act rows).
 //
-// Output tile: 192 weight rows x 128 slots of one expert (192 divides 5760 and 2880). Four
-// waves in a 2 x 2 arrangement; a wave owns 96 rows (three 32-row weight tiles) x 64 slots
-// (two 32-slot column groups): six v_mfma_f32_32x32x16_bf16 accumulators. Weights are the
-// cheap operand (0.53 B per element against 2 B for a bf16 activation), so the tile is wide
-// in weight rows.
+// Output tile: 64 RGW weight rows x 128 slots of one expert, RGW = 4 (256 rows) or 3 (192,
+// which divides 5760 and 2880; chosen by the padding each leaves). Four waves in a 2 x 2
+// arrangement; a wave owns 32 RGW rows (RGW 32-row weight tiles) x 64 slots (two 32-slot
+// column groups): 2 RGW v_mfma_f32_32x32x16_bf16 accumulators. Weights are the cheap operand
+// (0.53 B per element against 2 B for a bf16 activation), so the tile is tall in weight rows.
 //
 // Persistent: one workgroup per CU walks a list of tiles, and its load stream runs across
 // tile boundaries, so a tile's start-up (locating its expert, first loads) and its epilogue
@@ -22,9 +22,10 @@
 //   * 128 slot rows x 256 bytes of bf16 activations into a 3-deep ring; each row's 16-byte
 //     columns are XOR-swizzled by the row index so a wave's 16-row reads hit distinct banks
 //     (applied on the global side: lane l of a DMA writes LDS column l % 16);
-//   * the six 2 KB weight tiles, their 128-byte scale tiles and the tile's 192 bias values.
-// Each wave issues exactly 13 DMAs per stage, two stages ahead, spread over the eight MFMA
-// k-steps of the chunk before; a stage is consumed after an explicit s_waitcnt vmcnt(13)
+//   * the 2 RGW 2 KB weight tiles, their 128-byte scale tiles and the tile's bias values.
+// Each wave issues exactly 10 + RGW DMAs per stage, two stages ahead, spread over the eight
+// MFMA k-steps of the chunk before; a stage is consumed after an explicit s_waitcnt vmcnt
+// of that count
 // and a bare s_barrier (a fence would drain the prefetches). Every DMA reads a clamped,
 // in-bounds address (past the end of the list the last chunk is re-loaded into the ring
 // slot nobody reads), so the count is exact. Rows past N read tile 0 and are never stored;
@@ -42,21 +43,24 @@
 
 namespace moe {
 
-constexpr int kGCols = 128;                 // slots per tile
-constexpr int kGStages = 3;                 // LDS ring depth
-constexpr int kGRowBytes = 256;             // one 128-element bf16 chunk of a slot row
-constexpr int kGRGW = 3;                    // 32-row weight tiles per wave (96 rows)
-constexpr int kGRows = 2 * 32 * kGRGW;      // weight rows per tile
+constexpr int kGCols = 128;       // slots per tile
+constexpr int kGStages = 3;       // LDS ring depth
+constexpr int kGRowBytes = 256;   // one 128-element bf16 chunk of a slot row
 constexpr int kGActBytes = kGCols * kGRowBytes;
-constexpr int kGWBytes = 2 * kGRGW * 2048;  // codes of the six weight tiles
-constexpr int kGSBytes = 1024;              // their scales (768 bytes used)
-constexpr int kGBBytes = 1024;              // the tile's bias (384 bytes used)
-constexpr int kGStageBytes = kGActBytes + kGWBytes + kGSBytes + kGBBytes;
-constexpr int kGDma = 13;                   // DMAs per wave per stage
-constexpr int kGGroupM = 4;                 // m-tiles per group of the XCD-local tile order
+constexpr int kGSBytes = 1024;    // the tiles' scales (2 RGW x 128 bytes, padded)
+constexpr int kGBBytes = 1024;    // the tile's bias (64 RGW rows x 2 bytes, padded)
+constexpr int kGGroupM = 4;       // m-tiles per group of the XCD-local tile order
 constexpr int kXcds = 8;
 constexpr int kGMaxExperts = 256;
-constexpr size_t kGLds = (size_t)kGStages * kGStageBytes + (kGMaxExperts + 4) * sizeof(int32_t);
+// RGW = 32-row weight tiles per wave: a tile is 64 RGW weight rows x 128 slots
+template <int RGW>
+struct GShape {
+  static constexpr int kRows = 64 * RGW;
+  static constexpr int kWBytes = 2 * RGW * 2048;  // codes of the 2 RGW weight tiles
+  static constexpr int kStageBytes = kGActBytes + kWBytes + kGSBytes + kGBBytes;
+  static constexpr int kDma = 8 + RGW + 2;        // DMAs per wave per stage
+  static constexpr size_t kLds = (size_t)kGStages * kStageBytes + (kGMaxExperts + 4) * sizeof(int32_t);
+};
 
 __device__ __forceinline__ int g_off(int row, int col16) { return row * kGRowBytes + ((col16 ^ (row & 15)) << 4); }
 
@@ -114,13 +118,14 @@ __device__ GTile g_tile(int L, const int32_t *off, int E, int mt_total, int ntn,
   return t;
 }
 
-template <int EPI>
+template <int EPI, int RGW>
 __global__ __launch_bounds__(256) void ffn_gemm_kernel(const uint16_t *__restrict__ a, const int32_t *__restrict__ offsets,
                                                        int E, const uint8_t *__restrict__ pcodes,
                                                        const uint8_t *__restrict__ pscales,
                                                        const uint16_t *__restrict__ bias, int N, int K, int ntn,
                                                        void *__restrict__ out, float limit, float alpha) {
-  constexpr int RGW = kGRGW;
+  using SH = GShape<RGW>;
+  constexpr int kGRows = SH::kRows, kGWBytes = SH::kWBytes, kGStageBytes = SH::kStageBytes, kGDma = SH::kDma;
   extern __shared__ __attribute__((aligned(16))) unsigned char lds[];
   int32_t *off = reinterpret_cast<int32_t *>(lds + kGStages * kGStageBytes);
   const int tid = threadIdx.x, lane = tid % 64;
@@ -177,11 +182,12 @@ __global__ __launch_bounds__(256) void ffn_gemm_kernel(const uint16_t *__restric
       ci = nchunk - 1;  // past the end: keep re-loading the last chunk (into a free slot)
     }
   };
-  // DMA i (0..12) of the issue-side chunk into ring slot `slot`:
-  //   0..7  activation rows 32 wave + 4 i .. + 3;
-  //   8..10 1 KB of weight codes: tile m / 2, half m % 2, m = 3 wave + i - 8;
-  //   11    256 bytes of the scale block (2 RGW tiles x 128 bytes, then padding);
-  //   12    waves 0, 1: 256 bytes of the tile's 384-byte bias run; waves 2, 3: a dummy.
+  // DMA i (0 .. kDma - 1) of the issue-side chunk into ring slot `slot`:
+  //   0..7            activation rows 32 wave + 4 i .. + 3;
+  //   8..8+RGW-1      1 KB of weight codes: tile m / 2, half m % 2, m = RGW wave + i - 8;
+  //   8+RGW           256 bytes of the scale block (2 RGW tiles x 128 bytes, then padding);
+  //   8+RGW+1         waves 0, 1: 256 bytes of the tile's bias run (2 x 64 RGW bytes);
+  //                   waves 2, 3: a dummy.
   const uint8_t *ccode = pcodes + lane * 16;
   auto dma = [&](int i, int slot) {
     unsigned char *st = lds + slot * kGStageBytes;
@@ -191,12 +197,12 @@ __global__ __launch_bounds__(256) void ffn_gemm_kernel(const uint16_t *__restric
       int kk = ci * 128 + lcol[i];
       kk = kk < K ? kk : 0;  // past K: any in-bounds element (its weight is an exact zero)
       __builtin_amdgcn_global_load_lds(aptr[i] + kk, st + (32 * wave + 4 * i) * kGRowBytes, 16, 0, 0);
-    } else if (i < 11) {
-      const int m = 3 * wave + i - 8;
+    } else if (i < 8 + RGW) {
+      const int m = RGW * wave + i - 8;
       const int g = gt0 + m / 2;
       const int64_t t = (g < NG) ? ebase + (int64_t)g * nchunk + ci : 0;
       __builtin_amdgcn_global_load_lds(ccode + t * 2048 + (m % 2) * 1024, st + kGActBytes + m * 1024, 16, 0, 0);
-    } else if (i == 11) {
+    } else if (i == 8 + RGW) {
       const int o = 256 * wave + 4 * lane;
       const int tt = o / 128, g = gt0 + tt;
       const int64_t t = (tt < 2 * RGW && g < NG) ? ebase + (int64_t)g * nchunk + ci : 0;
@@ -318,7 +324,7 @@ __global__ __launch_bounds__(256) void ffn_gemm_kernel(const uint16_t *__restric
           if (np < 2) bload(np, nj, bnext);
           // this k-step's share of the stage-after-next DMAs, in the shadow of its MFMAs
           dma(s, nslot);
-          if (s < 5) dma(8 + s, nslot);
+          if (s < RGW + 2) dma(8 + s, nslot);
 #pragma unroll
           for (int g = 0; g < RGW; ++g) {
             const bf16x8_t wa = fp4x8_to_bf16x8(cw[g][j], sc[g]);
@@ -351,24 +357,38 @@ int gemm_grid_cap() {
   return cus[dev];
 }
 
+// Tile height: 256 weight rows (fewer bytes per flop and more time to hide each stage's
+// loads: 624 vs 674 us for the 5760-row gate_up at 16,384 slots) unless that pads more than
+// a tenth of the 32-row tiles; then 192 if it pads less.
 hipError_t launch_ffn_gemm(const uint16_t *a_sorted, const int32_t *offsets, int E, int64_t S, const MxWeight &w,
                            int epilogue, void *out, float limit, float alpha, hipStream_t stream) {
   if (E > kGMaxExperts) return hipErrorInvalidValue;
+  const int NG = w.N / 32;
+  const int pad4 = (NG + 7) / 8 * 8 - NG, pad3 = (NG + 5) / 6 * 6 - NG;
+  const bool tall = pad4 * 10 <= NG || pad4 <= pad3;
+  const int rows = tall ? GShape<4>::kRows : GShape<3>::kRows;
   const int64_t busy = (S < E) ? S : E;
   const int64_t mtiles = (S + kGCols - 1) / kGCols + busy;  // bound on the real m-tile count
-  const int ntn = (w.N + kGRows - 1) / kGRows;
+  const int ntn = (w.N + rows - 1) / rows;
   const int64_t bound = mtiles * ntn;
   const int cap = gemm_grid_cap();  // one workgroup per CU (the LDS ring takes most of a CU)
   dim3 grid((unsigned)(bound < cap ? bound : cap));
-#define MOE_LAUNCH_GEMM(EPI)                                                                                 \
-  hipLaunchKernelGGL(ffn_gemm_kernel<EPI>, grid, dim3(256), kGLds, stream, a_sorted, offsets, E, w.codes, \
-                     w.scales, w.bias, w.N, w.K, ntn, out, limit, alpha)
-  switch (epilogue) {
-    case kEpiSwigluBf16: MOE_LAUNCH_GEMM(kEpiSwigluBf16); break;
-    case kEpiPreactF32: MOE_LAUNCH_GEMM(kEpiPreactF32); break;
-    case kEpiActF32: MOE_LAUNCH_GEMM(kEpiActF32); break;
-    default: MOE_LAUNCH_GEMM(kEpiLinearF32); break;
+#define MOE_LAUNCH_GEMM(EPI, RG)                                                                               \
+  hipLaunchKernelGGL((ffn_gemm_kernel<EPI, RG>), grid, dim3(256), GShape<RG>::kLds, stream, a_sorted, offsets, E, \
+                     w.codes, w.scales, w.bias, w.N, w.K, ntn, out, limit, alpha)
+#define MOE_LAUNCH_GEMM_EPI(RG)                                               \
+  switch (epilogue) {                                                         \
+    case kEpiSwigluBf16: MOE_LAUNCH_GEMM(kEpiSwigluBf16, RG); break;          \
+    case kEpiPreactF32: MOE_LAUNCH_GEMM(kEpiPreactF32, RG); break;            \
+    case kEpiActF32: MOE_LAUNCH_GEMM(kEpiActF32, RG); break;                  \
+    default: MOE_LAUNCH_GEMM(kEpiLinearF32, RG); break;                       \
   }
+  if (tall) {
+    MOE_LAUNCH_GEMM_EPI(4)
+  } else {
+    MOE_LAUNCH_GEMM_EPI(3)
+  }
+#undef MOE_LAUNCH_GEMM_EPI
 #undef MOE_LAUNCH_GEMM
   return hipGetLastError();
 }

@@ -61,15 +61,23 @@ __device__ __forceinline__ float swiglu_unit(float g, float l, float limit, floa
 // Wave-wide helpers.
 __device__ __forceinline__ int lane_id() { return __lane_id(); }
 
+// Inclusive prefix sum over the wave's 64 lanes by DPP moves (register speed): shifts by 1,
+// 2, 4, 8 within each row of 16 (lanes shifted in from outside the row add 0), then lane 15
+// of rows 0 / 2 into rows 1 / 3 and lane 31 into rows 2 and 3.
 __device__ __forceinline__ int wave_inclusive_scan(int v) {
-  const int lane = __lane_id();
-#pragma unroll
-  for (int d = 1; d < kWave; d <<= 1) {
-    int o = __shfl_up(v, d, kWave);
-    if (lane >= d) v += o;
-  }
+#define MOE_DPP_ADD(CTRL, ROWS, BOUND) v += __builtin_amdgcn_update_dpp(0, v, CTRL, ROWS, 0xF, BOUND)
+  MOE_DPP_ADD(0x111, 0xF, true);   // row_shr:1
+  MOE_DPP_ADD(0x112, 0xF, true);   // row_shr:2
+  MOE_DPP_ADD(0x114, 0xF, true);   // row_shr:4
+  MOE_DPP_ADD(0x118, 0xF, true);   // row_shr:8
+  MOE_DPP_ADD(0x142, 0xA, false);  // row_bcast15 into rows 1 and 3
+  MOE_DPP_ADD(0x143, 0xC, false);  // row_bcast31 into rows 2 and 3
+#undef MOE_DPP_ADD
   return v;
 }
+
+// Value of lane `l` (wave-uniform) for every lane.
+__device__ __forceinline__ int wave_read(int v, int l) { return __builtin_amdgcn_readlane(v, l); }
 
 // Maximum over the wave's 64 lanes, for every lane. DPP moves (register speed, no LDS round
 // trip): swap neighbours, swap pairs, mirror within 8 and within 16 lanes (every row of 16

@@ -101,14 +101,14 @@ __device__ GTile g_tile(int L, const int32_t *off, int E, int mt_total, int ntn,
     if (hit) {
       const int src = __ffsll((unsigned long long)hit) - 1;
       const int e = eb + src;
-      const int m0 = (mt - __shfl(excl, src, 64)) * kGCols;
+      const int m0 = (mt - wave_read(excl, src)) * kGCols;
       const int cnt_e = off[e + 1] - off[e];
       t.e = e;
       t.row0 = off[e] + m0;
       t.mcount = (cnt_e - m0 < kGCols) ? cnt_e - m0 : kGCols;
       break;
     }
-    carry += __shfl(inc, 63, 64);
+    carry += wave_read(inc, 63);
   }
   // wave-uniform by construction; say so, so the fields live in scalar registers
   t.e = __builtin_amdgcn_readfirstlane(t.e);
@@ -139,7 +139,7 @@ __global__ __launch_bounds__(256) void ffn_gemm_kernel(const uint16_t *__restric
   for (int eb = 0; eb < E; eb += 64) {
     const int ex = eb + lane;
     const int cnt = (ex < E) ? off[ex + 1] - off[ex] : 0;
-    mt_total += __shfl(wave_inclusive_scan((cnt + kGCols - 1) / kGCols), 63, 64);
+    mt_total += wave_read(wave_inclusive_scan((cnt + kGCols - 1) / kGCols), 63);
   }
   mt_total = __builtin_amdgcn_readfirstlane(mt_total);
   const int nb = mt_total * ntn;

@@ -56,7 +56,7 @@ __global__ __launch_bounds__(kSWaves *kWave) void ffn_stream_kernel(
       const uint64_t hit = __ballot(tiles > 0 && mt >= excl && mt < excl + tiles);
       if (hit) {
         const int src = __ffsll((unsigned long long)hit) - 1;
-        const int sel_excl = __shfl(excl, src, kWave);
+        const int sel_excl = wave_read(excl, src);
         e = eb + src;
         m0 = (mt - sel_excl) * kSCols;
         rbase = offsets[e];
@@ -64,7 +64,7 @@ __global__ __launch_bounds__(kSWaves *kWave) void ffn_stream_kernel(
         mcount = (cnt_e - m0 < kSCols) ? cnt_e - m0 : kSCols;
         break;
       }
-      carry += __shfl(inc, kWave - 1, kWave);
+      carry += wave_read(inc, kWave - 1);
     }
   }
   if (e < 0) return;  // same decision in every wave: the whole workgroup leaves
@@ -207,7 +207,7 @@ __global__ __launch_bounds__(kSWaves *kWave) void ffn_stream_tiled_kernel(
       const uint64_t hit = __ballot(tiles > 0 && mt >= excl && mt < excl + tiles);
       if (hit) {
         const int src = __ffsll((unsigned long long)hit) - 1;
-        const int sel_excl = __shfl(excl, src, kWave);
+        const int sel_excl = wave_read(excl, src);
         e = eb + src;
         m0 = (mt - sel_excl) * kTCols;
         rbase = offsets[e];
@@ -215,7 +215,7 @@ __global__ __launch_bounds__(kSWaves *kWave) void ffn_stream_tiled_kernel(
         mcount = (cnt_e - m0 < kTCols) ? cnt_e - m0 : kTCols;
         break;
       }
-      carry += __shfl(inc, kWave - 1, kWave);
+      carry += wave_read(inc, kWave - 1);
     }
   }
   if (e < 0) return;
@@ -387,7 +387,7 @@ __global__ __launch_bounds__(kRWaves *kWave) void ffn_stream_rows_kernel(
       const uint64_t hit = __ballot(tiles > 0 && mt >= excl && mt < excl + tiles);
       if (hit) {
         const int src = __ffsll((unsigned long long)hit) - 1;
-        const int sel_excl = __shfl(excl, src, kWave);
+        const int sel_excl = wave_read(excl, src);
         e = eb + src;
         m0 = (mt - sel_excl) * kRCols;
         rbase = offsets[e];
@@ -395,7 +395,7 @@ __global__ __launch_bounds__(kRWaves *kWave) void ffn_stream_rows_kernel(
         mcount = (cnt_e - m0 < kRCols) ? cnt_e - m0 : kRCols;
         break;
       }
-      carry += __shfl(inc, kWave - 1, kWave);
+      carry += wave_read(inc, kWave - 1);
     }
   }
   if (e < 0) return;

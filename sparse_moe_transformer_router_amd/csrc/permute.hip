@@ -51,7 +51,7 @@ __global__ __launch_bounds__(kPermThreads) void permute_kernel(const int32_t *__
       const int v = scan[base + lane + 1];
       const int inc = wave_inclusive_scan(v);
       scan[base + lane + 1] = inc + carry;
-      carry += __shfl(inc, kWave - 1, kWave);
+      carry += wave_read(inc, kWave - 1);
     }
     if (lane == 0) scan[0] = 0;
   }

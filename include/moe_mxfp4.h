@@ -173,7 +173,10 @@ int moe_route(const uint16_t *x, int64_t T, int32_t H, const moe_router_t *route
  * Outputs: expert_offsets int32 [E+1] (exclusive prefix sum of per-expert slot counts,
  * expert_offsets[E] = T*k), sorted_slot int32 [T*k] (slots ordered by expert, then by
  * slot id), slot_row int32 [T*k] (position of slot s in that order).
- * ws/ws_bytes: unused by this version (may be NULL/0). Deterministic.
+ * ws/ws_bytes: a workspace of moe_workspace_size bytes for these T, E, k; with more than
+ * 8192 slots the sort spreads over several workgroups and keeps per-range counts there.
+ * ws may be NULL (then one workgroup sorts every slot: same result, slower for large T).
+ * Deterministic.
  */
 int moe_permute(const int32_t *topk_idx, int64_t T, int32_t E, int32_t k, int32_t *expert_offsets,
                 int32_t *sorted_slot, int32_t *slot_row, void *ws, size_t ws_bytes,

@@ -33,8 +33,11 @@ size_t router_partial_floats(int64_t T, int E, int H);
 hipError_t launch_router(const uint16_t *x, int64_t T, int H, const float *w, const float *b, int E, int k,
                          float *partial, int32_t *topk_idx, float *topk_w, hipStream_t stream);
 
+// Stable counting sort of the S slots by expert. More than 8192 slots use several workgroups
+// and need permute_scratch_ints(S, E) int32 of scratch (else one workgroup sorts them all).
+int64_t permute_scratch_ints(int64_t S, int E);
 hipError_t launch_permute(const int32_t *topk_idx, int64_t S, int E, int32_t *offsets,
-                          int32_t *sorted_slot, int32_t *slot_row, hipStream_t stream);
+                          int32_t *sorted_slot, int32_t *slot_row, int32_t *scratch, hipStream_t stream);
 
 // One expert GEMM over all sorted rows, weight-streaming kernel family.
 // a_src: bf16 rows; if a_by_token, sorted row r reads a_src[(sorted_slot[r] / k) * K], else

@@ -21,7 +21,7 @@ size_t align_up(size_t v) { return (v + kWsAlign - 1) / kWsAlign * kWsAlign; }
 
 // One workspace layout serves every entry point (each uses a subset of the regions).
 struct WsLayout {
-  size_t logits, topk_idx, topk_w, offsets, sorted_slot, slot_row, act, y, xs, total;
+  size_t logits, topk_idx, topk_w, offsets, sorted_slot, slot_row, act, y, xs, pscratch, total;
 };
 
 bool ws_layout(int64_t T, int E, int k, int H, int I, WsLayout *L) {
@@ -37,6 +37,7 @@ bool ws_layout(int64_t T, int E, int k, int H, int I, WsLayout *L) {
   L->act = off;         off = align_up(off + S * (size_t)I * sizeof(uint16_t));
   L->y = off;           off = align_up(off + S * (size_t)H * sizeof(float));
   L->xs = off;          off = align_up(off + S * (size_t)H * sizeof(uint16_t));  // sorted x (GEMM path)
+  L->pscratch = off;    off = align_up(off + (size_t)moe::permute_scratch_ints((int64_t)S, E) * sizeof(int32_t));
   L->total = off;
   return true;
 }
@@ -168,7 +169,8 @@ int forward_impl(const uint16_t *x, const moe_router_t *router, const moe_mxfp4_
   float *y = at<float>(ws, L.y);
   if (moe::launch_router(x, T, H, router->weight, router->bias, E, k, logits, idx, wts, stream) != hipSuccess)
     return MOE_ERR_HIP;
-  if (moe::launch_permute(idx, S, E, offsets, sorted_slot, slot_row, stream) != hipSuccess)
+  if (moe::launch_permute(idx, S, E, offsets, sorted_slot, slot_row, at<int32_t>(ws, L.pscratch), stream) !=
+      hipSuccess)
     return MOE_ERR_HIP;
   int st = run_ffn(x, T, k, E, offsets, sorted_slot, *gu, *dn, o, y, act, at<uint16_t>(ws, L.xs), stream);
   if (st != MOE_OK) return st;
@@ -288,14 +290,20 @@ int moe_permute(const int32_t *topk_idx, int64_t T, int32_t E, int32_t k, int32_
                 int32_t *sorted_slot, int32_t *slot_row, void *ws, size_t ws_bytes,
                 moe_stream_t stream) {
   MOE_GUARD_BEGIN
-  (void)ws;
-  (void)ws_bytes;
   int st = check_common(T, E, k);
   if (st != MOE_OK) return st;
   if (T == 0) return MOE_OK;
   if (topk_idx == nullptr || expert_offsets == nullptr || sorted_slot == nullptr || slot_row == nullptr)
     return MOE_ERR_INVALID_ARG;
-  return moe::launch_permute(topk_idx, T * k, E, expert_offsets, sorted_slot, slot_row,
+  // the multi-workgroup sort keeps its per-range counts at the start of the workspace (this
+  // call uses no other region); without a large enough workspace one workgroup sorts
+  int32_t *scratch = nullptr;
+  if (ws != nullptr) {
+    if (!aligned(ws, kWsAlign)) return MOE_ERR_INVALID_ARG;
+    const size_t need = (size_t)moe::permute_scratch_ints(T * k, E) * sizeof(int32_t);
+    if (need > 0 && ws_bytes >= need) scratch = static_cast<int32_t *>(ws);
+  }
+  return moe::launch_permute(topk_idx, T * k, E, expert_offsets, sorted_slot, slot_row, scratch,
                              (hipStream_t)stream) == hipSuccess
              ? MOE_OK
              : MOE_ERR_HIP;

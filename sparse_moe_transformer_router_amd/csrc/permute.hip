@@ -15,6 +15,7 @@ namespace moe {
 constexpr int kPermWaves = 16;
 constexpr int kPermThreads = kPermWaves * kWave;
 constexpr int kMaxExperts = 256;
+constexpr int64_t kPermSingleMax = 8192;  // up to this many slots one workgroup sorts them all
 
 __global__ __launch_bounds__(kPermThreads) void permute_kernel(const int32_t *__restrict__ topk_idx,
                                                                int64_t S, int E,
@@ -92,10 +93,119 @@ __global__ __launch_bounds__(kPermThreads) void permute_kernel(const int32_t *__
   }
 }
 
+// Many slots: the same counting sort over several workgroups. Chunk c of kPermChunk
+// consecutive slots belongs to workgroup c; wave w of it to the w-th sixteenth of the chunk.
+// Pass 1 writes every (chunk, wave) histogram; pass 2 has every workgroup add up, for each
+// expert, the totals (-> offsets) and the counts of all (chunk, wave) ranges before each of
+// its waves (-> that wave's base), then scatter its chunk exactly as above. Slot order is
+// chunk order, then wave order, then batch order, so the permutation stays stable.
+constexpr int kPermChunk = kPermWaves * 256;
+
+__global__ __launch_bounds__(kPermThreads) void permute_hist_kernel(const int32_t *__restrict__ topk_idx,
+                                                                    int64_t S, int E, int32_t *__restrict__ whist) {
+  __shared__ int hist[kPermWaves][kMaxExperts];
+  const int tid = threadIdx.x, wave = tid / kWave, lane = tid % kWave;
+  for (int i = tid; i < kPermWaves * kMaxExperts; i += kPermThreads) (&hist[0][0])[i] = 0;
+  __syncthreads();
+  const int64_t beg = (int64_t)blockIdx.x * kPermChunk + wave * 256;
+  const int64_t end = (beg + 256 < S) ? beg + 256 : S;
+  for (int64_t s = beg + lane; s < end; s += kWave) {
+    const int e = topk_idx[s];
+    if ((unsigned)e < (unsigned)E) atomicAdd(&hist[wave][e], 1);
+  }
+  __syncthreads();
+  for (int i = tid; i < kPermWaves * E; i += kPermThreads)
+    whist[((int64_t)blockIdx.x * kPermWaves + i / E) * E + i % E] = hist[i / E][i % E];
+}
+
+__global__ __launch_bounds__(kPermThreads) void permute_scatter_kernel(const int32_t *__restrict__ topk_idx,
+                                                                       int64_t S, int E, int nchunks,
+                                                                       const int32_t *__restrict__ whist,
+                                                                       int32_t *__restrict__ offsets,
+                                                                       int32_t *__restrict__ sorted_slot,
+                                                                       int32_t *__restrict__ slot_row) {
+  __shared__ int base[kPermWaves][kMaxExperts];
+  __shared__ int scan[kMaxExperts + 1];
+  const int tid = threadIdx.x, wave = tid / kWave, lane = tid % kWave;
+  const int nranges = nchunks * kPermWaves;
+  const int mine = blockIdx.x * kPermWaves;  // this workgroup's first (chunk, wave) range
+  // thread e: the expert's total and its count in the ranges before each of this chunk's waves
+  if (tid < kMaxExperts) {
+    int tot = 0;
+    if (tid < E) {
+      // ranges come in groups of kPermWaves (one chunk); load a group, then add in order
+      for (int g0 = 0; g0 < nranges; g0 += kPermWaves) {
+        int c[kPermWaves];
+#pragma unroll
+        for (int w = 0; w < kPermWaves; ++w) c[w] = whist[(int64_t)(g0 + w) * E + tid];
+#pragma unroll
+        for (int w = 0; w < kPermWaves; ++w) {
+          if (g0 == mine) base[w][tid] = tot;
+          tot += c[w];
+        }
+      }
+    }
+    scan[tid + 1] = tot;
+  }
+  __syncthreads();
+  if (wave == 0) {
+    int carry = 0;
+    for (int b = 0; b < kMaxExperts; b += kWave) {
+      const int v = scan[b + lane + 1];
+      const int inc = wave_inclusive_scan(v);
+      scan[b + lane + 1] = inc + carry;
+      carry += wave_read(inc, kWave - 1);
+    }
+    if (lane == 0) scan[0] = 0;
+  }
+  __syncthreads();
+  if (blockIdx.x == 0)
+    for (int e = tid; e <= E; e += kPermThreads) offsets[e] = scan[e];
+  if (tid < E)
+    for (int w = 0; w < kPermWaves; ++w) base[w][tid] += scan[tid];
+  __syncthreads();
+  const int64_t beg = (int64_t)blockIdx.x * kPermChunk + wave * 256;
+  const int64_t end = (beg + 256 < S) ? beg + 256 : S;
+  for (int64_t s0 = beg; s0 < end; s0 += kWave) {
+    const int64_t s = s0 + lane;
+    const int e = (s < end) ? topk_idx[s] : -1;
+    const bool active = (unsigned)e < (unsigned)E;
+    uint64_t same = __ballot(active);
+#pragma unroll
+    for (int bit = 0; bit < 8; ++bit) {
+      const uint64_t ones = __ballot(active && ((e >> bit) & 1));
+      same &= ((e >> bit) & 1) ? ones : ~ones;
+    }
+    if (active) {
+      const uint64_t below = (lane == 0) ? 0ull : (~0ull >> (kWave - lane));
+      const int rank = __popcll(same & below);
+      const int pos = base[wave][e] + rank;
+      sorted_slot[pos] = (int32_t)s;
+      slot_row[s] = pos;
+      __builtin_amdgcn_wave_barrier();
+      if (rank == 0) base[wave][e] += __popcll(same);
+    }
+    __builtin_amdgcn_wave_barrier();
+  }
+}
+
+int64_t permute_scratch_ints(int64_t S, int E) {
+  return S > kPermSingleMax ? ((S + kPermChunk - 1) / kPermChunk) * kPermWaves * (int64_t)E : 0;
+}
+
 hipError_t launch_permute(const int32_t *topk_idx, int64_t S, int E, int32_t *offsets,
-                          int32_t *sorted_slot, int32_t *slot_row, hipStream_t stream) {
-  hipLaunchKernelGGL(permute_kernel, dim3(1), dim3(kPermThreads), 0, stream, topk_idx, S, E, offsets,
-                     sorted_slot, slot_row);
+                          int32_t *sorted_slot, int32_t *slot_row, int32_t *scratch, hipStream_t stream) {
+  if (S <= kPermSingleMax || scratch == nullptr) {
+    hipLaunchKernelGGL(permute_kernel, dim3(1), dim3(kPermThreads), 0, stream, topk_idx, S, E, offsets,
+                       sorted_slot, slot_row);
+    return hipGetLastError();
+  }
+  const int nchunks = (int)((S + kPermChunk - 1) / kPermChunk);
+  hipLaunchKernelGGL(permute_hist_kernel, dim3(nchunks), dim3(kPermThreads), 0, stream, topk_idx, S, E, scratch);
+  hipError_t err = hipGetLastError();
+  if (err != hipSuccess) return err;
+  hipLaunchKernelGGL(permute_scatter_kernel, dim3(nchunks), dim3(kPermThreads), 0, stream, topk_idx, S, E, nchunks,
+                     scratch, offsets, sorted_slot, slot_row);
   return hipGetLastError();
 }
 

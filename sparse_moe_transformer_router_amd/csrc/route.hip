@@ -36,53 +36,90 @@ __device__ __forceinline__ void split3(const f32x4_t &a, const f32x4_t &b, bf16x
 
 constexpr int kMaxSplitVec = 12;  // at most 48 splits, read as 12 float4 per logit
 
-// One wave: 16 tokens x 16 experts over the MX-block range of split blockIdx.z.
-// Writes partial[(t * E + e) * nsp + split] (nsp = split count rounded up to 4).
+// One wave: 16 NTT tokens x 16 NET experts over the MX-block range of split blockIdx.z
+// (NTT x NET 16x16 accumulators, so each weight element loaded and split serves 16 NTT tokens
+// and each x element 16 NET experts). Writes partial[(t * E + e) * nsp + split] (nsp = split
+// count rounded up to 4).
+template <int NTT, int NET>
 __global__ __launch_bounds__(kWave) void router_partial_kernel(const uint16_t *__restrict__ x, int64_t T,
                                                                int H, const float *__restrict__ w, int E,
                                                                int blocks_per_split, int nsp,
                                                                float *__restrict__ partial) {
   const int lane = threadIdx.x;
-  const int64_t t0 = (int64_t)blockIdx.x * 16;
-  const int e0 = blockIdx.y * 16;
+  const int64_t t0 = (int64_t)blockIdx.x * 16 * NTT;
+  const int e0 = blockIdx.y * 16 * NET;
   const int split = blockIdx.z;
   const int KB = H / 32;
   const int b0 = split * blocks_per_split;
   const int b1 = (b0 + blocks_per_split < KB) ? b0 + blocks_per_split : KB;
   const int r = lane % 16, q = lane / 16;
-  const bool t_ok = t0 + r < T, e_ok = e0 + r < E;
-  const uint16_t *xp = x + (t_ok ? (t0 + r) : 0) * H + 8 * q;
-  const float *wp = w + (int64_t)(e_ok ? (e0 + r) : 0) * H + 8 * q;
-  f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
-  constexpr int U = 4;  // MX blocks per round: all of a round's loads are issued before any math
+  const uint16_t *xp[NTT];
+  bool t_ok[NTT];
+#pragma unroll
+  for (int i = 0; i < NTT; ++i) {
+    const int64_t t = t0 + 16 * i + r;
+    t_ok[i] = t < T;
+    xp[i] = x + (t_ok[i] ? t : 0) * H + 8 * q;
+  }
+  const float *wp[NET];
+  bool e_ok[NET];
+#pragma unroll
+  for (int j = 0; j < NET; ++j) {
+    const int e = e0 + 16 * j + r;
+    e_ok[j] = e < E;
+    wp[j] = w + (int64_t)(e_ok[j] ? e : 0) * H + 8 * q;
+  }
+  f32x4_t acc[NTT][NET];
+#pragma unroll
+  for (int i = 0; i < NTT; ++i)
+#pragma unroll
+    for (int j = 0; j < NET; ++j) acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  constexpr int U = (NTT * NET == 1) ? 4 : 2;  // MX blocks per round: all loads first, then the math
   for (int bb = b0; bb < b1; bb += U) {
-    u32x4_t xa[U];
-    f32x4_t wa[U], wb[U];
+    u32x4_t xa[U][NTT];
+    f32x4_t wa[U][NET], wb[U][NET];
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       const int b = bb + u;
       const bool ok = b < b1;
-      xa[u] = (ok && t_ok) ? *reinterpret_cast<const u32x4_t *>(xp + 32 * b) : u32x4_t{0u, 0u, 0u, 0u};
-      wa[u] = (ok && e_ok) ? *reinterpret_cast<const f32x4_t *>(wp + 32 * b) : f32x4_t{0.f, 0.f, 0.f, 0.f};
-      wb[u] = (ok && e_ok) ? *reinterpret_cast<const f32x4_t *>(wp + 32 * b + 4) : f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int i = 0; i < NTT; ++i)
+        xa[u][i] = (ok && t_ok[i]) ? *reinterpret_cast<const u32x4_t *>(xp[i] + 32 * b) : u32x4_t{0u, 0u, 0u, 0u};
+#pragma unroll
+      for (int j = 0; j < NET; ++j) {
+        wa[u][j] = (ok && e_ok[j]) ? *reinterpret_cast<const f32x4_t *>(wp[j] + 32 * b) : f32x4_t{0.f, 0.f, 0.f, 0.f};
+        wb[u][j] =
+            (ok && e_ok[j]) ? *reinterpret_cast<const f32x4_t *>(wp[j] + 32 * b + 4) : f32x4_t{0.f, 0.f, 0.f, 0.f};
+      }
     }
 #pragma unroll
     for (int u = 0; u < U; ++u) {
-      bf16x8_t hi, mid, lo;
-      split3(wa[u], wb[u], hi, mid, lo);
-      const bf16x8_t xb = as_bf16x8(xa[u]);
-      acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xb, lo, acc, 0, 0, 0);
-      acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xb, mid, acc, 0, 0, 0);
-      acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xb, hi, acc, 0, 0, 0);
+#pragma unroll
+      for (int j = 0; j < NET; ++j) {
+        bf16x8_t hi, mid, lo;
+        split3(wa[u][j], wb[u][j], hi, mid, lo);
+#pragma unroll
+        for (int i = 0; i < NTT; ++i) {
+          const bf16x8_t xb = as_bf16x8(xa[u][i]);
+          acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xb, lo, acc[i][j], 0, 0, 0);
+          acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xb, mid, acc[i][j], 0, 0, 0);
+          acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xb, hi, acc[i][j], 0, 0, 0);
+        }
+      }
     }
   }
-  // lane holds tokens t0 + 4q + i, expert e0 + r
-  if (e_ok) {
+  // lane holds tokens 16 i + 4q + ii, expert 16 j + r of the tile
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int64_t t = t0 + 4 * q + i;
-      if (t < T) partial[(t * E + e0 + r) * nsp + split] = acc[i];
-    }
+  for (int j = 0; j < NET; ++j) {
+    const int e = e0 + 16 * j + r;
+    if (!e_ok[j]) continue;
+#pragma unroll
+    for (int i = 0; i < NTT; ++i)
+#pragma unroll
+      for (int ii = 0; ii < 4; ++ii) {
+        const int64_t t = t0 + 16 * i + 4 * q + ii;
+        if (t < T) partial[(t * E + e) * nsp + split] = acc[i][j][ii];
+      }
   }
 }
 
@@ -169,10 +206,15 @@ __global__ __launch_bounds__(256) void router_topk_kernel(const float *__restric
   topk_softmax_wave(v, E, k, lane, topk_idx + t * k, topk_w + t * k);
 }
 
+// Tile shape: 64 tokens x 32 experts per wave once there are many tokens (fewer re-reads of
+// the router matrix and of x), else 16 x 16.
+static bool router_wide(int64_t T, int E) { return T >= 1024 && E >= 32; }
+
 // Split count for the router's input dimension: enough waves (about 2048, eight per SIMD) to
 // spread any batch over the chip, at most 4 * kMaxSplitVec, at least 2 MX blocks per split.
 int router_splits(int64_t T, int E, int H) {
-  const int64_t tiles = ((T + 15) / 16) * ((E + 15) / 16);
+  const int tt = router_wide(T, E) ? 64 : 16, et = router_wide(T, E) ? 32 : 16;
+  const int64_t tiles = ((T + tt - 1) / tt) * ((E + et - 1) / et);
   const int KB = H / 32;
   if (tiles <= 0 || KB < 2) return 1;
   int64_t s = (2048 + tiles - 1) / tiles;
@@ -194,8 +236,13 @@ hipError_t launch_router(const uint16_t *x, int64_t T, int H, const float *w, co
   const int ns = router_splits(T, E, H);
   const int bps = (KB + ns - 1) / ns;
   const int nsp = (ns + 3) / 4 * 4;
-  dim3 grid((unsigned)((T + 15) / 16), (unsigned)((E + 15) / 16), (unsigned)ns);
-  hipLaunchKernelGGL(router_partial_kernel, grid, dim3(kWave), 0, stream, x, T, H, w, E, bps, nsp, partial);
+  if (router_wide(T, E)) {
+    dim3 grid((unsigned)((T + 63) / 64), (unsigned)((E + 31) / 32), (unsigned)ns);
+    hipLaunchKernelGGL((router_partial_kernel<4, 2>), grid, dim3(kWave), 0, stream, x, T, H, w, E, bps, nsp, partial);
+  } else {
+    dim3 grid((unsigned)((T + 15) / 16), (unsigned)((E + 15) / 16), (unsigned)ns);
+    hipLaunchKernelGGL((router_partial_kernel<1, 1>), grid, dim3(kWave), 0, stream, x, T, H, w, E, bps, nsp, partial);
+  }
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
   hipLaunchKernelGGL(router_topk_kernel, dim3((unsigned)((T + 3) / 4)), dim3(256), 0, stream, partial, ns, nsp, b,

@@ -138,8 +138,10 @@ def moe_route(x: torch.Tensor, router: Router, k: int, topk_idx=None, topk_w=Non
     return topk_idx, topk_w
 
 
-def moe_permute(topk_idx: torch.Tensor, E: int, out=None, stream=None
+def moe_permute(topk_idx: torch.Tensor, E: int, out=None, ws=None, stream=None
                 ) -> Tuple[torch.Tensor, torch.Tensor, torch.Tensor]:
+    """ws: optional workspace (uint8 tensor); with it, more than 8192 slots are sorted by
+    several workgroups (same result)."""
     T, k = topk_idx.shape
     dev = topk_idx.device
     if out is None:
@@ -148,7 +150,8 @@ def moe_permute(topk_idx: torch.Tensor, E: int, out=None, stream=None
                torch.empty(T * k, dtype=torch.int32, device=dev))
     offsets, sorted_slot, slot_row = out
     L.check("moe_permute", L.lib().moe_permute(_ptr(topk_idx), T, E, k, _ptr(offsets), _ptr(sorted_slot),
-                                                  _ptr(slot_row), None, 0, _stream(stream)))
+                                                  _ptr(slot_row), _ptr(ws), 0 if ws is None else ws.numel(),
+                                                  _stream(stream)))
     return offsets, sorted_slot, slot_row
 
 

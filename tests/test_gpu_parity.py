@@ -56,10 +56,12 @@ def test_route(name, T):
     gu.check_routing(idx.cpu().numpy(), w.cpu().numpy(), logits, cfg.k)
 
 
-def test_route_ties_and_k_range():
-    rng = np.random.default_rng(7)
-    T, H = 37, 64
-    for E, k in [(8, 1), (8, 8), (16, 8), (256, 4), (5, 3), (130, 2)]:
+@pytest.mark.parametrize("T,cases", [(37, [(8, 1), (8, 8), (16, 8), (256, 4), (5, 3), (130, 2)]),
+                                     (1100, [(40, 4), (130, 2), (256, 8)])])  # 64x32 router tiles, ragged
+def test_route_ties_and_k_range(T, cases):
+    rng = np.random.default_rng(7 + T)
+    H = 64
+    for E, k in cases:
         x = synth.bf16_bits_from_f32(rng.standard_normal((T, H)).astype(np.float32))
         rw = (rng.standard_normal((E, H)) * 0.05).astype(np.float32)
         rb = rng.standard_normal(E).astype(np.float32)
@@ -80,18 +82,21 @@ def test_route_ties_and_k_range():
 # ------------------------------------------------------------------ a3: permutation
 @pytest.mark.parametrize("T,E,k,mode", [(1, 8, 4, "rand"), (16, 8, 4, "rand"), (4096, 32, 4, "rand"),
                                         (8192, 128, 4, "rand"), (1000, 256, 8, "rand"),
-                                        (300, 128, 4, "hot"), (77, 16, 1, "rand"), (50, 4, 4, "rand")])
+                                        (300, 128, 4, "hot"), (77, 16, 1, "rand"), (50, 4, 4, "rand"),
+                                        (2049, 256, 8, "rand"), (5000, 64, 4, "hot"), (2500, 3, 3, "rand")])
 def test_permute(T, E, k, mode):
     rng = np.random.default_rng(T * 131 + E)
     if mode == "hot":  # every token picks experts 0..k-1: most experts empty
         idx = np.tile(np.arange(k, dtype=np.int32), (T, 1))
     else:
         idx = np.argsort(rng.random((T, E)), axis=1)[:, :k].astype(np.int32)
-    off, ss, sr = moe.moe_permute(torch.from_numpy(idx).cuda(), E)
     counts, r_off, r_ss, r_sr = oracle.permute(idx, E)
-    assert np.array_equal(off.cpu().numpy(), r_off)
-    assert np.array_equal(ss.cpu().numpy(), r_ss)
-    assert np.array_equal(sr.cpu().numpy(), r_sr)
+    ws = moe.workspace(T, E, k, 64, 64)  # with a workspace, > 8192 slots use several workgroups
+    for w in (None, ws):
+        off, ss, sr = moe.moe_permute(torch.from_numpy(idx).cuda(), E, ws=w)
+        assert np.array_equal(off.cpu().numpy(), r_off)
+        assert np.array_equal(ss.cpu().numpy(), r_ss)
+        assert np.array_equal(sr.cpu().numpy(), r_sr)
 
 
 @pytest.mark.parametrize("E,N,K", [(2, 64, 256), (3, 5760, 2880), (1, 96, 96), (2, 32, 32)])

@@ -43,7 +43,7 @@ def parse():
                    choices=["decode20b", "prefill20b", "prefill120b", "decode120b_zipf"])
     p.add_argument("--T", type=int, default=0, help="batch size (default: the workload's largest)")
     p.add_argument("--layers", type=int, default=0, help="rotated weight copies (default 24 / 36)")
-    p.add_argument("--path", type=int, default=0, help="0 auto, 1 stream, 2 gemm")
+    p.add_argument("--path", type=int, default=0, help="0 auto, 1 stream, 2 gemm (bf16), 3 gemm (block-scaled)")
     p.add_argument("--layout", default="tiled", choices=["tiled", "rowmajor"],
                    help="weights prepacked once (untimed) into the kernel layout, or row-major")
     p.add_argument("--no-cpu-baseline", action="store_true")

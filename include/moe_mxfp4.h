@@ -56,9 +56,14 @@ extern "C" {
 /* expert-FFN kernel family */
 #define MOE_PATH_AUTO 0    /* chosen from T*k and E on the host */
 #define MOE_PATH_STREAM 1  /* weight-streaming kernels for decode-sized batches */
-#define MOE_PATH_GEMM 2    /* LDS-tiled grouped GEMM for prefill-sized batches; needs
-                              MOE_LAYOUT_TILED weights (else MOE_ERR_UNSUPPORTED). AUTO picks it
-                              for tiled weights when T*k >= 48*E. */
+#define MOE_PATH_GEMM 2    /* LDS-tiled grouped GEMM for prefill-sized batches, bf16 activations
+                              times MXFP4 weights decoded to bf16 in registers; needs
+                              MOE_LAYOUT_TILED weights (else MOE_ERR_UNSUPPORTED). */
+#define MOE_PATH_GEMM_MX 3 /* the same grouped GEMM on gfx950's block-scaled MFMA: the MXFP4
+                              weights are an operand as stored, each bf16 activation is split
+                              exactly into two MXFP8 (E4M3) terms with E8M0 block scales. Needs
+                              MOE_LAYOUT_TILED weights. AUTO picks it for tiled weights when
+                              T*k >= 48*E. */
 
 /* moe_mxfp4_weight_t.layout */
 #define MOE_LAYOUT_ROWMAJOR 0 /* codes [E][n][k/2], scales [E][n][k/32] as described below */

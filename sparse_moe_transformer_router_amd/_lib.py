@@ -27,6 +27,7 @@ MOE_DTYPE_F32 = 1
 MOE_PATH_AUTO = 0
 MOE_PATH_STREAM = 1
 MOE_PATH_GEMM = 2
+MOE_PATH_GEMM_MX = 3
 
 MOE_LAYOUT_ROWMAJOR = 0
 MOE_LAYOUT_TILED = 1

@@ -38,8 +38,20 @@
 //
 // Lane l of a weight tile holds MX block 4c + 2p + l/32 of row l%32 (p = 0, 1), split into
 // four 8-element k-steps; the B operand reads the same k-assignment from LDS.
+//
+// Block-scaled variant (MX = true): the activations arrive as two MXFP8 (E4M3) terms with one
+// E8M0 scale per 32 elements each (the layout in mx_act.h), and the MXFP4 weight tile is
+// the A operand of gfx950's v_mfma_scale_f32_32x32x64_f8f6f4 as it sits in memory: no
+// conversion of the weights at all, their E8M0 scales go to the instruction's scale operand
+// and the activation terms' scales to the other. Per 128-element chunk a wave issues
+// 2 (terms) x 2 (64-element halves) x RGW x 2 scaled MFMAs. The activation stage holds
+// 128 slot rows x (128 hi + 128 lo bytes), the same 32 KB as the bf16 rows, plus 1 KB of
+// term scales. The gate_up epilogue writes the activation in the same two-term form.
+#include <type_traits>
+
 #include "common.h"
 #include "kernels.h"
+#include "mx_act.h"
 
 namespace moe {
 
@@ -52,13 +64,16 @@ constexpr int kGBBytes = 1024;    // the tile's bias (64 RGW rows x 2 bytes, pad
 constexpr int kGGroupM = 4;       // m-tiles per group of the XCD-local tile order
 constexpr int kXcds = 8;
 constexpr int kGMaxExperts = 256;
-// RGW = 32-row weight tiles per wave: a tile is 64 RGW weight rows x 128 slots
-template <int RGW>
+// RGW = 32-row weight tiles per wave: a tile is 64 RGW weight rows x 128 slots. MX adds the
+// activation terms' scales (128 slots x 2 dwords) after the activation rows.
+template <int RGW, bool MX>
 struct GShape {
   static constexpr int kRows = 64 * RGW;
-  static constexpr int kWBytes = 2 * RGW * 2048;  // codes of the 2 RGW weight tiles
-  static constexpr int kStageBytes = kGActBytes + kWBytes + kGSBytes + kGBBytes;
-  static constexpr int kDma = 8 + RGW + 2;        // DMAs per wave per stage
+  static constexpr int kAScBytes = MX ? kGCols * 8 : 0;
+  static constexpr int kWOff = kGActBytes + kAScBytes;  // weight codes, then scales, then bias
+  static constexpr int kWBytes = 2 * RGW * 2048;       // codes of the 2 RGW weight tiles
+  static constexpr int kStageBytes = kWOff + kWBytes + kGSBytes + kGBBytes;
+  static constexpr int kDma = 8 + RGW + 2 + (MX ? 1 : 0);  // DMAs per wave per stage
   static constexpr size_t kLds = (size_t)kGStages * kStageBytes + (kGMaxExperts + 4) * sizeof(int32_t);
 };
 
@@ -77,6 +92,27 @@ __device__ __forceinline__ uint2 lds_read_b64_sync(const void *p) {
   uint2 v;
   asm volatile("ds_read_b64 %0, %1\n\ts_waitcnt lgkmcnt(0)" : "=v"(v) : "v"(a) : "memory");
   return v;
+}
+
+// The MX chunk's scale operands in one LDS round trip: four weight-scale dwords 128 bytes apart
+// (tiles g = 0..3 of the wave; a fourth read past RGW = 3 stays inside the stage's scale area)
+// and the two term-scale pairs of the lane's slot columns (32 slots = 256 bytes apart). The
+// reads wait for themselves inside the asm block, like lds_read_b64_sync; the outputs are
+// early-clobber, since later reads of the block still use the address registers.
+__device__ __forceinline__ void lds_read_mx_scales(const void *wsc, const void *asc, uint32_t (&w)[4], uint2 (&a)[2]) {
+  const uint32_t wa = (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void *)wsc;
+  const uint32_t aa = (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void *)asc;
+  asm volatile(
+      "ds_read_b32 %0, %6\n\t"
+      "ds_read_b32 %1, %6 offset:128\n\t"
+      "ds_read_b32 %2, %6 offset:256\n\t"
+      "ds_read_b32 %3, %6 offset:384\n\t"
+      "ds_read_b64 %4, %7\n\t"
+      "ds_read_b64 %5, %7 offset:256\n\t"
+      "s_waitcnt lgkmcnt(0)"
+      : "=&v"(w[0]), "=&v"(w[1]), "=&v"(w[2]), "=&v"(w[3]), "=&v"(a[0]), "=&v"(a[1])
+      : "v"(wa), "v"(aa)
+      : "memory");
 }
 
 struct GTile {
@@ -118,14 +154,21 @@ __device__ GTile g_tile(int L, const int32_t *off, int E, int mt_total, int ntn,
   return t;
 }
 
-template <int EPI, int RGW>
-__global__ __launch_bounds__(256) void ffn_gemm_kernel(const uint16_t *__restrict__ a, const int32_t *__restrict__ offsets,
-                                                       int E, const uint8_t *__restrict__ pcodes,
+// One workgroup per CU (the LDS ring takes most of it): the compiler is told so, and schedules
+// for one wave per SIMD instead of saving registers for more.
+template <int EPI, int RGW, bool MX>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) void ffn_gemm_kernel(const void *__restrict__ a_src, const uint8_t *__restrict__ a_scales,
+                                                       const int32_t *__restrict__ offsets, int E,
+                                                       const uint8_t *__restrict__ pcodes,
                                                        const uint8_t *__restrict__ pscales,
                                                        const uint16_t *__restrict__ bias, int N, int K, int ntn,
-                                                       void *__restrict__ out, float limit, float alpha) {
-  using SH = GShape<RGW>;
+                                                       void *__restrict__ out, uint8_t *__restrict__ out_scales,
+                                                       float limit, float alpha) {
+  using SH = GShape<RGW, MX>;
   constexpr int kGRows = SH::kRows, kGWBytes = SH::kWBytes, kGStageBytes = SH::kStageBytes, kGDma = SH::kDma;
+  constexpr int kWOff = SH::kWOff;
+  static_assert(EPI != kEpiMxAct || (MX && RGW == 4), "two-term output: one 128-element record per n-tile");
+  static_assert(EPI != kEpiSwigluBf16 || !MX, "bf16 activation output belongs to the bf16 path");
   extern __shared__ __attribute__((aligned(16))) unsigned char lds[];
   int32_t *off = reinterpret_cast<int32_t *>(lds + kGStages * kGStageBytes);
   const int tid = threadIdx.x, lane = tid % 64;
@@ -159,20 +202,65 @@ __global__ __launch_bounds__(256) void ffn_gemm_kernel(const uint16_t *__restric
   // ---- issue side: the tile and chunk whose stage is loaded next
   int ji = 0, ci = 0;
   GTile ti = g_tile(first, off, E, mt_total, ntn, lane);
-  const uint16_t *aptr[8];
-  int lcol[8];
+  // bytes per activation row: K bf16, or nchunk two-term records
+  const int64_t arow = MX ? (int64_t)nchunk * kMxRecBytes : (int64_t)K * 2;
+  // DMA i (0 .. kDma - 1) of the issue-side chunk into ring slot `slot`:
+  //   0..7            activation rows 32 wave + 4 i .. + 3 (bf16 elements, or a two-term record);
+  //   8..8+RGW-1      1 KB of weight codes: tile m / 2, half m % 2, m = RGW wave + i - 8;
+  //   8+RGW           256 bytes of the scale block (2 RGW tiles x 128 bytes, then padding);
+  //   8+RGW+1         waves 0, 1: 256 bytes of the tile's bias run (2 x 64 RGW bytes);
+  //                   waves 2, 3: a dummy;
+  //   8+RGW+2 (MX)    256 bytes of term scales: slots 32 wave .. 32 wave + 31, 8 bytes each.
+  // Sources are set once per tile as a byte offset and a per-chunk stride, so the chunk loop
+  // computes each address without a branch (branches would cut the loop body into blocks the
+  // instruction scheduler cannot interleave). Rows past N read weight tile 0 with stride 0;
+  // slots past an m-tile's count re-read its first slot; neither is ever stored.
+  const uint8_t *aptr[8];
+  int lcol[8];                    // byte offset of the lane's 16 bytes within a 256-byte row chunk
+  int64_t woff[RGW];              // weight codes of this wave's DMA m, chunk 0 (from pcodes)
+  int wstr[RGW];                  // 2048, or 0 for tiles past N
+  int64_t soff;                   // scale block, chunk 0 (from pscales)
+  int sstr;                       // 128, or 0
+  int64_t boff;                   // the tile's bias run (from bias), or -1: no bias here
+  const uint8_t *sptr = nullptr;  // MX: this lane's term-scale dword of slot (64 wave + lane) / 2, chunk 0
   auto set_rows = [&]() {
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
       const int row = 32 * wave + 4 * i + lane / 16;
-      aptr[i] = a + (int64_t)(ti.row0 + (row < ti.mcount ? row : 0)) * K;
+      aptr[i] = static_cast<const uint8_t *>(a_src) + (int64_t)(ti.row0 + (row < ti.mcount ? row : 0)) * arow;
+    }
+    const int gt0 = ti.nt * 2 * RGW;
+    const int64_t ebase = (int64_t)ti.e * NG * nchunk;
+#pragma unroll
+    for (int m = 0; m < RGW; ++m) {
+      const int mm = RGW * wave + m, g = gt0 + mm / 2;
+      const bool ok = g < NG;
+      woff[m] = (ok ? ebase + (int64_t)g * nchunk : 0) * 2048 + (mm % 2) * 1024 + lane * 16;
+      wstr[m] = ok ? 2048 : 0;
+    }
+    {
+      const int o = 256 * wave + 4 * lane;
+      const int tt = o / 128, g = gt0 + tt;
+      const bool ok = tt < 2 * RGW && g < NG;
+      soff = (ok ? ebase + (int64_t)g * nchunk : 0) * 128 + (o % 128);
+      sstr = ok ? 128 : 0;
+      const int n = ti.nt * kGRows + o / 2;  // byte o of the tile's bias run
+      boff = (bias != nullptr && o < 2 * kGRows && n < N) ? ((int64_t)ti.e * N + n) * 2 : -1;
+    }
+    if constexpr (MX) {
+      const int sl = (64 * wave + lane) >> 1;
+      sptr = a_scales + (int64_t)(ti.row0 + (sl < ti.mcount ? sl : 0)) * nchunk * kMxScBytes + (lane & 1) * 4;
     }
   };
 #pragma unroll
-  for (int i = 0; i < 8; ++i) lcol[i] = ((lane % 16) ^ ((32 * wave + 4 * i + lane / 16) & 15)) * 8;
+  for (int i = 0; i < 8; ++i) lcol[i] = ((lane % 16) ^ ((32 * wave + 4 * i + lane / 16) & 15)) * 16;
   set_rows();
+  // Called before a stage is issued (the chunk counter ci was advanced after the previous
+  // one): moves the issue side to its next tile when the chunks of this one are all issued.
+  // It runs at the top of a chunk, so no branch follows the chunk's MFMAs (the compiler would
+  // otherwise sink them past it, away from the loads they should hide).
   auto advance_issue = [&]() {
-    if (++ci < nchunk) return;
+    if (ci < nchunk) return;
     if (ji + 1 < ntiles) {
       ++ji;
       ci = 0;
@@ -182,38 +270,31 @@ __global__ __launch_bounds__(256) void ffn_gemm_kernel(const uint16_t *__restric
       ci = nchunk - 1;  // past the end: keep re-loading the last chunk (into a free slot)
     }
   };
-  // DMA i (0 .. kDma - 1) of the issue-side chunk into ring slot `slot`:
-  //   0..7            activation rows 32 wave + 4 i .. + 3;
-  //   8..8+RGW-1      1 KB of weight codes: tile m / 2, half m % 2, m = RGW wave + i - 8;
-  //   8+RGW           256 bytes of the scale block (2 RGW tiles x 128 bytes, then padding);
-  //   8+RGW+1         waves 0, 1: 256 bytes of the tile's bias run (2 x 64 RGW bytes);
-  //                   waves 2, 3: a dummy.
-  const uint8_t *ccode = pcodes + lane * 16;
   auto dma = [&](int i, int slot) {
     unsigned char *st = lds + slot * kGStageBytes;
-    const int gt0 = ti.nt * 2 * RGW;
-    const int64_t ebase = (int64_t)ti.e * NG * nchunk;
     if (i < 8) {
-      int kk = ci * 128 + lcol[i];
-      kk = kk < K ? kk : 0;  // past K: any in-bounds element (its weight is an exact zero)
-      __builtin_amdgcn_global_load_lds(aptr[i] + kk, st + (32 * wave + 4 * i) * kGRowBytes, 16, 0, 0);
+      const uint8_t *src;
+      if constexpr (MX) {
+        src = aptr[i] + ci * kMxRecBytes + lcol[i];
+      } else {
+        int kk = ci * 128 + lcol[i] / 2;
+        kk = kk < K ? kk : 0;  // past K: any in-bounds element (its weight is an exact zero)
+        src = aptr[i] + 2 * (int64_t)kk;
+      }
+      __builtin_amdgcn_global_load_lds(src, st + (32 * wave + 4 * i) * kGRowBytes, 16, 0, 0);
     } else if (i < 8 + RGW) {
-      const int m = RGW * wave + i - 8;
-      const int g = gt0 + m / 2;
-      const int64_t t = (g < NG) ? ebase + (int64_t)g * nchunk + ci : 0;
-      __builtin_amdgcn_global_load_lds(ccode + t * 2048 + (m % 2) * 1024, st + kGActBytes + m * 1024, 16, 0, 0);
+      const int m = i - 8;
+      // (the offset goes through a local: with the array reads inside the builtin's argument
+      // the host compilation silently drops the kernel's launch stub)
+      const int64_t wo = woff[m] + ci * wstr[m];
+      __builtin_amdgcn_global_load_lds(pcodes + wo, st + kWOff + (RGW * wave + m) * 1024, 16, 0, 0);
     } else if (i == 8 + RGW) {
-      const int o = 256 * wave + 4 * lane;
-      const int tt = o / 128, g = gt0 + tt;
-      const int64_t t = (tt < 2 * RGW && g < NG) ? ebase + (int64_t)g * nchunk + ci : 0;
-      __builtin_amdgcn_global_load_lds(pscales + t * 128 + (o % 128), st + kGActBytes + kGWBytes + 256 * wave, 4, 0,
-                                       0);
+      __builtin_amdgcn_global_load_lds(pscales + soff + ci * sstr, st + kWOff + kGWBytes + 256 * wave, 4, 0, 0);
+    } else if (i == 8 + RGW + 1) {
+      const uint8_t *src = boff >= 0 ? reinterpret_cast<const uint8_t *>(bias) + boff : pscales;  // else a dummy
+      __builtin_amdgcn_global_load_lds(src, st + kWOff + kGWBytes + kGSBytes + 256 * wave, 4, 0, 0);
     } else {
-      const int o = 256 * wave + 4 * lane;  // byte of the tile's bias run
-      const int n = ti.nt * kGRows + o / 2;
-      const uint16_t *src = (bias != nullptr && o < 2 * kGRows && n < N) ? bias + (int64_t)ti.e * N + n
-                                                                         : reinterpret_cast<const uint16_t *>(pscales);
-      __builtin_amdgcn_global_load_lds(src, st + kGActBytes + kGWBytes + kGSBytes + 256 * wave, 4, 0, 0);
+      __builtin_amdgcn_global_load_lds(sptr + ci * kMxScBytes, st + kGActBytes + 256 * wave, 4, 0, 0);
     }
   };
 
@@ -230,13 +311,12 @@ __global__ __launch_bounds__(256) void ffn_gemm_kernel(const uint16_t *__restric
   };
   zero();
 
-  // epilogue of the compute-side tile from ring slot `slot` (its last chunk's stage holds the
-  // tile's bias): lane holds slot column wx*64 + 32b + r32 and rows 8i + 4kh + jj of tile g
-  auto epilogue = [&](int slot) {
-    const unsigned char *bb = lds + slot * kGStageBytes + kGActBytes + kGWBytes + kGSBytes;
-    const int nloc0 = wy * 32 * RGW;
+  // The tile's bias from ring slot `slot` (its last chunk's stage holds the tile's bias run):
+  // lane holds slot column wx*64 + 32b + r32 and rows 8i + 4kh + jj of tile g.
+  const int nloc0 = wy * 32 * RGW;
+  auto bias_regs = [&](int slot, uint2 (&bq)[RGW][4]) {
+    const unsigned char *bb = lds + slot * kGStageBytes + kWOff + kGWBytes + kGSBytes;
     const uint32_t bmask = bias != nullptr ? 0xffffffffu : 0u;  // without bias the run holds junk
-    uint2 bq[RGW][4];
 #pragma unroll
     for (int g = 0; g < RGW; ++g)
 #pragma unroll
@@ -244,6 +324,10 @@ __global__ __launch_bounds__(256) void ffn_gemm_kernel(const uint16_t *__restric
         const uint2 v = lds_read_b64_sync(bb + 2 * (nloc0 + 32 * g + 8 * i + 4 * kh));
         bq[g][i] = uint2{v.x & bmask, v.y & bmask};
       }
+  };
+  auto epilogue = [&](int slot) {
+    uint2 bq[RGW][4];
+    bias_regs(slot, bq);
 #pragma unroll
     for (int b = 0; b < 2; ++b) {
       const int col = wx * 64 + 32 * b + r32;
@@ -279,66 +363,232 @@ __global__ __launch_bounds__(256) void ffn_gemm_kernel(const uint16_t *__restric
       }
     }
   };
+  // Two-term activation output (gate_up, 256-row tiles): the n-tile's 128 activations are
+  // record nt of each slot row; this wave's 64 of them (blocks 2 wy, 2 wy + 1 of the record)
+  // come from tiles g = 0, 1 (block 2 wy) and g = 2, 3 (block 2 wy + 1). A lane holds, per
+  // block, 16 of the 32 values (bytes 16 gg + 4 i + 2 kh + {0, 1} for tile 2j + gg); the
+  // lane pair l, l ^ 32 shares the block maximum, then swaps half its codes so that lane kh
+  // stores bytes 16 kh .. 16 kh + 15 of the block. Rows past N (the last n-tile) are zeros.
+  auto epilogue_mx = [&](int slot) {
+    uint2 bq[RGW][4];
+    bias_regs(slot, bq);
+    uint8_t *orec = static_cast<uint8_t *>(out);
+#pragma unroll
+    for (int b = 0; b < 2; ++b) {
+      const int col = wx * 64 + 32 * b + r32;
+      const bool live = col < tc.mcount;  // same for the lane pair; shuffles run on every lane
+      const int64_t r = tc.row0 + (live ? col : 0);
+      float av[RGW][4][2];
+#pragma unroll
+      for (int g = 0; g < RGW; ++g)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int n = tc.nt * kGRows + nloc0 + 32 * g + 8 * i + 4 * kh;
+          const float h0 = acc[g][b][4 * i + 0] + __uint_as_float(bq[g][i].x << 16);
+          const float h1 = acc[g][b][4 * i + 1] + __uint_as_float(bq[g][i].x & 0xffff0000u);
+          const float h2 = acc[g][b][4 * i + 2] + __uint_as_float(bq[g][i].y << 16);
+          const float h3 = acc[g][b][4 * i + 3] + __uint_as_float(bq[g][i].y & 0xffff0000u);
+          const float a0 = bf16_to_f32(f32_to_bf16_rne(swiglu_unit(h0, h1, limit, alpha)));
+          const float a1 = bf16_to_f32(f32_to_bf16_rne(swiglu_unit(h2, h3, limit, alpha)));
+          av[g][i][0] = n < N ? a0 : 0.0f;
+          av[g][i][1] = n < N ? a1 : 0.0f;
+        }
+      uint8_t *rec = orec + (r * ntn + tc.nt) * kMxRecBytes + 2 * wy * 32 + 16 * kh;
+      uint32_t sc_hi = 0, sc_lo = 0;
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        float m = 0.0f;
+#pragma unroll
+        for (int gg = 0; gg < 2; ++gg)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) m = fmaxf(m, fmaxf(fabsf(av[2 * j + gg][i][0]), fabsf(av[2 * j + gg][i][1])));
+        m = fmaxf(m, __shfl_xor(m, 32, kWave));
+        const MxBlockScale s = mx_block_scale(m);
+        sc_hi |= s.sh << (8 * j);
+        sc_lo |= s.sl << (8 * j);
+        uint32_t hp[2][4], lp[2][4];
+#pragma unroll
+        for (int gg = 0; gg < 2; ++gg)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) mx_split2(av[2 * j + gg][i][0], av[2 * j + gg][i][1], s, hp[gg][i], lp[gg][i]);
+        // own: the half this lane stores (gg == kh); send the other half to the partner
+        uint32_t oh[4], ol[4], sh[2], sl[2];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          oh[i] = kh ? hp[1][i] : hp[0][i];
+          ol[i] = kh ? lp[1][i] : lp[0][i];
+        }
+#pragma unroll
+        for (int d = 0; d < 2; ++d) {
+          sh[d] = (kh ? hp[0][2 * d] : hp[1][2 * d]) | ((kh ? hp[0][2 * d + 1] : hp[1][2 * d + 1]) << 16);
+          sl[d] = (kh ? lp[0][2 * d] : lp[1][2 * d]) | ((kh ? lp[0][2 * d + 1] : lp[1][2 * d + 1]) << 16);
+          sh[d] = (uint32_t)__shfl_xor((int)sh[d], 32, kWave);
+          sl[d] = (uint32_t)__shfl_xor((int)sl[d], 32, kWave);
+        }
+        u32x4_t wh, wl;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const uint32_t ph = (sh[i / 2] >> (16 * (i % 2))) & 0xffffu;  // partner's pair i
+          const uint32_t pl = (sl[i / 2] >> (16 * (i % 2))) & 0xffffu;
+          wh[i] = kh ? (ph | (oh[i] << 16)) : (oh[i] | (ph << 16));
+          wl[i] = kh ? (pl | (ol[i] << 16)) : (ol[i] | (pl << 16));
+        }
+        if (live) {
+          *reinterpret_cast<u32x4_t *>(rec + 32 * j) = wh;
+          *reinterpret_cast<u32x4_t *>(rec + 32 * j + 128) = wl;
+        }
+      }
+      if (live)
+        *reinterpret_cast<uint16_t *>(out_scales + (r * ntn + tc.nt) * kMxScBytes + 4 * kh + 2 * wy) =
+            (uint16_t)(kh ? sc_lo : sc_hi);
+    }
+  };
 
   // prologue: stages 0 and 1
 #pragma unroll
   for (int s = 0; s < 2; ++s) {
+    advance_issue();
 #pragma unroll
     for (int i = 0; i < kGDma; ++i) dma(i, s);
-    advance_issue();
+    ++ci;
   }
   int G = 0;  // global chunk counter: ring slot G % 3
   for (int jc = 0; jc < ntiles; ++jc) {
     for (int cc = 0; cc < nchunk; ++cc, ++G) {
-      // this wave's 13 loads of stage G are the oldest outstanding but for stage G+1's 13
+      // this wave's kDma loads of stage G are the oldest outstanding but for stage G+1's
       __builtin_amdgcn_s_waitcnt(vmcnt_imm(kGDma));
       __builtin_amdgcn_s_barrier();
+      asm volatile("" ::: "memory");  // no LDS read of this stage may be hoisted above the barrier
+      advance_issue();
       const int slot = G % kGStages, nslot = (G + 2) % kGStages;
       const unsigned char *abuf = lds + slot * kGStageBytes;
-      const unsigned char *wbuf = abuf + kGActBytes + (wy * RGW) * 2048 + lane * 16;
-      const unsigned char *sbuf = abuf + kGActBytes + kGWBytes + (wy * RGW) * 128 + r32 * 4;
-      uint32_t swd[RGW];
+      const unsigned char *wbuf = abuf + kWOff + (wy * RGW) * 2048 + lane * 16;
+      const unsigned char *sbuf = abuf + kWOff + kGWBytes + (wy * RGW) * 128 + r32 * 4;
+      if constexpr (MX) {
+        // four steps (64-element half p, term t), each RGW x 2 scaled MFMAs; lane group kh of
+        // the FP8 operand holds elements 16 kh .. 16 kh + 15 and 32 + 16 kh .. of the half,
+        // i.e. 16-byte columns 4p + kh and 4p + 2 + kh of the term's 128 bytes. Scale bytes:
+        // lane group kh needs block 2p + kh of its row / slot, so its dwords are pre-shifted
+        // by 8 kh and the instruction selects byte 2p.
+        auto bload = [&](int p, int t, i32x8_t *bv) {
 #pragma unroll
-      for (int g = 0; g < RGW; ++g) swd[g] = *reinterpret_cast<const uint32_t *>(sbuf + g * 128);
-      auto bload = [&](int p, int j, bf16x8_t *bv) {
+          for (int b = 0; b < 2; ++b) {
+            const int row = wx * 64 + 32 * b + r32;
+            const u32x4_t u0 = *reinterpret_cast<const u32x4_t *>(abuf + g_off(row, 8 * t + 4 * p + kh));
+            const u32x4_t u1 = *reinterpret_cast<const u32x4_t *>(abuf + g_off(row, 8 * t + 4 * p + 2 + kh));
+            bv[b] = i32x8_t{(int)u0[0], (int)u0[1], (int)u0[2], (int)u0[3],
+                            (int)u1[0], (int)u1[1], (int)u1[2], (int)u1[3]};
+          }
+        };
+        auto wload = [&](int p, u32x4_t *wv) {
 #pragma unroll
-        for (int b = 0; b < 2; ++b)
-          bv[b] = as_bf16x8(
-              *reinterpret_cast<const u32x4_t *>(abuf + g_off(wx * 64 + 32 * b + r32, 4 * (2 * p + kh) + j)));
-      };
-      bf16x8_t bcur[2], bnext[2];
-      bload(0, 0, bcur);
+          for (int g = 0; g < RGW; ++g) wv[g] = *reinterpret_cast<const u32x4_t *>(wbuf + g * 2048 + p * 1024);
+        };
+        // Two register sets each for the FP8 operand (by step) and the weights (by half), so
+        // every LDS read is issued a whole step (8 MFMAs) before its use; with one set the
+        // compiler re-used the registers and waited on each read right before its MFMA.
+        constexpr int kPerStep = (kGDma + 3) / 4;  // DMAs issued per step
+        i32x8_t bv[2][2];
+        u32x4_t wv[2][RGW];
+        bload(0, 0, bv[0]);
+        wload(0, wv[0]);
+        // the scales last: their wait inside the asm covers the operand reads above as well
+        // (a plain LDS read of the term scales makes the compiler wait for every DMA in flight)
+        uint32_t swd[RGW], ash[2][2];
+        {
+          uint32_t w4[4];
+          uint2 a2[2];
+          lds_read_mx_scales(sbuf, abuf + kGActBytes + (wx * 64 + r32) * 8, w4, a2);
 #pragma unroll
-      for (int p = 0; p < 2; ++p) {
-        u32x4_t cw[RGW];
-        float sc[RGW];
+          for (int g = 0; g < RGW; ++g) swd[g] = w4[g] >> (8 * kh);
 #pragma unroll
-        for (int g = 0; g < RGW; ++g) {
-          cw[g] = *reinterpret_cast<const u32x4_t *>(wbuf + g * 2048 + p * 1024);
-          sc[g] = e8m0_to_f32((swd[g] >> (8 * (2 * p + kh))) & 0xffu);
+          for (int b = 0; b < 2; ++b) {
+            ash[b][0] = a2[b].x >> (8 * kh);
+            ash[b][1] = a2[b].y >> (8 * kh);
+          }
         }
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const int s = 4 * p + j;
-          const int nj = (j + 1) & 3, np = p + (j == 3 ? 1 : 0);
-          if (np < 2) bload(np, nj, bnext);
-          // this k-step's share of the stage-after-next DMAs, in the shadow of its MFMAs
-          dma(s, nslot);
-          if (s < RGW + 2) dma(8 + s, nslot);
+        // Each step issues its first MFMA, then the next step's LDS reads (sched_barrier keeps
+        // them there), then its other MFMAs. With LDS DMA in flight the compiler can only wait
+        // for all LDS reads (lgkmcnt(0)); it does so before a step's first MFMA, which must
+        // therefore come before the reads it does not need (those have 7 MFMAs to arrive).
+        auto next_reads = [&](auto SC) {
+          constexpr int s = decltype(SC)::value;
+          if constexpr (s + 1 < 4) bload((s + 1) / 2, (s + 1) % 2, bv[(s + 1) % 2]);
+          if constexpr (s == 0) wload(1, wv[1]);
+          __builtin_amdgcn_sched_barrier(0);
+        };
+        auto step = [&](auto SC) {
+          constexpr int s = decltype(SC)::value, p = s / 2, t = s % 2;
 #pragma unroll
           for (int g = 0; g < RGW; ++g) {
-            const bf16x8_t wa = fp4x8_to_bf16x8(cw[g][j], sc[g]);
+            const u32x4_t u = wv[p][g];
+            const i32x8_t wa = i32x8_t{(int)u[0], (int)u[1], (int)u[2], (int)u[3], 0, 0, 0, 0};
 #pragma unroll
-            for (int b = 0; b < 2; ++b)
-              acc[g][b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wa, bcur[b], acc[g][b], 0, 0, 0);
+            for (int b = 0; b < 2; ++b) {
+              const int m = 2 * g + b;
+              if (m < kPerStep && s * kPerStep + m < kGDma) dma(s * kPerStep + m, nslot);
+              acc[g][b] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
+                  wa, bv[s % 2][b], acc[g][b], 4, 0, 2 * p, (int)swd[g], 2 * p, (int)ash[b][t]);
+              if (m == 0) {
+                __builtin_amdgcn_sched_barrier(0);
+                next_reads(SC);
+              }
+            }
           }
-          bcur[0] = bnext[0];
-          bcur[1] = bnext[1];
+        };
+        step(std::integral_constant<int, 0>{});
+        step(std::integral_constant<int, 1>{});
+        step(std::integral_constant<int, 2>{});
+        step(std::integral_constant<int, 3>{});
+      } else {
+        uint32_t swd[RGW];
+#pragma unroll
+        for (int g = 0; g < RGW; ++g) swd[g] = *reinterpret_cast<const uint32_t *>(sbuf + g * 128);
+        auto bload = [&](int p, int j, bf16x8_t *bv) {
+#pragma unroll
+          for (int b = 0; b < 2; ++b)
+            bv[b] = as_bf16x8(
+                *reinterpret_cast<const u32x4_t *>(abuf + g_off(wx * 64 + 32 * b + r32, 4 * (2 * p + kh) + j)));
+        };
+        bf16x8_t bcur[2], bnext[2];
+        bload(0, 0, bcur);
+#pragma unroll
+        for (int p = 0; p < 2; ++p) {
+          u32x4_t cw[RGW];
+          float sc[RGW];
+#pragma unroll
+          for (int g = 0; g < RGW; ++g) {
+            cw[g] = *reinterpret_cast<const u32x4_t *>(wbuf + g * 2048 + p * 1024);
+            sc[g] = e8m0_to_f32((swd[g] >> (8 * (2 * p + kh))) & 0xffu);
+          }
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            const int s = 4 * p + j;
+            const int nj = (j + 1) & 3, np = p + (j == 3 ? 1 : 0);
+            if (np < 2) bload(np, nj, bnext);
+            // this k-step's share of the stage-after-next DMAs, in the shadow of its MFMAs
+            dma(s, nslot);
+            if (s < RGW + 2) dma(8 + s, nslot);
+#pragma unroll
+            for (int g = 0; g < RGW; ++g) {
+              const bf16x8_t wa = fp4x8_to_bf16x8(cw[g][j], sc[g]);
+#pragma unroll
+              for (int b = 0; b < 2; ++b)
+                acc[g][b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wa, bcur[b], acc[g][b], 0, 0, 0);
+            }
+            bcur[0] = bnext[0];
+            bcur[1] = bnext[1];
+          }
         }
       }
-      advance_issue();
+      ++ci;
     }
-    epilogue((G - 1) % kGStages);  // the tile's last chunk is still in its ring slot
+    // the tile's last chunk is still in its ring slot
+    if constexpr (EPI == kEpiMxAct) {
+      epilogue_mx((G - 1) % kGStages);
+    } else {
+      epilogue((G - 1) % kGStages);
+    }
     zero();
     if (jc + 1 < ntiles) tc = g_tile(first + (jc + 1) * nq, off, E, mt_total, ntn, lane);
   }
@@ -359,36 +609,57 @@ int gemm_grid_cap() {
 
 // Tile height: 256 weight rows (fewer bytes per flop and more time to hide each stage's
 // loads: 624 vs 674 us for the 5760-row gate_up at 16,384 slots) unless that pads more than
-// a tenth of the 32-row tiles; then 192 if it pads less.
-hipError_t launch_ffn_gemm(const uint16_t *a_sorted, const int32_t *offsets, int E, int64_t S, const MxWeight &w,
-                           int epilogue, void *out, float limit, float alpha, hipStream_t stream) {
+// a tenth of the 32-row tiles; then 192 if it pads less. The two-term activation output
+// always uses 256 rows (one 128-element record per n-tile).
+hipError_t launch_ffn_gemm(const void *a, const uint8_t *a_scales, bool mx, const int32_t *offsets, int E, int64_t S,
+                           const MxWeight &w, int epilogue, void *out, uint8_t *out_scales, float limit, float alpha,
+                           hipStream_t stream) {
   if (E > kGMaxExperts) return hipErrorInvalidValue;
+  if (epilogue == kEpiMxAct && !mx) return hipErrorInvalidValue;
+  if (epilogue == kEpiSwigluBf16 && mx) return hipErrorInvalidValue;
   const int NG = w.N / 32;
   const int pad4 = (NG + 7) / 8 * 8 - NG, pad3 = (NG + 5) / 6 * 6 - NG;
-  const bool tall = pad4 * 10 <= NG || pad4 <= pad3;
-  const int rows = tall ? GShape<4>::kRows : GShape<3>::kRows;
+  const bool tall = epilogue == kEpiMxAct || pad4 * 10 <= NG || pad4 <= pad3;
+  const int rows = tall ? 256 : 192;
   const int64_t busy = (S < E) ? S : E;
   const int64_t mtiles = (S + kGCols - 1) / kGCols + busy;  // bound on the real m-tile count
   const int ntn = (w.N + rows - 1) / rows;
   const int64_t bound = mtiles * ntn;
   const int cap = gemm_grid_cap();  // one workgroup per CU (the LDS ring takes most of a CU)
   dim3 grid((unsigned)(bound < cap ? bound : cap));
-#define MOE_LAUNCH_GEMM(EPI, RG)                                                                               \
-  hipLaunchKernelGGL((ffn_gemm_kernel<EPI, RG>), grid, dim3(256), GShape<RG>::kLds, stream, a_sorted, offsets, E, \
-                     w.codes, w.scales, w.bias, w.N, w.K, ntn, out, limit, alpha)
-#define MOE_LAUNCH_GEMM_EPI(RG)                                               \
-  switch (epilogue) {                                                         \
-    case kEpiSwigluBf16: MOE_LAUNCH_GEMM(kEpiSwigluBf16, RG); break;          \
-    case kEpiPreactF32: MOE_LAUNCH_GEMM(kEpiPreactF32, RG); break;            \
-    case kEpiActF32: MOE_LAUNCH_GEMM(kEpiActF32, RG); break;                  \
-    default: MOE_LAUNCH_GEMM(kEpiLinearF32, RG); break;                       \
-  }
-  if (tall) {
-    MOE_LAUNCH_GEMM_EPI(4)
+#define MOE_LAUNCH_GEMM(EPI, RG, M)                                                                          \
+  hipLaunchKernelGGL((ffn_gemm_kernel<EPI, RG, M>), grid, dim3(256), (GShape<RG, M>::kLds), stream, a, a_scales, \
+                     offsets, E, w.codes, w.scales, w.bias, w.N, w.K, ntn, out, out_scales, limit, alpha)
+  if (mx) {
+    if (tall) {
+      switch (epilogue) {
+        case kEpiMxAct: MOE_LAUNCH_GEMM(kEpiMxAct, 4, true); break;
+        case kEpiPreactF32: MOE_LAUNCH_GEMM(kEpiPreactF32, 4, true); break;
+        case kEpiActF32: MOE_LAUNCH_GEMM(kEpiActF32, 4, true); break;
+        default: MOE_LAUNCH_GEMM(kEpiLinearF32, 4, true); break;
+      }
+    } else {
+      switch (epilogue) {
+        case kEpiPreactF32: MOE_LAUNCH_GEMM(kEpiPreactF32, 3, true); break;
+        case kEpiActF32: MOE_LAUNCH_GEMM(kEpiActF32, 3, true); break;
+        default: MOE_LAUNCH_GEMM(kEpiLinearF32, 3, true); break;
+      }
+    }
   } else {
-    MOE_LAUNCH_GEMM_EPI(3)
+#define MOE_LAUNCH_GEMM_EPI(RG)                                                  \
+  switch (epilogue) {                                                            \
+    case kEpiSwigluBf16: MOE_LAUNCH_GEMM(kEpiSwigluBf16, RG, false); break;      \
+    case kEpiPreactF32: MOE_LAUNCH_GEMM(kEpiPreactF32, RG, false); break;        \
+    case kEpiActF32: MOE_LAUNCH_GEMM(kEpiActF32, RG, false); break;              \
+    default: MOE_LAUNCH_GEMM(kEpiLinearF32, RG, false); break;                   \
   }
+    if (tall) {
+      MOE_LAUNCH_GEMM_EPI(4)
+    } else {
+      MOE_LAUNCH_GEMM_EPI(3)
+    }
 #undef MOE_LAUNCH_GEMM_EPI
+  }
 #undef MOE_LAUNCH_GEMM
   return hipGetLastError();
 }

@@ -4,6 +4,7 @@
 // needs no per-row index loads while its LDS DMA stream is in flight.
 #include "common.h"
 #include "kernels.h"
+#include "mx_act.h"
 
 namespace moe {
 
@@ -25,6 +26,63 @@ hipError_t launch_gather_rows(const uint16_t *x, const int32_t *sorted_slot, int
   if (S <= 0) return hipSuccess;
   hipLaunchKernelGGL(gather_rows_kernel, dim3((unsigned)((S + 3) / 4)), dim3(256), 0, stream, x, sorted_slot, k, S, H,
                      xs);
+  return hipGetLastError();
+}
+
+// Gather into the two-term MXFP8 form. One wave per sorted row; a lane takes 8 consecutive
+// elements (16 bytes of bf16), so a lane quad holds one 32-element block (its maximum by two
+// DPP quad swaps) and 16 lanes one 128-element record; a wave covers 4 records per pass.
+// Elements past H are zeros (the quad reads nothing there).
+__global__ __launch_bounds__(256) void gather_rows_mx_kernel(const uint16_t *__restrict__ x,
+                                                             const int32_t *__restrict__ sorted_slot, int k, int64_t S,
+                                                             int H, uint8_t *__restrict__ rec,
+                                                             uint8_t *__restrict__ scales) {
+  const int64_t r = (int64_t)blockIdx.x * 4 + threadIdx.x / kWave;
+  if (r >= S) return;  // wave-uniform
+  const int lane = threadIdx.x % kWave;
+  const int nrec = mx_records(H);
+  const int64_t t = sorted_slot[r] / k;
+  const uint16_t *src = x + t * H;
+  uint8_t *drow = rec + r * nrec * kMxRecBytes;
+  uint8_t *srow = scales + r * nrec * kMxScBytes;
+  for (int c0 = 0; c0 < nrec; c0 += 4) {
+    const int c = c0 + lane / 16, j = lane % 16;
+    const int e0 = c * kMxRecElems + 8 * j;  // H % 32 == 0: a piece is wholly inside or past H
+    u32x4_t v = {0u, 0u, 0u, 0u};
+    if (c < nrec && e0 < H) v = *reinterpret_cast<const u32x4_t *>(src + e0);
+    float f[8];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      f[2 * i] = __uint_as_float(v[i] << 16);
+      f[2 * i + 1] = __uint_as_float(v[i] & 0xffff0000u);
+    }
+    float m = 0.0f;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) m = fmaxf(m, fabsf(f[i]));
+    int mi = __float_as_int(m);
+    mi = __float_as_int(fmaxf(__int_as_float(mi), __int_as_float(__builtin_amdgcn_update_dpp(mi, mi, 0xB1, 0xF, 0xF, false))));
+    mi = __float_as_int(fmaxf(__int_as_float(mi), __int_as_float(__builtin_amdgcn_update_dpp(mi, mi, 0x4E, 0xF, 0xF, false))));
+    const MxBlockScale s = mx_block_scale(__int_as_float(mi));
+    uint32_t h[4], l[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) mx_split2(f[2 * i], f[2 * i + 1], s, h[i], l[i]);
+    if (c < nrec) {
+      uint8_t *d = drow + c * kMxRecBytes + 8 * j;
+      *reinterpret_cast<uint2 *>(d) = uint2{h[0] | (h[1] << 16), h[2] | (h[3] << 16)};
+      *reinterpret_cast<uint2 *>(d + 128) = uint2{l[0] | (l[1] << 16), l[2] | (l[3] << 16)};
+      if ((j & 3) == 0) {
+        srow[c * kMxScBytes + j / 4] = (uint8_t)s.sh;
+        srow[c * kMxScBytes + 4 + j / 4] = (uint8_t)s.sl;
+      }
+    }
+  }
+}
+
+hipError_t launch_gather_rows_mx(const uint16_t *x, const int32_t *sorted_slot, int k, int64_t S, int H,
+                                 uint8_t *rec, uint8_t *scales, hipStream_t stream) {
+  if (S <= 0) return hipSuccess;
+  hipLaunchKernelGGL(gather_rows_mx_kernel, dim3((unsigned)((S + 3) / 4)), dim3(256), 0, stream, x, sorted_slot, k, S,
+                     H, rec, scales);
   return hipGetLastError();
 }
 

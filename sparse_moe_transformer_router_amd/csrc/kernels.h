@@ -12,6 +12,7 @@ enum FfnEpilogue : int {
   kEpiPreactF32 = 1,   // gate_up: h -> fp32 [S][N]
   kEpiActF32 = 2,      // gate_up: bf16-rounded SwiGLU(h) widened to fp32 [S][N/2]
   kEpiLinearF32 = 3,   // down: W a + b -> fp32 [S][N]
+  kEpiMxAct = 4,       // gate_up: bf16-rounded SwiGLU(h) -> two-term MXFP8 records (mx_act.h)
 };
 
 struct MxWeight {
@@ -47,14 +48,22 @@ hipError_t launch_ffn_stream(const uint16_t *a_src, bool a_by_token, const int32
                              int epilogue, void *out, float limit, float alpha, hipStream_t stream);
 
 // One expert GEMM, persistent LDS-tiled grouped-GEMM family (tiled weights only): the
-// activations are expert-sorted rows a_sorted[r * K] (r = sorted row); output rows are
-// sorted rows. E at most 256.
-hipError_t launch_ffn_gemm(const uint16_t *a_sorted, const int32_t *offsets, int E, int64_t S, const MxWeight &w,
-                           int epilogue, void *out, float limit, float alpha, hipStream_t stream);
+// activations are expert-sorted rows (r = sorted row), either bf16 a[r * K] (mx false) or
+// two-term MXFP8 records with their scale array a_scales (mx true, layout in mx_act.h); output
+// rows are sorted rows. kEpiMxAct (mx only) writes records to out and their scales to
+// out_scales. E at most 256.
+hipError_t launch_ffn_gemm(const void *a, const uint8_t *a_scales, bool mx, const int32_t *offsets, int E, int64_t S,
+                           const MxWeight &w, int epilogue, void *out, uint8_t *out_scales, float limit, float alpha,
+                           hipStream_t stream);
 
 // xs[r] = x[sorted_slot[r] / k] for every sorted row r (rows of H bf16).
 hipError_t launch_gather_rows(const uint16_t *x, const int32_t *sorted_slot, int k, int64_t S, int H,
                               uint16_t *xs, hipStream_t stream);
+
+// The same gather, written as two-term MXFP8 records (mx_act.h): rec [S][ceil(H/128)][256],
+// scales [S][ceil(H/128)][8].
+hipError_t launch_gather_rows_mx(const uint16_t *x, const int32_t *sorted_slot, int k, int64_t S, int H,
+                                 uint8_t *rec, uint8_t *scales, hipStream_t stream);
 
 hipError_t launch_combine(const float *y, const int32_t *slot_row, const float *topk_w, int64_t T,
                           int k, int H, void *out, bool out_f32, hipStream_t stream);

@@ -8,6 +8,7 @@
 
 #include "kernels.h"
 #include "moe_mxfp4.h"
+#include "mx_act.h"
 
 namespace {
 
@@ -24,6 +25,15 @@ struct WsLayout {
   size_t logits, topk_idx, topk_w, offsets, sorted_slot, slot_row, act, y, xs, pscratch, total;
 };
 
+// Bytes of S activation rows of K elements: bf16, or the two-term records and their scales
+// (mx_act.h), whichever is larger; the records come first, their scales after S records.
+size_t act_rows_bytes(size_t S, int K) {
+  const size_t bf16 = S * (size_t)K * sizeof(uint16_t);
+  const size_t mx = S * (size_t)moe::mx_records(K) * (moe::kMxRecBytes + moe::kMxScBytes);
+  return bf16 > mx ? bf16 : mx;
+}
+size_t mx_scales_offset(size_t S, int K) { return S * (size_t)moe::mx_records(K) * moe::kMxRecBytes; }
+
 bool ws_layout(int64_t T, int E, int k, int H, int I, WsLayout *L) {
   if (T < 0 || E < 1 || k < 1 || H < 1 || I < 1) return false;
   const size_t S = (size_t)T * (size_t)k;
@@ -34,9 +44,9 @@ bool ws_layout(int64_t T, int E, int k, int H, int I, WsLayout *L) {
   L->offsets = off;     off = align_up(off + (size_t)(E + 1) * sizeof(int32_t));
   L->sorted_slot = off; off = align_up(off + S * sizeof(int32_t));
   L->slot_row = off;    off = align_up(off + S * sizeof(int32_t));
-  L->act = off;         off = align_up(off + S * (size_t)I * sizeof(uint16_t));
+  L->act = off;         off = align_up(off + act_rows_bytes(S, I));
   L->y = off;           off = align_up(off + S * (size_t)H * sizeof(float));
-  L->xs = off;          off = align_up(off + S * (size_t)H * sizeof(uint16_t));  // sorted x (GEMM path)
+  L->xs = off;          off = align_up(off + act_rows_bytes(S, H));  // sorted x (GEMM paths)
   L->pscratch = off;    off = align_up(off + (size_t)moe::permute_scratch_ints((int64_t)S, E) * sizeof(int32_t));
   L->total = off;
   return true;
@@ -82,55 +92,81 @@ moe_options_t default_options() {
 
 int check_options(const moe_options_t &o) {
   if (o.out_dtype != MOE_DTYPE_BF16 && o.out_dtype != MOE_DTYPE_F32) return MOE_ERR_INVALID_ARG;
-  if (o.path < MOE_PATH_AUTO || o.path > MOE_PATH_GEMM) return MOE_ERR_INVALID_ARG;
+  if (o.path < MOE_PATH_AUTO || o.path > MOE_PATH_GEMM_MX) return MOE_ERR_INVALID_ARG;
   if (!(o.swiglu_limit > 0.0f) || !(o.swiglu_alpha == o.swiglu_alpha)) return MOE_ERR_INVALID_ARG;
   if (o.flags & ~(MOE_FLAG_EMIT_PREACT | MOE_FLAG_EMIT_ACT)) return MOE_ERR_INVALID_ARG;
   if ((o.flags & MOE_FLAG_EMIT_PREACT) && (o.flags & MOE_FLAG_EMIT_ACT)) return MOE_ERR_INVALID_ARG;
   return MOE_OK;
 }
 
-// Which expert-GEMM family runs: the grouped GEMM (tiled weights only) when asked for, or on
+// Which expert-GEMM family runs: a grouped GEMM (tiled weights only) when asked for, or on
 // AUTO when the batch averages at least kGemmSlotsPerExpert slots per expert; otherwise the
-// weight-streaming kernels.
+// weight-streaming kernels. AUTO's grouped GEMM is the block-scaled one when kAutoMx is set.
 constexpr int64_t kGemmSlotsPerExpert = 48;
+constexpr bool kAutoMx = true;
+
+enum class Family { kStream, kGemm, kGemmMx };
 
 int check_path(const moe_options_t &o, const moe_mxfp4_weight_t &gu, const moe_mxfp4_weight_t &dn) {
-  if (o.path == MOE_PATH_GEMM && (gu.layout != MOE_LAYOUT_TILED || dn.layout != MOE_LAYOUT_TILED))
+  if ((o.path == MOE_PATH_GEMM || o.path == MOE_PATH_GEMM_MX) &&
+      (gu.layout != MOE_LAYOUT_TILED || dn.layout != MOE_LAYOUT_TILED))
     return MOE_ERR_UNSUPPORTED;
   return MOE_OK;
 }
 
-bool use_gemm(const moe_options_t &o, const moe_mxfp4_weight_t &gu, const moe_mxfp4_weight_t &dn, int64_t S,
+Family family(const moe_options_t &o, const moe_mxfp4_weight_t &gu, const moe_mxfp4_weight_t &dn, int64_t S,
               int E) {
   const bool tiled = gu.layout == MOE_LAYOUT_TILED && dn.layout == MOE_LAYOUT_TILED;
-  if (o.path == MOE_PATH_GEMM) return true;
-  if (o.path == MOE_PATH_STREAM || !tiled) return false;
-  return S >= kGemmSlotsPerExpert * (int64_t)E;
+  if (o.path == MOE_PATH_GEMM) return Family::kGemm;
+  if (o.path == MOE_PATH_GEMM_MX) return Family::kGemmMx;
+  if (o.path == MOE_PATH_STREAM || !tiled || S < kGemmSlotsPerExpert * (int64_t)E) return Family::kStream;
+  return kAutoMx ? Family::kGemmMx : Family::kGemm;
 }
 
 // The expert GEMMs that follow the permutation. Arguments already validated. The GEMM
-// family reads its gate_up activations from an expert-sorted copy of x (xs, S x H bf16).
+// families read their gate_up activations from an expert-sorted copy of x in the xs region
+// (S x H bf16, or two-term records); the act region holds the activation between the
+// projections (bf16 or two-term records).
 int run_ffn(const uint16_t *x, int64_t T, int k, int E, const int32_t *offsets, const int32_t *sorted_slot,
             const moe_mxfp4_weight_t &gu, const moe_mxfp4_weight_t &dn, const moe_options_t &o, float *y,
-            uint16_t *act, uint16_t *xs, hipStream_t stream) {
+            void *act, void *xs, hipStream_t stream) {
   const int64_t S = T * k;
+  const int H = gu.k, I = dn.k;
   const moe::MxWeight w1 = mx(gu);
   const moe::MxWeight w2 = mx(dn);
-  const bool gemm = use_gemm(o, gu, dn, S, E);
-  if (gemm && moe::launch_gather_rows(x, sorted_slot, k, S, gu.k, xs, stream) != hipSuccess) return MOE_ERR_HIP;
-  // a: x (first projection) or act (second); by_token says which
-  auto launch = [&](const uint16_t *a, bool by_token, const moe::MxWeight &w, int epi, void *out) {
-    return gemm ? moe::launch_ffn_gemm(by_token ? xs : a, offsets, E, S, w, epi, out, o.swiglu_limit,
-                                       o.swiglu_alpha, stream)
-                : moe::launch_ffn_stream(a, by_token, sorted_slot, k, offsets, E, S, w, epi, out, o.swiglu_limit,
-                                         o.swiglu_alpha, stream);
-  };
-  if (o.flags & MOE_FLAG_EMIT_PREACT)
-    return launch(x, true, w1, moe::kEpiPreactF32, y) == hipSuccess ? MOE_OK : MOE_ERR_HIP;
-  if (o.flags & MOE_FLAG_EMIT_ACT)
-    return launch(x, true, w1, moe::kEpiActF32, y) == hipSuccess ? MOE_OK : MOE_ERR_HIP;
-  if (launch(x, true, w1, moe::kEpiSwigluBf16, act) != hipSuccess) return MOE_ERR_HIP;
-  return launch(act, false, w2, moe::kEpiLinearF32, y) == hipSuccess ? MOE_OK : MOE_ERR_HIP;
+  const Family f = family(o, gu, dn, S, E);
+  const float lim = o.swiglu_limit, alpha = o.swiglu_alpha;
+  const int first_epi = (o.flags & MOE_FLAG_EMIT_PREACT) ? moe::kEpiPreactF32
+                        : (o.flags & MOE_FLAG_EMIT_ACT)  ? moe::kEpiActF32
+                                                         : -1;
+  if (f == Family::kStream) {
+    auto launch = [&](const uint16_t *a, bool by_token, const moe::MxWeight &w, int epi, void *out) {
+      return moe::launch_ffn_stream(a, by_token, sorted_slot, k, offsets, E, S, w, epi, out, lim, alpha, stream);
+    };
+    if (first_epi >= 0) return launch(x, true, w1, first_epi, y) == hipSuccess ? MOE_OK : MOE_ERR_HIP;
+    if (launch(x, true, w1, moe::kEpiSwigluBf16, act) != hipSuccess) return MOE_ERR_HIP;
+    return launch(static_cast<uint16_t *>(act), false, w2, moe::kEpiLinearF32, y) == hipSuccess ? MOE_OK
+                                                                                              : MOE_ERR_HIP;
+  }
+  const bool mxp = f == Family::kGemmMx;
+  uint8_t *xs_sc = mxp ? static_cast<uint8_t *>(xs) + mx_scales_offset((size_t)S, H) : nullptr;
+  uint8_t *act_sc = mxp ? static_cast<uint8_t *>(act) + mx_scales_offset((size_t)S, I) : nullptr;
+  const hipError_t g = mxp ? moe::launch_gather_rows_mx(x, sorted_slot, k, S, H, static_cast<uint8_t *>(xs), xs_sc,
+                                                        stream)
+                           : moe::launch_gather_rows(x, sorted_slot, k, S, H, static_cast<uint16_t *>(xs), stream);
+  if (g != hipSuccess) return MOE_ERR_HIP;
+  if (first_epi >= 0)
+    return moe::launch_ffn_gemm(xs, xs_sc, mxp, offsets, E, S, w1, first_epi, y, nullptr, lim, alpha, stream) ==
+                   hipSuccess
+               ? MOE_OK
+               : MOE_ERR_HIP;
+  if (moe::launch_ffn_gemm(xs, xs_sc, mxp, offsets, E, S, w1, mxp ? moe::kEpiMxAct : moe::kEpiSwigluBf16, act,
+                           act_sc, lim, alpha, stream) != hipSuccess)
+    return MOE_ERR_HIP;
+  return moe::launch_ffn_gemm(act, act_sc, mxp, offsets, E, S, w2, moe::kEpiLinearF32, y, nullptr, lim, alpha,
+                              stream) == hipSuccess
+             ? MOE_OK
+             : MOE_ERR_HIP;
 }
 
 int check_layer(const uint16_t *x, const moe_router_t *router, const moe_mxfp4_weight_t *gu,
@@ -165,14 +201,14 @@ int forward_impl(const uint16_t *x, const moe_router_t *router, const moe_mxfp4_
   int32_t *offsets = at<int32_t>(ws, L.offsets);
   int32_t *sorted_slot = at<int32_t>(ws, L.sorted_slot);
   int32_t *slot_row = at<int32_t>(ws, L.slot_row);
-  uint16_t *act = at<uint16_t>(ws, L.act);
+  void *act = at<void>(ws, L.act);
   float *y = at<float>(ws, L.y);
   if (moe::launch_router(x, T, H, router->weight, router->bias, E, k, logits, idx, wts, stream) != hipSuccess)
     return MOE_ERR_HIP;
   if (moe::launch_permute(idx, S, E, offsets, sorted_slot, slot_row, at<int32_t>(ws, L.pscratch), stream) !=
       hipSuccess)
     return MOE_ERR_HIP;
-  int st = run_ffn(x, T, k, E, offsets, sorted_slot, *gu, *dn, o, y, act, at<uint16_t>(ws, L.xs), stream);
+  int st = run_ffn(x, T, k, E, offsets, sorted_slot, *gu, *dn, o, y, act, at<void>(ws, L.xs), stream);
   if (st != MOE_OK) return st;
   if (moe::launch_combine(y, slot_row, wts, T, k, H, out, o.out_dtype == MOE_DTYPE_F32, stream) !=
       hipSuccess)
@@ -215,7 +251,7 @@ const char *moe_status_string(int status) {
 }
 
 size_t moe_workspace_size(int64_t T, int32_t E, int32_t k, int32_t H, int32_t I, int32_t path) {
-  if (path < MOE_PATH_AUTO || path > MOE_PATH_GEMM) return 0;
+  if (path < MOE_PATH_AUTO || path > MOE_PATH_GEMM_MX) return 0;
   if (check_common(T, E, k) != MOE_OK || check_dim(H) != MOE_OK || check_dim(I) != MOE_OK) return 0;
   WsLayout L;
   if (!ws_layout(T, E, k, H, I, &L)) return 0;
@@ -333,8 +369,8 @@ int moe_mxfp4_ffn(const uint16_t *x, int64_t T, int32_t k, int32_t E, const int3
   ws_layout(T, E, k, H, I, &L);
   if (ws == nullptr || ws_bytes < L.total) return MOE_ERR_WORKSPACE;
   if (!aligned(ws, kWsAlign)) return MOE_ERR_INVALID_ARG;
-  return run_ffn(x, T, k, E, expert_offsets, sorted_slot, *gate_up, *down, o, y, at<uint16_t>(ws, L.act),
-                 at<uint16_t>(ws, L.xs), (hipStream_t)stream);
+  return run_ffn(x, T, k, E, expert_offsets, sorted_slot, *gate_up, *down, o, y, at<void>(ws, L.act),
+                 at<void>(ws, L.xs), (hipStream_t)stream);
   MOE_GUARD_END
 }
 

@@ -121,7 +121,7 @@ def _ffn_inputs(E, H, I, scale_lo, scale_hi, seed):
     return w1c, w1s, w2c, w2s
 
 
-@pytest.mark.parametrize("tiled,path", [(False, 1), (True, 1), (True, 2)])
+@pytest.mark.parametrize("tiled,path", [(False, 1), (True, 1), (True, 2), (True, 3)])
 @pytest.mark.parametrize("scale_lo,scale_hi", [(4, 252), (123, 127)])
 def test_ffn_preact_identity_decode(scale_lo, scale_hi, tiled, path):
     """One-hot activations and no bias: h = W1 x is one decoded weight column, exactly."""
@@ -146,7 +146,7 @@ def test_ffn_preact_identity_decode(scale_lo, scale_hi, tiled, path):
             assert np.array_equal(y[r], W1[:, t]), (e, t)
 
 
-@pytest.mark.parametrize("tiled,path", [(False, 1), (True, 1), (True, 2)])
+@pytest.mark.parametrize("tiled,path", [(False, 1), (True, 1), (True, 2), (True, 3)])
 def test_ffn_activation_step(tiled, path):
     """Stop after the SwiGLU: the bf16-rounded activation of every slot."""
     cfg = synth.get_config("tiny").with_(scale_bytes=(118, 122))
@@ -162,6 +162,59 @@ def test_ffn_activation_step(tiled, path):
     err = np.abs(act - ref)
     assert (err <= 1e-2 * rms + gu.bf16_half_ulp(ref)).all(), err.max() / rms
     assert np.abs(act).max() <= 7.0 / (1 + np.exp(-7.0)) * 8.0 + 1e-3  # clamp bound holds on the GPU
+
+
+def _e4m3_values() -> np.ndarray:
+    """All 256 E4M3 codes (OCP MX v1.0 FP8 E4M3: bias 7, subnormals, 0x7F/0xFF NaN) as float32."""
+    c = np.arange(256)
+    e, m = (c >> 3) & 0xF, (c & 7).astype(np.float64)
+    v = np.where(e == 0, m / 8.0 * 2.0 ** -6, (1 + m / 8.0) * np.exp2(e - 7.0))
+    v = np.where((c & 0x7F) == 0x7F, np.nan, v)
+    return (np.where(c & 0x80, -v, v)).astype(np.float32)
+
+
+@pytest.mark.parametrize("kind,tol", [("narrow", 1e-6), ("plain", 2e-4), ("spread", 2e-3)])
+def test_mx_preact_matches_bf16_gemm(kind, tol):
+    """Pre-activations of the block-scaled GEMM against the bf16 GEMM (exact products, fp32 sums).
+
+    narrow: x are E4M3 values in [1, 4), so both terms are exact and every product of a
+    32-element block lies within 2^5 of the others: the two paths agree to fp32 summation
+    order, which pins the operand layout and both scale operands.
+    plain / spread: the synthetic x, and x spread over 16 binades inside each block. The split
+    is still exact, but the scaled MFMA sums a block's products in reduced internal precision
+    when they span a wide range (measured: 4.6e-5 and 4.7e-4 of the RMS, against 3e-7 for the
+    bf16 path); the bounds keep a 4x margin and stay far inside the layer's 2e-2 RMS tolerance."""
+    cfg = synth.get_config("tiny").with_(scale_bytes=(118, 122))
+    inp = synth.make_inputs(cfg)
+    rng = np.random.default_rng(77)
+    if kind == "narrow":
+        codes = rng.integers(0x38, 0x48, inp.x.shape) | (rng.integers(0, 2, inp.x.shape) << 7)
+        inp.x[...] = synth.bf16_bits_from_f32(_e4m3_values()[codes])
+    elif kind == "spread":
+        xf = synth.f32_from_bf16_bits(inp.x) * np.exp2(rng.integers(-12, 4, inp.x.shape)).astype(np.float32)
+        inp.x[...] = synth.bf16_bits_from_f32(xf)
+    dev = gu.device_layer(inp, tiled=True)
+    _, off, ss, _ = oracle.permute(gu.oracle_forward(inp, None, keep_intermediates=True).idx, cfg.E)
+    out = {}
+    for path in (2, 3):
+        out[path] = moe.moe_mxfp4_ffn(dev.x, cfg.k, cfg.E, torch.from_numpy(off).cuda(), torch.from_numpy(ss).cuda(),
+                                      dev.w1, dev.w2, moe.Options(flags=moe.MOE_FLAG_EMIT_PREACT, path=path)
+                                      ).cpu().numpy()
+    scale = np.sqrt(np.mean(out[2] ** 2))
+    assert np.abs(out[3] - out[2]).max() <= tol * scale, np.abs(out[3] - out[2]).max() / scale
+
+
+def test_mx_and_bf16_gemm_agree_prefill():
+    """Whole layer, 2048 tokens of the 20b shape: the two grouped GEMMs give the same output up
+    to summation order (the activation is rounded to bf16 in both, then split exactly)."""
+    cfg = synth.get_config("decode20b")
+    inp = synth.make_inputs(cfg, 2048)
+    dev = gu.device_layer(inp, tiled=True)
+    o2 = _run_forward(dev, moe.MOE_DTYPE_F32, 2).cpu().numpy()
+    o3 = _run_forward(dev, moe.MOE_DTYPE_F32, 3).cpu().numpy()
+    rms = np.sqrt(np.mean(o2 ** 2))
+    assert np.isfinite(o3).all()
+    assert np.abs(o3 - o2).max() <= 2e-3 * rms, np.abs(o3 - o2).max() / rms
 
 
 # ------------------------------------------------------------------ whole layer
@@ -194,12 +247,12 @@ def _check_layer(inp, tokens=None, path=0, tiled=True):
     return rel32, rel16
 
 
-@pytest.mark.parametrize("tiled,path", [(False, 0), (True, 0), (True, 2)])
+@pytest.mark.parametrize("tiled,path", [(False, 0), (True, 0), (True, 2), (True, 3)])
 def test_layer_tiny(tiled, path):
     _check_layer(synth.make_inputs(synth.get_config("tiny")), tiled=tiled, path=path)
 
 
-@pytest.mark.parametrize("path", [1, 2])
+@pytest.mark.parametrize("path", [1, 2, 3])
 def test_gemm_and_stream_agree(path):
     """Both kernel families on the same 1024-token batch: each against the oracle on samples."""
     cfg = synth.get_config("decode20b")
@@ -240,7 +293,7 @@ def test_layer_decode120b_zipf(T):
     _check_layer(synth.make_inputs(cfg, T))
 
 
-@pytest.mark.parametrize("path", [0, 1])
+@pytest.mark.parametrize("path", [0, 1, 2])
 def test_layer_prefill20b_sampled(path):
     cfg = synth.get_config("prefill20b")
     inp = synth.make_inputs(cfg)
@@ -260,7 +313,7 @@ def _small_cfg(E, k, H=128, I=96, T=24, seed=31, scales=(119, 123)):
     return synth.LayerConfig("edge", (T,), H, I, E, k, seed, scale_bytes=scales)
 
 
-@pytest.mark.parametrize("tiled,path", [(False, 0), (True, 0), (True, 2)])
+@pytest.mark.parametrize("tiled,path", [(False, 0), (True, 0), (True, 2), (True, 3)])
 @pytest.mark.parametrize("E,k,H,I,T", [(4, 4, 128, 96, 9), (16, 1, 64, 64, 33), (16, 8, 96, 160, 21),
                                        (256, 4, 64, 32, 40), (8, 2, 32, 32, 1), (2, 1, 160, 96, 70),
                                        (4, 2, 288, 160, 300), (8, 4, 256, 128, 100)])
@@ -268,7 +321,7 @@ def test_layer_shapes(E, k, H, I, T, tiled, path):
     _check_layer(synth.make_inputs(_small_cfg(E, k, H, I, T)), tiled=tiled, path=path)
 
 
-@pytest.mark.parametrize("path", [0, 2])
+@pytest.mark.parametrize("path", [0, 2, 3])
 def test_layer_all_tokens_one_group(path):
     """A router bias that sends every token to experts 0..3: most experts are empty and the
     four busy experts hold many m-tiles each."""

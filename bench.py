@@ -243,10 +243,16 @@ def main():
         roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": stored_traffic(cfg.name, T)}
     else:
+        # Both grouped-GEMM paths do the algorithmic flops at a 2.5 PFLOP/s ceiling: the bf16 one
+        # on the bf16 MFMA; the block-scaled one on the FP8xFP4 scaled MFMA (5.0 PFLOP/s) with two
+        # E4M3 terms per bf16 activation, i.e. two instruction flops per algorithmic flop.
+        mx = args.path in (0, 3)
+        basis = ("FP8xFP4 scaled MFMA 5.0 PFLOP/s / 2 (two E4M3 terms per bf16 activation)" if mx
+                 else "bf16 MFMA 2.5 PFLOP/s")
         achieved = ffn_flops / (ffn_ms * 1e-3) / 1e12
         roofline = {"bound": "mfma", "achieved": round(achieved, 1), "peak": BF16_PEAK_TFLOPS,
                     "unit": "TFLOP/s", "frac": round(achieved / BF16_PEAK_TFLOPS, 4),
-                    "traffic": stored_traffic(cfg.name, T),
+                    "traffic": stored_traffic(cfg.name, T), "peak_basis": basis,
                     "frac_of_mxfp4_peak": round(achieved / MXFP4_PEAK_TFLOPS, 4)}
     roofline.update({"kernel": "moe_mxfp4_ffn (gate_up + down)", "ms_per_launch": round(ffn_ms, 5),
                      "algorithmic_bytes": int(ffn_bytes), "algorithmic_flops": ffn_flops})

@@ -96,7 +96,7 @@ __device__ __forceinline__ uint2 lds_read_b64_sync(const void *p) {
 
 // The MX chunk's scale operands in one LDS round trip: four weight-scale dwords 128 bytes apart
 // (tiles g = 0..3 of the wave; a fourth read past RGW = 3 stays inside the stage's scale area)
-// and the two term-scale pairs of the lane's slot columns (32 slots = 256 bytes apart). The
+// and the two term-scale pairs of the lane's slot columns (64 slots = 512 bytes apart). The
 // reads wait for themselves inside the asm block, like lds_read_b64_sync; the outputs are
 // early-clobber, since later reads of the block still use the address registers.
 __device__ __forceinline__ void lds_read_mx_scales(const void *wsc, const void *asc, uint32_t (&w)[4], uint2 (&a)[2]) {
@@ -108,7 +108,7 @@ __device__ __forceinline__ void lds_read_mx_scales(const void *wsc, const void *
       "ds_read_b32 %2, %6 offset:256\n\t"
       "ds_read_b32 %3, %6 offset:384\n\t"
       "ds_read_b64 %4, %7\n\t"
-      "ds_read_b64 %5, %7 offset:256\n\t"
+      "ds_read_b64 %5, %7 offset:512\n\t"
       "s_waitcnt lgkmcnt(0)"
       : "=&v"(w[0]), "=&v"(w[1]), "=&v"(w[2]), "=&v"(w[3]), "=&v"(a[0]), "=&v"(a[1])
       : "v"(wa), "v"(aa)
@@ -299,6 +299,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
   };
 
   // ---- compute side
+  // A wave's two 32-slot column groups b = 0, 1 are slots 32 (wx + 2b) .. + 31 of the tile, so
+  // a tile of at most 64 slots gives every wave one group and half the MFMAs (no imbalance).
+  auto scol = [&](int b) { return 32 * (wx + 2 * b) + r32; };
   GTile tc = ti;
   f32x16_t acc[RGW][2];
   auto zero = [&]() {
@@ -330,7 +333,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
     bias_regs(slot, bq);
 #pragma unroll
     for (int b = 0; b < 2; ++b) {
-      const int col = wx * 64 + 32 * b + r32;
+      const int col = scol(b);
       if (col >= tc.mcount) continue;
       const int64_t r = tc.row0 + col;
 #pragma unroll
@@ -375,7 +378,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
     uint8_t *orec = static_cast<uint8_t *>(out);
 #pragma unroll
     for (int b = 0; b < 2; ++b) {
-      const int col = wx * 64 + 32 * b + r32;
+      const int col = scol(b);
       const bool live = col < tc.mcount;  // same for the lane pair; shuffles run on every lane
       const int64_t r = tc.row0 + (live ? col : 0);
       float av[RGW][4][2];
@@ -453,7 +456,11 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
     ++ci;
   }
   int G = 0;  // global chunk counter: ring slot G % 3
-  for (int jc = 0; jc < ntiles; ++jc) {
+  // The chunk loop of one tile with NB column groups per wave (1 for tiles of at most 64
+  // slots). Chosen once per tile: a choice per chunk made the compiler copy the accumulators
+  // between the two loop bodies every chunk.
+  auto tile_chunks = [&](auto NBC) {
+    constexpr int NB = decltype(NBC)::value;
     for (int cc = 0; cc < nchunk; ++cc, ++G) {
       // this wave's kDma loads of stage G are the oldest outstanding but for stage G+1's
       __builtin_amdgcn_s_waitcnt(vmcnt_imm(kGDma));
@@ -470,119 +477,132 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
         // i.e. 16-byte columns 4p + kh and 4p + 2 + kh of the term's 128 bytes. Scale bytes:
         // lane group kh needs block 2p + kh of its row / slot, so its dwords are pre-shifted
         // by 8 kh and the instruction selects byte 2p.
-        auto bload = [&](int p, int t, i32x8_t *bv) {
-#pragma unroll
-          for (int b = 0; b < 2; ++b) {
-            const int row = wx * 64 + 32 * b + r32;
-            const u32x4_t u0 = *reinterpret_cast<const u32x4_t *>(abuf + g_off(row, 8 * t + 4 * p + kh));
-            const u32x4_t u1 = *reinterpret_cast<const u32x4_t *>(abuf + g_off(row, 8 * t + 4 * p + 2 + kh));
-            bv[b] = i32x8_t{(int)u0[0], (int)u0[1], (int)u0[2], (int)u0[3],
-                            (int)u1[0], (int)u1[1], (int)u1[2], (int)u1[3]};
-          }
-        };
-        auto wload = [&](int p, u32x4_t *wv) {
-#pragma unroll
-          for (int g = 0; g < RGW; ++g) wv[g] = *reinterpret_cast<const u32x4_t *>(wbuf + g * 2048 + p * 1024);
-        };
-        // Two register sets each for the FP8 operand (by step) and the weights (by half), so
-        // every LDS read is issued a whole step (8 MFMAs) before its use; with one set the
-        // compiler re-used the registers and waited on each read right before its MFMA.
-        constexpr int kPerStep = (kGDma + 3) / 4;  // DMAs issued per step
-        i32x8_t bv[2][2];
-        u32x4_t wv[2][RGW];
-        bload(0, 0, bv[0]);
-        wload(0, wv[0]);
-        // the scales last: their wait inside the asm covers the operand reads above as well
-        // (a plain LDS read of the term scales makes the compiler wait for every DMA in flight)
-        uint32_t swd[RGW], ash[2][2];
         {
-          uint32_t w4[4];
-          uint2 a2[2];
-          lds_read_mx_scales(sbuf, abuf + kGActBytes + (wx * 64 + r32) * 8, w4, a2);
+          auto bload = [&](int p, int t, i32x8_t *bv) {
 #pragma unroll
-          for (int g = 0; g < RGW; ++g) swd[g] = w4[g] >> (8 * kh);
+            for (int b = 0; b < NB; ++b) {
+              const int row = scol(b);
+              const u32x4_t u0 = *reinterpret_cast<const u32x4_t *>(abuf + g_off(row, 8 * t + 4 * p + kh));
+              const u32x4_t u1 = *reinterpret_cast<const u32x4_t *>(abuf + g_off(row, 8 * t + 4 * p + 2 + kh));
+              bv[b] = i32x8_t{(int)u0[0], (int)u0[1], (int)u0[2], (int)u0[3],
+                              (int)u1[0], (int)u1[1], (int)u1[2], (int)u1[3]};
+            }
+          };
+          auto wload = [&](int p, u32x4_t *wv) {
 #pragma unroll
-          for (int b = 0; b < 2; ++b) {
-            ash[b][0] = a2[b].x >> (8 * kh);
-            ash[b][1] = a2[b].y >> (8 * kh);
-          }
-        }
-        // Each step issues its first MFMA, then the next step's LDS reads (sched_barrier keeps
-        // them there), then its other MFMAs. With LDS DMA in flight the compiler can only wait
-        // for all LDS reads (lgkmcnt(0)); it does so before a step's first MFMA, which must
-        // therefore come before the reads it does not need (those have 7 MFMAs to arrive).
-        auto next_reads = [&](auto SC) {
-          constexpr int s = decltype(SC)::value;
-          if constexpr (s + 1 < 4) bload((s + 1) / 2, (s + 1) % 2, bv[(s + 1) % 2]);
-          if constexpr (s == 0) wload(1, wv[1]);
-          __builtin_amdgcn_sched_barrier(0);
-        };
-        auto step = [&](auto SC) {
-          constexpr int s = decltype(SC)::value, p = s / 2, t = s % 2;
+            for (int g = 0; g < RGW; ++g) wv[g] = *reinterpret_cast<const u32x4_t *>(wbuf + g * 2048 + p * 1024);
+          };
+          // Two register sets each for the FP8 operand (by step) and the weights (by half), so
+          // every LDS read is issued a whole step (8 MFMAs) before its use; with one set the
+          // compiler re-used the registers and waited on each read right before its MFMA.
+          constexpr int kPerStep = (kGDma + 3) / 4;  // DMAs issued per step
+          i32x8_t bv[2][2];
+          u32x4_t wv[2][RGW];
+          bload(0, 0, bv[0]);
+          wload(0, wv[0]);
+          // the scales last: their wait inside the asm covers the operand reads above as well
+          // (a plain LDS read of the term scales makes the compiler wait for every DMA in flight)
+          uint32_t swd[RGW], ash[2][2];
+          {
+            uint32_t w4[4];
+            uint2 a2[2];
+            lds_read_mx_scales(sbuf, abuf + kGActBytes + scol(0) * 8, w4, a2);
 #pragma unroll
-          for (int g = 0; g < RGW; ++g) {
-            const u32x4_t u = wv[p][g];
-            const i32x8_t wa = i32x8_t{(int)u[0], (int)u[1], (int)u[2], (int)u[3], 0, 0, 0, 0};
+            for (int g = 0; g < RGW; ++g) swd[g] = w4[g] >> (8 * kh);
 #pragma unroll
             for (int b = 0; b < 2; ++b) {
-              const int m = 2 * g + b;
-              if (m < kPerStep && s * kPerStep + m < kGDma) dma(s * kPerStep + m, nslot);
-              acc[g][b] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
-                  wa, bv[s % 2][b], acc[g][b], 4, 0, 2 * p, (int)swd[g], 2 * p, (int)ash[b][t]);
-              if (m == 0) {
-                __builtin_amdgcn_sched_barrier(0);
-                next_reads(SC);
-              }
+              ash[b][0] = a2[b].x >> (8 * kh);
+              ash[b][1] = a2[b].y >> (8 * kh);
             }
           }
-        };
-        step(std::integral_constant<int, 0>{});
-        step(std::integral_constant<int, 1>{});
-        step(std::integral_constant<int, 2>{});
-        step(std::integral_constant<int, 3>{});
-      } else {
-        uint32_t swd[RGW];
-#pragma unroll
-        for (int g = 0; g < RGW; ++g) swd[g] = *reinterpret_cast<const uint32_t *>(sbuf + g * 128);
-        auto bload = [&](int p, int j, bf16x8_t *bv) {
-#pragma unroll
-          for (int b = 0; b < 2; ++b)
-            bv[b] = as_bf16x8(
-                *reinterpret_cast<const u32x4_t *>(abuf + g_off(wx * 64 + 32 * b + r32, 4 * (2 * p + kh) + j)));
-        };
-        bf16x8_t bcur[2], bnext[2];
-        bload(0, 0, bcur);
-#pragma unroll
-        for (int p = 0; p < 2; ++p) {
-          u32x4_t cw[RGW];
-          float sc[RGW];
-#pragma unroll
-          for (int g = 0; g < RGW; ++g) {
-            cw[g] = *reinterpret_cast<const u32x4_t *>(wbuf + g * 2048 + p * 1024);
-            sc[g] = e8m0_to_f32((swd[g] >> (8 * (2 * p + kh))) & 0xffu);
-          }
-#pragma unroll
-          for (int j = 0; j < 4; ++j) {
-            const int s = 4 * p + j;
-            const int nj = (j + 1) & 3, np = p + (j == 3 ? 1 : 0);
-            if (np < 2) bload(np, nj, bnext);
-            // this k-step's share of the stage-after-next DMAs, in the shadow of its MFMAs
-            dma(s, nslot);
-            if (s < RGW + 2) dma(8 + s, nslot);
+          // Each step issues its first MFMA, then the next step's LDS reads (sched_barrier keeps
+          // them there), then its other MFMAs. With LDS DMA in flight the compiler can only wait
+          // for all LDS reads (lgkmcnt(0)); it does so before a step's first MFMA, which must
+          // therefore come before the reads it does not need (those have 7 MFMAs to arrive).
+          auto next_reads = [&](auto SC) {
+            constexpr int s = decltype(SC)::value;
+            if constexpr (s + 1 < 4) bload((s + 1) / 2, (s + 1) % 2, bv[(s + 1) % 2]);
+            if constexpr (s == 0) wload(1, wv[1]);
+            __builtin_amdgcn_sched_barrier(0);
+          };
+          auto step = [&](auto SC) {
+            constexpr int s = decltype(SC)::value, p = s / 2, t = s % 2;
 #pragma unroll
             for (int g = 0; g < RGW; ++g) {
-              const bf16x8_t wa = fp4x8_to_bf16x8(cw[g][j], sc[g]);
+              const u32x4_t u = wv[p][g];
+              const i32x8_t wa = i32x8_t{(int)u[0], (int)u[1], (int)u[2], (int)u[3], 0, 0, 0, 0};
 #pragma unroll
-              for (int b = 0; b < 2; ++b)
-                acc[g][b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wa, bcur[b], acc[g][b], 0, 0, 0);
+              for (int b = 0; b < NB; ++b) {
+                const int m = NB * g + b;
+                if (m < kPerStep && s * kPerStep + m < kGDma) dma(s * kPerStep + m, nslot);
+                acc[g][b] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
+                    wa, bv[s % 2][b], acc[g][b], 4, 0, 2 * p, (int)swd[g], 2 * p, (int)ash[b][t]);
+                if (m == 0) {
+                  __builtin_amdgcn_sched_barrier(0);
+                  next_reads(SC);
+                }
+              }
             }
-            bcur[0] = bnext[0];
-            bcur[1] = bnext[1];
+            // this step's DMAs the MFMAs did not carry (fewer MFMAs than DMAs per step)
+#pragma unroll
+            for (int m = RGW * NB; m < kPerStep; ++m)
+              if (s * kPerStep + m < kGDma) dma(s * kPerStep + m, nslot);
+          };
+          step(std::integral_constant<int, 0>{});
+          step(std::integral_constant<int, 1>{});
+          step(std::integral_constant<int, 2>{});
+          step(std::integral_constant<int, 3>{});
+        }
+      } else {
+        {
+          uint32_t swd[RGW];
+#pragma unroll
+          for (int g = 0; g < RGW; ++g) swd[g] = *reinterpret_cast<const uint32_t *>(sbuf + g * 128);
+          auto bload = [&](int p, int j, bf16x8_t *bv) {
+#pragma unroll
+            for (int b = 0; b < NB; ++b)
+              bv[b] = as_bf16x8(*reinterpret_cast<const u32x4_t *>(abuf + g_off(scol(b), 4 * (2 * p + kh) + j)));
+          };
+          bf16x8_t bcur[2], bnext[2];
+          bload(0, 0, bcur);
+#pragma unroll
+          for (int p = 0; p < 2; ++p) {
+            u32x4_t cw[RGW];
+            float sc[RGW];
+#pragma unroll
+            for (int g = 0; g < RGW; ++g) {
+              cw[g] = *reinterpret_cast<const u32x4_t *>(wbuf + g * 2048 + p * 1024);
+              sc[g] = e8m0_to_f32((swd[g] >> (8 * (2 * p + kh))) & 0xffu);
+            }
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+              const int s = 4 * p + j;
+              const int nj = (j + 1) & 3, np = p + (j == 3 ? 1 : 0);
+              if (np < 2) bload(np, nj, bnext);
+              // this k-step's share of the stage-after-next DMAs, in the shadow of its MFMAs
+              dma(s, nslot);
+              if (s < RGW + 2) dma(8 + s, nslot);
+#pragma unroll
+              for (int g = 0; g < RGW; ++g) {
+                const bf16x8_t wa = fp4x8_to_bf16x8(cw[g][j], sc[g]);
+#pragma unroll
+                for (int b = 0; b < NB; ++b)
+                  acc[g][b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wa, bcur[b], acc[g][b], 0, 0, 0);
+              }
+#pragma unroll
+              for (int b = 0; b < NB; ++b) bcur[b] = bnext[b];
+            }
           }
         }
       }
       ++ci;
     }
+  };
+  for (int jc = 0; jc < ntiles; ++jc) {
+    if (tc.mcount > 64)
+      tile_chunks(std::integral_constant<int, 2>{});
+    else
+      tile_chunks(std::integral_constant<int, 1>{});
     // the tile's last chunk is still in its ring slot
     if constexpr (EPI == kEpiMxAct) {
       epilogue_mx((G - 1) % kGStages);

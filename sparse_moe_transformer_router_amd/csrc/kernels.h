@@ -31,6 +31,9 @@ hipError_t launch_dequant(const uint8_t *codes, const uint8_t *scales, int64_t n
 
 // Router: split-K partial logits into `partial` (router_partial_floats() floats), then top-k.
 size_t router_partial_floats(int64_t T, int E, int H);
+int router_splits(int64_t T, int E, int H);
+hipError_t launch_router_partial(const uint16_t *x, int64_t T, int H, const float *w, int E, float *partial,
+                                 hipStream_t stream);
 hipError_t launch_router(const uint16_t *x, int64_t T, int H, const float *w, const float *b, int E, int k,
                          float *partial, int32_t *topk_idx, float *topk_w, hipStream_t stream);
 
@@ -39,6 +42,7 @@ hipError_t launch_router(const uint16_t *x, int64_t T, int H, const float *w, co
 int64_t permute_scratch_ints(int64_t S, int E);
 hipError_t launch_permute(const int32_t *topk_idx, int64_t S, int E, int32_t *offsets,
                           int32_t *sorted_slot, int32_t *slot_row, int32_t *scratch, hipStream_t stream);
+
 
 // One expert GEMM over all sorted rows, weight-streaming kernel family.
 // a_src: bf16 rows; if a_by_token, sorted row r reads a_src[(sorted_slot[r] / k) * K], else

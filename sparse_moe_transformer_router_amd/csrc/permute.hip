@@ -17,13 +17,11 @@ constexpr int kPermThreads = kPermWaves * kWave;
 constexpr int kMaxExperts = 256;
 constexpr int64_t kPermSingleMax = 8192;  // up to this many slots one workgroup sorts them all
 
-__global__ __launch_bounds__(kPermThreads) void permute_kernel(const int32_t *__restrict__ topk_idx,
-                                                               int64_t S, int E,
-                                                               int32_t *__restrict__ offsets,
-                                                               int32_t *__restrict__ sorted_slot,
-                                                               int32_t *__restrict__ slot_row) {
-  __shared__ int hist[kPermWaves][kMaxExperts];
-  __shared__ int scan[kMaxExperts + 1];
+// The single-workgroup sort; idx(s) yields slot s's expert id (from global memory or LDS).
+template <typename Idx>
+__device__ __forceinline__ void permute_block(Idx idx, int64_t S, int E, int32_t *__restrict__ offsets,
+                                              int32_t *__restrict__ sorted_slot, int32_t *__restrict__ slot_row,
+                                              int (&hist)[kPermWaves][kMaxExperts], int (&scan)[kMaxExperts + 1]) {
   const int tid = threadIdx.x, wave = tid / kWave, lane = tid % kWave;
   for (int i = tid; i < kPermWaves * kMaxExperts; i += kPermThreads) (&hist[0][0])[i] = 0;
   __syncthreads();
@@ -33,7 +31,7 @@ __global__ __launch_bounds__(kPermThreads) void permute_kernel(const int32_t *__
   const int64_t end = (beg + per_wave < S) ? beg + per_wave : S;
   // ids outside [0, E) are skipped (their slots get no position), never indexed
   for (int64_t s = beg + lane; s < end; s += kWave) {
-    const int e = topk_idx[s];
+    const int e = idx(s);
     if ((unsigned)e < (unsigned)E) atomicAdd(&hist[wave][e], 1);
   }
   __syncthreads();
@@ -71,7 +69,7 @@ __global__ __launch_bounds__(kPermThreads) void permute_kernel(const int32_t *__
   // stable scatter: lanes of a batch are in slot order; equal experts are ranked by lane
   for (int64_t s0 = beg; s0 < end; s0 += kWave) {
     const int64_t s = s0 + lane;
-    const int e = (s < end) ? topk_idx[s] : -1;
+    const int e = (s < end) ? idx(s) : -1;
     const bool active = (unsigned)e < (unsigned)E;
     uint64_t same = __ballot(active);
 #pragma unroll
@@ -91,6 +89,16 @@ __global__ __launch_bounds__(kPermThreads) void permute_kernel(const int32_t *__
     }
     __builtin_amdgcn_wave_barrier();
   }
+}
+
+__global__ __launch_bounds__(kPermThreads) void permute_kernel(const int32_t *__restrict__ topk_idx,
+                                                               int64_t S, int E,
+                                                               int32_t *__restrict__ offsets,
+                                                               int32_t *__restrict__ sorted_slot,
+                                                               int32_t *__restrict__ slot_row) {
+  __shared__ int hist[kPermWaves][kMaxExperts];
+  __shared__ int scan[kMaxExperts + 1];
+  permute_block([&](int64_t s) { return topk_idx[s]; }, S, E, offsets, sorted_slot, slot_row, hist, scan);
 }
 
 // Many slots: the same counting sort over several workgroups. Chunk c of kPermChunk

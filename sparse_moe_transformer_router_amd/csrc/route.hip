@@ -11,6 +11,7 @@
 // the partial sums are added in a fixed order by the top-k kernel.
 #include "common.h"
 #include "kernels.h"
+#include "topk.h"
 
 namespace moe {
 
@@ -33,8 +34,6 @@ __device__ __forceinline__ void split3(const f32x4_t &a, const f32x4_t &b, bf16x
   mid = as_bf16x8(m);
   lo = as_bf16x8(l);
 }
-
-constexpr int kMaxSplitVec = 12;  // at most 48 splits, read as 12 float4 per logit
 
 // One wave: 16 NTT tokens x 16 NET experts over the MX-block range of split blockIdx.z
 // (NTT x NET 16x16 accumulators, so each weight element loaded and split serves 16 NTT tokens
@@ -123,57 +122,6 @@ __global__ __launch_bounds__(kWave) void router_partial_kernel(const uint16_t *_
   }
 }
 
-// k rounds of a wave-wide argmax over a token's logits (lane holds experts lane + 64 i;
-// larger logit wins, equal logits go to the lower expert id): the maximum by DPP moves, then
-// the lowest id holding it by ballots. Then softmax over the k picked logits; lane 0 writes
-// the token's ids and weights.
-__device__ __forceinline__ void topk_softmax_wave(const float (&v)[4], int E, int k, int lane,
-                                                  int32_t *__restrict__ idx_out, float *__restrict__ w_out) {
-  int taken = 0;
-#pragma unroll
-  for (int i = 0; i < 4; ++i)
-    if (lane + i * kWave >= E) taken |= 1 << i;
-  float sel_v[8];
-  int sel_e[8];
-#pragma unroll
-  for (int j = 0; j < 8; ++j) {
-    sel_v[j] = 0.f;
-    sel_e[j] = 0;
-    if (j < k) {
-      float lm = -INFINITY;
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-        if (!(taken & (1 << i))) lm = fmaxf(lm, v[i]);
-      const float m = wave_max_f32(lm);
-      int be = -1;
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {  // ids ascend with i, then with the lane
-        const uint64_t hit = __ballot(!(taken & (1 << i)) && v[i] == m);
-        if (be < 0 && hit != 0) be = i * kWave + __ffsll((unsigned long long)hit) - 1;
-      }
-      sel_v[j] = m;
-      sel_e[j] = be;
-      if ((be % kWave) == lane) taken |= 1 << (be / kWave);
-    }
-  }
-  if (lane == 0) {
-    float z[8], sum = 0.f;
-#pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      z[j] = (j < k) ? expf(sel_v[j] - sel_v[0]) : 0.f;
-      sum += z[j];
-    }
-    const float inv = 1.0f / sum;
-#pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      if (j < k) {
-        idx_out[j] = sel_e[j];
-        w_out[j] = z[j] * inv;
-      }
-    }
-  }
-}
-
 // One wave per token: sum the split partials in order and add the bias, then the top k and
 // their softmax.
 __global__ __launch_bounds__(256) void router_topk_kernel(const float *__restrict__ partial, int nsplit,
@@ -187,21 +135,7 @@ __global__ __launch_bounds__(256) void router_topk_kernel(const float *__restric
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     const int e = lane + i * kWave;
-    float s = 0.f;
-    if (e < E) {
-      // every split's partial of this logit is contiguous: issue all loads, then add in order
-      const f32x4_t *p = reinterpret_cast<const f32x4_t *>(partial + (t * E + e) * nsp);
-      f32x4_t pv[kMaxSplitVec];
-#pragma unroll
-      for (int c = 0; c < kMaxSplitVec; ++c) pv[c] = (4 * c < nsplit) ? p[c] : f32x4_t{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int c = 0; c < kMaxSplitVec; ++c)
-#pragma unroll
-        for (int u = 0; u < 4; ++u)
-          if (4 * c + u < nsplit) s += pv[c][u];
-      if (bias) s += bias[e];
-    }
-    v[i] = s;
+    v[i] = (e < E) ? router_logit(partial, nsplit, nsp, bias, t, e, E) : 0.f;
   }
   topk_softmax_wave(v, E, k, lane, topk_idx + t * k, topk_w + t * k);
 }
@@ -230,8 +164,8 @@ size_t router_partial_floats(int64_t T, int E, int H) {
   return (size_t)nsp * T * E;
 }
 
-hipError_t launch_router(const uint16_t *x, int64_t T, int H, const float *w, const float *b, int E, int k,
-                         float *partial, int32_t *topk_idx, float *topk_w, hipStream_t stream) {
+hipError_t launch_router_partial(const uint16_t *x, int64_t T, int H, const float *w, int E, float *partial,
+                                 hipStream_t stream) {
   const int KB = H / 32;
   const int ns = router_splits(T, E, H);
   const int bps = (KB + ns - 1) / ns;
@@ -243,10 +177,16 @@ hipError_t launch_router(const uint16_t *x, int64_t T, int H, const float *w, co
     dim3 grid((unsigned)((T + 15) / 16), (unsigned)((E + 15) / 16), (unsigned)ns);
     hipLaunchKernelGGL((router_partial_kernel<1, 1>), grid, dim3(kWave), 0, stream, x, T, H, w, E, bps, nsp, partial);
   }
-  hipError_t err = hipGetLastError();
+  return hipGetLastError();
+}
+
+hipError_t launch_router(const uint16_t *x, int64_t T, int H, const float *w, const float *b, int E, int k,
+                         float *partial, int32_t *topk_idx, float *topk_w, hipStream_t stream) {
+  const hipError_t err = launch_router_partial(x, T, H, w, E, partial, stream);
   if (err != hipSuccess) return err;
-  hipLaunchKernelGGL(router_topk_kernel, dim3((unsigned)((T + 3) / 4)), dim3(256), 0, stream, partial, ns, nsp, b,
-                     T, E, k, topk_idx, topk_w);
+  const int ns = router_splits(T, E, H);
+  hipLaunchKernelGGL(router_topk_kernel, dim3((unsigned)((T + 3) / 4)), dim3(256), 0, stream, partial, ns,
+                     (ns + 3) / 4 * 4, b, T, E, k, topk_idx, topk_w);
   return hipGetLastError();
 }
 

@@ -61,6 +61,8 @@ constexpr int kGRowBytes = 256;   // one 128-element bf16 chunk of a slot row
 constexpr int kGActBytes = kGCols * kGRowBytes;
 constexpr int kGSBytes = 1024;    // the tiles' scales (2 RGW x 128 bytes, padded)
 constexpr int kGBBytes = 1024;    // the tile's bias (64 RGW rows x 2 bytes, padded)
+constexpr int kGBiasAreas = 3;    // tile j's bias lives in area j % 3 (the DMA side is at most
+                                  // two tiles ahead of the epilogue that reads it)
 constexpr int kGGroupM = 4;       // m-tiles per group of the XCD-local tile order
 constexpr int kXcds = 8;
 constexpr int kGMaxExperts = 256;
@@ -72,9 +74,11 @@ struct GShape {
   static constexpr int kAScBytes = MX ? kGCols * 8 : 0;
   static constexpr int kWOff = kGActBytes + kAScBytes;  // weight codes, then scales, then bias
   static constexpr int kWBytes = 2 * RGW * 2048;       // codes of the 2 RGW weight tiles
-  static constexpr int kStageBytes = kWOff + kWBytes + kGSBytes + kGBBytes;
+  static constexpr int kStageBytes = kWOff + kWBytes + kGSBytes;
+  static constexpr int kBiasOff = kGStages * kStageBytes;  // 3 tile-bias areas after the ring
   static constexpr int kDma = 8 + RGW + 2 + (MX ? 1 : 0);  // DMAs per wave per stage
-  static constexpr size_t kLds = (size_t)kGStages * kStageBytes + (kGMaxExperts + 4) * sizeof(int32_t);
+  static constexpr size_t kLds =
+      (size_t)kBiasOff + kGBiasAreas * kGBBytes + (kGMaxExperts + 4) * sizeof(int32_t);
 };
 
 __device__ __forceinline__ int g_off(int row, int col16) { return row * kGRowBytes + ((col16 ^ (row & 15)) << 4); }
@@ -112,6 +116,25 @@ __device__ __forceinline__ void lds_read_mx_scales(const void *wsc, const void *
       "s_waitcnt lgkmcnt(0)"
       : "=&v"(w[0]), "=&v"(w[1]), "=&v"(w[2]), "=&v"(w[3]), "=&v"(a[0]), "=&v"(a[1])
       : "v"(wa), "v"(aa)
+      : "memory");
+}
+
+// The epilogue's bias pieces in one LDS round trip: 16 dwords-pairs at 16-byte steps from p
+// (tile g, row group i of the wave: offset 64 g + 16 i; pieces past RGW tiles stay inside the
+// bias area and are ignored). Early-clobber outputs, like lds_read_mx_scales.
+__device__ __forceinline__ void lds_read_bias16(const void *p, uint2 (&v)[16]) {
+  const uint32_t a = (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void *)p;
+  asm volatile(
+      "ds_read_b64 %0, %16\n\tds_read_b64 %1, %16 offset:16\n\tds_read_b64 %2, %16 offset:32\n\t"
+      "ds_read_b64 %3, %16 offset:48\n\tds_read_b64 %4, %16 offset:64\n\tds_read_b64 %5, %16 offset:80\n\t"
+      "ds_read_b64 %6, %16 offset:96\n\tds_read_b64 %7, %16 offset:112\n\tds_read_b64 %8, %16 offset:128\n\t"
+      "ds_read_b64 %9, %16 offset:144\n\tds_read_b64 %10, %16 offset:160\n\tds_read_b64 %11, %16 offset:176\n\t"
+      "ds_read_b64 %12, %16 offset:192\n\tds_read_b64 %13, %16 offset:208\n\tds_read_b64 %14, %16 offset:224\n\t"
+      "ds_read_b64 %15, %16 offset:240\n\ts_waitcnt lgkmcnt(0)"
+      : "=&v"(v[0]), "=&v"(v[1]), "=&v"(v[2]), "=&v"(v[3]), "=&v"(v[4]), "=&v"(v[5]), "=&v"(v[6]), "=&v"(v[7]),
+        "=&v"(v[8]), "=&v"(v[9]), "=&v"(v[10]), "=&v"(v[11]), "=&v"(v[12]), "=&v"(v[13]), "=&v"(v[14]),
+        "=&v"(v[15])
+      : "v"(a)
       : "memory");
 }
 
@@ -170,7 +193,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
   static_assert(EPI != kEpiMxAct || (MX && RGW == 4), "two-term output: one 128-element record per n-tile");
   static_assert(EPI != kEpiSwigluBf16 || !MX, "bf16 activation output belongs to the bf16 path");
   extern __shared__ __attribute__((aligned(16))) unsigned char lds[];
-  int32_t *off = reinterpret_cast<int32_t *>(lds + kGStages * kGStageBytes);
+  int32_t *off = reinterpret_cast<int32_t *>(lds + SH::kBiasOff + kGBiasAreas * kGBBytes);
   const int tid = threadIdx.x, lane = tid % 64;
   const int wave = __builtin_amdgcn_readfirstlane(tid / 64);  // uniform: LDS targets stay scalar
   const int wy = wave >> 1, wx = wave & 1;                      // weight-row half, slot half
@@ -208,8 +231,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
   //   0..7            activation rows 32 wave + 4 i .. + 3 (bf16 elements, or a two-term record);
   //   8..8+RGW-1      1 KB of weight codes: tile m / 2, half m % 2, m = RGW wave + i - 8;
   //   8+RGW           256 bytes of the scale block (2 RGW tiles x 128 bytes, then padding);
-  //   8+RGW+1         waves 0, 1: 256 bytes of the tile's bias run (2 x 64 RGW bytes);
-  //                   waves 2, 3: a dummy;
+  //   8+RGW+1         waves 0, 1: 256 bytes of the tile's bias run (2 x 64 RGW bytes) into
+  //                   bias area ji % 3 (outside the ring); waves 2, 3: a dummy;
   //   8+RGW+2 (MX)    256 bytes of term scales: slots 32 wave .. 32 wave + 31, 8 bytes each.
   // Sources are set once per tile as a byte offset and a per-chunk stride, so the chunk loop
   // computes each address without a branch (branches would cut the loop body into blocks the
@@ -292,7 +315,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
       __builtin_amdgcn_global_load_lds(pscales + soff + ci * sstr, st + kWOff + kGWBytes + 256 * wave, 4, 0, 0);
     } else if (i == 8 + RGW + 1) {
       const uint8_t *src = boff >= 0 ? reinterpret_cast<const uint8_t *>(bias) + boff : pscales;  // else a dummy
-      __builtin_amdgcn_global_load_lds(src, st + kWOff + kGWBytes + kGSBytes + 256 * wave, 4, 0, 0);
+      __builtin_amdgcn_global_load_lds(src, lds + SH::kBiasOff + (ji % kGBiasAreas) * kGBBytes + 256 * wave, 4, 0, 0);
     } else {
       __builtin_amdgcn_global_load_lds(sptr + ci * kMxScBytes, st + kGActBytes + 256 * wave, 4, 0, 0);
     }
@@ -314,23 +337,22 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
   };
   zero();
 
-  // The tile's bias from ring slot `slot` (its last chunk's stage holds the tile's bias run):
-  // lane holds slot column wx*64 + 32b + r32 and rows 8i + 4kh + jj of tile g.
+  // The bias of compute tile jc from bias area jc % 3: lane holds slot column scol(b) and rows
+  // 8i + 4kh + jj of tile g.
   const int nloc0 = wy * 32 * RGW;
-  auto bias_regs = [&](int slot, uint2 (&bq)[RGW][4]) {
-    const unsigned char *bb = lds + slot * kGStageBytes + kWOff + kGWBytes + kGSBytes;
+  auto bias_regs = [&](int jc, uint2 (&bq)[RGW][4]) {
+    const unsigned char *bb = lds + SH::kBiasOff + (jc % kGBiasAreas) * kGBBytes;
     const uint32_t bmask = bias != nullptr ? 0xffffffffu : 0u;  // without bias the run holds junk
+    uint2 v[16];
+    lds_read_bias16(bb + 2 * (nloc0 + 4 * kh), v);
 #pragma unroll
     for (int g = 0; g < RGW; ++g)
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const uint2 v = lds_read_b64_sync(bb + 2 * (nloc0 + 32 * g + 8 * i + 4 * kh));
-        bq[g][i] = uint2{v.x & bmask, v.y & bmask};
-      }
+      for (int i = 0; i < 4; ++i) bq[g][i] = uint2{v[4 * g + i].x & bmask, v[4 * g + i].y & bmask};
   };
-  auto epilogue = [&](int slot) {
+  auto epilogue = [&](int jc) {
     uint2 bq[RGW][4];
-    bias_regs(slot, bq);
+    bias_regs(jc, bq);
 #pragma unroll
     for (int b = 0; b < 2; ++b) {
       const int col = scol(b);
@@ -372,9 +394,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
   // block, 16 of the 32 values (bytes 16 gg + 4 i + 2 kh + {0, 1} for tile 2j + gg); the
   // lane pair l, l ^ 32 shares the block maximum, then swaps half its codes so that lane kh
   // stores bytes 16 kh .. 16 kh + 15 of the block. Rows past N (the last n-tile) are zeros.
-  auto epilogue_mx = [&](int slot) {
+  auto epilogue_mx = [&](int jc) {
     uint2 bq[RGW][4];
-    bias_regs(slot, bq);
+    bias_regs(jc, bq);
     uint8_t *orec = static_cast<uint8_t *>(out);
 #pragma unroll
     for (int b = 0; b < 2; ++b) {
@@ -456,103 +478,143 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
     ++ci;
   }
   int G = 0;  // global chunk counter: ring slot G % 3
+
+  // Block-scaled path. Operands of a chunk's step 0 and its scale operands are read at the end
+  // of the chunk before (step 3), right after the barrier that makes that stage complete: the
+  // LDS round trip after the barrier then overlaps the last step's MFMAs instead of stalling
+  // every wave at the top of the chunk. They live across chunks (and tiles), so they are
+  // declared here. Lane group kh of the FP8 operand holds elements 16 kh .. 16 kh + 15 and
+  // 32 + 16 kh .. of a 64-element half, i.e. 16-byte columns 4p + kh and 4p + 2 + kh of the
+  // term's 128 bytes; scale dwords are pre-shifted by 8 kh so the instruction's byte select 2p
+  // picks block 2p + kh.
+  i32x8_t bv[2][2];
+  u32x4_t wv[2][RGW];
+  uint32_t swd[RGW], ash[2][2];
+  auto bload = [&](const unsigned char *abuf, int p, int t, i32x8_t *b8, int nb) {
+#pragma unroll
+    for (int b = 0; b < 2; ++b) {
+      if (b >= nb) break;
+      const int row = scol(b);
+      const u32x4_t u0 = *reinterpret_cast<const u32x4_t *>(abuf + g_off(row, 8 * t + 4 * p + kh));
+      const u32x4_t u1 = *reinterpret_cast<const u32x4_t *>(abuf + g_off(row, 8 * t + 4 * p + 2 + kh));
+      b8[b] = i32x8_t{(int)u0[0], (int)u0[1], (int)u0[2], (int)u0[3], (int)u1[0], (int)u1[1], (int)u1[2], (int)u1[3]};
+    }
+  };
+  auto wload = [&](const unsigned char *abuf, int p, u32x4_t *w4) {
+#pragma unroll
+    for (int g = 0; g < RGW; ++g)
+      w4[g] = *reinterpret_cast<const u32x4_t *>(abuf + kWOff + (wy * RGW + g) * 2048 + p * 1024 + lane * 16);
+  };
+  // the scales of the stage at abuf (one asm block that waits for itself: a plain LDS read of
+  // the term scales makes the compiler wait for every DMA in flight)
+  auto sload = [&](const unsigned char *abuf) {
+    uint32_t w4[4];
+    uint2 a2[2];
+    lds_read_mx_scales(abuf + kWOff + kGWBytes + (wy * RGW) * 128 + r32 * 4, abuf + kGActBytes + scol(0) * 8, w4, a2);
+#pragma unroll
+    for (int g = 0; g < RGW; ++g) swd[g] = w4[g] >> (8 * kh);
+#pragma unroll
+    for (int b = 0; b < 2; ++b) {
+      ash[b][0] = a2[b].x >> (8 * kh);
+      ash[b][1] = a2[b].y >> (8 * kh);
+    }
+  };
+  // Wait for stage G + 1 while stage G + 2's DMAs of steps 0..2 (the youngest) may still fly.
+  constexpr int kPerStep = (kGDma + 3) / 4;  // DMAs issued per step
+  constexpr int kYounger = (3 * kPerStep < kGDma) ? 3 * kPerStep : kGDma;
+  if constexpr (MX) {
+    __builtin_amdgcn_s_waitcnt(vmcnt_imm(kGDma));  // stage 0 complete (this wave)
+    __builtin_amdgcn_s_barrier();                  // ... and every wave's
+    asm volatile("" ::: "memory");
+    sload(lds);
+    bload(lds, 0, 0, bv[0], 2);
+    wload(lds, 0, wv[0]);
+  }
+
   // The chunk loop of one tile with NB column groups per wave (1 for tiles of at most 64
   // slots). Chosen once per tile: a choice per chunk made the compiler copy the accumulators
   // between the two loop bodies every chunk.
   auto tile_chunks = [&](auto NBC) {
     constexpr int NB = decltype(NBC)::value;
     for (int cc = 0; cc < nchunk; ++cc, ++G) {
-      // this wave's kDma loads of stage G are the oldest outstanding but for stage G+1's
-      __builtin_amdgcn_s_waitcnt(vmcnt_imm(kGDma));
-      __builtin_amdgcn_s_barrier();
-      asm volatile("" ::: "memory");  // no LDS read of this stage may be hoisted above the barrier
+      if constexpr (!MX) {
+        // this wave's kDma loads of stage G are the oldest outstanding but for stage G+1's
+        __builtin_amdgcn_s_waitcnt(vmcnt_imm(kGDma));
+        __builtin_amdgcn_s_barrier();
+        asm volatile("" ::: "memory");  // no LDS read of this stage may be hoisted above the barrier
+      }
       advance_issue();
       const int slot = G % kGStages, nslot = (G + 2) % kGStages;
       const unsigned char *abuf = lds + slot * kGStageBytes;
       const unsigned char *wbuf = abuf + kWOff + (wy * RGW) * 2048 + lane * 16;
       const unsigned char *sbuf = abuf + kWOff + kGWBytes + (wy * RGW) * 128 + r32 * 4;
       if constexpr (MX) {
-        // four steps (64-element half p, term t), each RGW x 2 scaled MFMAs; lane group kh of
-        // the FP8 operand holds elements 16 kh .. 16 kh + 15 and 32 + 16 kh .. of the half,
-        // i.e. 16-byte columns 4p + kh and 4p + 2 + kh of the term's 128 bytes. Scale bytes:
-        // lane group kh needs block 2p + kh of its row / slot, so its dwords are pre-shifted
-        // by 8 kh and the instruction selects byte 2p.
-        {
-          auto bload = [&](int p, int t, i32x8_t *bv) {
+        // Four steps (64-element half p, term t), each RGW x NB scaled MFMAs. Each step issues
+        // its first MFMA, then the next step's LDS reads (sched_barrier keeps them there), then
+        // its other MFMAs: with LDS DMA in flight the compiler can only wait for all LDS reads
+        // (lgkmcnt(0)), which it does before a step's first MFMA. Step 3 instead waits for the
+        // next stage, passes the barrier, and reads the next chunk's step-0 operands and scales;
+        // its own DMAs go out after the barrier, so the wait's count of younger DMAs is exact.
+        const unsigned char *nbuf = lds + ((G + 1) % kGStages) * kGStageBytes;
+        uint32_t sw_c[RGW], as_c[2][2];  // this chunk's scale operands (sload overwrites swd / ash)
+#pragma unroll
+        for (int g = 0; g < RGW; ++g) sw_c[g] = swd[g];
+#pragma unroll
+        for (int b = 0; b < 2; ++b) {
+          as_c[b][0] = ash[b][0];
+          as_c[b][1] = ash[b][1];
+        }
+        auto next_reads = [&](auto SC) {
+          constexpr int s = decltype(SC)::value;
+          if constexpr (s < 3) {
+            bload(abuf, (s + 1) / 2, (s + 1) % 2, bv[(s + 1) % 2], NB);
+            if constexpr (s == 0) wload(abuf, 1, wv[1]);
+          } else {
+            __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0): every read of this stage has landed
+            __builtin_amdgcn_s_waitcnt(vmcnt_imm(kYounger));
+            __builtin_amdgcn_s_barrier();
+            asm volatile("" ::: "memory");
+            sload(nbuf);
+            bload(nbuf, 0, 0, bv[0], 2);  // both column groups: the next tile may be a full one
+            wload(nbuf, 0, wv[0]);
+          }
+          __builtin_amdgcn_sched_barrier(0);
+        };
+        auto step = [&](auto SC) {
+          constexpr int s = decltype(SC)::value, p = s / 2, t = s % 2;
+#pragma unroll
+          for (int g = 0; g < RGW; ++g) {
+            const u32x4_t u = wv[p][g];
+            const i32x8_t wa = i32x8_t{(int)u[0], (int)u[1], (int)u[2], (int)u[3], 0, 0, 0, 0};
 #pragma unroll
             for (int b = 0; b < NB; ++b) {
-              const int row = scol(b);
-              const u32x4_t u0 = *reinterpret_cast<const u32x4_t *>(abuf + g_off(row, 8 * t + 4 * p + kh));
-              const u32x4_t u1 = *reinterpret_cast<const u32x4_t *>(abuf + g_off(row, 8 * t + 4 * p + 2 + kh));
-              bv[b] = i32x8_t{(int)u0[0], (int)u0[1], (int)u0[2], (int)u0[3],
-                              (int)u1[0], (int)u1[1], (int)u1[2], (int)u1[3]};
-            }
-          };
-          auto wload = [&](int p, u32x4_t *wv) {
+              const int m = NB * g + b;
+              if (s < 3 && m < kPerStep && s * kPerStep + m < kGDma) dma(s * kPerStep + m, nslot);
+              acc[g][b] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
+                  wa, bv[s % 2][b], acc[g][b], 4, 0, 2 * p, (int)sw_c[g], 2 * p, (int)as_c[b][t]);
+              if (m == 0) {
+                __builtin_amdgcn_sched_barrier(0);
+                next_reads(SC);
+                if constexpr (s == 3) {
 #pragma unroll
-            for (int g = 0; g < RGW; ++g) wv[g] = *reinterpret_cast<const u32x4_t *>(wbuf + g * 2048 + p * 1024);
-          };
-          // Two register sets each for the FP8 operand (by step) and the weights (by half), so
-          // every LDS read is issued a whole step (8 MFMAs) before its use; with one set the
-          // compiler re-used the registers and waited on each read right before its MFMA.
-          constexpr int kPerStep = (kGDma + 3) / 4;  // DMAs issued per step
-          i32x8_t bv[2][2];
-          u32x4_t wv[2][RGW];
-          bload(0, 0, bv[0]);
-          wload(0, wv[0]);
-          // the scales last: their wait inside the asm covers the operand reads above as well
-          // (a plain LDS read of the term scales makes the compiler wait for every DMA in flight)
-          uint32_t swd[RGW], ash[2][2];
-          {
-            uint32_t w4[4];
-            uint2 a2[2];
-            lds_read_mx_scales(sbuf, abuf + kGActBytes + scol(0) * 8, w4, a2);
-#pragma unroll
-            for (int g = 0; g < RGW; ++g) swd[g] = w4[g] >> (8 * kh);
-#pragma unroll
-            for (int b = 0; b < 2; ++b) {
-              ash[b][0] = a2[b].x >> (8 * kh);
-              ash[b][1] = a2[b].y >> (8 * kh);
-            }
-          }
-          // Each step issues its first MFMA, then the next step's LDS reads (sched_barrier keeps
-          // them there), then its other MFMAs. With LDS DMA in flight the compiler can only wait
-          // for all LDS reads (lgkmcnt(0)); it does so before a step's first MFMA, which must
-          // therefore come before the reads it does not need (those have 7 MFMAs to arrive).
-          auto next_reads = [&](auto SC) {
-            constexpr int s = decltype(SC)::value;
-            if constexpr (s + 1 < 4) bload((s + 1) / 2, (s + 1) % 2, bv[(s + 1) % 2]);
-            if constexpr (s == 0) wload(1, wv[1]);
-            __builtin_amdgcn_sched_barrier(0);
-          };
-          auto step = [&](auto SC) {
-            constexpr int s = decltype(SC)::value, p = s / 2, t = s % 2;
-#pragma unroll
-            for (int g = 0; g < RGW; ++g) {
-              const u32x4_t u = wv[p][g];
-              const i32x8_t wa = i32x8_t{(int)u[0], (int)u[1], (int)u[2], (int)u[3], 0, 0, 0, 0};
-#pragma unroll
-              for (int b = 0; b < NB; ++b) {
-                const int m = NB * g + b;
-                if (m < kPerStep && s * kPerStep + m < kGDma) dma(s * kPerStep + m, nslot);
-                acc[g][b] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
-                    wa, bv[s % 2][b], acc[g][b], 4, 0, 2 * p, (int)swd[g], 2 * p, (int)ash[b][t]);
-                if (m == 0) {
-                  __builtin_amdgcn_sched_barrier(0);
-                  next_reads(SC);
+                  for (int i = 3 * kPerStep; i < kGDma; ++i) dma(i, nslot);
                 }
               }
             }
-            // this step's DMAs the MFMAs did not carry (fewer MFMAs than DMAs per step)
+          }
+          // this step's DMAs the MFMAs did not carry (fewer MFMAs than DMAs per step)
+          if constexpr (s < 3) {
 #pragma unroll
             for (int m = RGW * NB; m < kPerStep; ++m)
               if (s * kPerStep + m < kGDma) dma(s * kPerStep + m, nslot);
-          };
-          step(std::integral_constant<int, 0>{});
-          step(std::integral_constant<int, 1>{});
-          step(std::integral_constant<int, 2>{});
-          step(std::integral_constant<int, 3>{});
-        }
+          }
+        };
+        step(std::integral_constant<int, 0>{});
+        step(std::integral_constant<int, 1>{});
+        step(std::integral_constant<int, 2>{});
+        step(std::integral_constant<int, 3>{});
+        (void)wbuf;
+        (void)sbuf;
       } else {
         {
           uint32_t swd[RGW];
@@ -603,11 +665,10 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
       tile_chunks(std::integral_constant<int, 2>{});
     else
       tile_chunks(std::integral_constant<int, 1>{});
-    // the tile's last chunk is still in its ring slot
     if constexpr (EPI == kEpiMxAct) {
-      epilogue_mx((G - 1) % kGStages);
+      epilogue_mx(jc);
     } else {
-      epilogue((G - 1) % kGStages);
+      epilogue(jc);
     }
     zero();
     if (jc + 1 < ntiles) tc = g_tile(first + (jc + 1) * nq, off, E, mt_total, ntn, lane);

@@ -15,13 +15,8 @@ typedef int i32x8_t __attribute__((ext_vector_type(8)));  // operand of the scal
 
 constexpr int kWave = 64;
 
-// fp32 -> bf16 bits, round to nearest even; NaN stays a quiet NaN.
-__device__ __forceinline__ uint16_t f32_to_bf16_rne(float f) {
-  uint32_t u = __float_as_uint(f);
-  if ((u & 0x7fffffffu) > 0x7f800000u) return (uint16_t)((u >> 16) | 0x40u);
-  u += 0x7fffu + ((u >> 16) & 1u);
-  return (uint16_t)(u >> 16);
-}
+// fp32 -> bf16 bits, round to nearest even (gfx950's v_cvt_pk_bf16_f32; a NaN stays a NaN).
+__device__ __forceinline__ uint16_t f32_to_bf16_rne(float f) { return __builtin_bit_cast(uint16_t, (__bf16)f); }
 
 __device__ __forceinline__ float bf16_to_f32(uint16_t b) { return __uint_as_float((uint32_t)b << 16); }
 
@@ -56,7 +51,10 @@ __device__ __forceinline__ bf16x8_t as_bf16x8(u32x4_t v) { return __builtin_bit_
 __device__ __forceinline__ float swiglu_unit(float g, float l, float limit, float alpha) {
   g = fminf(fmaxf(g, -limit), limit);
   l = fminf(fmaxf(l, -limit), limit);
-  return g / (1.0f + expf(-alpha * g)) * (l + 1.0f);
+  // sigma(alpha g) = 1 / (1 + 2^(-alpha g log2 e)) on the hardware's base-2 exponential and
+  // reciprocal (about 1 ulp each: far inside the bf16 rounding that follows)
+  const float e = __builtin_amdgcn_exp2f(-alpha * 1.44269504088896341f * g);
+  return g * __builtin_amdgcn_rcpf(1.0f + e) * (l + 1.0f);
 }
 
 // Wave-wide helpers.

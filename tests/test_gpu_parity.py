@@ -239,6 +239,9 @@ def _check_layer(inp, tokens=None, path=0, tiled=True):
     out16 = gu.bf16_bits(_run_forward(dev, moe.MOE_DTYPE_BF16, path))
     o16 = synth.f32_from_bf16_bits(out16)
     rel16 = gu.check_output(o16[tok], ref.out, bf16=True)
+    # both dtypes sum the same fp32 values: the bf16 output is the fp32 one rounded to nearest
+    # even, bit for bit (checks the hardware conversion against the definition)
+    assert np.array_equal(out16, synth.bf16_bits_from_f32(out32))
     # moe_forward (library-owned workspace, AUTO path) gives the same bits as moe_forward_ex on
     # the same path (another kernel family sums in another order)
     if path == 0:

@@ -550,7 +550,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
       const unsigned char *sbuf = abuf + kWOff + kGWBytes + (wy * RGW) * 128 + r32 * 4;
       if constexpr (MX) {
         // Four steps (64-element half p, term t), each RGW x NB scaled MFMAs. Each step issues
-        // its first MFMA, then the next step's LDS reads (sched_barrier keeps them there), then
+        // its first MFMA, then the next step's LDS reads and its share of the DMAs spread over
         // its other MFMAs: with LDS DMA in flight the compiler can only wait for all LDS reads
         // (lgkmcnt(0)), which it does before a step's first MFMA. Step 3 instead waits for the
         // next stage, passes the barrier, and reads the next chunk's step-0 operands and scales;
@@ -564,49 +564,63 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
           as_c[b][0] = ash[b][0];
           as_c[b][1] = ash[b][1];
         }
-        auto next_reads = [&](auto SC) {
-          constexpr int s = decltype(SC)::value;
-          if constexpr (s < 3) {
-            bload(abuf, (s + 1) / 2, (s + 1) % 2, bv[(s + 1) % 2], NB);
-            if constexpr (s == 0) wload(abuf, 1, wv[1]);
+        // Read k of a step's LDS reads into the next operands: k < 2 nb, half k % 2 of the FP8
+        // operand of column group k / 2 (64-element half p, term t); then weight tile k - 2 nb
+        // of half pw.
+        auto read_op = [&](const unsigned char *buf, int k, int nb, int p, int t, i32x8_t *bd, int pw, u32x4_t *wd) {
+          if (k < 2 * nb) {
+            const int b = k / 2, h = k % 2;
+            const u32x4_t u = *reinterpret_cast<const u32x4_t *>(buf + g_off(scol(b), 8 * t + 4 * p + 2 * h + kh));
+#pragma unroll
+            for (int i = 0; i < 4; ++i) bd[b][4 * h + i] = (int)u[i];
           } else {
+            const int g = k - 2 * nb;
+            wd[g] = *reinterpret_cast<const u32x4_t *>(buf + kWOff + (wy * RGW + g) * 2048 + pw * 1024 + lane * 16);
+          }
+        };
+        auto step = [&](auto SC) {
+          constexpr int s = decltype(SC)::value, p = s / 2, t = s % 2;
+          constexpr int NM = RGW * NB;
+          // this step's reads (of the next step's operands, or at step 3 of the next chunk's
+          // first) and DMAs
+          constexpr int NR = s < 3 ? 2 * NB + (s == 0 ? RGW : 0) : 4 + RGW;
+          constexpr int D0 = s < 3 ? s * kPerStep : 3 * kPerStep;
+          constexpr int ND = s < 3 ? (kGDma - D0 < kPerStep ? kGDma - D0 : kPerStep) : kGDma - D0;
+          constexpr int kPerR = (NR + NM - 2) / (NM - 1), kPerD = (ND + NM - 3) / (NM - 2);
+          auto mfma = [&](int g, int b) {
+            const u32x4_t u = wv[p][g];
+            const i32x8_t wa = i32x8_t{(int)u[0], (int)u[1], (int)u[2], (int)u[3], 0, 0, 0, 0};
+            acc[g][b] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
+                wa, bv[s % 2][b], acc[g][b], 4, 0, 2 * p, (int)sw_c[g], 2 * p, (int)as_c[b][t]);
+          };
+          mfma(0, 0);
+          if constexpr (s == 3) {
+            __builtin_amdgcn_sched_barrier(0);
             __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0): every read of this stage has landed
             __builtin_amdgcn_s_waitcnt(vmcnt_imm(kYounger));
             __builtin_amdgcn_s_barrier();
             asm volatile("" ::: "memory");
             sload(nbuf);
-            bload(nbuf, 0, 0, bv[0], 2);  // both column groups: the next tile may be a full one
-            wload(nbuf, 0, wv[0]);
           }
-          __builtin_amdgcn_sched_barrier(0);
-        };
-        auto step = [&](auto SC) {
-          constexpr int s = decltype(SC)::value, p = s / 2, t = s % 2;
+          // Issue order, held by scheduling fences: before MFMA j (j >= 1) up to kPerR reads and,
+          // from j = 2 on, up to kPerD DMAs. A wave stalled issuing a run of them would leave the
+          // matrix core idle; spread out, each issues in the shadow of an MFMA.
 #pragma unroll
-          for (int g = 0; g < RGW; ++g) {
-            const u32x4_t u = wv[p][g];
-            const i32x8_t wa = i32x8_t{(int)u[0], (int)u[1], (int)u[2], (int)u[3], 0, 0, 0, 0};
+          for (int j = 1; j <= NM; ++j) {
+            __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-            for (int b = 0; b < NB; ++b) {
-              const int m = NB * g + b;
-              if (s < 3 && m < kPerStep && s * kPerStep + m < kGDma) dma(s * kPerStep + m, nslot);
-              acc[g][b] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
-                  wa, bv[s % 2][b], acc[g][b], 4, 0, 2 * p, (int)sw_c[g], 2 * p, (int)as_c[b][t]);
-              if (m == 0) {
-                __builtin_amdgcn_sched_barrier(0);
-                next_reads(SC);
-                if constexpr (s == 3) {
-#pragma unroll
-                  for (int i = 3 * kPerStep; i < kGDma; ++i) dma(i, nslot);
-                }
-              }
+            for (int k = (j - 1) * kPerR; k < j * kPerR && k < NR; ++k) {
+              if constexpr (s < 3)
+                read_op(abuf, k, NB, (s + 1) / 2, (s + 1) % 2, bv[(s + 1) % 2], 1, wv[1]);
+              else
+                read_op(nbuf, k, 2, 0, 0, bv[0], 0, wv[0]);  // both column groups: the next tile may be full
             }
-          }
-          // this step's DMAs the MFMAs did not carry (fewer MFMAs than DMAs per step)
-          if constexpr (s < 3) {
+            if (j >= 2) {
 #pragma unroll
-            for (int m = RGW * NB; m < kPerStep; ++m)
-              if (s * kPerStep + m < kGDma) dma(s * kPerStep + m, nslot);
+              for (int i = (j - 2) * kPerD; i < (j - 1) * kPerD && i < ND; ++i) dma(D0 + i, nslot);
+            }
+            __builtin_amdgcn_sched_barrier(0);
+            if (j < NM) mfma(j / NB, j % NB);
           }
         };
         step(std::integral_constant<int, 0>{});

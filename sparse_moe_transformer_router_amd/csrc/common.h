@@ -49,8 +49,8 @@ __device__ __forceinline__ bf16x8_t as_bf16x8(u32x4_t v) { return __builtin_bit_
 
 // Clamped gated SwiGLU with the +1 on the linear branch, for one (gate, linear) pair.
 __device__ __forceinline__ float swiglu_unit(float g, float l, float limit, float alpha) {
-  g = fminf(fmaxf(g, -limit), limit);
-  l = fminf(fmaxf(l, -limit), limit);
+  g = __builtin_amdgcn_fmed3f(g, -limit, limit);  // clamp to [-limit, limit] in one instruction
+  l = __builtin_amdgcn_fmed3f(l, -limit, limit);
   // sigma(alpha g) = 1 / (1 + 2^(-alpha g log2 e)) on the hardware's base-2 exponential and
   // reciprocal (about 1 ulp each: far inside the bf16 rounding that follows)
   const float e = __builtin_amdgcn_exp2f(-alpha * 1.44269504088896341f * g);

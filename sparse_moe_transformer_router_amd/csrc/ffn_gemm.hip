@@ -88,40 +88,11 @@ __device__ __forceinline__ constexpr int vmcnt_imm(int n) {
   return (n & 0xf) | ((n >> 4) << 14) | (0x7 << 4) | (0xf << 8);
 }
 
-// An 8-byte LDS read that waits for its own result (inside the asm block). The compiler
-// cannot see that it reads LDS the in-flight DMAs do not touch, and would otherwise wait
-// for every load in flight before it.
-__device__ __forceinline__ uint2 lds_read_b64_sync(const void *p) {
-  const uint32_t a = (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void *)p;
-  uint2 v;
-  asm volatile("ds_read_b64 %0, %1\n\ts_waitcnt lgkmcnt(0)" : "=v"(v) : "v"(a) : "memory");
-  return v;
-}
-
-// The MX chunk's scale operands in one LDS round trip: four weight-scale dwords 128 bytes apart
-// (tiles g = 0..3 of the wave; a fourth read past RGW = 3 stays inside the stage's scale area)
-// and the two term-scale pairs of the lane's slot columns (64 slots = 512 bytes apart). The
-// reads wait for themselves inside the asm block, like lds_read_b64_sync; the outputs are
-// early-clobber, since later reads of the block still use the address registers.
-__device__ __forceinline__ void lds_read_mx_scales(const void *wsc, const void *asc, uint32_t (&w)[4], uint2 (&a)[2]) {
-  const uint32_t wa = (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void *)wsc;
-  const uint32_t aa = (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void *)asc;
-  asm volatile(
-      "ds_read_b32 %0, %6\n\t"
-      "ds_read_b32 %1, %6 offset:128\n\t"
-      "ds_read_b32 %2, %6 offset:256\n\t"
-      "ds_read_b32 %3, %6 offset:384\n\t"
-      "ds_read_b64 %4, %7\n\t"
-      "ds_read_b64 %5, %7 offset:512\n\t"
-      "s_waitcnt lgkmcnt(0)"
-      : "=&v"(w[0]), "=&v"(w[1]), "=&v"(w[2]), "=&v"(w[3]), "=&v"(a[0]), "=&v"(a[1])
-      : "v"(wa), "v"(aa)
-      : "memory");
-}
-
 // The epilogue's bias pieces in one LDS round trip: 16 dwords-pairs at 16-byte steps from p
 // (tile g, row group i of the wave: offset 64 g + 16 i; pieces past RGW tiles stay inside the
-// bias area and are ignored). Early-clobber outputs, like lds_read_mx_scales.
+// bias area and are ignored). The reads wait for themselves inside the asm block (the compiler
+// would take plain reads for possible targets of the DMAs in flight and wait for all of them);
+// the outputs are early-clobber, since later reads of the block still use the address register.
 __device__ __forceinline__ void lds_read_bias16(const void *p, uint2 (&v)[16]) {
   const uint32_t a = (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void *)p;
   asm volatile(
@@ -350,9 +321,27 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
 #pragma unroll
       for (int i = 0; i < 4; ++i) bq[g][i] = uint2{v[4 * g + i].x & bmask, v[4 * g + i].y & bmask};
   };
-  auto epilogue = [&](int jc) {
+  // Block-scaled path: the accumulators of compute tile jc start from its bias (rows are the
+  // same for both column groups), so the epilogues add none. Called once the tile's bias area
+  // is complete: after the barrier that completes the tile's first stage.
+  auto init_acc = [&](int jc) {
     uint2 bq[RGW][4];
     bias_regs(jc, bq);
+#pragma unroll
+    for (int g = 0; g < RGW; ++g)
+#pragma unroll
+      for (int b = 0; b < 2; ++b)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          acc[g][b][4 * i + 0] = __uint_as_float(bq[g][i].x << 16);
+          acc[g][b][4 * i + 1] = __uint_as_float(bq[g][i].x & 0xffff0000u);
+          acc[g][b][4 * i + 2] = __uint_as_float(bq[g][i].y << 16);
+          acc[g][b][4 * i + 3] = __uint_as_float(bq[g][i].y & 0xffff0000u);
+        }
+  };
+  auto epilogue = [&](int jc) {
+    uint2 bq[RGW][4];
+    if constexpr (!MX) bias_regs(jc, bq);
 #pragma unroll
     for (int b = 0; b < 2; ++b) {
       const int col = scol(b);
@@ -365,10 +354,15 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
           const int n = tc.nt * kGRows + nloc0 + 32 * g + 8 * i + 4 * kh;
           if (n >= N) continue;
           float h[4];
-          h[0] = acc[g][b][4 * i + 0] + __uint_as_float(bq[g][i].x << 16);
-          h[1] = acc[g][b][4 * i + 1] + __uint_as_float(bq[g][i].x & 0xffff0000u);
-          h[2] = acc[g][b][4 * i + 2] + __uint_as_float(bq[g][i].y << 16);
-          h[3] = acc[g][b][4 * i + 3] + __uint_as_float(bq[g][i].y & 0xffff0000u);
+          if constexpr (MX) {
+#pragma unroll
+            for (int jj = 0; jj < 4; ++jj) h[jj] = acc[g][b][4 * i + jj];
+          } else {
+            h[0] = acc[g][b][4 * i + 0] + __uint_as_float(bq[g][i].x << 16);
+            h[1] = acc[g][b][4 * i + 1] + __uint_as_float(bq[g][i].x & 0xffff0000u);
+            h[2] = acc[g][b][4 * i + 2] + __uint_as_float(bq[g][i].y << 16);
+            h[3] = acc[g][b][4 * i + 3] + __uint_as_float(bq[g][i].y & 0xffff0000u);
+          }
           if (EPI == kEpiSwigluBf16 || EPI == kEpiActF32) {
             const int half = N / 2;
             const uint16_t a0 = f32_to_bf16_rne(swiglu_unit(h[0], h[1], limit, alpha));
@@ -395,8 +389,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
   // lane pair l, l ^ 32 shares the block maximum, then swaps half its codes so that lane kh
   // stores bytes 16 kh .. 16 kh + 15 of the block. Rows past N (the last n-tile) are zeros.
   auto epilogue_mx = [&](int jc) {
-    uint2 bq[RGW][4];
-    bias_regs(jc, bq);
+    (void)jc;
     uint8_t *orec = static_cast<uint8_t *>(out);
 #pragma unroll
     for (int b = 0; b < 2; ++b) {
@@ -409,10 +402,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           const int n = tc.nt * kGRows + nloc0 + 32 * g + 8 * i + 4 * kh;
-          const float h0 = acc[g][b][4 * i + 0] + __uint_as_float(bq[g][i].x << 16);
-          const float h1 = acc[g][b][4 * i + 1] + __uint_as_float(bq[g][i].x & 0xffff0000u);
-          const float h2 = acc[g][b][4 * i + 2] + __uint_as_float(bq[g][i].y << 16);
-          const float h3 = acc[g][b][4 * i + 3] + __uint_as_float(bq[g][i].y & 0xffff0000u);
+          const float h0 = acc[g][b][4 * i + 0], h1 = acc[g][b][4 * i + 1];  // bias included
+          const float h2 = acc[g][b][4 * i + 2], h3 = acc[g][b][4 * i + 3];
           const float a0 = bf16_to_f32(f32_to_bf16_rne(swiglu_unit(h0, h1, limit, alpha)));
           const float a1 = bf16_to_f32(f32_to_bf16_rne(swiglu_unit(h2, h3, limit, alpha)));
           av[g][i][0] = n < N ? a0 : 0.0f;
@@ -485,8 +476,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
   // every wave at the top of the chunk. They live across chunks (and tiles), so they are
   // declared here. Lane group kh of the FP8 operand holds elements 16 kh .. 16 kh + 15 and
   // 32 + 16 kh .. of a 64-element half, i.e. 16-byte columns 4p + kh and 4p + 2 + kh of the
-  // term's 128 bytes; scale dwords are pre-shifted by 8 kh so the instruction's byte select 2p
-  // picks block 2p + kh.
+  // term's 128 bytes.
   i32x8_t bv[2][2];
   u32x4_t wv[2][RGW];
   uint32_t swd[RGW], ash[2][2];
@@ -507,16 +497,18 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
   };
   // the scales of the stage at abuf (one asm block that waits for itself: a plain LDS read of
   // the term scales makes the compiler wait for every DMA in flight)
+  // The scale operands of the stage at abuf, unshifted (shifted where a chunk starts, after the
+  // wait its first MFMA needs anyway). The term scales are read as two dwords each: written as
+  // one 8-byte read, the compiler took them for a possible target of the DMAs in flight and
+  // waited for all of them.
   auto sload = [&](const unsigned char *abuf) {
-    uint32_t w4[4];
-    uint2 a2[2];
-    lds_read_mx_scales(abuf + kWOff + kGWBytes + (wy * RGW) * 128 + r32 * 4, abuf + kGActBytes + scol(0) * 8, w4, a2);
 #pragma unroll
-    for (int g = 0; g < RGW; ++g) swd[g] = w4[g] >> (8 * kh);
+    for (int g = 0; g < RGW; ++g)
+      swd[g] = *reinterpret_cast<const uint32_t *>(abuf + kWOff + kGWBytes + (wy * RGW + g) * 128 + r32 * 4);
 #pragma unroll
     for (int b = 0; b < 2; ++b) {
-      ash[b][0] = a2[b].x >> (8 * kh);
-      ash[b][1] = a2[b].y >> (8 * kh);
+      ash[b][0] = *reinterpret_cast<const uint32_t *>(abuf + kGActBytes + scol(b) * 8);
+      ash[b][1] = *reinterpret_cast<const uint32_t *>(abuf + kGActBytes + scol(b) * 8 + 4);
     }
   };
   // Wait for stage G + 1 while stage G + 2's DMAs of steps 0..2 (the youngest) may still fly.
@@ -529,6 +521,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
     sload(lds);
     bload(lds, 0, 0, bv[0], 2);
     wload(lds, 0, wv[0]);
+    init_acc(0);
   }
 
   // The chunk loop of one tile with NB column groups per wave (1 for tiles of at most 64
@@ -556,26 +549,27 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
         // next stage, passes the barrier, and reads the next chunk's step-0 operands and scales;
         // its own DMAs go out after the barrier, so the wait's count of younger DMAs is exact.
         const unsigned char *nbuf = lds + ((G + 1) % kGStages) * kGStageBytes;
-        uint32_t sw_c[RGW], as_c[2][2];  // this chunk's scale operands (sload overwrites swd / ash)
+        // this chunk's scale operands (sload overwrites swd / ash), shifted by 8 kh so that the
+        // instruction's byte select 2p picks block 2p + kh
+        uint32_t sw_c[RGW], as_c[2][2];
 #pragma unroll
-        for (int g = 0; g < RGW; ++g) sw_c[g] = swd[g];
+        for (int g = 0; g < RGW; ++g) sw_c[g] = swd[g] >> (8 * kh);
 #pragma unroll
         for (int b = 0; b < 2; ++b) {
-          as_c[b][0] = ash[b][0];
-          as_c[b][1] = ash[b][1];
+          as_c[b][0] = ash[b][0] >> (8 * kh);
+          as_c[b][1] = ash[b][1] >> (8 * kh);
         }
-        // Read k of a step's LDS reads into the next operands: k < 2 nb, half k % 2 of the FP8
-        // operand of column group k / 2 (64-element half p, term t); then weight tile k - 2 nb
-        // of half pw.
-        auto read_op = [&](const unsigned char *buf, int k, int nb, int p, int t, i32x8_t *bd, int pw, u32x4_t *wd) {
-          if (k < 2 * nb) {
-            const int b = k / 2, h = k % 2;
+        // Read k of a step's LDS reads into the next operands: k < nw, weight tile k of half pw;
+        // then half (k - nw) % 2 of the FP8 operand of column group (k - nw) / 2 (64-element half
+        // p, term t).
+        auto read_op = [&](const unsigned char *buf, int k, int nw, int p, int t, i32x8_t *bd, int pw, u32x4_t *wd) {
+          if (k < nw) {
+            wd[k] = *reinterpret_cast<const u32x4_t *>(buf + kWOff + (wy * RGW + k) * 2048 + pw * 1024 + lane * 16);
+          } else {
+            const int b = (k - nw) / 2, h = (k - nw) % 2;
             const u32x4_t u = *reinterpret_cast<const u32x4_t *>(buf + g_off(scol(b), 8 * t + 4 * p + 2 * h + kh));
 #pragma unroll
             for (int i = 0; i < 4; ++i) bd[b][4 * h + i] = (int)u[i];
-          } else {
-            const int g = k - 2 * nb;
-            wd[g] = *reinterpret_cast<const u32x4_t *>(buf + kWOff + (wy * RGW + g) * 2048 + pw * 1024 + lane * 16);
           }
         };
         auto step = [&](auto SC) {
@@ -611,9 +605,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
 #pragma unroll
             for (int k = (j - 1) * kPerR; k < j * kPerR && k < NR; ++k) {
               if constexpr (s < 3)
-                read_op(abuf, k, NB, (s + 1) / 2, (s + 1) % 2, bv[(s + 1) % 2], 1, wv[1]);
+                read_op(abuf, k, s == 0 ? RGW : 0, (s + 1) / 2, (s + 1) % 2, bv[(s + 1) % 2], 1, wv[1]);
               else
-                read_op(nbuf, k, 2, 0, 0, bv[0], 0, wv[0]);  // both column groups: the next tile may be full
+                read_op(nbuf, k, RGW, 0, 0, bv[0], 0, wv[0]);  // both column groups: the next tile may be full
             }
             if (j >= 2) {
 #pragma unroll
@@ -684,7 +678,10 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
     } else {
       epilogue(jc);
     }
-    zero();
+    if constexpr (MX)
+      init_acc(jc + 1);  // (past the last tile: a harmless read of a bias area)
+    else
+      zero();
     if (jc + 1 < ntiles) tc = g_tile(first + (jc + 1) * nq, off, E, mt_total, ntn, lane);
   }
   __builtin_amdgcn_s_waitcnt(0);  // no DMA may still target this workgroup's LDS when it ends

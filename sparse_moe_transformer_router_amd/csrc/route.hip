@@ -37,12 +37,12 @@ __device__ __forceinline__ void split3(const f32x4_t &a, const f32x4_t &b, bf16x
 
 // One wave: 16 NTT tokens x 16 NET experts over the MX-block range of split blockIdx.z
 // (NTT x NET 16x16 accumulators, so each weight element loaded and split serves 16 NTT tokens
-// and each x element 16 NET experts). Writes partial[(t * E + e) * nsp + split] (nsp = split
-// count rounded up to 4).
+// and each x element 16 NET experts). Writes partial[(split * T + t) * E + e]: a wave's
+// stores for one split are runs of consecutive experts.
 template <int NTT, int NET>
 __global__ __launch_bounds__(kWave) void router_partial_kernel(const uint16_t *__restrict__ x, int64_t T,
                                                                int H, const float *__restrict__ w, int E,
-                                                               int blocks_per_split, int nsp,
+                                                               int blocks_per_split,
                                                                float *__restrict__ partial) {
   const int lane = threadIdx.x;
   const int64_t t0 = (int64_t)blockIdx.x * 16 * NTT;
@@ -117,7 +117,7 @@ __global__ __launch_bounds__(kWave) void router_partial_kernel(const uint16_t *_
 #pragma unroll
       for (int ii = 0; ii < 4; ++ii) {
         const int64_t t = t0 + 16 * i + 4 * q + ii;
-        if (t < T) partial[(t * E + e) * nsp + split] = acc[i][j][ii];
+        if (t < T) partial[((int64_t)split * T + t) * E + e] = acc[i][j][ii];
       }
   }
 }
@@ -125,7 +125,7 @@ __global__ __launch_bounds__(kWave) void router_partial_kernel(const uint16_t *_
 // One wave per token: sum the split partials in order and add the bias, then the top k and
 // their softmax.
 __global__ __launch_bounds__(256) void router_topk_kernel(const float *__restrict__ partial, int nsplit,
-                                                          int nsp, const float *__restrict__ bias, int64_t T,
+                                                          const float *__restrict__ bias, int64_t T,
                                                           int E, int k, int32_t *__restrict__ topk_idx,
                                                           float *__restrict__ topk_w) {
   const int lane = threadIdx.x % kWave;
@@ -135,7 +135,7 @@ __global__ __launch_bounds__(256) void router_topk_kernel(const float *__restric
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     const int e = lane + i * kWave;
-    v[i] = (e < E) ? router_logit(partial, nsplit, nsp, bias, t, e, E) : 0.f;
+    v[i] = (e < E) ? router_logit(partial, nsplit, bias, t, e, T, E) : 0.f;
   }
   topk_softmax_wave(v, E, k, lane, topk_idx + t * k, topk_w + t * k);
 }
@@ -145,7 +145,7 @@ __global__ __launch_bounds__(256) void router_topk_kernel(const float *__restric
 static bool router_wide(int64_t T, int E) { return T >= 1024 && E >= 32; }
 
 // Split count for the router's input dimension: enough waves (about 2048, eight per SIMD) to
-// spread any batch over the chip, at most 4 * kMaxSplitVec, at least 2 MX blocks per split.
+// spread any batch over the chip, at most kMaxSplits, at least 2 MX blocks per split.
 int router_splits(int64_t T, int E, int H) {
   const int tt = router_wide(T, E) ? 64 : 16, et = router_wide(T, E) ? 32 : 16;
   const int64_t tiles = ((T + tt - 1) / tt) * ((E + et - 1) / et);
@@ -153,15 +153,14 @@ int router_splits(int64_t T, int E, int H) {
   if (tiles <= 0 || KB < 2) return 1;
   int64_t s = (2048 + tiles - 1) / tiles;
   if (s > KB / 2) s = KB / 2;
-  if (s > 4 * kMaxSplitVec) s = 4 * kMaxSplitVec;
+  if (s > kMaxSplits) s = kMaxSplits;
   if (s < 1) s = 1;
   const int bps = (KB + (int)s - 1) / (int)s;
   return (KB + bps - 1) / bps;
 }
 
 size_t router_partial_floats(int64_t T, int E, int H) {
-  const int nsp = (router_splits(T, E, H) + 3) / 4 * 4;
-  return (size_t)nsp * T * E;
+  return (size_t)router_splits(T, E, H) * T * E;
 }
 
 hipError_t launch_router_partial(const uint16_t *x, int64_t T, int H, const float *w, int E, float *partial,
@@ -169,13 +168,12 @@ hipError_t launch_router_partial(const uint16_t *x, int64_t T, int H, const floa
   const int KB = H / 32;
   const int ns = router_splits(T, E, H);
   const int bps = (KB + ns - 1) / ns;
-  const int nsp = (ns + 3) / 4 * 4;
   if (router_wide(T, E)) {
     dim3 grid((unsigned)((T + 63) / 64), (unsigned)((E + 31) / 32), (unsigned)ns);
-    hipLaunchKernelGGL((router_partial_kernel<4, 2>), grid, dim3(kWave), 0, stream, x, T, H, w, E, bps, nsp, partial);
+    hipLaunchKernelGGL((router_partial_kernel<4, 2>), grid, dim3(kWave), 0, stream, x, T, H, w, E, bps, partial);
   } else {
     dim3 grid((unsigned)((T + 15) / 16), (unsigned)((E + 15) / 16), (unsigned)ns);
-    hipLaunchKernelGGL((router_partial_kernel<1, 1>), grid, dim3(kWave), 0, stream, x, T, H, w, E, bps, nsp, partial);
+    hipLaunchKernelGGL((router_partial_kernel<1, 1>), grid, dim3(kWave), 0, stream, x, T, H, w, E, bps, partial);
   }
   return hipGetLastError();
 }
@@ -185,8 +183,8 @@ hipError_t launch_router(const uint16_t *x, int64_t T, int H, const float *w, co
   const hipError_t err = launch_router_partial(x, T, H, w, E, partial, stream);
   if (err != hipSuccess) return err;
   const int ns = router_splits(T, E, H);
-  hipLaunchKernelGGL(router_topk_kernel, dim3((unsigned)((T + 3) / 4)), dim3(256), 0, stream, partial, ns,
-                     (ns + 3) / 4 * 4, b, T, E, k, topk_idx, topk_w);
+  hipLaunchKernelGGL(router_topk_kernel, dim3((unsigned)((T + 3) / 4)), dim3(256), 0, stream, partial, ns, b, T,
+                     E, k, topk_idx, topk_w);
   return hipGetLastError();
 }
 

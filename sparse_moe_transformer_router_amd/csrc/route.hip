@@ -37,12 +37,14 @@ __device__ __forceinline__ void split3(const f32x4_t &a, const f32x4_t &b, bf16x
 
 // One wave: 16 NTT tokens x 16 NET experts over the MX-block range of split blockIdx.z
 // (NTT x NET 16x16 accumulators, so each weight element loaded and split serves 16 NTT tokens
-// and each x element 16 NET experts). Writes partial[(split * T + t) * E + e]: a wave's
-// stores for one split are runs of consecutive experts.
-template <int NTT, int NET>
+// and each x element 16 NET experts). Split-major (SM, many tokens): writes
+// partial[(split * T + t) * E + e], so a wave's stores are runs of consecutive experts. Else
+// token-major: partial[(t * E + e) * nsp + split] (nsp = split count rounded up to 4), so the
+// top-k kernel reads a logit's partials as a few 16-byte loads.
+template <int NTT, int NET, bool SM>
 __global__ __launch_bounds__(kWave) void router_partial_kernel(const uint16_t *__restrict__ x, int64_t T,
                                                                int H, const float *__restrict__ w, int E,
-                                                               int blocks_per_split,
+                                                               int blocks_per_split, int nsp,
                                                                float *__restrict__ partial) {
   const int lane = threadIdx.x;
   const int64_t t0 = (int64_t)blockIdx.x * 16 * NTT;
@@ -117,13 +119,19 @@ __global__ __launch_bounds__(kWave) void router_partial_kernel(const uint16_t *_
 #pragma unroll
       for (int ii = 0; ii < 4; ++ii) {
         const int64_t t = t0 + 16 * i + 4 * q + ii;
-        if (t < T) partial[((int64_t)split * T + t) * E + e] = acc[i][j][ii];
+        if (t < T) {
+          if constexpr (SM)
+            partial[((int64_t)split * T + t) * E + e] = acc[i][j][ii];
+          else
+            partial[(t * E + e) * nsp + split] = acc[i][j][ii];
+        }
       }
   }
 }
 
 // One wave per token: sum the split partials in order and add the bias, then the top k and
 // their softmax.
+template <bool SM>
 __global__ __launch_bounds__(256) void router_topk_kernel(const float *__restrict__ partial, int nsplit,
                                                           const float *__restrict__ bias, int64_t T,
                                                           int E, int k, int32_t *__restrict__ topk_idx,
@@ -135,7 +143,10 @@ __global__ __launch_bounds__(256) void router_topk_kernel(const float *__restric
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     const int e = lane + i * kWave;
-    v[i] = (e < E) ? router_logit(partial, nsplit, bias, t, e, T, E) : 0.f;
+    if constexpr (SM)
+      v[i] = (e < E) ? router_logit_sm(partial, nsplit, bias, t, e, T, E) : 0.f;
+    else
+      v[i] = (e < E) ? router_logit_tm(partial, nsplit, (nsplit + 3) / 4 * 4, bias, t, e, E) : 0.f;
   }
   topk_softmax_wave(v, E, k, lane, topk_idx + t * k, topk_w + t * k);
 }
@@ -160,7 +171,8 @@ int router_splits(int64_t T, int E, int H) {
 }
 
 size_t router_partial_floats(int64_t T, int E, int H) {
-  return (size_t)router_splits(T, E, H) * T * E;
+  const int ns = router_splits(T, E, H);
+  return (size_t)(router_wide(T, E) ? ns : (ns + 3) / 4 * 4) * T * E;
 }
 
 hipError_t launch_router_partial(const uint16_t *x, int64_t T, int H, const float *w, int E, float *partial,
@@ -170,10 +182,12 @@ hipError_t launch_router_partial(const uint16_t *x, int64_t T, int H, const floa
   const int bps = (KB + ns - 1) / ns;
   if (router_wide(T, E)) {
     dim3 grid((unsigned)((T + 63) / 64), (unsigned)((E + 31) / 32), (unsigned)ns);
-    hipLaunchKernelGGL((router_partial_kernel<4, 2>), grid, dim3(kWave), 0, stream, x, T, H, w, E, bps, partial);
+    hipLaunchKernelGGL((router_partial_kernel<4, 2, true>), grid, dim3(kWave), 0, stream, x, T, H, w, E, bps, ns,
+                       partial);
   } else {
     dim3 grid((unsigned)((T + 15) / 16), (unsigned)((E + 15) / 16), (unsigned)ns);
-    hipLaunchKernelGGL((router_partial_kernel<1, 1>), grid, dim3(kWave), 0, stream, x, T, H, w, E, bps, partial);
+    hipLaunchKernelGGL((router_partial_kernel<1, 1, false>), grid, dim3(kWave), 0, stream, x, T, H, w, E, bps,
+                       (ns + 3) / 4 * 4, partial);
   }
   return hipGetLastError();
 }
@@ -183,8 +197,12 @@ hipError_t launch_router(const uint16_t *x, int64_t T, int H, const float *w, co
   const hipError_t err = launch_router_partial(x, T, H, w, E, partial, stream);
   if (err != hipSuccess) return err;
   const int ns = router_splits(T, E, H);
-  hipLaunchKernelGGL(router_topk_kernel, dim3((unsigned)((T + 3) / 4)), dim3(256), 0, stream, partial, ns, b, T,
-                     E, k, topk_idx, topk_w);
+  if (router_wide(T, E))
+    hipLaunchKernelGGL(router_topk_kernel<true>, dim3((unsigned)((T + 3) / 4)), dim3(256), 0, stream, partial, ns, b,
+                       T, E, k, topk_idx, topk_w);
+  else
+    hipLaunchKernelGGL(router_topk_kernel<false>, dim3((unsigned)((T + 3) / 4)), dim3(256), 0, stream, partial, ns, b,
+                       T, E, k, topk_idx, topk_w);
   return hipGetLastError();
 }
 

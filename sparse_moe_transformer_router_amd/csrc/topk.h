@@ -11,10 +11,12 @@ namespace moe {
 
 constexpr int kMaxSplits = 48;  // split-K pieces of a router logit
 
-// Logit (t, e): its split partials partial[(s * T + t) * E + e], s = 0 .. nsplit - 1 (all
-// loads issued before the first add), added in split order, then the bias.
-__device__ __forceinline__ float router_logit(const float *__restrict__ partial, int nsplit,
-                                              const float *__restrict__ bias, int64_t t, int e, int64_t T, int E) {
+constexpr int kMaxSplitVec = kMaxSplits / 4;
+
+// Logit (t, e) from split-major partials partial[(s * T + t) * E + e], s = 0 .. nsplit - 1
+// (all loads issued before the first add), added in split order, then the bias.
+__device__ __forceinline__ float router_logit_sm(const float *__restrict__ partial, int nsplit,
+                                                 const float *__restrict__ bias, int64_t t, int e, int64_t T, int E) {
   const float *p = partial + t * E + e;
   const int64_t stride = T * E;
   float pv[kMaxSplits];
@@ -24,6 +26,24 @@ __device__ __forceinline__ float router_logit(const float *__restrict__ partial,
 #pragma unroll
   for (int c = 0; c < kMaxSplits; ++c)
     if (c < nsplit) s += pv[c];
+  if (bias) s += bias[e];
+  return s;
+}
+
+// The same from token-major partials partial[(t * E + e) * nsp + s] (contiguous, nsp a
+// multiple of 4, read as 16-byte loads).
+__device__ __forceinline__ float router_logit_tm(const float *__restrict__ partial, int nsplit, int nsp,
+                                                 const float *__restrict__ bias, int64_t t, int e, int E) {
+  const f32x4_t *p = reinterpret_cast<const f32x4_t *>(partial + (t * E + e) * nsp);
+  f32x4_t pv[kMaxSplitVec];
+#pragma unroll
+  for (int c = 0; c < kMaxSplitVec; ++c) pv[c] = (4 * c < nsplit) ? p[c] : f32x4_t{0.f, 0.f, 0.f, 0.f};
+  float s = 0.f;
+#pragma unroll
+  for (int c = 0; c < kMaxSplitVec; ++c)
+#pragma unroll
+    for (int u = 0; u < 4; ++u)
+      if (4 * c + u < nsplit) s += pv[c][u];
   if (bias) s += bias[e];
   return s;
 }

@@ -57,6 +57,8 @@ def test_route(name, T):
 
 
 @pytest.mark.parametrize("T,cases", [(37, [(8, 1), (8, 8), (16, 8), (256, 4), (5, 3), (130, 2)]),
+                                     (256, [(32, 4), (33, 4)]),   # 16x16 router tiles, E ragged
+                                     (257, [(32, 4)]),            # one token in the last 16-token tile
                                      (1100, [(40, 4), (130, 2), (256, 8)])])  # 64x32 router tiles, ragged
 def test_route_ties_and_k_range(T, cases):
     rng = np.random.default_rng(7 + T)

@@ -339,6 +339,49 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
           acc[g][b][4 * i + 3] = __uint_as_float(bq[g][i].y & 0xffff0000u);
         }
   };
+  // fp32 rows of the block-scaled path (the down projection) leave through LDS: a lane holds
+  // 16-byte pieces of 32 different slot rows, so storing them straight makes every store
+  // instruction touch 32 rows 32 bytes each. Staged per wave in the 8 KB of LDS that only its
+  // own DMAs write (its activation rows of ring slot fs, which the ring does not refill before
+  // this wave's next chunk), 32 slots x 64 rows per round (two 32-row tiles, XOR-swizzled
+  // 16-byte units), each store then writes 4 slots x 256 contiguous bytes.
+  auto epilogue_staged = [&](int fs) {
+    unsigned char *stg = lds + fs * kGStageBytes + wave * 32 * kGRowBytes;
+    float *outp = static_cast<float *>(out);
+    const int nb_live = tc.mcount > 64 ? 2 : 1;
+#pragma unroll
+    for (int b = 0; b < 2; ++b) {
+      if (b >= nb_live) break;
+#pragma unroll
+      for (int gp = 0; gp < (RGW + 1) / 2; ++gp) {
+#pragma unroll
+        for (int gg = 0; gg < 2; ++gg) {
+          const int g = 2 * gp + gg;
+          if (g >= RGW) break;
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const int u = 8 * gg + 2 * i + kh;
+            *reinterpret_cast<f32x4_t *>(stg + r32 * 256 + ((u ^ (r32 & 15)) << 4)) =
+                f32x4_t{acc[g][b][4 * i], acc[g][b][4 * i + 1], acc[g][b][4 * i + 2], acc[g][b][4 * i + 3]};
+          }
+        }
+        f32x4_t v[8];  // all reads before the first (conditional) store
+        const int u = lane % 16;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          const int sl = 4 * j + lane / 16;
+          v[j] = *reinterpret_cast<const f32x4_t *>(stg + sl * 256 + ((u ^ (sl & 15)) << 4));
+        }
+        const int n = tc.nt * kGRows + nloc0 + 64 * gp + 4 * u;
+        const bool n_ok = n < N && (u < 8 || 2 * gp + 1 < RGW);
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          const int col = 32 * (wx + 2 * b) + 4 * j + lane / 16;
+          if (n_ok && col < tc.mcount) *reinterpret_cast<f32x4_t *>(outp + (int64_t)(tc.row0 + col) * N + n) = v[j];
+        }
+      }
+    }
+  };
   auto epilogue = [&](int jc) {
     uint2 bq[RGW][4];
     if constexpr (!MX) bias_regs(jc, bq);
@@ -676,7 +719,10 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
     if constexpr (EPI == kEpiMxAct) {
       epilogue_mx(jc);
     } else {
-      epilogue(jc);
+      if constexpr (MX && EPI == kEpiLinearF32)
+        epilogue_staged((G + 2) % kGStages);  // the slot of the tile's last chunk, free until the next chunk's DMAs
+      else
+        epilogue(jc);
     }
     if constexpr (MX)
       init_acc(jc + 1);  // (past the last tile: a harmless read of a bias area)

@@ -292,6 +292,22 @@ def test_layer_decode20b(T, tiled):
     _check_layer(synth.make_inputs(cfg, T), tiled=tiled)
 
 
+@pytest.mark.parametrize("name,T", [("decode20b", 1), ("decode20b", 64), ("decode20b", 256),
+                                    ("decode120b_zipf", 64), ("tiny", 16)])
+def test_forward_matches_composed_steps(name, T):
+    """moe_forward_ex gives the same bits as the four steps called one by one through the C ABI
+    (route, permute, expert FFN, combine) with their own workspaces."""
+    cfg = synth.get_config(name)
+    dev = gu.device_layer(synth.make_inputs(cfg, T), tiled=True)
+    E = int(dev.router.weight.shape[0])
+    out_fw = gu.bf16_bits(moe.moe_forward_ex(dev.x, dev.router, dev.w1, dev.w2, dev.k, moe.Options()))
+    idx, w = moe.moe_route(dev.x, dev.router, dev.k)
+    off, ss, sr = moe.moe_permute(idx, E)
+    y = moe.moe_mxfp4_ffn(dev.x, dev.k, E, off, ss, dev.w1, dev.w2, moe.Options())
+    out = gu.bf16_bits(moe.moe_combine(y, sr, w))
+    assert np.array_equal(out_fw, out)
+
+
 @pytest.mark.parametrize("T", [1, 16, 64, 256])
 def test_layer_decode120b_zipf(T):
     cfg = synth.get_config("decode120b_zipf")

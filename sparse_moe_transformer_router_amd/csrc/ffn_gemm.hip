@@ -77,8 +77,9 @@ struct GShape {
   static constexpr int kStageBytes = kWOff + kWBytes + kGSBytes;
   static constexpr int kBiasOff = kGStages * kStageBytes;  // 3 tile-bias areas after the ring
   static constexpr int kDma = 8 + RGW + 2 + (MX ? 1 : 0);  // DMAs per wave per stage
-  static constexpr size_t kLds =
-      (size_t)kBiasOff + kGBiasAreas * kGBBytes + (kGMaxExperts + 4) * sizeof(int32_t);
+  // the expert offsets, then (block-scaled) each wave's 256-byte area for row-map entries
+  static constexpr int kMapOff = kBiasOff + kGBiasAreas * kGBBytes + (kGMaxExperts + 4) * 4;
+  static constexpr size_t kLds = (size_t)kMapOff + (MX ? 4 * 256 : 0);
 };
 
 __device__ __forceinline__ int g_off(int row, int col16) { return row * kGRowBytes + ((col16 ^ (row & 15)) << 4); }
@@ -86,6 +87,15 @@ __device__ __forceinline__ int g_off(int row, int col16) { return row * kGRowByt
 __device__ __forceinline__ constexpr int vmcnt_imm(int n) {
   // s_waitcnt immediate with vmcnt = n (split field) and expcnt / lgkmcnt left at their maxima
   return (n & 0xf) | ((n >> 4) << 14) | (0x7 << 4) | (0xf << 8);
+}
+
+// A 4-byte LDS read that waits for its own result inside the asm block (a plain read of a
+// DMA-written area makes the compiler wait for every DMA in flight). Early-clobber output.
+__device__ __forceinline__ int lds_read_b32_sync(const void *p) {
+  const uint32_t a = (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void *)p;
+  int v;
+  asm volatile("ds_read_b32 %0, %1\n\ts_waitcnt lgkmcnt(0)" : "=&v"(v) : "v"(a) : "memory");
+  return v;
 }
 
 // The epilogue's bias pieces in one LDS round trip: 16 dwords-pairs at 16-byte steps from p
@@ -152,6 +162,7 @@ __device__ GTile g_tile(int L, const int32_t *off, int E, int mt_total, int ntn,
 // for one wave per SIMD instead of saving registers for more.
 template <int EPI, int RGW, bool MX>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) void ffn_gemm_kernel(const void *__restrict__ a_src, const uint8_t *__restrict__ a_scales,
+                                                       const int32_t *__restrict__ a_rows, int a_div,
                                                        const int32_t *__restrict__ offsets, int E,
                                                        const uint8_t *__restrict__ pcodes,
                                                        const uint8_t *__restrict__ pscales,
@@ -217,11 +228,30 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
   int sstr;                       // 128, or 0
   int64_t boff;                   // the tile's bias run (from bias), or -1: no bias here
   const uint8_t *sptr = nullptr;  // MX: this lane's term-scale dword of slot (64 wave + lane) / 2, chunk 0
+  // Block-scaled path with a row map: the map entries of the wave's 32 rows of an issue-side
+  // tile come by LDS DMA (lane j: tile row 32 wave + j; lanes 32.. repeat them) into the
+  // wave's own area, issued at the top of the chunk before the tile starts, so the wait for
+  // the next stage covers them; at the switch the wave reads its area back.
+  const bool mapped = MX && a_rows != nullptr;
+  unsigned char *mapl = lds + SH::kMapOff + 256 * wave;
+  auto dma_map = [&](const GTile &t) {
+    const int rr = 32 * wave + (lane & 31);
+    __builtin_amdgcn_global_load_lds(a_rows + t.row0 + (rr < t.mcount ? rr : 0), mapl, 4, 0, 0);
+  };
   auto set_rows = [&]() {
+    // source row of each tile row: the row itself, or with the row map the two-term row
+    // a_rows[r] / a_div (e.g. a slot's token); lane j holds tile row 32 wave + j's source,
+    // and each lane takes its rows' entries with a cross-lane read
+    int srcv = 0;
+    if (mapped) {
+      srcv = lds_read_b32_sync(mapl + (lane & 31) * 4) / a_div;
+    } else {
+      srcv = ti.row0 + ((32 * wave + (lane & 31)) < ti.mcount ? 32 * wave + (lane & 31) : 0);
+    }
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
-      const int row = 32 * wave + 4 * i + lane / 16;
-      aptr[i] = static_cast<const uint8_t *>(a_src) + (int64_t)(ti.row0 + (row < ti.mcount ? row : 0)) * arow;
+      const int src = __builtin_amdgcn_ds_bpermute((4 * i + lane / 16) * 4, srcv);
+      aptr[i] = static_cast<const uint8_t *>(a_src) + (int64_t)src * arow;
     }
     const int gt0 = ti.nt * 2 * RGW;
     const int64_t ebase = (int64_t)ti.e * NG * nchunk;
@@ -243,25 +273,41 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
     }
     if constexpr (MX) {
       const int sl = (64 * wave + lane) >> 1;
-      sptr = a_scales + (int64_t)(ti.row0 + (sl < ti.mcount ? sl : 0)) * nchunk * kMxScBytes + (lane & 1) * 4;
+      const int src = __builtin_amdgcn_ds_bpermute((sl - 32 * wave) * 4, srcv);
+      sptr = a_scales + (int64_t)src * nchunk * kMxScBytes + (lane & 1) * 4;
     }
   };
 #pragma unroll
   for (int i = 0; i < 8; ++i) lcol[i] = ((lane % 16) ^ ((32 * wave + 4 * i + lane / 16) & 15)) * 16;
+  if (mapped) {
+    dma_map(ti);
+    __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));  // this wave's map entries are in its area
+  }
   set_rows();
   // Called before a stage is issued (the chunk counter ci was advanced after the previous
   // one): moves the issue side to its next tile when the chunks of this one are all issued.
   // It runs at the top of a chunk, so no branch follows the chunk's MFMAs (the compiler would
   // otherwise sink them past it, away from the loads they should hide).
+  GTile tnext = ti;
   auto advance_issue = [&]() {
-    if (ci < nchunk) return;
-    if (ji + 1 < ntiles) {
-      ++ji;
-      ci = 0;
-      ti = g_tile(first + ji * nq, off, E, mt_total, ntn, lane);
-      set_rows();
-    } else {
-      ci = nchunk - 1;  // past the end: keep re-loading the last chunk (into a free slot)
+    if (ci >= nchunk) {
+      if (ji + 1 < ntiles) {
+        ++ji;
+        ci = 0;
+        if (mapped)
+          ti = tnext;
+        else
+          ti = g_tile(first + ji * nq, off, E, mt_total, ntn, lane);
+        set_rows();
+      } else {
+        ci = nchunk - 1;  // past the end: keep re-loading the last chunk (into a free slot)
+      }
+    }
+    // the next tile's row map, a chunk ahead (its DMA is older than the chunk's own DMAs, so
+    // the chunk's wait for the next stage covers it)
+    if (mapped && ci == nchunk - 1 && ji + 1 < ntiles) {
+      tnext = g_tile(first + (ji + 1) * nq, off, E, mt_total, ntn, lane);
+      dma_map(tnext);
     }
   };
   auto dma = [&](int i, int slot) {
@@ -749,9 +795,10 @@ int gemm_grid_cap() {
 // loads: 624 vs 674 us for the 5760-row gate_up at 16,384 slots) unless that pads more than
 // a tenth of the 32-row tiles; then 192 if it pads less. The two-term activation output
 // always uses 256 rows (one 128-element record per n-tile).
-hipError_t launch_ffn_gemm(const void *a, const uint8_t *a_scales, bool mx, const int32_t *offsets, int E, int64_t S,
-                           const MxWeight &w, int epilogue, void *out, uint8_t *out_scales, float limit, float alpha,
-                           hipStream_t stream) {
+hipError_t launch_ffn_gemm(const void *a, const uint8_t *a_scales, const int32_t *a_rows, int a_div, bool mx,
+                           const int32_t *offsets, int E, int64_t S, const MxWeight &w, int epilogue, void *out,
+                           uint8_t *out_scales, float limit, float alpha, hipStream_t stream) {
+  if (a_rows != nullptr && (!mx || a_div < 1)) return hipErrorInvalidValue;
   if (E > kGMaxExperts) return hipErrorInvalidValue;
   if (epilogue == kEpiMxAct && !mx) return hipErrorInvalidValue;
   if (epilogue == kEpiSwigluBf16 && mx) return hipErrorInvalidValue;
@@ -767,7 +814,7 @@ hipError_t launch_ffn_gemm(const void *a, const uint8_t *a_scales, bool mx, cons
   dim3 grid((unsigned)(bound < cap ? bound : cap));
 #define MOE_LAUNCH_GEMM(EPI, RG, M)                                                                          \
   hipLaunchKernelGGL((ffn_gemm_kernel<EPI, RG, M>), grid, dim3(256), (GShape<RG, M>::kLds), stream, a, a_scales, \
-                     offsets, E, w.codes, w.scales, w.bias, w.N, w.K, ntn, out, out_scales, limit, alpha)
+                     a_rows, a_div, offsets, E, w.codes, w.scales, w.bias, w.N, w.K, ntn, out, out_scales, limit, alpha)
   if (mx) {
     if (tall) {
       switch (epilogue) {

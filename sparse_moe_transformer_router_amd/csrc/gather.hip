@@ -15,7 +15,7 @@ __global__ __launch_bounds__(256) void gather_rows_kernel(const uint16_t *__rest
   const int64_t r = (int64_t)blockIdx.x * 4 + threadIdx.x / kWave;
   if (r >= S) return;
   const int lane = threadIdx.x % kWave;
-  const int64_t t = sorted_slot[r] / k;
+  const int64_t t = sorted_slot != nullptr ? sorted_slot[r] / k : r;
   const u32x4_t *src = reinterpret_cast<const u32x4_t *>(x + t * H);
   u32x4_t *dst = reinterpret_cast<u32x4_t *>(xs + r * H);
   for (int c = lane; c < H / 8; c += kWave) dst[c] = src[c];
@@ -41,7 +41,7 @@ __global__ __launch_bounds__(256) void gather_rows_mx_kernel(const uint16_t *__r
   if (r >= S) return;  // wave-uniform
   const int lane = threadIdx.x % kWave;
   const int nrec = mx_records(H);
-  const int64_t t = sorted_slot[r] / k;
+  const int64_t t = sorted_slot != nullptr ? sorted_slot[r] / k : r;
   const uint16_t *src = x + t * H;
   uint8_t *drow = rec + r * nrec * kMxRecBytes;
   uint8_t *srow = scales + r * nrec * kMxScBytes;

@@ -53,19 +53,20 @@ hipError_t launch_ffn_stream(const uint16_t *a_src, bool a_by_token, const int32
 
 // One expert GEMM, persistent LDS-tiled grouped-GEMM family (tiled weights only): the
 // activations are expert-sorted rows (r = sorted row), either bf16 a[r * K] (mx false) or
-// two-term MXFP8 records with their scale array a_scales (mx true, layout in mx_act.h); output
-// rows are sorted rows. kEpiMxAct (mx only) writes records to out and their scales to
-// out_scales. E at most 256.
-hipError_t launch_ffn_gemm(const void *a, const uint8_t *a_scales, bool mx, const int32_t *offsets, int E, int64_t S,
-                           const MxWeight &w, int epilogue, void *out, uint8_t *out_scales, float limit, float alpha,
-                           hipStream_t stream);
+// two-term MXFP8 records with their scale array a_scales (mx true, layout in mx_act.h); with
+// a_rows (mx only), sorted row r reads record row a_rows[r] / a_div instead (a slot's token:
+// a_rows = sorted_slot, a_div = k). Output rows are sorted rows. kEpiMxAct (mx only) writes
+// records to out and their scales to out_scales. E at most 256.
+hipError_t launch_ffn_gemm(const void *a, const uint8_t *a_scales, const int32_t *a_rows, int a_div, bool mx,
+                           const int32_t *offsets, int E, int64_t S, const MxWeight &w, int epilogue, void *out,
+                           uint8_t *out_scales, float limit, float alpha, hipStream_t stream);
 
 // xs[r] = x[sorted_slot[r] / k] for every sorted row r (rows of H bf16).
 hipError_t launch_gather_rows(const uint16_t *x, const int32_t *sorted_slot, int k, int64_t S, int H,
                               uint16_t *xs, hipStream_t stream);
 
 // The same gather, written as two-term MXFP8 records (mx_act.h): rec [S][ceil(H/128)][256],
-// scales [S][ceil(H/128)][8].
+// scales [S][ceil(H/128)][8]. With sorted_slot null, row r is x's row r (records per token).
 hipError_t launch_gather_rows_mx(const uint16_t *x, const int32_t *sorted_slot, int k, int64_t S, int H,
                                  uint8_t *rec, uint8_t *scales, hipStream_t stream);
 

@@ -151,20 +151,22 @@ int run_ffn(const uint16_t *x, int64_t T, int k, int E, const int32_t *offsets, 
   const bool mxp = f == Family::kGemmMx;
   uint8_t *xs_sc = mxp ? static_cast<uint8_t *>(xs) + mx_scales_offset((size_t)S, H) : nullptr;
   uint8_t *act_sc = mxp ? static_cast<uint8_t *>(act) + mx_scales_offset((size_t)S, I) : nullptr;
-  const hipError_t g = mxp ? moe::launch_gather_rows_mx(x, sorted_slot, k, S, H, static_cast<uint8_t *>(xs), xs_sc,
-                                                        stream)
+  // block-scaled: x's T rows become two-term records once, and gate_up reads each sorted row's
+  // token record (a_rows = sorted_slot, a_div = k); bf16: an expert-sorted copy of x
+  const hipError_t g = mxp ? moe::launch_gather_rows_mx(x, nullptr, 1, T, H, static_cast<uint8_t *>(xs), xs_sc, stream)
                            : moe::launch_gather_rows(x, sorted_slot, k, S, H, static_cast<uint16_t *>(xs), stream);
   if (g != hipSuccess) return MOE_ERR_HIP;
+  const int32_t *rows = mxp ? sorted_slot : nullptr;
   if (first_epi >= 0)
-    return moe::launch_ffn_gemm(xs, xs_sc, mxp, offsets, E, S, w1, first_epi, y, nullptr, lim, alpha, stream) ==
-                   hipSuccess
+    return moe::launch_ffn_gemm(xs, xs_sc, rows, k, mxp, offsets, E, S, w1, first_epi, y, nullptr, lim, alpha,
+                                stream) == hipSuccess
                ? MOE_OK
                : MOE_ERR_HIP;
-  if (moe::launch_ffn_gemm(xs, xs_sc, mxp, offsets, E, S, w1, mxp ? moe::kEpiMxAct : moe::kEpiSwigluBf16, act,
-                           act_sc, lim, alpha, stream) != hipSuccess)
+  if (moe::launch_ffn_gemm(xs, xs_sc, rows, k, mxp, offsets, E, S, w1, mxp ? moe::kEpiMxAct : moe::kEpiSwigluBf16,
+                           act, act_sc, lim, alpha, stream) != hipSuccess)
     return MOE_ERR_HIP;
-  return moe::launch_ffn_gemm(act, act_sc, mxp, offsets, E, S, w2, moe::kEpiLinearF32, y, nullptr, lim, alpha,
-                              stream) == hipSuccess
+  return moe::launch_ffn_gemm(act, act_sc, nullptr, 1, mxp, offsets, E, S, w2, moe::kEpiLinearF32, y, nullptr, lim,
+                              alpha, stream) == hipSuccess
              ? MOE_OK
              : MOE_ERR_HIP;
 }

@@ -22,6 +22,7 @@
 // (a wave-wide scan over experts), so no tile list is materialised and the grid is sized
 // from host-known bounds only; surplus workgroups exit at once.
 #include <type_traits>
+#include <utility>
 
 #include "common.h"
 #include "kernels.h"
@@ -360,6 +361,20 @@ __global__ __launch_bounds__(kSWaves *kWave) void ffn_stream_tiled_kernel(
 // register loads stays exact only without it. All loads are issued unconditionally from
 // clamped in-bounds addresses (values past K or of absent slots are zeroed after the
 // load), so no control path skips a load and the compiler's waits stay tight.
+// Chunks c + J of a D-deep weight ring, fully unrolled: weight set J % D, activation register
+// set (J + 1) % 2 (D is even).
+template <int D, typename F, int... J>
+__device__ __forceinline__ void ring_unroll(F &&body, int c, std::integer_sequence<int, J...>) {
+  (body(c + J, std::integral_constant<int, J % D>{}, std::integral_constant<int, (J + 1) % 2>{}), ...);
+}
+template <int D, typename F, int... J>
+__device__ __forceinline__ void ring_tail(F &&body, int c, int nchunk, std::integer_sequence<int, J...>) {
+  ((c + J < nchunk ? (body(c + J, std::integral_constant<int, J % D>{}, std::integral_constant<int, (J + 1) % 2>{}),
+                      0)
+                   : 0),
+   ...);
+}
+
 constexpr int kRWaves = 4;
 constexpr int kRCols = 32;            // slots per m-tile
 constexpr int kRowSplitMinSlots = 16; // below this the K-split form keeps more waves busy
@@ -477,23 +492,11 @@ __global__ __launch_bounds__(kRWaves *kWave) void ffn_stream_rows_kernel(
     aload(c + 3, a);
     wload(c + D, u);
   };
-  using I0 = std::integral_constant<int, 0>;
-  using I1 = std::integral_constant<int, 1>;
-  using I2 = std::integral_constant<int, 2 % D>;
-  using I3 = std::integral_constant<int, 3 % D>;
+  // D chunks per iteration (weight set J % D, activation register set (J + 1) % 2), then the
+  // remainder peeled
   int c = 0;
-  for (; c + D <= nchunk; c += D) {
-    body(c, I0{}, I1{});
-    body(c + 1, I1{}, I0{});
-    if constexpr (D > 2) {
-      body(c + 2, I2{}, I1{});
-      body(c + 3, I3{}, I0{});
-    }
-  }
-  if (c < nchunk) body(c, I0{}, I1{});
-  if (c + 1 < nchunk) body(c + 1, I1{}, I0{});
-  if constexpr (D > 2)
-    if (c + 2 < nchunk) body(c + 2, I2{}, I1{});
+  for (; c + D <= nchunk; c += D) ring_unroll<D>(body, c, std::make_integer_sequence<int, D>{});
+  ring_tail<D>(body, c, nchunk, std::make_integer_sequence<int, D - 1>{});
 
   // epilogue: lane holds slot lane % 32 and rows 32 g + 8 i + 4 kh + jj of the output
   if (g >= NG || r32 >= mcount) return;

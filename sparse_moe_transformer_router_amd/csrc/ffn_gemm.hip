@@ -5,7 +5,9 @@
 // are multiplied by its MXFP4 weights (gpt-oss walkthrough at pnsm.cn, sections 1 and 4),
 // with the clamped SwiGLU (+1 on the linear branch) fused into the gate_up epilogue
 // (walkthrough section 2.2; review section 3.3). Weights must be in the tiled layout; the
-// activations are expert-sorted rows (x gathered by launch_gather_rows, or the act rows).
+// activations are expert-sorted rows (x gathered by launch_gather_rows, or the act rows), or
+// on the block-scaled path optionally rows picked through a row map (sorted row r reads
+// a_rows[r] / a_div: a slot's token record, so x is converted once per token).
 //
 // Output tile: 64 RGW weight rows x 128 slots of one expert, RGW = 4 (256 rows) or 3 (192,
 // which divides 5760 and 2880; chosen by the padding each leaves). Four waves in a 2 x 2
@@ -23,10 +25,11 @@
 //     columns are XOR-swizzled by the row index so a wave's 16-row reads hit distinct banks
 //     (applied on the global side: lane l of a DMA writes LDS column l % 16);
 //   * the 2 RGW 2 KB weight tiles, their 128-byte scale tiles and the tile's bias values.
-// Each wave issues exactly 10 + RGW DMAs per stage, two stages ahead, spread over the eight
-// MFMA k-steps of the chunk before; a stage is consumed after an explicit s_waitcnt vmcnt
-// of that count
-// and a bare s_barrier (a fence would drain the prefetches). Every DMA reads a clamped,
+// Each wave issues exactly 10 + RGW DMAs per stage (11 + RGW block-scaled), two stages
+// ahead, spread over the MFMAs of the chunk before; a stage is consumed after an explicit
+// s_waitcnt vmcnt of that count and a bare s_barrier (a fence would drain the prefetches).
+// With a row map, one more DMA a chunk before each tile brings the wave's 32 map entries;
+// it is older than the chunk's own DMAs, so the same waits cover it. Every DMA reads a clamped,
 // in-bounds address (past the end of the list the last chunk is re-loaded into the ring
 // slot nobody reads), so the count is exact. Rows past N read tile 0 and are never stored;
 // slots past an m-tile's count re-read its first slot and are never stored.
@@ -46,7 +49,8 @@
 // and the activation terms' scales to the other. Per 128-element chunk a wave issues
 // 2 (terms) x 2 (64-element halves) x RGW x 2 scaled MFMAs. The activation stage holds
 // 128 slot rows x (128 hi + 128 lo bytes), the same 32 KB as the bf16 rows, plus 1 KB of
-// term scales. The gate_up epilogue writes the activation in the same two-term form.
+// term scales. Its accumulators start from the bias; the gate_up epilogue writes the
+// activation in the same two-term form, the down epilogue stages its fp32 rows through LDS.
 #include <type_traits>
 
 #include "common.h"

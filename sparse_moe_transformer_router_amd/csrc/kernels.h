@@ -30,10 +30,11 @@ hipError_t launch_dequant(const uint8_t *codes, const uint8_t *scales, int64_t n
                           hipStream_t stream);
 
 // Router: split-K partial logits into `partial` (router_partial_floats() floats), then top-k.
+// launch_router_partial zeroes *counter too when it is given.
 size_t router_partial_floats(int64_t T, int E, int H);
 int router_splits(int64_t T, int E, int H);
 hipError_t launch_router_partial(const uint16_t *x, int64_t T, int H, const float *w, int E, float *partial,
-                                 hipStream_t stream);
+                                 hipStream_t stream, int *counter = nullptr);
 hipError_t launch_router(const uint16_t *x, int64_t T, int H, const float *w, const float *b, int E, int k,
                          float *partial, int32_t *topk_idx, float *topk_w, hipStream_t stream);
 
@@ -42,6 +43,14 @@ hipError_t launch_router(const uint16_t *x, int64_t T, int H, const float *w, co
 int64_t permute_scratch_ints(int64_t S, int E);
 hipError_t launch_permute(const int32_t *topk_idx, int64_t S, int E, int32_t *offsets,
                           int32_t *sorted_slot, int32_t *slot_row, int32_t *scratch, hipStream_t stream);
+
+// Decode-sized batches (topk_permute_fits): the top-k step of launch_router on the partials of
+// launch_router_partial (token-major; counter zeroed by that launch), and the permutation of
+// launch_permute, in one launch. Same outputs as the two separate steps.
+bool topk_permute_fits(int64_t T, int E, int k);
+hipError_t launch_router_topk_permute(const float *partial, int nsplit, const float *bias, int64_t T, int E, int k,
+                                      int32_t *topk_idx, float *topk_w, int *counter, int32_t *offsets,
+                                      int32_t *sorted_slot, int32_t *slot_row, hipStream_t stream);
 
 
 // One expert GEMM over all sorted rows, weight-streaming kernel family.

@@ -22,7 +22,7 @@ size_t align_up(size_t v) { return (v + kWsAlign - 1) / kWsAlign * kWsAlign; }
 
 // One workspace layout serves every entry point (each uses a subset of the regions).
 struct WsLayout {
-  size_t logits, topk_idx, topk_w, offsets, sorted_slot, slot_row, act, y, xs, pscratch, total;
+  size_t logits, topk_idx, topk_w, offsets, counter, sorted_slot, slot_row, act, y, xs, pscratch, total;
 };
 
 // Bytes of S activation rows of K elements: bf16, or the two-term records and their scales
@@ -42,6 +42,7 @@ bool ws_layout(int64_t T, int E, int k, int H, int I, WsLayout *L) {
   L->topk_idx = off;    off = align_up(off + S * sizeof(int32_t));
   L->topk_w = off;      off = align_up(off + S * sizeof(float));
   L->offsets = off;     off = align_up(off + (size_t)(E + 1) * sizeof(int32_t));
+  L->counter = off;     off = align_up(off + sizeof(int32_t));
   L->sorted_slot = off; off = align_up(off + S * sizeof(int32_t));
   L->slot_row = off;    off = align_up(off + S * sizeof(int32_t));
   L->act = off;         off = align_up(off + act_rows_bytes(S, I));
@@ -205,11 +206,19 @@ int forward_impl(const uint16_t *x, const moe_router_t *router, const moe_mxfp4_
   int32_t *slot_row = at<int32_t>(ws, L.slot_row);
   void *act = at<void>(ws, L.act);
   float *y = at<float>(ws, L.y);
-  if (moe::launch_router(x, T, H, router->weight, router->bias, E, k, logits, idx, wts, stream) != hipSuccess)
-    return MOE_ERR_HIP;
-  if (moe::launch_permute(idx, S, E, offsets, sorted_slot, slot_row, at<int32_t>(ws, L.pscratch), stream) !=
-      hipSuccess)
-    return MOE_ERR_HIP;
+  if (moe::topk_permute_fits(T, E, k)) {  // decode batches: top-k and permutation in one launch
+    int *counter = at<int>(ws, L.counter);
+    if (moe::launch_router_partial(x, T, H, router->weight, E, logits, stream, counter) != hipSuccess ||
+        moe::launch_router_topk_permute(logits, moe::router_splits(T, E, H), router->bias, T, E, k, idx, wts,
+                                        counter, offsets, sorted_slot, slot_row, stream) != hipSuccess)
+      return MOE_ERR_HIP;
+  } else {
+    if (moe::launch_router(x, T, H, router->weight, router->bias, E, k, logits, idx, wts, stream) != hipSuccess)
+      return MOE_ERR_HIP;
+    if (moe::launch_permute(idx, S, E, offsets, sorted_slot, slot_row, at<int32_t>(ws, L.pscratch), stream) !=
+        hipSuccess)
+      return MOE_ERR_HIP;
+  }
   int st = run_ffn(x, T, k, E, offsets, sorted_slot, *gu, *dn, o, y, act, at<void>(ws, L.xs), stream);
   if (st != MOE_OK) return st;
   if (moe::launch_combine(y, slot_row, wts, T, k, H, out, o.out_dtype == MOE_DTYPE_F32, stream) !=

@@ -9,6 +9,7 @@
 // Deterministic: positions depend only on slot order, never on atomics' timing.
 #include "common.h"
 #include "kernels.h"
+#include "topk.h"
 
 namespace moe {
 
@@ -17,16 +18,19 @@ constexpr int kPermThreads = kPermWaves * kWave;
 constexpr int kMaxExperts = 256;
 constexpr int64_t kPermSingleMax = 8192;  // up to this many slots one workgroup sorts them all
 
-// The single-workgroup sort; idx(s) yields slot s's expert id (from global memory or LDS).
-template <typename Idx>
+// The single-workgroup sort by NW waves (NW * 64 >= 256 threads); idx(s) yields slot s's
+// expert id.
+template <int NW, typename Idx>
 __device__ __forceinline__ void permute_block(Idx idx, int64_t S, int E, int32_t *__restrict__ offsets,
                                               int32_t *__restrict__ sorted_slot, int32_t *__restrict__ slot_row,
-                                              int (&hist)[kPermWaves][kMaxExperts], int (&scan)[kMaxExperts + 1]) {
+                                              int (&hist)[NW][kMaxExperts], int (&scan)[kMaxExperts + 1]) {
+  static_assert(NW * kWave >= kMaxExperts, "one thread per expert for the totals");
+  constexpr int kThreads = NW * kWave;
   const int tid = threadIdx.x, wave = tid / kWave, lane = tid % kWave;
-  for (int i = tid; i < kPermWaves * kMaxExperts; i += kPermThreads) (&hist[0][0])[i] = 0;
+  for (int i = tid; i < NW * kMaxExperts; i += kThreads) (&hist[0][0])[i] = 0;
   __syncthreads();
 
-  const int64_t per_wave = (((S + kPermWaves - 1) / kPermWaves) + kWave - 1) / kWave * kWave;
+  const int64_t per_wave = (((S + NW - 1) / NW) + kWave - 1) / kWave * kWave;
   const int64_t beg = (int64_t)wave * per_wave;
   const int64_t end = (beg + per_wave < S) ? beg + per_wave : S;
   // ids outside [0, E) are skipped (their slots get no position), never indexed
@@ -40,7 +44,7 @@ __device__ __forceinline__ void permute_block(Idx idx, int64_t S, int E, int32_t
   if (tid < kMaxExperts) {
     int tot = 0;
     if (tid < E)
-      for (int w = 0; w < kPermWaves; ++w) tot += hist[w][tid];
+      for (int w = 0; w < NW; ++w) tot += hist[w][tid];
     scan[tid + 1] = tot;
   }
   __syncthreads();
@@ -55,10 +59,10 @@ __device__ __forceinline__ void permute_block(Idx idx, int64_t S, int E, int32_t
     if (lane == 0) scan[0] = 0;
   }
   __syncthreads();
-  for (int e = tid; e <= E; e += kPermThreads) offsets[e] = scan[e];
+  for (int e = tid; e <= E; e += kThreads) offsets[e] = scan[e];
   if (tid < E) {
     int run = scan[tid];
-    for (int w = 0; w < kPermWaves; ++w) {
+    for (int w = 0; w < NW; ++w) {
       const int c = hist[w][tid];
       hist[w][tid] = run;
       run += c;
@@ -98,7 +102,7 @@ __global__ __launch_bounds__(kPermThreads) void permute_kernel(const int32_t *__
                                                                int32_t *__restrict__ slot_row) {
   __shared__ int hist[kPermWaves][kMaxExperts];
   __shared__ int scan[kMaxExperts + 1];
-  permute_block([&](int64_t s) { return topk_idx[s]; }, S, E, offsets, sorted_slot, slot_row, hist, scan);
+  permute_block<kPermWaves>([&](int64_t s) { return topk_idx[s]; }, S, E, offsets, sorted_slot, slot_row, hist, scan);
 }
 
 // Many slots: the same counting sort over several workgroups. Chunk c of kPermChunk
@@ -195,6 +199,56 @@ __global__ __launch_bounds__(kPermThreads) void permute_scatter_kernel(const int
     }
     __builtin_amdgcn_wave_barrier();
   }
+}
+
+// Decode-sized batches: the router's top-k step (one wave per token, as router_topk_kernel
+// on token-major partials) and, in the workgroup that finishes last, the permutation (the
+// counting sort above on 4 waves), in one launch. Every workgroup publishes its picks
+// (device-scope fence) before counting itself in; the last one to count in reads all picks
+// back at device scope. No workgroup waits for another. The counter is zeroed by
+// router_partial_kernel of the same call.
+constexpr int64_t kTopkPermMaxSlots = 2048;
+
+__global__ __launch_bounds__(256) void router_topk_permute_kernel(
+    const float *__restrict__ partial, int nsplit, const float *__restrict__ bias, int64_t T, int E, int k,
+    int32_t *__restrict__ topk_idx, float *__restrict__ topk_w, int *__restrict__ counter,
+    int32_t *__restrict__ offsets, int32_t *__restrict__ sorted_slot, int32_t *__restrict__ slot_row) {
+  __shared__ int hist[4][kMaxExperts];
+  __shared__ int scan[kMaxExperts + 1];
+  __shared__ int last;
+  const int lane = threadIdx.x % kWave;
+  const int64_t t = (int64_t)blockIdx.x * 4 + threadIdx.x / kWave;
+  if (t < T) {
+    float v[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int e = lane + i * kWave;
+      v[i] = (e < E) ? router_logit_tm(partial, nsplit, (nsplit + 3) / 4 * 4, bias, t, e, E) : 0.f;
+    }
+    topk_softmax_wave(v, E, k, lane, topk_idx + t * k, topk_w + t * k);
+  }
+  __threadfence();
+  __syncthreads();
+  if (threadIdx.x == 0) last = atomicAdd(counter, 1) == (int)gridDim.x - 1;
+  __syncthreads();
+  if (!last) return;
+  __threadfence();
+  permute_block<4>(
+      [&](int64_t s) { return __hip_atomic_load(topk_idx + s, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT); },
+      T * k, E, offsets, sorted_slot, slot_row, hist, scan);
+}
+
+bool topk_permute_fits(int64_t T, int E, int k) {
+  return T * k <= kTopkPermMaxSlots && T < 1024 && E <= kMaxExperts && k <= 8;
+}
+
+hipError_t launch_router_topk_permute(const float *partial, int nsplit, const float *bias, int64_t T, int E, int k,
+                                      int32_t *topk_idx, float *topk_w, int *counter, int32_t *offsets,
+                                      int32_t *sorted_slot, int32_t *slot_row, hipStream_t stream) {
+  if (T <= 0) return hipSuccess;
+  hipLaunchKernelGGL(router_topk_permute_kernel, dim3((unsigned)((T + 3) / 4)), dim3(256), 0, stream, partial, nsplit,
+                     bias, T, E, k, topk_idx, topk_w, counter, offsets, sorted_slot, slot_row);
+  return hipGetLastError();
 }
 
 int64_t permute_scratch_ints(int64_t S, int E) {

@@ -45,8 +45,10 @@ template <int NTT, int NET, bool SM>
 __global__ __launch_bounds__(kWave) void router_partial_kernel(const uint16_t *__restrict__ x, int64_t T,
                                                                int H, const float *__restrict__ w, int E,
                                                                int blocks_per_split, int nsp,
-                                                               float *__restrict__ partial) {
+                                                               float *__restrict__ partial,
+                                                               int *__restrict__ counter) {
   const int lane = threadIdx.x;
+  if (counter != nullptr && blockIdx.x == 0 && blockIdx.y == 0 && blockIdx.z == 0 && lane == 0) *counter = 0;
   const int64_t t0 = (int64_t)blockIdx.x * 16 * NTT;
   const int e0 = blockIdx.y * 16 * NET;
   const int split = blockIdx.z;
@@ -176,18 +178,18 @@ size_t router_partial_floats(int64_t T, int E, int H) {
 }
 
 hipError_t launch_router_partial(const uint16_t *x, int64_t T, int H, const float *w, int E, float *partial,
-                                 hipStream_t stream) {
+                                 hipStream_t stream, int *counter) {
   const int KB = H / 32;
   const int ns = router_splits(T, E, H);
   const int bps = (KB + ns - 1) / ns;
   if (router_wide(T, E)) {
     dim3 grid((unsigned)((T + 63) / 64), (unsigned)((E + 31) / 32), (unsigned)ns);
     hipLaunchKernelGGL((router_partial_kernel<4, 2, true>), grid, dim3(kWave), 0, stream, x, T, H, w, E, bps, ns,
-                       partial);
+                       partial, counter);
   } else {
     dim3 grid((unsigned)((T + 15) / 16), (unsigned)((E + 15) / 16), (unsigned)ns);
     hipLaunchKernelGGL((router_partial_kernel<1, 1, false>), grid, dim3(kWave), 0, stream, x, T, H, w, E, bps,
-                       (ns + 3) / 4 * 4, partial);
+                       (ns + 3) / 4 * 4, partial, counter);
   }
   return hipGetLastError();
 }

@@ -293,10 +293,13 @@ def test_layer_decode20b(T, tiled):
 
 
 @pytest.mark.parametrize("name,T", [("decode20b", 1), ("decode20b", 64), ("decode20b", 256),
+                                    ("decode20b", 512), ("decode20b", 513), ("decode20b", 1023),
                                     ("decode120b_zipf", 64), ("tiny", 16)])
 def test_forward_matches_composed_steps(name, T):
     """moe_forward_ex gives the same bits as the four steps called one by one through the C ABI
-    (route, permute, expert FFN, combine) with their own workspaces."""
+    (route, permute, expert FFN, combine) with their own workspaces. Up to 2048 slots the
+    layer picks and sorts in one launch (the last workgroup to finish the top-k sorts), above
+    that in two; 512 / 513 tokens sit on either side of that switch."""
     cfg = synth.get_config(name)
     dev = gu.device_layer(synth.make_inputs(cfg, T), tiled=True)
     E = int(dev.router.weight.shape[0])

@@ -9,7 +9,8 @@ What it computes, and where each step comes from:
   - [walkthrough] the gpt-oss architecture walkthrough at pnsm.cn/news/1975454
     (sections 1, 2.2 "MoE layer", 2.4 "comparison with GPT-2 / Qwen3", 4 "config.toml").
   - [review] the review of the from-scratch PyTorch gpt-oss-20B at
-    pomoai.com/hubs/HamzaElshafie/gpt-oss-20B (sections 3.3 "SwiGLU", 3.4 "MoE", 5).
+    pomoai.com/hubs/HamzaElshafie/gpt-oss-20B (sections 3.2 "RMSNorm", 3.3 "SwiGLU",
+    3.4 "MoE", 5).
   - [config] the config.json read-through at m.youleyou.com/wenzhang/3183859 (Part.01).
   - [OCP-MX] OCP Microscaling Formats (MX) Specification v1.0 -- the public definition of
     the MXFP4 element (E2M1) and scale (E8M0) encodings; the pages only name the format.
@@ -239,3 +240,64 @@ def moe_layer(x_bits: np.ndarray, router_w: np.ndarray, router_b: Optional[np.nd
         out += w[:, j:j + 1] * y_slots[:, j, :]
     return MoEResult(out, tok, logits, idx, w, h_slots, a_slots,
                      y_slots if keep_intermediates else None)
+
+
+def rms_norm(x: np.ndarray, scale: np.ndarray, eps: float = 0.0) -> np.ndarray:
+    """RMSNorm of each row [review §3.2; walkthrough §2.3]: the row divided by its root mean
+    square, times a per-feature scale, with no mean subtraction and no bias.
+
+    x float64 [..., H]; scale [H]. RMS(x) = sqrt(mean over the row of x^2 + eps): the pages
+    give RMS(x) with no epsilon; eps (0 = the pages' form) is the usual guard against an
+    all-zero row and is a caller's parameter.
+    """
+    x = np.asarray(x, np.float64)
+    ms = np.mean(x * x, axis=-1, keepdims=True)
+    return x / np.sqrt(ms + float(eps)) * np.asarray(scale, np.float64)
+
+
+def f64_to_bf16_bits(v: np.ndarray) -> np.ndarray:
+    """Round float64 values to bfloat16 (8 significant bits, fp32's exponent range), to
+    nearest with ties to even, in one rounding; returns the uint16 bit patterns.
+
+    The quantum of v is 2^(e-8) for v = m 2^e with m in [0.5, 1), and never below 2^-133,
+    the spacing of bf16 subnormals. Magnitudes that round to 2^128 or above become inf.
+    """
+    v = np.asarray(v, np.float64)
+    if not np.all(np.isfinite(v)):
+        raise ValueError("finite values only")
+    _, e = np.frexp(v)
+    q = np.ldexp(1.0, np.maximum(e - 8, -133))
+    r = np.rint(v / q) * q  # v / q is exact (a power-of-two scaling); rint ties to even
+    r = np.where(np.abs(r) >= 2.0 ** 128, np.copysign(np.inf, r), r)
+    return (r.astype(np.float32).view(np.uint32) >> 16).astype(np.uint16)
+
+
+@dataclasses.dataclass
+class BlockResult:
+    out: np.ndarray       # float64 [n_tok][H]: x + MoE(xn)
+    xn_bits: np.ndarray   # uint16 [n_tok][H]: the normalised rows as the layer's bf16 input
+    moe: MoEResult        # the layer on xn (its .tokens are rows of x)
+
+
+def moe_block(x_bits: np.ndarray, norm_scale: np.ndarray, norm_eps: float,
+              router_w: np.ndarray, router_b: Optional[np.ndarray],
+              get_expert: Callable[[int], ExpertTensors], k: int,
+              limit: float = 7.0, alpha: float = 1.0,
+              tokens: Optional[Sequence[int]] = None,
+              forced_idx: Optional[np.ndarray] = None) -> BlockResult:
+    """The MoE half of a decoder block around the layer: out = x + MoE(RMSNorm(x))
+    [walkthrough §2 and §2.3: each block normalises the stream before the MoE layer;
+    review §3.2 RMSNorm, §3.3: a residual path joins the FFN's output and its input].
+
+    Reading taken: the normalised row is the layer's bf16 input, so it is rounded to bf16
+    once (to nearest, ties to even) before the router and the experts see it; the residual
+    adds the un-normalised x to the layer's output.
+    """
+    x_bits = np.asarray(x_bits, np.uint16)
+    tok = np.arange(x_bits.shape[0]) if tokens is None else np.asarray(tokens, np.int64)
+    x = bf16_to_f64(x_bits[tok])
+    xn_bits = f64_to_bf16_bits(rms_norm(x, norm_scale, norm_eps))
+    res = moe_layer(xn_bits, router_w, router_b, get_expert, k, limit, alpha,
+                    forced_idx=forced_idx)
+    res.tokens = tok
+    return BlockResult(x + res.out, xn_bits, res)

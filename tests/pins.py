@@ -349,6 +349,87 @@ def pin_token_subset():
     assert np.array_equal(part.idx, full.idx[sub])
 
 
+# --------------------------------------------------------------------------- block wrap
+def pin_rms_norm_closed_forms():
+    """RMSNorm (review §3.2: the row over its root mean square, times a scale): closed forms.
+
+    A row of one repeated value c has RMS |c|, so it maps to sign(c) * scale; with eps the
+    RMS is sqrt(c^2 + eps) (1 and eps 3 give 2, so 0.5 * scale: eps inside the root, not
+    added after it). A row (3, 4) has mean square 12.5. Rows are normalised separately."""
+    scale = np.array([0.5, -2.0, 3.0, 1.25])
+    rows = np.array([[2.0] * 4, [-0.75] * 4, [1e-3] * 4])
+    out = om.rms_norm(rows, scale)
+    assert np.array_equal(out, np.sign(rows) * scale[None, :])
+    assert np.allclose(om.rms_norm(np.ones((1, 4)), scale, 3.0), 0.5 * scale, rtol=0, atol=1e-15)
+    assert np.allclose(om.rms_norm(np.full((1, 4), 2.0), scale, 12.0), 0.5 * scale, rtol=0, atol=1e-15)
+    two = om.rms_norm(np.array([[3.0, 4.0]]), np.ones(2))
+    assert abs(two[0, 0] - 3.0 / math.sqrt(12.5)) < 1e-15 and abs(two[0, 1] - 4.0 / math.sqrt(12.5)) < 1e-15
+
+
+def pin_rms_norm_invariants(seed=21):
+    """Unit scale and no eps: every output row has mean square 1; the map ignores a positive
+    factor on the row and commutes with a permutation of the features (scale permuted too)."""
+    rng = np.random.default_rng(seed)
+    x = rng.standard_normal((7, 96)) * rng.uniform(0.1, 10.0, (7, 1))
+    out = om.rms_norm(x, np.ones(96))
+    assert np.allclose(np.mean(out * out, axis=1), 1.0, rtol=1e-14)
+    scale = rng.standard_normal(96)
+    base = om.rms_norm(x, scale)
+    assert np.allclose(om.rms_norm(3.5 * x, scale), base, rtol=1e-13, atol=1e-15)
+    perm = rng.permutation(96)
+    assert np.allclose(om.rms_norm(x[:, perm], scale[perm]), base[:, perm], rtol=1e-13, atol=1e-15)
+
+
+def pin_bf16_rounding():
+    """One rounding to bf16, to nearest with ties to even: hand cases (a tie on each side of
+    an even mantissa, just past a tie, subnormals, overflow), then torch's float32 -> bfloat16
+    cast (round to nearest even) on random float32 values, which reach it without a prior
+    rounding."""
+    import torch
+    cases = {1.0: 0x3F80, 1.0 + 2.0 ** -8: 0x3F80, 1.0 + 3 * 2.0 ** -8: 0x3F82,
+             1.0 + 2.0 ** -8 + 2.0 ** -30: 0x3F81, -2.0: 0xC000, math.pi: 0x4049,
+             1.5 * 2.0 ** -133: 0x0002, 2.0 ** -134: 0x0000, 3 * 2.0 ** -135: 0x0001,
+             3.4e38: 0x7F80, -3.39e38: 0xFF7F, 3.38e38: 0x7F7E, 0.0: 0x0000}
+    got = om.f64_to_bf16_bits(np.array(list(cases.keys())))
+    assert [int(g) for g in got] == list(cases.values()), [hex(int(g)) for g in got]
+    rng = np.random.default_rng(22)
+    v = (rng.standard_normal(20000) * np.exp(rng.uniform(-80, 80, 20000))).astype(np.float32)
+    want = torch.from_numpy(v).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    assert np.array_equal(om.f64_to_bf16_bits(v.astype(np.float64)), want)
+
+
+def pin_block_reductions():
+    """The block out = x + MoE(bf16(RMSNorm(x))) in three special cases: experts with all-zero
+    weights and biases give out = x exactly (the residual is the un-normalised x); a zero
+    norm scale feeds every expert a zero row, so E = 1, k = 1 gives x + W2 swiglu(b1) + b2;
+    and the normalised input handed to the layer is the bf16 rounding of the norm."""
+    T, E, k, H, I = 6, 4, 2, 64, 32
+    x_bits, rw, rb, ws = _tiny_layer(23, T, E, k, H, I)
+    x = om.bf16_to_f64(x_bits)
+    rng = np.random.default_rng(24)
+    scale = rng.uniform(0.5, 2.0, H)
+    zeros = (np.zeros_like(ws[0]), np.full_like(ws[1], 127), None,
+             np.zeros_like(ws[3]), np.full_like(ws[4], 127), None)
+    blk = om.moe_block(x_bits, scale, 1e-5, rw, rb, om.experts_from_arrays(*zeros), k)
+    assert np.array_equal(blk.out, x)
+    ms = np.array([sum(float(v) ** 2 for v in row) / H for row in x])
+    for t in range(T):
+        for h in range(H):
+            ref = float(x[t, h]) / math.sqrt(ms[t] + 1e-5) * scale[h]
+            got = float(om.bf16_to_f64(blk.xn_bits[t:t + 1, h:h + 1])[0, 0])
+            # the bf16 neighbours of ref: the rounding must pick the nearer one
+            assert abs(got - ref) <= abs(ref) * 2.0 ** -8 * (1 + 1e-9), (t, h, got, ref)
+    x_bits1, rw1, rb1, ws1 = _tiny_layer(25, T, 1, 1, H, I)
+    blk1 = om.moe_block(x_bits1, np.zeros(H), 1e-5, rw1, rb1, om.experts_from_arrays(*ws1), 1)
+    b1 = om.bf16_to_f64(ws1[2][0])
+    g = np.clip(b1[0::2], -7, 7)
+    lin = np.clip(b1[1::2], -7, 7)
+    act = g / (1.0 + np.exp(-g)) * (lin + 1.0)
+    const = om.mxfp4_decode(ws1[3][0], ws1[4][0]) @ act + om.bf16_to_f64(ws1[5][0])
+    want = om.bf16_to_f64(x_bits1) + const[None, :]
+    assert np.allclose(blk1.out, want, rtol=1e-12, atol=1e-12 * np.abs(want).max())
+
+
 # --------------------------------------------------------------------------- shapes vs pages
 GIB = 2.0 ** 30
 
@@ -396,5 +477,6 @@ ALL_PINS = [
     pin_bits_per_weight, pin_router_bruteforce, pin_topk_bruteforce, pin_topk_ties, pin_softmax,
     pin_route_end_to_end, pin_permute_bruteforce, pin_swiglu_identities, pin_swiglu_interleave,
     pin_single_expert_reduction, pin_dense_masked_bruteforce, pin_token_subset,
-    pin_shapes_against_pages,
+    pin_shapes_against_pages, pin_rms_norm_closed_forms, pin_rms_norm_invariants,
+    pin_bf16_rounding, pin_block_reductions,
 ]

@@ -19,6 +19,9 @@ _orig_permute = om.permute
 _orig_route = om.route
 _orig_e2m1 = om.e2m1_value
 _orig_e8m0 = om.e8m0_value
+_orig_rms = om.rms_norm
+_orig_bf16 = om.f64_to_bf16_bits
+_orig_block = om.moe_block
 
 
 def _decode_nibbles_swapped(codes, scales):
@@ -132,6 +135,51 @@ def _route_weights_reversed(x_bits, w, b, k, forced_idx=None):
     return logits, idx, wt[..., ::-1].copy()
 
 
+def _rms_no_sqrt(x, scale, eps=0.0):
+    x = np.asarray(x, float)
+    return x / (np.mean(x * x, axis=-1, keepdims=True) + eps) * scale
+
+
+def _rms_sum_not_mean(x, scale, eps=0.0):
+    x = np.asarray(x, float)
+    return x / np.sqrt(np.sum(x * x, axis=-1, keepdims=True) + eps) * scale
+
+
+def _rms_eps_outside(x, scale, eps=0.0):
+    x = np.asarray(x, float)
+    return x / (np.sqrt(np.mean(x * x, axis=-1, keepdims=True)) + eps) * scale
+
+
+def _rms_over_tokens(x, scale, eps=0.0):
+    x = np.asarray(x, float)
+    return x / np.sqrt(np.mean(x * x, axis=0, keepdims=True) + eps) * scale
+
+
+def _bf16_via_f32(v):
+    return _orig_bf16(np.asarray(v, np.float64).astype(np.float32).astype(np.float64))
+
+
+def _bf16_truncate(v):
+    return (np.asarray(v, np.float64).astype(np.float32).view(np.uint32) >> 16).astype(np.uint16)
+
+
+def _block_residual_of_xn(x_bits, norm_scale, norm_eps, *a, **kw):
+    r = _orig_block(x_bits, norm_scale, norm_eps, *a, **kw)
+    tok = r.moe.tokens
+    r.out = r.out - om.bf16_to_f64(np.asarray(x_bits, np.uint16)[tok]) + om.bf16_to_f64(r.xn_bits)
+    return r
+
+
+def _block_no_residual(x_bits, norm_scale, norm_eps, *a, **kw):
+    r = _orig_block(x_bits, norm_scale, norm_eps, *a, **kw)
+    r.out = r.moe.out
+    return r
+
+
+def _block_norm_skipped(x_bits, norm_scale, norm_eps, *a, **kw):
+    return _orig_block(x_bits, np.ones(np.asarray(x_bits).shape[-1]), 0.0, *a, **kw)
+
+
 MUTATIONS = {
     "decode_nibbles_swapped": ("mxfp4_decode", _decode_nibbles_swapped),
     "decode_scale_per_16": ("mxfp4_decode", _decode_block16),
@@ -153,6 +201,16 @@ MUTATIONS = {
     "ffn_down_bias_dropped": ("expert_ffn", _ffn_no_b2),
     "permute_unstable": ("permute", _permute_unstable),
     "combine_weights_reversed": ("route", _route_weights_reversed),
+    "rmsnorm_no_sqrt": ("rms_norm", _rms_no_sqrt),
+    "rmsnorm_sum_not_mean": ("rms_norm", _rms_sum_not_mean),
+    "rmsnorm_eps_outside_root": ("rms_norm", _rms_eps_outside),
+    "rmsnorm_over_tokens": ("rms_norm", _rms_over_tokens),
+    "rmsnorm_scale_dropped": ("rms_norm", lambda x, scale, eps=0.0: _orig_rms(x, np.ones_like(scale), eps)),
+    "bf16_double_rounding": ("f64_to_bf16_bits", _bf16_via_f32),
+    "bf16_truncation": ("f64_to_bf16_bits", _bf16_truncate),
+    "block_residual_of_normed_x": ("moe_block", _block_residual_of_xn),
+    "block_no_residual": ("moe_block", _block_no_residual),
+    "block_norm_skipped": ("moe_block", _block_norm_skipped),
 }
 
 

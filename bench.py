@@ -8,6 +8,9 @@ resident in HBM. Steps rotate over L distinct copies of the layer's weights (24 
 20b-shaped layer, 36 for the 120b-shaped one, like the models' depth) so the 256 MB
 last-level cache cannot hold the weights between steps.
 
+With --block a step is the block around the layer instead: RMSNorm of the residual-stream
+rows, the layer on the normalised rows, and the residual add (moe_block_forward_ex).
+
 The roofline object covers the dominant step, the expert FFN (moe_mxfp4_ffn: the gate_up
 and down kernels), timed with HIP events on the stream it runs on. cpu_baseline times
 the fp64 oracle on a bounded sample of the same workload on the host cores.
@@ -31,6 +34,8 @@ HBM_PEAK_GBS = 8000.0
 BF16_PEAK_TFLOPS = 2500.0
 MXFP4_PEAK_TFLOPS = 10100.0
 
+NORM_EPS = 1e-5  # the block's RMSNorm epsilon
+
 EXPERT_BYTES_PER_ROW = lambda K: K // 2 + K // 32 + 2  # codes + scales + bf16 bias
 
 
@@ -46,6 +51,9 @@ def parse():
     p.add_argument("--path", type=int, default=0, help="0 auto, 1 stream, 2 gemm (bf16), 3 gemm (block-scaled)")
     p.add_argument("--layout", default="tiled", choices=["tiled", "rowmajor"],
                    help="weights prepacked once (untimed) into the kernel layout, or row-major")
+    p.add_argument("--block", action="store_true",
+                   help="time the block around the layer, x + layer(RMSNorm(x)) (moe_block_forward_ex), "
+                        "on residual-stream inputs with per-token scales")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--no-sweep", action="store_true")
     p.add_argument("--pmc-summary", nargs=4, metavar=("COPY_FETCH", "COPY_WRITE", "FETCH", "WRITE"),
@@ -180,20 +188,29 @@ def main():
     for _ in range(L - 1):  # device-side copies at distinct addresses
         layers.append((moe.Router(base_rt.weight.clone(), base_rt.bias.clone()), clone(base_w1), clone(base_w2)))
     x = bf16(inp.x)
+    if args.block:  # the block's input: the residual stream, normalised inside the timed step
+        x = bf16(synth.make_block_x(cfg, T))
+        inp.x = synth.make_block_x(cfg, T)
+        norm_scale_np = synth.make_norm_scale(cfg)
+        norm_scale = torch.from_numpy(norm_scale_np).to(dev)
     opts = moe.Options(path=args.path)
     ws = moe.workspace(T, E, k, H, I, args.path, device=dev)
     out = torch.empty((T, H), dtype=torch.bfloat16, device=dev)
     torch.cuda.synchronize()
     log(f"{L} layer copies resident ({L * (base_w1.codes.numel() + base_w1.scales.numel() + base_w2.codes.numel() + base_w2.scales.numel()) / 1e9:.1f} GB)")
 
-    # realised routing of this batch (same for every copy)
-    idx, _ = moe.moe_route(x, base_rt, k)
+    # realised routing of this batch (same for every copy); the block routes the normalised rows
+    x_layer = moe.moe_rmsnorm(x, norm_scale, NORM_EPS) if args.block else x
+    idx, _ = moe.moe_route(x_layer, base_rt, k)
     counts = np.bincount(idx.cpu().numpy().ravel(), minlength=E)
     touched = int((counts > 0).sum())
 
     def step(i):
         rt, w1, w2 = layers[i % L]
-        moe.moe_forward_ex(x, rt, w1, w2, k, opts, out=out, ws=ws)
+        if args.block:
+            moe.moe_block_forward_ex(x, norm_scale, NORM_EPS, rt, w1, w2, k, opts, out=out, ws=ws)
+        else:
+            moe.moe_forward_ex(x, rt, w1, w2, k, opts, out=out, ws=ws)
 
     def timed_steps(n, warm):
         for i in range(warm):
@@ -223,11 +240,11 @@ def main():
     for rep in range(2):  # first pass warms up
         for i in range(n_ffn):
             rt, w1, w2 = layers[i % L]
-            moe.moe_route(x, rt, k, topk_idx=ti, topk_w=tw, ws=ws)
+            moe.moe_route(x_layer, rt, k, topk_idx=ti, topk_w=tw, ws=ws)
             moe.moe_permute(ti, E, out=(offsets, sorted_slot, slot_row))
             if rep:
                 evs[i][0].record()
-            moe.moe_mxfp4_ffn(x, k, E, offsets, sorted_slot, w1, w2, opts, y=y, ws=ws)
+            moe.moe_mxfp4_ffn(x_layer, k, E, offsets, sorted_slot, w1, w2, opts, y=y, ws=ws)
             if rep:
                 evs[i][1].record()
             moe.moe_combine(y, slot_row, tw, out=out)
@@ -259,7 +276,7 @@ def main():
     log(f"ffn: {ffn_ms * 1e3:.1f} us, {roofline['achieved']} {roofline['unit']} ({roofline['frac']:.1%})")
 
     sweep = []
-    if not args.no_sweep and decode_like:
+    if not args.no_sweep and decode_like and not args.block:
         for Ts in cfg.T_list:
             if Ts == T:
                 continue
@@ -289,7 +306,7 @@ def main():
 
     cpu = None
     if not args.no_cpu_baseline:
-        cpu = cpu_baseline(cfg, inp, T, log)
+        cpu = cpu_baseline(cfg, inp, T, log, norm_scale_np if args.block else None)
 
     layer_bytes = touched * expert_bytes + E * H * 4 + E * 4 + T * H * 4 + T * k * 8
     line = {
@@ -313,14 +330,17 @@ def main():
         "roofline": roofline,
         "cpu_baseline": cpu,
     }
+    if args.block:
+        line["config"]["block"] = f"x + layer(RMSNorm(x)), eps {NORM_EPS:g}"
     if sweep:
         line["sweep"] = sweep
     print(json.dumps(line), flush=True)
 
 
-def cpu_baseline(cfg, inp, T, log, min_seconds=10.0, max_reps=16):
+def cpu_baseline(cfg, inp, T, log, norm_scale=None, min_seconds=10.0, max_reps=16):
     """The fp64 oracle as it stands, on a bounded token sample of the same batch, repeated
-    until about min_seconds of host work have been timed."""
+    until about min_seconds of host work have been timed (the block around the layer when
+    norm_scale is given)."""
     import oracle
     n = min(T, 64 if cfg.E <= 32 else 16)
     tokens = np.arange(n)
@@ -330,12 +350,15 @@ def cpu_baseline(cfg, inp, T, log, min_seconds=10.0, max_reps=16):
     reps, dt = 0, 0.0
     while reps < max_reps and (reps == 0 or dt < min_seconds):
         t0 = time.perf_counter()
-        oracle.moe_layer(inp.x, inp.router_w, inp.router_b, get, cfg.k, tokens=tokens)
+        if norm_scale is None:
+            oracle.moe_layer(inp.x, inp.router_w, inp.router_b, get, cfg.k, tokens=tokens)
+        else:
+            oracle.moe_block(inp.x, norm_scale, NORM_EPS, inp.router_w, inp.router_b, get, cfg.k, tokens=tokens)
         dt += time.perf_counter() - t0
         reps += 1
     log(f"oracle: {reps} x {n} tokens in {dt:.1f}s on {threads} threads")
     return {"value": round(reps * n / dt, 3), "unit": "tokens/s", "cores": threads, "kind": "oracle",
-            "sample": f"first {n} of the {T} tokens, {reps} repetitions, full layer in fp64 numpy (router, "
+            "sample": f"first {n} of the {T} tokens, {reps} repetitions, full {'block' if norm_scale is not None else 'layer'} in fp64 numpy (router, "
                       f"top-{cfg.k}, per-expert MXFP4 decode, FFN, combine); {dt:.1f} s"}
 
 

@@ -231,6 +231,36 @@ int moe_forward_ex(const uint16_t *x, const moe_router_t *router,
                    int64_t T, int32_t E, int32_t k, const moe_options_t *opts, void *out, void *ws,
                    size_t ws_bytes, moe_stream_t stream);
 
+/*
+ * RMSNorm of each row [review section 3.2: the row over its root mean square, times a
+ * per-feature scale; walkthrough section 2.3: RMSNorm without bias]:
+ *   out[t][h] = bf16( x[t][h] / sqrt(mean_h x[t][h]^2 + eps) * scale[h] )
+ * x bf16 [T][H]; scale fp32 [H]; out bf16 [T][H], rounded to nearest-even once. The mean of
+ * squares is an fp32 sum, the root and the divisions are correctly rounded fp32, and the
+ * products are (x * r) * scale, so an element can differ by one bf16 step from the exactly
+ * rounded value when the exact value lies within fp32 rounding of a rounding boundary.
+ * eps >= 0 and finite (else MOE_ERR_INVALID_ARG); eps = 0 is the pages' plain RMS, for which
+ * an all-zero row gives NaN. x, scale and out 16-byte aligned; H a multiple of 32.
+ */
+int moe_rmsnorm(const uint16_t *x, int64_t T, int32_t H, const float *scale, float eps, uint16_t *out,
+                moe_stream_t stream);
+
+/*
+ * The MoE half of a decoder block around the layer [walkthrough section 2: each block
+ * normalises its input before the MoE layer; review section 3.3: a residual path joins the
+ * FFN's output and its input]:
+ *   xn  = moe_rmsnorm(x, norm_scale, norm_eps)          (bf16, as above)
+ *   out = x + layer(xn)                                 (the layer of moe_forward_ex on xn)
+ * The residual x is added to the fp32 weighted sum of the experts' outputs, after it, and the
+ * result is rounded once (out bf16 or fp32 per opts->out_dtype). norm_scale fp32 [H], 16-byte
+ * aligned; norm_eps as for moe_rmsnorm. Workspace, options and limits as moe_forward_ex (the
+ * same moe_workspace_size covers the normalised copy of x).
+ */
+int moe_block_forward_ex(const uint16_t *x, const float *norm_scale, float norm_eps, const moe_router_t *router,
+                         const moe_mxfp4_weight_t *w_gate_up, const moe_mxfp4_weight_t *w_down, int64_t T,
+                         int32_t E, int32_t k, const moe_options_t *opts, void *out, void *ws, size_t ws_bytes,
+                         moe_stream_t stream);
+
 /* Free moe_forward's workspace on the current device (synchronises the device). */
 int moe_release_workspace(void);
 

@@ -19,4 +19,8 @@ from .moe_oracle import (  # noqa: F401
     experts_from_arrays,
     moe_layer,
     MoEResult,
+    rms_norm,
+    f64_to_bf16_bits,
+    moe_block,
+    BlockResult,
 )

@@ -284,19 +284,25 @@ def moe_block(x_bits: np.ndarray, norm_scale: np.ndarray, norm_eps: float,
               get_expert: Callable[[int], ExpertTensors], k: int,
               limit: float = 7.0, alpha: float = 1.0,
               tokens: Optional[Sequence[int]] = None,
-              forced_idx: Optional[np.ndarray] = None) -> BlockResult:
+              forced_idx: Optional[np.ndarray] = None,
+              forced_xn_bits: Optional[np.ndarray] = None) -> BlockResult:
     """The MoE half of a decoder block around the layer: out = x + MoE(RMSNorm(x))
     [walkthrough §2 and §2.3: each block normalises the stream before the MoE layer;
     review §3.2 RMSNorm, §3.3: a residual path joins the FFN's output and its input].
 
     Reading taken: the normalised row is the layer's bf16 input, so it is rounded to bf16
     once (to nearest, ties to even) before the router and the experts see it; the residual
-    adds the un-normalised x to the layer's output.
+    adds the un-normalised x to the layer's output. ``forced_xn_bits`` (rows of the selected
+    tokens) replaces that rounding: used to grade rows where an element lies so close to a
+    bf16 rounding boundary that a float32 evaluation of the norm rounds it the other way.
     """
     x_bits = np.asarray(x_bits, np.uint16)
     tok = np.arange(x_bits.shape[0]) if tokens is None else np.asarray(tokens, np.int64)
     x = bf16_to_f64(x_bits[tok])
-    xn_bits = f64_to_bf16_bits(rms_norm(x, norm_scale, norm_eps))
+    if forced_xn_bits is None:
+        xn_bits = f64_to_bf16_bits(rms_norm(x, norm_scale, norm_eps))
+    else:
+        xn_bits = np.asarray(forced_xn_bits, np.uint16)
     res = moe_layer(xn_bits, router_w, router_b, get_expert, k, limit, alpha,
                     forced_idx=forced_idx)
     res.tokens = tok

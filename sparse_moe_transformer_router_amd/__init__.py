@@ -23,6 +23,7 @@ from .ops import (  # noqa: F401
     Options,
     Router,
     abi_version,
+    moe_block_forward_ex,
     moe_combine,
     moe_forward,
     moe_forward_ex,
@@ -32,6 +33,7 @@ from .ops import (  # noqa: F401
     moe_mxfp4_tiled_bytes,
     moe_permute,
     moe_release_workspace,
+    moe_rmsnorm,
     moe_route,
     moe_workspace_size,
     workspace,

@@ -79,6 +79,11 @@ SIGNATURES = {
     "moe_forward_ex": (c_int32, [c_void_p, ctypes.POINTER(MoeRouter), ctypes.POINTER(MoeMxfp4Weight),
                                  ctypes.POINTER(MoeMxfp4Weight), c_int64, c_int32, c_int32,
                                  ctypes.POINTER(MoeOptions), c_void_p, c_void_p, c_size_t, c_void_p]),
+    "moe_rmsnorm": (c_int32, [c_void_p, c_int64, c_int32, c_void_p, ctypes.c_float, c_void_p, c_void_p]),
+    "moe_block_forward_ex": (c_int32, [c_void_p, c_void_p, ctypes.c_float, ctypes.POINTER(MoeRouter),
+                                       ctypes.POINTER(MoeMxfp4Weight), ctypes.POINTER(MoeMxfp4Weight),
+                                       c_int64, c_int32, c_int32, ctypes.POINTER(MoeOptions), c_void_p,
+                                       c_void_p, c_size_t, c_void_p]),
     "moe_release_workspace": (c_int32, []),
 }
 

@@ -33,6 +33,7 @@ SOURCES = [
     "gather.hip",
     "pack.hip",
     "combine.hip",
+    "norm.hip",
 ]
 
 ARCH = "gfx950"

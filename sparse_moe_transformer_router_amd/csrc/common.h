@@ -96,6 +96,14 @@ __device__ __forceinline__ float wave_max_f32(float v) {
   return __int_as_float(__builtin_amdgcn_readlane(x, 63));
 }
 
+// Sum over the wave's 64 lanes by butterfly exchanges, for every lane; the same pairing on
+// every lane, so the result is the same on all of them and from run to run.
+__device__ __forceinline__ float wave_sum_f32(float v) {
+#pragma unroll
+  for (int d = kWave / 2; d >= 1; d >>= 1) v += __shfl_xor(v, d, kWave);
+  return v;
+}
+
 __device__ __forceinline__ int wave_sum(int v) {
 #pragma unroll
   for (int d = kWave / 2; d >= 1; d >>= 1) v += __shfl_xor(v, d, kWave);

@@ -30,9 +30,9 @@ hipError_t launch_gather_rows(const uint16_t *x, const int32_t *sorted_slot, int
 }
 
 // Gather into the two-term MXFP8 form. One wave per sorted row; a lane takes 8 consecutive
-// elements (16 bytes of bf16), so a lane quad holds one 32-element block (its maximum by two
-// DPP quad swaps) and 16 lanes one 128-element record; a wave covers 4 records per pass.
-// Elements past H are zeros (the quad reads nothing there).
+// elements (16 bytes of bf16), so a lane quad holds one 32-element block and 16 lanes one
+// 128-element record (mx_store_piece); a wave covers 4 records per pass. Elements past H are
+// zeros (the quad reads nothing there).
 __global__ __launch_bounds__(256) void gather_rows_mx_kernel(const uint16_t *__restrict__ x,
                                                              const int32_t *__restrict__ sorted_slot, int k, int64_t S,
                                                              int H, uint8_t *__restrict__ rec,
@@ -56,25 +56,7 @@ __global__ __launch_bounds__(256) void gather_rows_mx_kernel(const uint16_t *__r
       f[2 * i] = __uint_as_float(v[i] << 16);
       f[2 * i + 1] = __uint_as_float(v[i] & 0xffff0000u);
     }
-    float m = 0.0f;
-#pragma unroll
-    for (int i = 0; i < 8; ++i) m = fmaxf(m, fabsf(f[i]));
-    int mi = __float_as_int(m);
-    mi = __float_as_int(fmaxf(__int_as_float(mi), __int_as_float(__builtin_amdgcn_update_dpp(mi, mi, 0xB1, 0xF, 0xF, false))));
-    mi = __float_as_int(fmaxf(__int_as_float(mi), __int_as_float(__builtin_amdgcn_update_dpp(mi, mi, 0x4E, 0xF, 0xF, false))));
-    const MxBlockScale s = mx_block_scale(__int_as_float(mi));
-    uint32_t h[4], l[4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) mx_split2(f[2 * i], f[2 * i + 1], s, h[i], l[i]);
-    if (c < nrec) {
-      uint8_t *d = drow + c * kMxRecBytes + 8 * j;
-      *reinterpret_cast<uint2 *>(d) = uint2{h[0] | (h[1] << 16), h[2] | (h[3] << 16)};
-      *reinterpret_cast<uint2 *>(d + 128) = uint2{l[0] | (l[1] << 16), l[2] | (l[3] << 16)};
-      if ((j & 3) == 0) {
-        srow[c * kMxScBytes + j / 4] = (uint8_t)s.sh;
-        srow[c * kMxScBytes + 4 + j / 4] = (uint8_t)s.sl;
-      }
-    }
+    mx_store_piece(f, c, j, nrec, drow, srow);
   }
 }
 

@@ -79,7 +79,15 @@ hipError_t launch_gather_rows(const uint16_t *x, const int32_t *sorted_slot, int
 hipError_t launch_gather_rows_mx(const uint16_t *x, const int32_t *sorted_slot, int k, int64_t S, int H,
                                  uint8_t *rec, uint8_t *scales, hipStream_t stream);
 
+// residual (bf16 [T][H], nullable) is added to the weighted sum before the rounding.
 hipError_t launch_combine(const float *y, const int32_t *slot_row, const float *topk_w, int64_t T,
-                          int k, int H, void *out, bool out_f32, hipStream_t stream);
+                          int k, int H, void *out, bool out_f32, hipStream_t stream,
+                          const uint16_t *residual = nullptr);
+
+// xn = bf16(x / sqrt(mean(x^2) + eps) * scale) per row of H; with rec non-null also the rows'
+// two-term MXFP8 records and scales (as launch_gather_rows_mx with sorted_slot null, of xn).
+// scale: fp32 [H], 16-byte aligned.
+hipError_t launch_rmsnorm(const uint16_t *x, int64_t T, int H, const float *scale, float eps, uint16_t *xn,
+                          uint8_t *rec, uint8_t *rec_scales, hipStream_t stream);
 
 }  // namespace moe

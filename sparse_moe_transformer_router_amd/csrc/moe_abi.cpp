@@ -2,6 +2,7 @@
 // HIP call), workspace layout, kernel-family choice, and launches on the caller's stream.
 #include <hip/hip_runtime.h>
 
+#include <cmath>
 #include <mutex>
 #include <new>
 #include <unordered_map>
@@ -22,7 +23,7 @@ size_t align_up(size_t v) { return (v + kWsAlign - 1) / kWsAlign * kWsAlign; }
 
 // One workspace layout serves every entry point (each uses a subset of the regions).
 struct WsLayout {
-  size_t logits, topk_idx, topk_w, offsets, counter, sorted_slot, slot_row, act, y, xs, pscratch, total;
+  size_t logits, topk_idx, topk_w, offsets, counter, sorted_slot, slot_row, act, y, xs, xn, pscratch, total;
 };
 
 // Bytes of S activation rows of K elements: bf16, or the two-term records and their scales
@@ -48,6 +49,7 @@ bool ws_layout(int64_t T, int E, int k, int H, int I, WsLayout *L) {
   L->act = off;         off = align_up(off + act_rows_bytes(S, I));
   L->y = off;           off = align_up(off + S * (size_t)H * sizeof(float));
   L->xs = off;          off = align_up(off + act_rows_bytes(S, H));  // sorted x (GEMM paths)
+  L->xn = off;          off = align_up(off + (size_t)T * (size_t)H * sizeof(uint16_t));  // normalised x (block)
   L->pscratch = off;    off = align_up(off + (size_t)moe::permute_scratch_ints((int64_t)S, E) * sizeof(int32_t));
   L->total = off;
   return true;
@@ -128,9 +130,11 @@ Family family(const moe_options_t &o, const moe_mxfp4_weight_t &gu, const moe_mx
 // families read their gate_up activations from an expert-sorted copy of x in the xs region
 // (S x H bf16, or two-term records); the act region holds the activation between the
 // projections (bf16 or two-term records).
+// x_records_ready: the block-scaled family's per-token records of x are already in xs (the
+// block's normalisation writes them), so the gather is skipped.
 int run_ffn(const uint16_t *x, int64_t T, int k, int E, const int32_t *offsets, const int32_t *sorted_slot,
             const moe_mxfp4_weight_t &gu, const moe_mxfp4_weight_t &dn, const moe_options_t &o, float *y,
-            void *act, void *xs, hipStream_t stream) {
+            void *act, void *xs, hipStream_t stream, bool x_records_ready = false) {
   const int64_t S = T * k;
   const int H = gu.k, I = dn.k;
   const moe::MxWeight w1 = mx(gu);
@@ -154,8 +158,10 @@ int run_ffn(const uint16_t *x, int64_t T, int k, int E, const int32_t *offsets, 
   uint8_t *act_sc = mxp ? static_cast<uint8_t *>(act) + mx_scales_offset((size_t)S, I) : nullptr;
   // block-scaled: x's T rows become two-term records once, and gate_up reads each sorted row's
   // token record (a_rows = sorted_slot, a_div = k); bf16: an expert-sorted copy of x
-  const hipError_t g = mxp ? moe::launch_gather_rows_mx(x, nullptr, 1, T, H, static_cast<uint8_t *>(xs), xs_sc, stream)
-                           : moe::launch_gather_rows(x, sorted_slot, k, S, H, static_cast<uint16_t *>(xs), stream);
+  const hipError_t g =
+      mxp ? (x_records_ready ? hipSuccess
+                             : moe::launch_gather_rows_mx(x, nullptr, 1, T, H, static_cast<uint8_t *>(xs), xs_sc, stream))
+          : moe::launch_gather_rows(x, sorted_slot, k, S, H, static_cast<uint16_t *>(xs), stream);
   if (g != hipSuccess) return MOE_ERR_HIP;
   const int32_t *rows = mxp ? sorted_slot : nullptr;
   if (first_epi >= 0)
@@ -189,15 +195,32 @@ int check_layer(const uint16_t *x, const moe_router_t *router, const moe_mxfp4_w
   return MOE_OK;
 }
 
+// The layer; with norm_scale non-null, the block around it: the layer runs on
+// xn = bf16(RMSNorm(x)) and x is added to its output.
 int forward_impl(const uint16_t *x, const moe_router_t *router, const moe_mxfp4_weight_t *gu,
                  const moe_mxfp4_weight_t *dn, int64_t T, int E, int k, const moe_options_t &o, void *out,
-                 void *ws, size_t ws_bytes, hipStream_t stream) {
+                 void *ws, size_t ws_bytes, hipStream_t stream, const float *norm_scale = nullptr,
+                 float norm_eps = 0.0f) {
   const int H = gu->k, I = dn->k;
   WsLayout L;
   ws_layout(T, E, k, H, I, &L);
   if (ws == nullptr || ws_bytes < L.total) return MOE_ERR_WORKSPACE;
   if (!aligned(ws, kWsAlign)) return MOE_ERR_INVALID_ARG;
   const int64_t S = T * k;
+  const uint16_t *residual = nullptr;
+  bool records_ready = false;
+  if (norm_scale != nullptr) {
+    // the block-scaled family reads x as per-token records: the normalisation writes them
+    const bool mxp = family(o, *gu, *dn, S, E) == Family::kGemmMx;
+    uint8_t *xs = at<uint8_t>(ws, L.xs);
+    uint16_t *xn = at<uint16_t>(ws, L.xn);
+    if (moe::launch_rmsnorm(x, T, H, norm_scale, norm_eps, xn, mxp ? xs : nullptr,
+                            mxp ? xs + mx_scales_offset((size_t)S, H) : nullptr, stream) != hipSuccess)
+      return MOE_ERR_HIP;
+    residual = x;
+    x = xn;
+    records_ready = mxp;
+  }
   float *logits = at<float>(ws, L.logits);
   int32_t *idx = at<int32_t>(ws, L.topk_idx);
   float *wts = at<float>(ws, L.topk_w);
@@ -219,9 +242,9 @@ int forward_impl(const uint16_t *x, const moe_router_t *router, const moe_mxfp4_
         hipSuccess)
       return MOE_ERR_HIP;
   }
-  int st = run_ffn(x, T, k, E, offsets, sorted_slot, *gu, *dn, o, y, act, at<void>(ws, L.xs), stream);
+  int st = run_ffn(x, T, k, E, offsets, sorted_slot, *gu, *dn, o, y, act, at<void>(ws, L.xs), stream, records_ready);
   if (st != MOE_OK) return st;
-  if (moe::launch_combine(y, slot_row, wts, T, k, H, out, o.out_dtype == MOE_DTYPE_F32, stream) !=
+  if (moe::launch_combine(y, slot_row, wts, T, k, H, out, o.out_dtype == MOE_DTYPE_F32, stream, residual) !=
       hipSuccess)
     return MOE_ERR_HIP;
   return MOE_OK;
@@ -417,6 +440,40 @@ int moe_forward_ex(const uint16_t *x, const moe_router_t *router,
   if ((st = check_path(o, *w_gate_up, *w_down)) != MOE_OK) return st;
   if (T == 0) return MOE_OK;
   return forward_impl(x, router, w_gate_up, w_down, T, E, k, o, out, ws, ws_bytes, (hipStream_t)stream);
+  MOE_GUARD_END
+}
+
+int moe_rmsnorm(const uint16_t *x, int64_t T, int32_t H, const float *scale, float eps, uint16_t *out,
+                moe_stream_t stream) {
+  MOE_GUARD_BEGIN
+  if (T < 0 || !(eps >= 0.0f) || !std::isfinite(eps)) return MOE_ERR_INVALID_ARG;
+  int st = check_dim(H);
+  if (st != MOE_OK) return st;
+  if (T == 0) return MOE_OK;
+  if (x == nullptr || scale == nullptr || out == nullptr) return MOE_ERR_INVALID_ARG;
+  if (!aligned(x, 16) || !aligned(scale, 16) || !aligned(out, 16)) return MOE_ERR_INVALID_ARG;
+  return moe::launch_rmsnorm(x, T, H, scale, eps, out, nullptr, nullptr, (hipStream_t)stream) == hipSuccess
+             ? MOE_OK
+             : MOE_ERR_HIP;
+  MOE_GUARD_END
+}
+
+int moe_block_forward_ex(const uint16_t *x, const float *norm_scale, float norm_eps, const moe_router_t *router,
+                         const moe_mxfp4_weight_t *w_gate_up, const moe_mxfp4_weight_t *w_down, int64_t T,
+                         int32_t E, int32_t k, const moe_options_t *opts, void *out, void *ws, size_t ws_bytes,
+                         moe_stream_t stream) {
+  MOE_GUARD_BEGIN
+  int st = check_layer(x, router, w_gate_up, w_down, T, E, k, out);
+  if (st != MOE_OK) return st;
+  const moe_options_t o = opts ? *opts : default_options();
+  if ((st = check_options(o)) != MOE_OK) return st;
+  if (o.flags != 0) return MOE_ERR_INVALID_ARG;
+  if ((st = check_path(o, *w_gate_up, *w_down)) != MOE_OK) return st;
+  if (!(norm_eps >= 0.0f) || !std::isfinite(norm_eps)) return MOE_ERR_INVALID_ARG;
+  if (T == 0) return MOE_OK;
+  if (norm_scale == nullptr || !aligned(norm_scale, 16)) return MOE_ERR_INVALID_ARG;
+  return forward_impl(x, router, w_gate_up, w_down, T, E, k, o, out, ws, ws_bytes, (hipStream_t)stream,
+                      norm_scale, norm_eps);
   MOE_GUARD_END
 }
 

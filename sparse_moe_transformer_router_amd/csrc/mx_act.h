@@ -58,4 +58,30 @@ __device__ __forceinline__ void mx_split2(float v0, float v1, const MxBlockScale
   lo = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(r0, r1, 0, false) & 0xffffu;
 }
 
+// One lane's share of a row's records: elements 8j..8j+7 of record c (lane j = 0..15 of a
+// 16-lane group; a lane quad is one 32-element block). Every lane of the quad must call it
+// (the block maximum moves between them by two DPP quad swaps); c >= nrec stores nothing.
+__device__ __forceinline__ void mx_store_piece(const float (&f)[8], int c, int j, int nrec, uint8_t *__restrict__ drow,
+                                               uint8_t *__restrict__ srow) {
+  float m = 0.0f;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) m = fmaxf(m, fabsf(f[i]));
+  int mi = __float_as_int(m);
+  mi = __float_as_int(fmaxf(__int_as_float(mi), __int_as_float(__builtin_amdgcn_update_dpp(mi, mi, 0xB1, 0xF, 0xF, false))));
+  mi = __float_as_int(fmaxf(__int_as_float(mi), __int_as_float(__builtin_amdgcn_update_dpp(mi, mi, 0x4E, 0xF, 0xF, false))));
+  const MxBlockScale s = mx_block_scale(__int_as_float(mi));
+  uint32_t h[4], l[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) mx_split2(f[2 * i], f[2 * i + 1], s, h[i], l[i]);
+  if (c < nrec) {
+    uint8_t *d = drow + c * kMxRecBytes + 8 * j;
+    *reinterpret_cast<uint2 *>(d) = uint2{h[0] | (h[1] << 16), h[2] | (h[3] << 16)};
+    *reinterpret_cast<uint2 *>(d + 128) = uint2{l[0] | (l[1] << 16), l[2] | (l[3] << 16)};
+    if ((j & 3) == 0) {
+      srow[c * kMxScBytes + j / 4] = (uint8_t)s.sh;
+      srow[c * kMxScBytes + 4 + j / 4] = (uint8_t)s.sl;
+    }
+  }
+}
+
 }  // namespace moe

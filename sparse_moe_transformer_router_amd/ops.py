@@ -216,5 +216,35 @@ def moe_forward_ex(x: torch.Tensor, router: Router, w_gate_up: MXFP4Weight, w_do
     return out
 
 
+def moe_rmsnorm(x: torch.Tensor, scale: torch.Tensor, eps: float = 1e-5, out: Optional[torch.Tensor] = None,
+                stream=None) -> torch.Tensor:
+    """bf16(x / sqrt(mean(x^2) + eps) * scale) per row; x bf16 [T][H], scale fp32 [H]."""
+    T, H = x.shape
+    if out is None:
+        out = torch.empty((T, H), dtype=torch.bfloat16, device=x.device)
+    L.check("moe_rmsnorm", L.lib().moe_rmsnorm(_ptr(x), T, H, _ptr(scale), float(eps), _ptr(out),
+                                                  _stream(stream)))
+    return out
+
+
+def moe_block_forward_ex(x: torch.Tensor, norm_scale: torch.Tensor, norm_eps: float, router: Router,
+                         w_gate_up: MXFP4Weight, w_down: MXFP4Weight, k: int, opts: Optional[Options] = None,
+                         out: Optional[torch.Tensor] = None, ws=None, stream=None) -> torch.Tensor:
+    """x + layer(bf16(RMSNorm(x))): the MoE half of a decoder block."""
+    T, H = x.shape
+    E = int(router.weight.shape[0])
+    o = opts or Options()
+    if out is None:
+        dt = torch.bfloat16 if o.out_dtype == L.MOE_DTYPE_BF16 else torch.float32
+        out = torch.empty((T, H), dtype=dt, device=x.device)
+    if ws is None:
+        ws = workspace(T, E, k, H, w_down.k, o.path, device=x.device)
+    r, g, d, od = router.desc(), w_gate_up.desc(), w_down.desc(), o.desc()
+    L.check("moe_block_forward_ex", L.lib().moe_block_forward_ex(
+        _ptr(x), _ptr(norm_scale), float(norm_eps), ctypes.byref(r), ctypes.byref(g), ctypes.byref(d), T, E, k,
+        ctypes.byref(od), _ptr(out), _ptr(ws), ws.numel(), _stream(stream)))
+    return out
+
+
 def moe_release_workspace() -> None:
     L.check("moe_release_workspace", L.lib().moe_release_workspace())

@@ -11,7 +11,9 @@ from .generators import (  # noqa: F401
     ExpertWeights,
     bf16_bits_from_f32,
     f32_from_bf16_bits,
+    make_block_x,
     make_inputs,
+    make_norm_scale,
     make_x,
     make_expert,
     make_router,

@@ -8,6 +8,9 @@ Distributions (the workloads of the gpt-oss pages, stood in for by random data b
 trained weights and real hidden states are not available):
 
 * x: bf16(N(0, 1)) per element, a stand-in for RMS-normalised hidden states.
+* block input (the residual stream before the block's RMSNorm): bf16(N(0, 1) * 2^u) with
+  one u ~ U(-2, 2) per token, so tokens differ in scale by up to 16x and the normalisation
+  matters; RMSNorm scale: fp32 U(0.5, 1.5) per feature.
 * router weight: fp32 N(0, 0.02^2); router bias: zero, or a stored calibration vector.
 * expert weights: MXFP4 -- every 4-bit code uniform over all 16 codes (so every packed
   byte is uniform over 0..255), one E8M0 scale byte per 32 consecutive input features,
@@ -40,6 +43,9 @@ _TID_W1_BIAS = 12
 _TID_W2_CODES = 20
 _TID_W2_SCALES = 21
 _TID_W2_BIAS = 22
+_TID_BLOCK_X = 30
+_TID_BLOCK_TOKEN_SCALE = 31
+_TID_NORM_SCALE = 32
 
 
 def _rng(*key: int) -> np.random.Generator:
@@ -152,6 +158,18 @@ def make_x(cfg: LayerConfig, T: int, offset: int = 0) -> np.ndarray:
     """bf16 bits [T][H] ~ N(0,1). ``offset`` selects an independent stream (calibration batches)."""
     g = _rng(cfg.seed, _TID_X, T, offset)
     return bf16_bits_from_f32(g.standard_normal((T, cfg.H), dtype=np.float32))
+
+
+def make_block_x(cfg: LayerConfig, T: int) -> np.ndarray:
+    """bf16 bits [T][H]: the block's input, N(0,1) per element times 2^u per token, u ~ U(-2, 2)."""
+    z = _rng(cfg.seed, _TID_BLOCK_X, T).standard_normal((T, cfg.H), dtype=np.float32)
+    u = _rng(cfg.seed, _TID_BLOCK_TOKEN_SCALE, T).uniform(-2.0, 2.0, size=(T, 1))
+    return bf16_bits_from_f32(z * np.exp2(u).astype(np.float32))
+
+
+def make_norm_scale(cfg: LayerConfig) -> np.ndarray:
+    """fp32 [H]: the RMSNorm's per-feature scale, U(0.5, 1.5)."""
+    return _rng(cfg.seed, _TID_NORM_SCALE).uniform(0.5, 1.5, size=cfg.H).astype(np.float32)
 
 
 def make_router(cfg: LayerConfig, bias: Optional[np.ndarray] = None) -> Tuple[np.ndarray, np.ndarray]:

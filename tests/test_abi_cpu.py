@@ -125,6 +125,34 @@ def test_ffn_and_forward_errors():
                               ctypes.byref(flagged), FAKE, FAKE, big, None) == L.MOE_ERR_INVALID_ARG
 
 
+def test_rmsnorm_and_block_errors():
+    """Argument checks of moe_rmsnorm and moe_block_forward_ex (before any HIP call)."""
+    lib = L.lib()
+    H, I, E, k = 64, 96, 8, 4
+    g, d = _weight(2 * I, H), _weight(H, I)
+    r = _router()
+    o = L.MoeOptions(7.0, 1.0, 0, 0, 0)
+    big = 1 << 40
+    assert lib.moe_rmsnorm(FAKE, 4, 64, FAKE, -1.0, FAKE, None) == L.MOE_ERR_INVALID_ARG
+    assert lib.moe_rmsnorm(FAKE, 4, 64, FAKE, float("nan"), FAKE, None) == L.MOE_ERR_INVALID_ARG
+    assert lib.moe_rmsnorm(FAKE, 4, 64, FAKE, float("inf"), FAKE, None) == L.MOE_ERR_INVALID_ARG
+    assert lib.moe_rmsnorm(FAKE, -1, 64, FAKE, 1e-5, FAKE, None) == L.MOE_ERR_INVALID_ARG
+    assert lib.moe_rmsnorm(FAKE, 4, 48, FAKE, 1e-5, FAKE, None) == L.MOE_ERR_UNSUPPORTED
+    assert lib.moe_rmsnorm(FAKE, 4, 64, None, 1e-5, FAKE, None) == L.MOE_ERR_INVALID_ARG
+    assert lib.moe_rmsnorm(FAKE, 4, 64, FAKE + 4, 1e-5, FAKE, None) == L.MOE_ERR_INVALID_ARG
+    assert lib.moe_rmsnorm(None, 0, 64, None, 1e-5, None, None) == L.MOE_OK
+    blk = lambda scale, eps, T=4, ws=FAKE, wsb=big: lib.moe_block_forward_ex(
+        FAKE, scale, eps, ctypes.byref(r), ctypes.byref(g), ctypes.byref(d), T, E, k, ctypes.byref(o), FAKE,
+        ws, wsb, None)
+    assert blk(None, 1e-5) == L.MOE_ERR_INVALID_ARG
+    assert blk(FAKE + 8, 1e-5) == L.MOE_ERR_INVALID_ARG
+    assert blk(FAKE, -1.0) == L.MOE_ERR_INVALID_ARG
+    assert blk(FAKE, 1e-5, wsb=64) == L.MOE_ERR_WORKSPACE
+    assert blk(None, 1e-5, T=0) == L.MOE_OK
+    # the block's workspace holds the normalised copy of x: the size grows by T * H * 2
+    assert lib.moe_workspace_size(1000, E, k, H, I, 0) - lib.moe_workspace_size(999, E, k, H, I, 0) >= 2 * H
+
+
 def test_tiled_bytes_and_pack_errors():
     lib = L.lib()
     cb, sb = ctypes.c_size_t(0), ctypes.c_size_t(0)

@@ -340,7 +340,8 @@ def _small_cfg(E, k, H=128, I=96, T=24, seed=31, scales=(119, 123)):
 @pytest.mark.parametrize("tiled,path", [(False, 0), (True, 0), (True, 2), (True, 3)])
 @pytest.mark.parametrize("E,k,H,I,T", [(4, 4, 128, 96, 9), (16, 1, 64, 64, 33), (16, 8, 96, 160, 21),
                                        (256, 4, 64, 32, 40), (8, 2, 32, 32, 1), (2, 1, 160, 96, 70),
-                                       (4, 2, 288, 160, 300), (8, 4, 256, 128, 100)])
+                                       (4, 2, 288, 160, 300), (8, 4, 256, 128, 100), (256, 8, 64, 64, 50),
+                                       (32, 8, 2880, 2880, 40)])
 def test_layer_shapes(E, k, H, I, T, tiled, path):
     _check_layer(synth.make_inputs(_small_cfg(E, k, H, I, T)), tiled=tiled, path=path)
 

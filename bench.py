@@ -71,15 +71,20 @@ CALIBRATION_MIB = 1024
 FFN_KERNELS = ("ffn_", "gather_rows")  # kernels one moe_mxfp4_ffn call launches, once each
 
 
+# the sources of what one moe_mxfp4_ffn call runs: its kernels, their headers and the host
+# code that picks and launches them
+FFN_SOURCES = ("ffn_stream.hip", "ffn_gemm.hip", "gather.hip", "common.h", "mx_act.h", "kernels.h",
+               "moe_abi.cpp")
+
+
 def kernel_source_hash():
-    """Hash of the library's kernel sources: a stored traffic figure is valid for these only."""
+    """Hash of the expert-FFN sources: a stored traffic figure is valid for these only."""
     import hashlib
     csrc = os.path.join(ROOT, "sparse_moe_transformer_router_amd", "csrc")
     h = hashlib.sha256()
-    for name in sorted(os.listdir(csrc)):
-        if name.endswith((".hip", ".h", ".cpp")):
-            with open(os.path.join(csrc, name), "rb") as f:
-                h.update(name.encode() + b"\0" + f.read())
+    for name in FFN_SOURCES:
+        with open(os.path.join(csrc, name), "rb") as f:
+            h.update(name.encode() + b"\0" + f.read())
     return h.hexdigest()[:16]
 
 

@@ -49,8 +49,11 @@ def _check_norm_bits(gpu_bits, x_bits, scale, eps=EPS):
     return int(diff.sum())
 
 
+WIDE = synth.LayerConfig("wide", (20,), 4608, 64, 4, 2, 41, scale_bytes=(119, 123))  # rows past 4096
+
+
 def _block_layer(name, T, tiled=True):
-    cfg = synth.get_config(name)
+    cfg = WIDE if name == "wide" else synth.get_config(name)
     inp = synth.make_inputs(cfg, T)
     inp.x = synth.make_block_x(cfg, T)
     scale = synth.make_norm_scale(cfg)
@@ -68,7 +71,7 @@ def test_rmsnorm_matches_oracle(name, T):
     _check_norm_bits(gu.bf16_bits(out), x, scale)
 
 
-@pytest.mark.parametrize("H", [32, 160, 2880])
+@pytest.mark.parametrize("H", [32, 160, 2880, 4096, 8192])
 def test_rmsnorm_edge_rows(H):
     """Rows of one repeated value, a zero row with eps > 0 (zeros out), large and small
     magnitudes (2^+-40: the fp32 sum of squares stays finite and normal), and eps = 0 (the
@@ -94,7 +97,8 @@ def _gpu_block(dev, scale_d, out_dtype, path=0):
 
 @pytest.mark.parametrize("name,T,path", [("tiny", 16, 0), ("tiny", 16, 1), ("tiny", 16, 2), ("tiny", 16, 3),
                                          ("decode20b", 64, 0), ("decode20b", 1024, 2), ("decode20b", 1024, 3),
-                                         ("decode20b", 3, 3), ("prefill20b", 4096, 0)])
+                                         ("decode20b", 3, 3), ("prefill20b", 4096, 0), ("wide", 20, 0),
+                                         ("wide", 20, 3)])
 def test_block_equals_layer_on_normalised_rows(name, T, path):
     """Kernel against kernel: the block's fp32 output is the layer's fp32 output on
     moe_rmsnorm's rows plus x, bit for bit (so the records the normalisation writes for the
@@ -153,6 +157,10 @@ def test_block_tiny(tiled, path):
 @pytest.mark.parametrize("T", [1, 64])
 def test_block_decode20b(T):
     _check_block("decode20b", T)
+
+
+def test_block_wide_rows():
+    _check_block("wide", 20, 3)
 
 
 def test_block_decode120b_zipf():

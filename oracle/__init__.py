@@ -23,4 +23,5 @@ from .moe_oracle import (  # noqa: F401
     f64_to_bf16_bits,
     moe_block,
     BlockResult,
+    attention_decode,
 )

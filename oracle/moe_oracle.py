@@ -10,8 +10,10 @@ What it computes, and where each step comes from:
     (sections 1, 2.2 "MoE layer", 2.4 "comparison with GPT-2 / Qwen3", 4 "config.toml").
   - [review] the review of the from-scratch PyTorch gpt-oss-20B at
     pomoai.com/hubs/HamzaElshafie/gpt-oss-20B (sections 3.2 "RMSNorm", 3.3 "SwiGLU",
-    3.4 "MoE", 5).
+    3.4 "MoE", 3.5 "GQA + sliding window + attention sinks", 5).
   - [config] the config.json read-through at m.youleyou.com/wenzhang/3183859 (Part.01).
+  - [retrospective] the gpt-oss launch retrospective at youniszhang.com ("工程影响": KV
+    heads, head dimension and cache bytes).
   - [OCP-MX] OCP Microscaling Formats (MX) Specification v1.0 -- the public definition of
     the MXFP4 element (E2M1) and scale (E8M0) encodings; the pages only name the format.
 * Every floating-point step runs in float64 on exact inputs (bf16 and fp32 inputs widen
@@ -307,3 +309,50 @@ def moe_block(x_bits: np.ndarray, norm_scale: np.ndarray, norm_eps: float,
                     forced_idx=forced_idx)
     res.tokens = tok
     return BlockResult(x + res.out, xn_bits, res)
+
+
+# --------------------------------------------------------------------------- decode attention
+def attention_decode(q: np.ndarray, k_cache: np.ndarray, v_cache: np.ndarray, lens: np.ndarray,
+                     sinks: Optional[np.ndarray], window: int = 0) -> np.ndarray:
+    """One decode step of grouped-query attention with per-head sink logits
+    [walkthrough §2.1: 64 query heads share 8 key/value heads; layers alternate between a
+    128-token banded window and dense attention; each head learns a logit that joins the
+    softmax's denominator, so a head can attend to nothing; review §3.5 the same three;
+    retrospective "工程影响": 8 KV heads of dimension 64 with a 2-byte cache].
+
+    q       [B][Hq][D]     the new token's queries (positional rotation already applied)
+    k_cache [B][Hkv][L][D] keys of positions 0..L-1; v_cache the same for values
+    lens    [B]            sequence b's tokens in the cache (the new one is position lens[b]-1)
+    sinks   [Hq] or None   the per-head sink logit (None: no sink)
+    window  0 for dense attention, else the band: the query at position i sees keys
+            i-window+1 .. i (the last `window` tokens, itself included)
+
+    Readings taken: query head h reads key/value head h // (Hq / Hkv) (consecutive query heads
+    share one); the score is q.k / sqrt(D); the sink is one more logit in the softmax whose
+    value vector is zero, so the weights of the real keys sum to less than one.
+    Returns float64 [B][Hq][D].
+    """
+    q = np.asarray(q, np.float64)
+    kc = np.asarray(k_cache, np.float64)
+    vc = np.asarray(v_cache, np.float64)
+    B, Hq, D = q.shape
+    Hkv = kc.shape[1]
+    group = Hq // Hkv
+    out = np.zeros((B, Hq, D), np.float64)
+    for b in range(B):
+        n = int(lens[b])
+        lo = 0 if window <= 0 else max(0, n - window)
+        for h in range(Hq):
+            g = h // group
+            keys = kc[b, g, lo:n]      # [n - lo][D]
+            vals = vc[b, g, lo:n]
+            s = keys @ q[b, h] / np.sqrt(D)
+            if sinks is not None:
+                s_all = np.concatenate([s, [float(sinks[h])]])
+            else:
+                s_all = s
+            m = s_all.max()
+            e = np.exp(s_all - m)
+            w = e[:n - lo] / e.sum()
+            out[b, h] = w @ vals
+    return out

@@ -430,6 +430,83 @@ def pin_block_reductions():
     assert np.allclose(blk1.out, want, rtol=1e-12, atol=1e-12 * np.abs(want).max())
 
 
+# --------------------------------------------------------------------------- decode attention
+def _attn_case(seed, B=3, Hq=16, Hkv=2, D=64, L=40):
+    rng = np.random.default_rng(seed)
+    q = rng.standard_normal((B, Hq, D))
+    k = rng.standard_normal((B, Hkv, L, D))
+    v = rng.standard_normal((B, Hkv, L, D))
+    lens = rng.integers(1, L + 1, B)
+    lens[0] = L
+    return q, k, v, lens
+
+
+def _sdpa(q, k, v, lens, window, sink_keys=None):
+    """torch's scaled_dot_product_attention (float64, CPU) with the key/value heads repeated
+    for their query-head groups and an explicit boolean mask of the visible positions; with
+    sink_keys ([B][Hq][D]), one extra key per query head whose value is zero."""
+    import torch
+    import torch.nn.functional as F
+    B, Hq, D = q.shape
+    Hkv, L = k.shape[1], k.shape[2]
+    kk = torch.from_numpy(k).repeat_interleave(Hq // Hkv, dim=1)  # [B][Hq][L][D]
+    vv = torch.from_numpy(v).repeat_interleave(Hq // Hkv, dim=1)
+    qq = torch.from_numpy(q)[:, :, None, :]                       # [B][Hq][1][D]
+    pos = torch.arange(L)
+    out = np.zeros((B, Hq, D))
+    for b in range(B):
+        n = int(lens[b])
+        lo = 0 if window <= 0 else max(0, n - window)
+        mask = ((pos >= lo) & (pos < n))[None, None, :].expand(1, Hq, L)
+        kb, vb = kk[b:b + 1], vv[b:b + 1]
+        if sink_keys is not None:
+            kb = torch.cat([kb, torch.from_numpy(sink_keys[b])[None, :, None, :]], dim=2)
+            vb = torch.cat([vb, torch.zeros(1, Hq, 1, D, dtype=vb.dtype)], dim=2)
+            mask = torch.cat([mask, torch.ones(1, Hq, 1, dtype=torch.bool)], dim=2)
+        o = F.scaled_dot_product_attention(qq[b:b + 1], kb, vb, attn_mask=mask[:, :, None, :])
+        out[b] = o[0, :, 0, :].numpy()
+    return out
+
+
+def pin_attention_library_reductions(seed=41):
+    """Without sinks the decode step is torch's scaled_dot_product_attention over the visible
+    positions (dense, and windows of 1, 7 and 128); with sinks it is the same attention with
+    one more key per head whose score is the sink logit and whose value is zero."""
+    q, k, v, lens = _attn_case(seed)
+    for window in (0, 1, 7, 128):
+        got = om.attention_decode(q, k, v, lens, None, window)
+        assert np.allclose(got, _sdpa(q, k, v, lens, window), rtol=1e-12, atol=1e-12), window
+    rng = np.random.default_rng(seed + 1)
+    sinks = rng.standard_normal(q.shape[1]) * 2.0
+    D = q.shape[2]
+    # a key k_s with q.k_s / sqrt(D) = sink: k_s = sink * sqrt(D) * q / |q|^2
+    ks = sinks[None, :, None] * math.sqrt(D) * q / np.sum(q * q, axis=2, keepdims=True)
+    for window in (0, 5):
+        got = om.attention_decode(q, k, v, lens, sinks, window)
+        assert np.allclose(got, _sdpa(q, k, v, lens, window, ks), rtol=1e-11, atol=1e-11), window
+
+
+def pin_attention_closed_forms():
+    """One visible key whose score equals the sink: half the value; a sink far below: the value
+    itself; n equal keys of score s with sink c: the value times n e^s / (n e^s + e^c)."""
+    D = 64
+    q = np.zeros((1, 1, D))
+    q[0, 0, 0] = 8.0                      # score = 8 * key[0] / 8 = key[0]
+    k = np.zeros((1, 1, 5, D))
+    k[0, 0, :, 0] = 1.5                   # every score 1.5
+    v = np.tile(np.linspace(-1, 1, D), (1, 1, 5, 1))
+    out = om.attention_decode(q, k, v, np.array([1]), np.array([1.5]), 0)
+    assert np.allclose(out[0, 0], 0.5 * v[0, 0, 0], rtol=0, atol=1e-15)
+    out = om.attention_decode(q, k, v, np.array([1]), np.array([-1e4]), 0)
+    assert np.allclose(out[0, 0], v[0, 0, 0], rtol=0, atol=1e-15)
+    out = om.attention_decode(q, k, v, np.array([5]), np.array([0.25]), 0)
+    want = v[0, 0, 0] * 5 * math.exp(1.5) / (5 * math.exp(1.5) + math.exp(0.25))
+    assert np.allclose(out[0, 0], want, rtol=1e-14, atol=1e-15)
+    out = om.attention_decode(q, k, v, np.array([5]), np.array([0.25]), 2)  # only 2 keys in view
+    want = v[0, 0, 0] * 2 * math.exp(1.5) / (2 * math.exp(1.5) + math.exp(0.25))
+    assert np.allclose(out[0, 0], want, rtol=1e-14, atol=1e-15)
+
+
 # --------------------------------------------------------------------------- shapes vs pages
 GIB = 2.0 ** 30
 
@@ -478,5 +555,6 @@ ALL_PINS = [
     pin_route_end_to_end, pin_permute_bruteforce, pin_swiglu_identities, pin_swiglu_interleave,
     pin_single_expert_reduction, pin_dense_masked_bruteforce, pin_token_subset,
     pin_shapes_against_pages, pin_rms_norm_closed_forms, pin_rms_norm_invariants,
-    pin_bf16_rounding, pin_block_reductions,
+    pin_bf16_rounding, pin_block_reductions, pin_attention_library_reductions,
+    pin_attention_closed_forms,
 ]

@@ -22,6 +22,7 @@ _orig_e8m0 = om.e8m0_value
 _orig_rms = om.rms_norm
 _orig_bf16 = om.f64_to_bf16_bits
 _orig_block = om.moe_block
+_orig_attn = om.attention_decode
 
 
 def _decode_nibbles_swapped(codes, scales):
@@ -180,6 +181,28 @@ def _block_norm_skipped(x_bits, norm_scale, norm_eps, *a, **kw):
     return _orig_block(x_bits, np.ones(np.asarray(x_bits).shape[-1]), 0.0, *a, **kw)
 
 
+def _attn_generic(q, k, v, lens, sinks, window, *, scale=None, head_map=None, lo_shift=0, sink_mode="denominator",
+                  ignore_lens=False):
+    """The decode step with one planted change (a compact second formulation)."""
+    q, k, v = (np.asarray(a, float) for a in (q, k, v))
+    B, Hq, D = q.shape
+    Hkv, L = k.shape[1], k.shape[2]
+    out = np.zeros((B, Hq, D))
+    for b in range(B):
+        n = L if ignore_lens else int(lens[b])
+        lo = 0 if window <= 0 else max(0, n - window + lo_shift)
+        for h in range(Hq):
+            g = head_map(h, Hq, Hkv) if head_map else h // (Hq // Hkv)
+            sc = k[b, g, lo:n] @ q[b, h] * (scale if scale is not None else 1 / np.sqrt(D))
+            m = sc.max()
+            e = np.exp(sc - m)
+            den = e.sum()
+            if sinks is not None and sink_mode == "denominator":
+                den += np.exp(float(sinks[h]) - m)
+            out[b, h] = (e / den) @ v[b, g, lo:n]
+    return out
+
+
 MUTATIONS = {
     "decode_nibbles_swapped": ("mxfp4_decode", _decode_nibbles_swapped),
     "decode_scale_per_16": ("mxfp4_decode", _decode_block16),
@@ -211,6 +234,13 @@ MUTATIONS = {
     "block_residual_of_normed_x": ("moe_block", _block_residual_of_xn),
     "block_no_residual": ("moe_block", _block_no_residual),
     "block_norm_skipped": ("moe_block", _block_norm_skipped),
+    "attn_sink_dropped": ("attention_decode", lambda *a: _attn_generic(*a, sink_mode="none")),
+    "attn_no_score_scale": ("attention_decode", lambda *a: _attn_generic(*a, scale=1.0)),
+    "attn_heads_interleaved": ("attention_decode",
+                               lambda *a: _attn_generic(*a, head_map=lambda h, hq, hkv: h % hkv)),
+    "attn_window_one_wider": ("attention_decode", lambda *a: _attn_generic(*a, lo_shift=-1)),
+    "attn_window_one_narrower": ("attention_decode", lambda *a: _attn_generic(*a, lo_shift=1)),
+    "attn_lens_ignored": ("attention_decode", lambda *a: _attn_generic(*a, ignore_lens=True)),
 }
 
 

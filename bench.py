@@ -8,6 +8,8 @@ resident in HBM. Steps rotate over L distinct copies of the layer's weights (24 
 20b-shaped layer, 36 for the 120b-shaped one, like the models' depth) so the 256 MB
 last-level cache cannot hold the weights between steps.
 
+With --workload attn_decode a step is one decode step of the model's attention instead
+(moe_attn_decode over --T sequences of --context positions, dense or --window).
 With --block a step is the block around the layer instead: RMSNorm of the residual-stream
 rows, the layer on the normalised rows, and the residual add (moe_block_forward_ex).
 
@@ -45,7 +47,10 @@ def parse():
     p.add_argument("--steps", type=int, default=200)
     p.add_argument("--warmup", type=int, default=20)
     p.add_argument("--workload", default="decode20b",
-                   choices=["decode20b", "prefill20b", "prefill120b", "decode120b_zipf"])
+                   choices=["decode20b", "prefill20b", "prefill120b", "decode120b_zipf", "attn_decode"])
+    p.add_argument("--context", type=int, default=4096,
+                   help="attn_decode: positions in every sequence's cache (all visible unless --window)")
+    p.add_argument("--window", type=int, default=0, help="attn_decode: 0 dense, else the band (gpt-oss: 128)")
     p.add_argument("--T", type=int, default=0, help="batch size (default: the workload's largest)")
     p.add_argument("--layers", type=int, default=0, help="rotated weight copies (default 24 / 36)")
     p.add_argument("--path", type=int, default=0, help="0 auto, 1 stream, 2 gemm (bf16), 3 gemm (block-scaled)")
@@ -162,6 +167,9 @@ def main():
             dst.copy_(src)
         torch.cuda.synchronize()
         print(json.dumps({"copy_calibration_bytes": n, "copies": 4}), flush=True)
+        return
+    if args.workload == "attn_decode":
+        attn_main(args, torch, synth, moe, dev)
         return
     cfg = synth.get_config(args.workload)
     T = args.T or cfg.T_list[-1]
@@ -339,6 +347,85 @@ def main():
         line["config"]["block"] = f"x + layer(RMSNorm(x)), eps {NORM_EPS:g}"
     if sweep:
         line["sweep"] = sweep
+    print(json.dumps(line), flush=True)
+
+
+def attn_main(args, torch, synth, moe, dev):
+    """One decode step of the model's attention (64 query heads over 8 key/value heads of
+    dimension 64, per-head sinks) for a batch of T sequences with `--context` cached positions;
+    steps rotate over cache copies larger together than the last-level cache."""
+    def log(msg):
+        print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+    B = args.T or 64
+    Lctx, W = args.context, args.window
+    Hq, Hkv, D = 64, 8, 64
+    t0 = time.time()
+    inp = synth.make_attn_inputs(B, Lctx, Hq, Hkv, D, seed=1, full=True)
+    log(f"generated attention inputs B={B} context={Lctx} in {time.time() - t0:.1f}s")
+
+    def bf16(a):
+        return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).to(dev).view(torch.bfloat16)
+
+    cache_bytes = 2 * inp.k.nbytes
+    copies = args.layers or max(2, int(np.ceil(2e9 / cache_bytes)))
+    kv = [(bf16(inp.k), bf16(inp.v))]
+    for _ in range(copies - 1):
+        kv.append((kv[0][0].clone(), kv[0][1].clone()))
+    q = bf16(inp.q)
+    lens = torch.from_numpy(inp.lens).to(dev)
+    sinks = torch.from_numpy(inp.sinks).to(dev)
+    out = torch.empty((B, Hq, D), dtype=torch.bfloat16, device=dev)
+    ws = torch.empty(int(moe.lib().moe_attn_workspace_size(B, Hkv, Lctx, W)), dtype=torch.uint8, device=dev)
+    torch.cuda.synchronize()
+    log(f"{copies} cache copies resident ({copies * cache_bytes / 1e9:.1f} GB)")
+
+    def step(i):
+        k, v = kv[i % copies]
+        moe.moe_attn_decode(q, k, v, lens, sinks, W, out=out, ws=ws)
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record()
+    for i in range(args.steps):
+        step(i)
+    b.record()
+    torch.cuda.synchronize()
+    ms = a.elapsed_time(b) / args.steps
+    visible = min(W, Lctx) if W > 0 else Lctx
+    nbytes = B * Hkv * visible * D * 2 * 2 + 2 * B * Hq * D * 2
+    achieved = nbytes / (ms * 1e-3) / 1e9
+    log(f"B={B} context={Lctx} window={W}: {ms * 1e3:.1f} us/step, {achieved:.0f} GB/s")
+    roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+                "kernel": "moe_attn_decode (split + merge)", "ms_per_launch": round(ms, 5),
+                "algorithmic_bytes": int(nbytes)}
+    cpu = None
+    if not args.no_cpu_baseline:
+        import oracle
+        n = min(B, 2)
+        qf, kf, vf = (oracle.bf16_to_f64(x[:n]) for x in (inp.q, inp.k, inp.v))
+        threads = len(os.sched_getaffinity(0)) if hasattr(os, "sched_getaffinity") else (os.cpu_count() or 1)
+        reps, dt = 0, 0.0
+        while reps < 16 and (reps == 0 or dt < 10.0):
+            t1 = time.perf_counter()
+            oracle.attention_decode(qf, kf, vf, inp.lens[:n], inp.sinks, W)
+            dt += time.perf_counter() - t1
+            reps += 1
+        log(f"oracle: {reps} x {n} sequences in {dt:.1f}s")
+        cpu = {"value": round(reps * n / dt, 3), "unit": "tokens/s", "cores": threads, "kind": "oracle",
+               "sample": f"first {n} of the {B} sequences, {reps} repetitions, fp64 numpy decode attention; {dt:.1f} s"}
+    line = {
+        "metric": "decode attention tokens/s (one new token per sequence)",
+        "value": round(B / (ms * 1e-3), 1), "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(ms, 5), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": "attn_decode", "sequences": B, "context": Lctx, "window": W, "q_heads": Hq,
+                   "kv_heads": Hkv, "head_dim": D, "sinks": True, "cache_copies": copies},
+        "roofline": roofline, "cpu_baseline": cpu,
+    }
     print(json.dumps(line), flush=True)
 
 

@@ -261,6 +261,32 @@ int moe_block_forward_ex(const uint16_t *x, const float *norm_scale, float norm_
                          int32_t E, int32_t k, const moe_options_t *opts, void *out, void *ws, size_t ws_bytes,
                          moe_stream_t stream);
 
+/*
+ * One decode step of grouped-query attention with per-head sink logits, the other per-layer
+ * hot path of the same model [walkthrough section 2.1: 64 query heads share 8 key/value
+ * heads, layers alternate between a 128-token banded window and dense attention, each head
+ * learns a logit added to the softmax's denominator; review section 3.5; retrospective
+ * "工程影响": head dimension 64, 2-byte cache]. For sequence b and query head h (key/value
+ * head h / (n_q_heads / n_kv_heads): consecutive query heads share one), over the visible
+ * positions j (0 <= j < lens[b]; with window > 0 only lens[b] - window <= j):
+ *   s_j = q[b][h] . k[b][kvh][j] / sqrt(64)
+ *   out[b][h] = sum_j e^(s_j) v[b][kvh][j] / (sum_j e^(s_j) + e^(sinks[h]))
+ * (without the sink term when sinks is NULL; 0 for a sequence with no visible position).
+ * q bf16 [B][n_q_heads][64] (positional rotation already applied); k_cache, v_cache bf16
+ * [B][n_kv_heads][max_len][64] (the new token's key and value already written at position
+ * lens[b] - 1); lens int32 [B], values clamped into [0, max_len]; sinks fp32 [n_q_heads] or
+ * NULL; out bf16 or fp32 [B][n_q_heads][64] per out_dtype. Scores, exponentials and sums are
+ * fp32; the weights enter the weighted sum of values as two bf16 terms (relative error about
+ * 2^-17). head_dim must be 64 and n_q_heads / n_kv_heads at most 16 (else
+ * MOE_ERR_UNSUPPORTED). ws: at least moe_attn_workspace_size(B, n_kv_heads, max_len, window)
+ * bytes, 256-byte aligned. Deterministic.
+ */
+size_t moe_attn_workspace_size(int64_t B, int32_t n_kv_heads, int64_t max_len, int32_t window);
+int moe_attn_decode(const uint16_t *q, const uint16_t *k_cache, const uint16_t *v_cache, const int32_t *lens,
+                    const float *sinks, int64_t B, int32_t n_q_heads, int32_t n_kv_heads, int32_t head_dim,
+                    int64_t max_len, int32_t window, void *out, int32_t out_dtype, void *ws, size_t ws_bytes,
+                    moe_stream_t stream);
+
 /* Free moe_forward's workspace on the current device (synchronises the device). */
 int moe_release_workspace(void);
 

@@ -23,6 +23,7 @@ from .ops import (  # noqa: F401
     Options,
     Router,
     abi_version,
+    moe_attn_decode,
     moe_block_forward_ex,
     moe_combine,
     moe_forward,

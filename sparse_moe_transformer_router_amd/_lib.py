@@ -84,6 +84,9 @@ SIGNATURES = {
                                        ctypes.POINTER(MoeMxfp4Weight), ctypes.POINTER(MoeMxfp4Weight),
                                        c_int64, c_int32, c_int32, ctypes.POINTER(MoeOptions), c_void_p,
                                        c_void_p, c_size_t, c_void_p]),
+    "moe_attn_workspace_size": (c_size_t, [c_int64, c_int32, c_int64, c_int32]),
+    "moe_attn_decode": (c_int32, [c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_int64, c_int32, c_int32,
+                                  c_int32, c_int64, c_int32, c_void_p, c_int32, c_void_p, c_size_t, c_void_p]),
     "moe_release_workspace": (c_int32, []),
 }
 

@@ -34,6 +34,7 @@ SOURCES = [
     "pack.hip",
     "combine.hip",
     "norm.hip",
+    "attn.hip",
 ]
 
 ARCH = "gfx950"

@@ -90,4 +90,13 @@ hipError_t launch_combine(const float *y, const int32_t *slot_row, const float *
 hipError_t launch_rmsnorm(const uint16_t *x, int64_t T, int H, const float *scale, float eps, uint16_t *xn,
                           uint8_t *rec, uint8_t *rec_scales, hipStream_t stream);
 
+// One decode step of grouped-query attention with per-head sinks (attn.hip). q [B][Hq][64],
+// kc / vc [B][Hkv][L][64] bf16, lens [B], sinks [Hq] fp32 or null, window 0 = dense; out
+// [B][Hq][64] bf16 or fp32; ws: attn_partial_floats(B, Hkv, L, window) floats. Hq / Hkv <= 16.
+int attn_splits(int64_t L, int window);
+size_t attn_partial_floats(int64_t B, int Hkv, int64_t L, int window);
+hipError_t launch_attn_decode(const uint16_t *q, const uint16_t *kc, const uint16_t *vc, const int32_t *lens,
+                              const float *sinks, int64_t B, int Hq, int Hkv, int64_t L, int window, void *out,
+                              bool out_f32, float *ws, hipStream_t stream);
+
 }  // namespace moe

@@ -477,6 +477,37 @@ int moe_block_forward_ex(const uint16_t *x, const float *norm_scale, float norm_
   MOE_GUARD_END
 }
 
+size_t moe_attn_workspace_size(int64_t B, int32_t n_kv_heads, int64_t max_len, int32_t window) {
+  if (B < 0 || n_kv_heads < 1 || max_len < 1 || window < 0) return 0;
+  return moe::attn_partial_floats(B, n_kv_heads, max_len, window) * sizeof(float);
+}
+
+int moe_attn_decode(const uint16_t *q, const uint16_t *k_cache, const uint16_t *v_cache, const int32_t *lens,
+                    const float *sinks, int64_t B, int32_t n_q_heads, int32_t n_kv_heads, int32_t head_dim,
+                    int64_t max_len, int32_t window, void *out, int32_t out_dtype, void *ws, size_t ws_bytes,
+                    moe_stream_t stream) {
+  MOE_GUARD_BEGIN
+  if (B < 0 || n_kv_heads < 1 || n_q_heads < 1 || max_len < 1 || window < 0) return MOE_ERR_INVALID_ARG;
+  if (out_dtype != MOE_DTYPE_BF16 && out_dtype != MOE_DTYPE_F32) return MOE_ERR_INVALID_ARG;
+  if (head_dim != 64 || n_q_heads % n_kv_heads != 0 || n_q_heads / n_kv_heads > 16) return MOE_ERR_UNSUPPORTED;
+  if (B > 65535 || n_kv_heads > 65535 || max_len > ((int64_t)1 << 31)) return MOE_ERR_UNSUPPORTED;
+  if (B == 0) return MOE_OK;
+  if (q == nullptr || k_cache == nullptr || v_cache == nullptr || lens == nullptr || out == nullptr)
+    return MOE_ERR_INVALID_ARG;
+  if (!aligned(q, 16) || !aligned(k_cache, 16) || !aligned(v_cache, 16) || !aligned(out, 16) || !aligned(lens, 4) ||
+      !aligned(sinks, 4))
+    return MOE_ERR_INVALID_ARG;
+  const size_t need = moe::attn_partial_floats(B, n_kv_heads, max_len, window) * sizeof(float);
+  if (ws == nullptr || ws_bytes < need) return MOE_ERR_WORKSPACE;
+  if (!aligned(ws, kWsAlign)) return MOE_ERR_INVALID_ARG;
+  return moe::launch_attn_decode(q, k_cache, v_cache, lens, sinks, B, n_q_heads, n_kv_heads, max_len, window, out,
+                                 out_dtype == MOE_DTYPE_F32, static_cast<float *>(ws), (hipStream_t)stream) ==
+                 hipSuccess
+             ? MOE_OK
+             : MOE_ERR_HIP;
+  MOE_GUARD_END
+}
+
 int moe_forward(const uint16_t *x, const moe_router_t *router, const moe_mxfp4_weight_t *w_gate_up,
                 const moe_mxfp4_weight_t *w_down, int64_t T, int32_t E, int32_t k, uint16_t *out,
                 moe_stream_t stream) {

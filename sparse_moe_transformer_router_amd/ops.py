@@ -246,5 +246,25 @@ def moe_block_forward_ex(x: torch.Tensor, norm_scale: torch.Tensor, norm_eps: fl
     return out
 
 
+def moe_attn_decode(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor, lens: torch.Tensor,
+                    sinks: Optional[torch.Tensor] = None, window: int = 0, out_dtype: int = L.MOE_DTYPE_BF16,
+                    out: Optional[torch.Tensor] = None, ws: Optional[torch.Tensor] = None,
+                    stream=None) -> torch.Tensor:
+    """One decode step of grouped-query attention with per-head sinks: q [B][Hq][64] bf16, caches
+    [B][Hkv][L][64] bf16, lens [B] int32, sinks [Hq] fp32 or None; window 0 = dense."""
+    B, Hq, D = q.shape
+    Hkv, Lmax = int(k_cache.shape[1]), int(k_cache.shape[2])
+    if out is None:
+        dt = torch.bfloat16 if out_dtype == L.MOE_DTYPE_BF16 else torch.float32
+        out = torch.empty((B, Hq, D), dtype=dt, device=q.device)
+    if ws is None:
+        ws = torch.empty(int(L.lib().moe_attn_workspace_size(B, Hkv, Lmax, window)), dtype=torch.uint8,
+                         device=q.device)
+    L.check("moe_attn_decode", L.lib().moe_attn_decode(
+        _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(lens), _ptr(sinks), B, Hq, Hkv, D, Lmax, window, _ptr(out),
+        out_dtype, _ptr(ws), ws.numel(), _stream(stream)))
+    return out
+
+
 def moe_release_workspace() -> None:
     L.check("moe_release_workspace", L.lib().moe_release_workspace())

@@ -11,6 +11,8 @@ from .generators import (  # noqa: F401
     ExpertWeights,
     bf16_bits_from_f32,
     f32_from_bf16_bits,
+    AttnInputs,
+    make_attn_inputs,
     make_block_x,
     make_inputs,
     make_norm_scale,

@@ -8,6 +8,9 @@ Distributions (the workloads of the gpt-oss pages, stood in for by random data b
 trained weights and real hidden states are not available):
 
 * x: bf16(N(0, 1)) per element, a stand-in for RMS-normalised hidden states.
+* decode attention (the model's other per-layer hot path): q, k, v = bf16(N(0, 1)) per
+  element (q times ``q_scale`` for sharper score distributions), sink logits fp32 N(0, 1),
+  per-sequence lengths uniform over 1..L with the first sequence at L.
 * block input (the residual stream before the block's RMSNorm): bf16(N(0, 1) * 2^u) with
   one u ~ U(-2, 2) per token, so tokens differ in scale by up to 16x and the normalisation
   matters; RMSNorm scale: fp32 U(0.5, 1.5) per feature.
@@ -46,6 +49,7 @@ _TID_W2_BIAS = 22
 _TID_BLOCK_X = 30
 _TID_BLOCK_TOKEN_SCALE = 31
 _TID_NORM_SCALE = 32
+_TID_ATTN = 40
 
 
 def _rng(*key: int) -> np.random.Generator:
@@ -170,6 +174,29 @@ def make_block_x(cfg: LayerConfig, T: int) -> np.ndarray:
 def make_norm_scale(cfg: LayerConfig) -> np.ndarray:
     """fp32 [H]: the RMSNorm's per-feature scale, U(0.5, 1.5)."""
     return _rng(cfg.seed, _TID_NORM_SCALE).uniform(0.5, 1.5, size=cfg.H).astype(np.float32)
+
+
+@dataclasses.dataclass
+class AttnInputs:
+    q: np.ndarray       # uint16 bf16 bits [B][Hq][D]
+    k: np.ndarray       # uint16 bf16 bits [B][Hkv][L][D]
+    v: np.ndarray       # uint16 bf16 bits [B][Hkv][L][D]
+    lens: np.ndarray    # int32 [B]
+    sinks: np.ndarray   # float32 [Hq]
+
+
+def make_attn_inputs(B: int, L: int, Hq: int = 64, Hkv: int = 8, D: int = 64, seed: int = 0,
+                     q_scale: float = 1.0, full: bool = False) -> AttnInputs:
+    """One decode step's attention inputs (key/value caches filled at every position; positions
+    at or past lens[b] are not visible). ``full``: every sequence at length L."""
+    g = _rng(seed, _TID_ATTN, B, L, Hq, Hkv)
+    q = bf16_bits_from_f32(g.standard_normal((B, Hq, D), dtype=np.float32) * np.float32(q_scale))
+    k = bf16_bits_from_f32(g.standard_normal((B, Hkv, L, D), dtype=np.float32))
+    v = bf16_bits_from_f32(g.standard_normal((B, Hkv, L, D), dtype=np.float32))
+    lens = np.full(B, L, np.int32) if full else g.integers(1, L + 1, B).astype(np.int32)
+    lens[0] = L
+    sinks = g.standard_normal(Hq).astype(np.float32)
+    return AttnInputs(q, k, v, lens, sinks)
 
 
 def make_router(cfg: LayerConfig, bias: Optional[np.ndarray] = None) -> Tuple[np.ndarray, np.ndarray]:

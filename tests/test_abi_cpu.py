@@ -153,6 +153,28 @@ def test_rmsnorm_and_block_errors():
     assert lib.moe_workspace_size(1000, E, k, H, I, 0) - lib.moe_workspace_size(999, E, k, H, I, 0) >= 2 * H
 
 
+def test_attn_errors():
+    """Argument checks of moe_attn_decode (before any HIP call) and its workspace size."""
+    lib = L.lib()
+    big = 1 << 40
+    call = lambda B=2, hq=64, hkv=8, d=64, Lm=100, w=0, dt=0, ws=FAKE, wsb=big, sinks=FAKE, q=FAKE: \
+        lib.moe_attn_decode(q, FAKE, FAKE, FAKE, sinks, B, hq, hkv, d, Lm, w, FAKE, dt, ws, wsb, None)
+    assert call(d=128) == L.MOE_ERR_UNSUPPORTED
+    assert call(hq=60) == L.MOE_ERR_UNSUPPORTED            # not a multiple of the key heads
+    assert call(hq=136, hkv=8) == L.MOE_ERR_UNSUPPORTED    # groups above 16
+    assert call(B=-1) == L.MOE_ERR_INVALID_ARG
+    assert call(w=-1) == L.MOE_ERR_INVALID_ARG
+    assert call(dt=5) == L.MOE_ERR_INVALID_ARG
+    assert call(q=None) == L.MOE_ERR_INVALID_ARG
+    assert call(q=FAKE + 8) == L.MOE_ERR_INVALID_ARG
+    assert call(wsb=16) == L.MOE_ERR_WORKSPACE
+    assert call(B=0, q=None) == L.MOE_OK
+    # partials: per (sequence, key head, 256-position range) 16 rows of 66 floats
+    assert lib.moe_attn_workspace_size(2, 8, 1000, 0) == 2 * 8 * 4 * 16 * 66 * 4
+    assert lib.moe_attn_workspace_size(2, 8, 1000, 128) == 2 * 8 * 1 * 16 * 66 * 4
+    assert lib.moe_attn_workspace_size(2, 0, 1000, 0) == 0
+
+
 def test_tiled_bytes_and_pack_errors():
     lib = L.lib()
     cb, sb = ctypes.c_size_t(0), ctypes.c_size_t(0)

@@ -76,18 +76,22 @@ CALIBRATION_MIB = 1024
 FFN_KERNELS = ("ffn_", "gather_rows")  # kernels one moe_mxfp4_ffn call launches, once each
 
 
-# the sources of what one moe_mxfp4_ffn call runs: its kernels, their headers and the host
-# code that picks and launches them
-FFN_SOURCES = ("ffn_stream.hip", "ffn_gemm.hip", "gather.hip", "common.h", "mx_act.h", "kernels.h",
-               "moe_abi.cpp")
+# the sources of what one moe_mxfp4_ffn call runs at decode (the weight-streaming kernels) and
+# at prefill (the gather and the grouped GEMM): kernels, their headers and the host code that
+# picks and launches them
+FFN_SOURCES = {
+    "stream": ("ffn_stream.hip", "common.h", "kernels.h", "moe_abi.cpp"),
+    "gemm": ("ffn_gemm.hip", "gather.hip", "common.h", "mx_act.h", "kernels.h", "moe_abi.cpp"),
+}
 
 
-def kernel_source_hash():
-    """Hash of the expert-FFN sources: a stored traffic figure is valid for these only."""
+def kernel_source_hash(workload):
+    """Hash of the expert-FFN sources the workload runs: a stored traffic figure is valid for
+    these only."""
     import hashlib
     csrc = os.path.join(ROOT, "sparse_moe_transformer_router_amd", "csrc")
     h = hashlib.sha256()
-    for name in FFN_SOURCES:
+    for name in FFN_SOURCES["stream" if workload.startswith("decode") else "gemm"]:
         with open(os.path.join(csrc, name), "rb") as f:
             h.update(name.encode() + b"\0" + f.read())
     return h.hexdigest()[:16]
@@ -122,7 +126,7 @@ def pmc_summary(args, T):
     fk = sum(f[k] for k in names)
     wk = sum(w.get(k, 0.0) for k in names)
     nbytes = int(round((fk * fetch_scale + wk * write_scale) * 1024))
-    print(f"traffic workload={args.workload} T={T} src={kernel_source_hash()} bytes={nbytes} "
+    print(f"traffic workload={args.workload} T={T} src={kernel_source_hash(args.workload)} bytes={nbytes} "
           f"fetch_kib={fk:.0f} write_kib={wk:.0f} fetch_scale={fetch_scale:.4f} write_scale={write_scale:.4f} "
           f"kernels={'+'.join(n.replace(' ', '') for n in names)}", flush=True)
 
@@ -131,7 +135,7 @@ def stored_traffic(workload, T):
     """HBM bytes per expert-FFN call measured by rocprofv3 for these exact kernel sources, or None."""
     if not os.path.exists(TRAFFIC_FILE):
         return None
-    src = kernel_source_hash()
+    src = kernel_source_hash(workload)
     with open(TRAFFIC_FILE) as f:
         for line in f:
             if not line.startswith("traffic "):

@@ -511,7 +511,10 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
         for (int gg = 0; gg < 2; ++gg)
 #pragma unroll
           for (int i = 0; i < 4; ++i) m = fmaxf(m, fmaxf(fabsf(av[2 * j + gg][i][0]), fabsf(av[2 * j + gg][i][1])));
-        m = fmaxf(m, __shfl_xor(m, 32, kWave));
+        {  // the block maximum over the lane pair (l, l + 32): one half swap, no LDS round trip
+          const auto mm = __builtin_amdgcn_permlane32_swap(__float_as_uint(m), __float_as_uint(m), false, false);
+          m = fmaxf(__uint_as_float(mm[0]), __uint_as_float(mm[1]));
+        }
         const MxBlockScale s = mx_block_scale(m);
         sc_hi |= s.sh << (8 * j);
         sc_lo |= s.sl << (8 * j);
@@ -520,27 +523,21 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
         for (int gg = 0; gg < 2; ++gg)
 #pragma unroll
           for (int i = 0; i < 4; ++i) mx_split2(av[2 * j + gg][i][0], av[2 * j + gg][i][1], s, hp[gg][i], lp[gg][i]);
-        // own: the half this lane stores (gg == kh); send the other half to the partner
-        uint32_t oh[4], ol[4], sh[2], sl[2];
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          oh[i] = kh ? hp[1][i] : hp[0][i];
-          ol[i] = kh ? lp[1][i] : lp[0][i];
-        }
-#pragma unroll
-        for (int d = 0; d < 2; ++d) {
-          sh[d] = (kh ? hp[0][2 * d] : hp[1][2 * d]) | ((kh ? hp[0][2 * d + 1] : hp[1][2 * d + 1]) << 16);
-          sl[d] = (kh ? lp[0][2 * d] : lp[1][2 * d]) | ((kh ? lp[0][2 * d + 1] : lp[1][2 * d + 1]) << 16);
-          sh[d] = (uint32_t)__shfl_xor((int)sh[d], 32, kWave);
-          sl[d] = (uint32_t)__shfl_xor((int)sl[d], 32, kWave);
-        }
+        // Lane kh of the pair stores half gg = kh: its own pairs hp[kh] and the partner's
+        // hp[kh]. permlane32_swap(x = hp[0], y = hp[1]) returns [x lanes 0-31, y lanes 0-31] and
+        // [x lanes 32-63, y lanes 32-63]: in the low lanes own hp[0], then the partner's; in the
+        // high lanes the partner's hp[1], then own -- so both store r0 | r1 << 16.
         u32x4_t wh, wl;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const uint32_t ph = (sh[i / 2] >> (16 * (i % 2))) & 0xffffu;  // partner's pair i
-          const uint32_t pl = (sl[i / 2] >> (16 * (i % 2))) & 0xffffu;
-          wh[i] = kh ? (ph | (oh[i] << 16)) : (oh[i] | (ph << 16));
-          wl[i] = kh ? (pl | (ol[i] << 16)) : (ol[i] | (pl << 16));
+        for (int d = 0; d < 2; ++d) {
+          const uint32_t xh = hp[0][2 * d] | (hp[0][2 * d + 1] << 16), yh = hp[1][2 * d] | (hp[1][2 * d + 1] << 16);
+          const uint32_t xl = lp[0][2 * d] | (lp[0][2 * d + 1] << 16), yl = lp[1][2 * d] | (lp[1][2 * d + 1] << 16);
+          const auto rh = __builtin_amdgcn_permlane32_swap(xh, yh, false, false);
+          const auto rl = __builtin_amdgcn_permlane32_swap(xl, yl, false, false);
+          wh[2 * d] = (rh[0] & 0xffffu) | (rh[1] << 16);
+          wh[2 * d + 1] = (rh[0] >> 16) | (rh[1] & 0xffff0000u);
+          wl[2 * d] = (rl[0] & 0xffffu) | (rl[1] << 16);
+          wl[2 * d + 1] = (rl[0] >> 16) | (rl[1] & 0xffff0000u);
         }
         if (live) {
           *reinterpret_cast<u32x4_t *>(rec + 32 * j) = wh;

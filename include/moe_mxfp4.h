@@ -63,7 +63,7 @@ extern "C" {
                               weights are an operand as stored, each bf16 activation is split
                               exactly into two MXFP8 (E4M3) terms with E8M0 block scales. Needs
                               MOE_LAYOUT_TILED weights. AUTO picks it for tiled weights when
-                              T*k >= 48*E. */
+                              T*k >= 32*E. */
 
 /* moe_mxfp4_weight_t.layout */
 #define MOE_LAYOUT_ROWMAJOR 0 /* codes [E][n][k/2], scales [E][n][k/32] as described below */

@@ -105,7 +105,9 @@ int check_options(const moe_options_t &o) {
 // Which expert-GEMM family runs: a grouped GEMM (tiled weights only) when asked for, or on
 // AUTO when the batch averages at least kGemmSlotsPerExpert slots per expert; otherwise the
 // weight-streaming kernels. AUTO's grouped GEMM is the block-scaled one when kAutoMx is set.
-constexpr int64_t kGemmSlotsPerExpert = 48;
+// Measured crossover (FFN time, stream vs block-scaled GEMM): E = 32 at 24 slots per expert
+// 105 vs 142 us, at 32: 150 vs 145 us; E = 128 at 16: 354 vs 467 us, at 32: 544 vs 485 us.
+constexpr int64_t kGemmSlotsPerExpert = 32;
 constexpr bool kAutoMx = true;
 
 enum class Family { kStream, kGemm, kGemmMx };

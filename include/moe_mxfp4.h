@@ -254,7 +254,9 @@ int moe_rmsnorm(const uint16_t *x, int64_t T, int32_t H, const float *scale, flo
  * The residual x is added to the fp32 weighted sum of the experts' outputs, after it, and the
  * result is rounded once (out bf16 or fp32 per opts->out_dtype). norm_scale fp32 [H], 16-byte
  * aligned; norm_eps as for moe_rmsnorm. Workspace, options and limits as moe_forward_ex (the
- * same moe_workspace_size covers the normalised copy of x).
+ * same moe_workspace_size covers the normalised copy of x). With a bf16 output, out may be x
+ * itself (an in-place residual update): x is last read by the kernel that writes out, element
+ * by element before the write.
  */
 int moe_block_forward_ex(const uint16_t *x, const float *norm_scale, float norm_eps, const moe_router_t *router,
                          const moe_mxfp4_weight_t *w_gate_up, const moe_mxfp4_weight_t *w_down, int64_t T,

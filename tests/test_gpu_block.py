@@ -170,3 +170,13 @@ def test_block_decode120b_zipf():
 def test_block_prefill20b_sampled():
     tokens = np.sort(np.random.default_rng(31).choice(4096, 16, replace=False))
     _check_block("prefill20b", 4096, 0, tokens=tokens)
+
+
+def test_block_in_place():
+    """out = x: the residual update in place gives the same bits as a separate output."""
+    for name, T in [("decode20b", 64), ("prefill20b", 4096)]:
+        inp, scale, dev, scale_d = _block_layer(name, T)
+        want = gu.bf16_bits(_gpu_block(dev, scale_d, moe.MOE_DTYPE_BF16))
+        x = dev.x.clone()
+        moe.moe_block_forward_ex(x, scale_d, EPS, dev.router, dev.w1, dev.w2, dev.k, moe.Options(), out=x)
+        assert np.array_equal(gu.bf16_bits(x), want), name

@@ -103,3 +103,9 @@ def test_attn_zero_length_and_determinism():
     assert np.all(out[1] == 0.0)
     again = moe.moe_attn_decode(q, k, v, lens, sinks, 0, out_dtype=moe.MOE_DTYPE_F32).cpu().numpy()
     assert np.array_equal(out, again)
+
+
+@pytest.mark.parametrize("window", [0, 128])
+def test_attn_bench_configuration(window):
+    """The benchmark's launch configuration: 64 sequences, every one at 4096 positions."""
+    _check(synth.make_attn_inputs(64, 4096, seed=1, full=True), window)

@@ -1,0 +1,80 @@
+"""The library's entry points under HIP graph capture (torch.cuda.CUDAGraph): no allocation,
+no host synchronisation and no memset node inside a call, so a captured layer, block or
+attention step replays to the same bits as the eager call, replay after replay, with other
+eager work and synchronisations in between."""
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import gpu_util as gu
+import synth
+
+pytestmark = pytest.mark.gpu
+
+moe = pytest.importorskip("sparse_moe_transformer_router_amd")
+
+
+@pytest.fixture(autouse=True)
+def _announce(request):
+    sys.__stderr__.write(f"\n[gpu case] {request.node.nodeid}\n")
+    sys.__stderr__.flush()
+    yield
+    torch.cuda.synchronize()
+
+
+def _replays_match(run, eager_out, graph_out, other):
+    g = torch.cuda.CUDAGraph()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        run()  # a warm call on the side stream before capture
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    with torch.cuda.graph(g):
+        run()
+    want = eager_out.cpu().numpy().copy()
+    for _ in range(3):
+        graph_out.zero_()
+        g.replay()
+        torch.cuda.synchronize()
+        assert np.array_equal(graph_out.cpu().numpy(), want)
+        other()  # unrelated eager work between replays
+        torch.cuda.synchronize()
+
+
+@pytest.mark.parametrize("name,T", [("decode20b", 64), ("prefill20b", 4096)])
+def test_layer_and_block_replay(name, T):
+    cfg = synth.get_config(name)
+    inp = synth.make_inputs(cfg, T)
+    dev = gu.device_layer(inp, tiled=True)
+    E, H, I, k = cfg.E, cfg.H, cfg.I, cfg.k
+    opts = moe.Options(out_dtype=moe.MOE_DTYPE_F32)
+    ws_e, ws_g = moe.workspace(T, E, k, H, I), moe.workspace(T, E, k, H, I)
+    out_e = torch.empty((T, H), dtype=torch.float32, device="cuda")
+    out_g = torch.empty_like(out_e)
+    moe.moe_forward_ex(dev.x, dev.router, dev.w1, dev.w2, k, opts, out=out_e, ws=ws_e)
+    x2 = gu.to_dev_bf16(synth.make_x(cfg, T, offset=1))
+    other = lambda: moe.moe_forward_ex(x2, dev.router, dev.w1, dev.w2, k, opts, out=out_e.clone(), ws=ws_e)
+    _replays_match(lambda: moe.moe_forward_ex(dev.x, dev.router, dev.w1, dev.w2, k, opts, out=out_g, ws=ws_g),
+                   out_e, out_g, other)
+    scale = gu.to_dev_f32(synth.make_norm_scale(cfg))
+    moe.moe_block_forward_ex(dev.x, scale, 1e-5, dev.router, dev.w1, dev.w2, k, opts, out=out_e, ws=ws_e)
+    _replays_match(lambda: moe.moe_block_forward_ex(dev.x, scale, 1e-5, dev.router, dev.w1, dev.w2, k, opts,
+                                                    out=out_g, ws=ws_g), out_e, out_g, other)
+
+
+@pytest.mark.parametrize("window", [0, 128])
+def test_attention_replay(window):
+    inp = synth.make_attn_inputs(16, 2048, seed=9)
+    q, k, v = gu.to_dev_bf16(inp.q), gu.to_dev_bf16(inp.k), gu.to_dev_bf16(inp.v)
+    lens, sinks = torch.from_numpy(inp.lens).to("cuda"), gu.to_dev_f32(inp.sinks)
+    nws = int(moe.lib().moe_attn_workspace_size(16, 8, 2048, window))
+    ws_e = torch.empty(nws, dtype=torch.uint8, device="cuda")
+    ws_g = torch.empty(nws, dtype=torch.uint8, device="cuda")
+    out_e = moe.moe_attn_decode(q, k, v, lens, sinks, window, out_dtype=moe.MOE_DTYPE_F32, ws=ws_e)
+    out_g = torch.empty_like(out_e)
+    other = lambda: moe.moe_attn_decode(q, k, v, lens, None, window, out_dtype=moe.MOE_DTYPE_F32, ws=ws_e)
+    _replays_match(lambda: moe.moe_attn_decode(q, k, v, lens, sinks, window, out_dtype=moe.MOE_DTYPE_F32,
+                                               out=out_g, ws=ws_g), out_e, out_g, other)

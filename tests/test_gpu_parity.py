@@ -346,6 +346,13 @@ def test_layer_shapes(E, k, H, I, T, tiled, path):
     _check_layer(synth.make_inputs(_small_cfg(E, k, H, I, T)), tiled=tiled, path=path)
 
 
+@pytest.mark.parametrize("tiled,path", [(False, 0), (True, 1), (True, 2), (True, 3)])
+@pytest.mark.parametrize("E,k,H,I,T", [(2, 1, 16384, 256, 5), (2, 2, 256, 16384, 7)])
+def test_layer_largest_widths(E, k, H, I, T, tiled, path):
+    """The ABI's largest hidden and expert widths (16384 = 512 MX blocks, 128 chunks of K)."""
+    _check_layer(synth.make_inputs(_small_cfg(E, k, H, I, T)), tiled=tiled, path=path)
+
+
 @pytest.mark.parametrize("path", [0, 2, 3])
 def test_layer_all_tokens_one_group(path):
     """A router bias that sends every token to experts 0..3: most experts are empty and the

@@ -105,6 +105,12 @@ def test_attn_zero_length_and_determinism():
     assert np.array_equal(out, again)
 
 
+def test_attn_longest_context():
+    """One sequence at the gpt-oss context length (131072 positions: 512 ranges, the
+    four-wave merge)."""
+    _check(synth.make_attn_inputs(1, 131072, seed=2, full=True), 0)
+
+
 @pytest.mark.parametrize("window", [0, 128])
 def test_attn_bench_configuration(window):
     """The benchmark's launch configuration: 64 sequences, every one at 4096 positions."""

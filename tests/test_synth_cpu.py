@@ -59,3 +59,23 @@ def test_zipf_decode_is_skewed():
     c = np.bincount(idx.ravel(), minlength=cfg.E)
     assert c.max() >= 0.2 * 256  # the hot expert sees (almost) every token
     assert (c == 0).sum() >= 10  # many cold experts
+
+
+def test_block_and_attention_generators():
+    """Seeded, order-independent draws with the documented shapes and laws."""
+    import numpy as np
+    import synth
+    cfg = synth.get_config("decode20b")
+    x = synth.make_block_x(cfg, 8)
+    assert x.shape == (8, cfg.H) and x.dtype == np.uint16
+    assert np.array_equal(x, synth.make_block_x(cfg, 8))
+    rms = np.sqrt(np.mean(synth.f32_from_bf16_bits(x).astype(np.float64) ** 2, axis=1))
+    assert rms.min() > 0.2 and rms.max() < 4.5 and rms.max() / rms.min() > 1.5  # per-token scales 2^U(-2,2)
+    s = synth.make_norm_scale(cfg)
+    assert s.shape == (cfg.H,) and s.dtype == np.float32 and 0.5 <= s.min() and s.max() <= 1.5
+    a = synth.make_attn_inputs(3, 40, Hq=16, Hkv=2, seed=5)
+    assert a.q.shape == (3, 16, 64) and a.k.shape == (3, 2, 40, 64) and a.v.shape == a.k.shape
+    assert a.lens[0] == 40 and a.lens.min() >= 1 and a.lens.max() <= 40 and a.sinks.shape == (16,)
+    b = synth.make_attn_inputs(3, 40, Hq=16, Hkv=2, seed=5)
+    assert all(np.array_equal(getattr(a, f), getattr(b, f)) for f in ("q", "k", "v", "lens", "sinks"))
+    assert np.all(synth.make_attn_inputs(4, 10, seed=1, full=True).lens == 10)

@@ -136,6 +136,9 @@ def oracle_forward(inp: synth.MoEInputs, gpu_idx: Optional[np.ndarray], tokens: 
         res.out[tie] = forced.out
         res.idx[tie] = forced.idx
         res.w[tie] = forced.w
+        if keep_intermediates:
+            res.h[tie] = forced.h
+            res.act[tie] = forced.act
     return res
 
 
@@ -146,11 +149,36 @@ def bf16_half_ulp(v: np.ndarray) -> np.ndarray:
     return np.ldexp(1.0, (e - 8).astype(np.int64))
 
 
-def check_output(gpu_out: np.ndarray, ref_out: np.ndarray, bf16: bool, tol: float = OUT_TOL):
-    """max|gpu - ref| <= tol * RMS(ref) (+ half a bf16 ulp of ref for bf16 outputs)."""
+def check_output(gpu_out: np.ndarray, ref_out: np.ndarray, bf16: bool, tol: float = OUT_TOL,
+                 act_bound=None):
+    """max|gpu - ref| <= tol * RMS(ref) (+ half a bf16 ulp of ref for bf16 outputs).
+
+    act_bound (optional callable returning an array shaped like ref_out): the most that
+    rounding the activation to bf16 between the two products -- the layer's specified
+    precision, which the oracle does not apply -- can move each output. It is consulted only if
+    the bar above fails, and then each output may exceed the bar by at most that amount: with a
+    short down projection (a few dozen terms, shapes far below the pages' 2880) one output at
+    several times the RMS can move by more than 2e-2 of the RMS from that rounding alone."""
     rms = float(np.sqrt(np.mean(ref_out ** 2)))
     err = np.abs(gpu_out.astype(np.float64) - ref_out)
     bound = tol * rms + (bf16_half_ulp(ref_out) if bf16 else 0.0)
     worst = float((err - bound).max())
+    if worst > 0.0 and act_bound is not None:
+        worst = float((err - bound - act_bound()).max())
     assert worst <= 0.0, f"max err {err.max():.4g} (rms {rms:.4g}, rel {err.max() / rms:.4g}) exceeds bound"
     return float(err.max() / rms)
+
+
+def act_rounding_bound(inp: synth.MoEInputs, res: oracle.MoEResult) -> np.ndarray:
+    """Per output of res (needs its activations, keep_intermediates): sum over the picks j of
+    w_j * sum_i |W2_e[n, i]| |a_ji| * 2^-8 -- twice the bound of one round-to-nearest bf16 step on
+    every activation (2^-9 relative), with room for the fp32 sums."""
+    tok = res.tokens
+    out = np.zeros_like(res.out)
+    idx = res.idx
+    for e in np.unique(idx):
+        W2 = np.abs(oracle.mxfp4_decode(inp.w2_codes[e], inp.w2_scales[e]))
+        rows, ranks = np.nonzero(idx == e)
+        out[rows] += res.w[rows, ranks][:, None] * (np.abs(res.act[rows, ranks]) @ W2.T)
+    assert out.shape[0] == len(tok)
+    return out * 2.0 ** -8

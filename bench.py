@@ -61,6 +61,8 @@ def parse():
                         "on residual-stream inputs with per-token scales")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--no-sweep", action="store_true")
+    p.add_argument("--no-prefill", action="store_true",
+                   help="decode workloads: skip the 4096-token prefill20b record added to the line")
     p.add_argument("--pmc-summary", nargs=4, metavar=("COPY_FETCH", "COPY_WRITE", "FETCH", "WRITE"),
                    help="only print the traffic line for --workload/--T from four rocprofv3 --pmc csv "
                         "output folders (FETCH_SIZE and WRITE_SIZE of --copy-calibration 1024, then of "
@@ -146,6 +148,182 @@ def stored_traffic(workload, T):
     return None
 
 
+def host_description():
+    """The host the oracle baseline runs on: the CPU model name (the field lscpu shows, read
+    from /proc/cpuinfo) and NumPy's BLAS backend."""
+    import platform
+    model = None
+    try:
+        with open("/proc/cpuinfo") as f:
+            for ln in f:
+                if ln.startswith("model name"):
+                    model = ln.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    if model is None:
+        model = platform.processor() or platform.machine()
+    blas = None
+    try:
+        dep = np.__config__.CONFIG["Build Dependencies"]["blas"]
+        blas = f"{dep.get('name')} {dep.get('version')}"
+    except Exception:
+        pass
+    return model, blas
+
+
+def event_time(torch, fn, min_ms=100.0, warm_ms=100.0, max_calls=50000):
+    """Average device time of fn(i) over back-to-back calls between one pair of HIP events on
+    the current stream (the one the library launches on): calls for at least warm_ms of wall
+    time first (clocks settle), then at least min_ms of timed calls, whatever --steps is."""
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    n = 0
+    while True:
+        fn(n)
+        n += 1
+        if n % 8 == 0:
+            torch.cuda.synchronize()
+            if (time.perf_counter() - t0) * 1e3 >= warm_ms:
+                break
+    per_call = (time.perf_counter() - t0) / n
+    calls = int(min(max_calls, max(20, np.ceil(min_ms * 1e-3 / per_call))))
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    a.record()
+    for i in range(calls):
+        fn(n + i)
+    b.record()
+    torch.cuda.synchronize()
+    return a.elapsed_time(b) / calls, calls
+
+
+class LayerBench:
+    """One workload's weights (L rotated device copies) and the timing of layer steps and of
+    the expert FFN at any batch size."""
+
+    def __init__(self, args, torch, synth, moe, dev, cfg, T0, log):
+        self.args, self.torch, self.synth, self.moe, self.dev, self.cfg, self.log = args, torch, synth, moe, dev, cfg, log
+        self.L = args.layers or (24 if cfg.E <= 32 else 36)
+        t0 = time.time()
+        self.inp = synth.make_inputs(cfg, T0)
+        log(f"generated {cfg.name} T={T0} in {time.time() - t0:.1f}s")
+        inp = self.inp
+        base_w1 = moe.MXFP4Weight(self.u8(inp.w1_codes), self.u8(inp.w1_scales), self.bf16(inp.w1_bias))
+        base_w2 = moe.MXFP4Weight(self.u8(inp.w2_codes), self.u8(inp.w2_scales), self.bf16(inp.w2_bias))
+        if args.layout == "tiled":  # one-time load-time conversion, outside the timed region
+            base_w1, base_w2 = moe.moe_mxfp4_pack(base_w1), moe.moe_mxfp4_pack(base_w2)
+        self.base_rt = moe.Router(torch.from_numpy(inp.router_w).to(dev), torch.from_numpy(inp.router_b).to(dev))
+        self.layers = [(self.base_rt, base_w1, base_w2)]
+
+        def clone(w):
+            return moe.MXFP4Weight(w.codes.clone(), w.scales.clone(), w.bias.clone(), w.layout, w.shape_nk)
+        for _ in range(self.L - 1):  # device-side copies at distinct addresses
+            self.layers.append((moe.Router(self.base_rt.weight.clone(), self.base_rt.bias.clone()), clone(base_w1),
+                                clone(base_w2)))
+        gb = self.L * sum(t.numel() for t in (base_w1.codes, base_w1.scales, base_w2.codes, base_w2.scales)) / 1e9
+        log(f"{self.L} layer copies resident ({gb:.1f} GB)")
+        H, I = cfg.H, cfg.I
+        self.expert_bytes = 2 * I * EXPERT_BYTES_PER_ROW(H) + H * EXPERT_BYTES_PER_ROW(I)
+
+    def u8(self, a):
+        return self.torch.from_numpy(np.ascontiguousarray(a)).to(self.dev)
+
+    def bf16(self, a):
+        return self.torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).to(self.dev).view(self.torch.bfloat16)
+
+    def batch(self, T, x_np=None, block=False, norm_scale=None):
+        """Device buffers of one batch of T tokens (x from the workload's generator unless given)."""
+        torch, moe, cfg, dev = self.torch, self.moe, self.cfg, self.dev
+        H, I, E, k = cfg.H, cfg.I, cfg.E, cfg.k
+        x = self.bf16(self.synth.make_x(cfg, T) if x_np is None else x_np)
+        b = {"T": T, "x": x, "ws": moe.workspace(T, E, k, H, I, self.args.path, device=dev),
+             "out": torch.empty((T, H), dtype=torch.bfloat16, device=dev), "block": block,
+             "norm_scale": norm_scale}
+        # the realised routing (same for every copy); the block routes the normalised rows
+        b["x_layer"] = moe.moe_rmsnorm(x, norm_scale, NORM_EPS) if block else x
+        idx, tw = moe.moe_route(b["x_layer"], self.base_rt, k)
+        b["counts"] = np.bincount(idx.cpu().numpy().ravel(), minlength=E)
+        b["touched"] = int((b["counts"] > 0).sum())
+        b["offsets"], b["sorted_slot"], b["slot_row"] = moe.moe_permute(idx, E)
+        b["y"] = torch.empty((T * k, H), dtype=torch.float32, device=dev)
+        return b
+
+    def step(self, b, i):
+        rt, w1, w2 = self.layers[i % self.L]
+        opts = self.moe.Options(path=self.args.path)
+        if b["block"]:
+            self.moe.moe_block_forward_ex(b["x"], b["norm_scale"], NORM_EPS, rt, w1, w2, self.cfg.k, opts,
+                                          out=b["out"], ws=b["ws"])
+        else:
+            self.moe.moe_forward_ex(b["x"], rt, w1, w2, self.cfg.k, opts, out=b["out"], ws=b["ws"])
+
+    def time_steps(self, b, steps, warmup):
+        """Exactly `warmup` untimed steps, then exactly `steps` timed steps between two events."""
+        torch = self.torch
+        for i in range(warmup):
+            self.step(b, i)
+        torch.cuda.synchronize()
+        ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        ev0.record()
+        for i in range(steps):
+            self.step(b, i)
+        ev1.record()
+        torch.cuda.synchronize()
+        return ev0.elapsed_time(ev1) / steps
+
+    def ffn_roofline(self, b):
+        """The dominant step, the expert FFN (moe_mxfp4_ffn: gate_up + down, plus the gather on
+        the grouped-GEMM paths), timed with events around back-to-back calls over the rotated
+        copies (the routing is the same for every copy, so it is computed once)."""
+        cfg, moe, T = self.cfg, self.moe, b["T"]
+        H, I, E, k = cfg.H, cfg.I, cfg.E, cfg.k
+        opts = moe.Options(path=self.args.path)
+
+        def call(i):
+            _, w1, w2 = self.layers[i % self.L]
+            moe.moe_mxfp4_ffn(b["x_layer"], k, E, b["offsets"], b["sorted_slot"], w1, w2, opts, y=b["y"], ws=b["ws"])
+        ffn_ms, calls = event_time(self.torch, call)
+        ffn_bytes = b["touched"] * self.expert_bytes + T * H * 2
+        ffn_flops = 2.0 * T * k * (2 * I * H + H * I)
+        if cfg.name.startswith("decode"):
+            achieved = ffn_bytes / (ffn_ms * 1e-3) / 1e9
+            r = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                 "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": stored_traffic(cfg.name, T)}
+        else:
+            # The metric's prefill figure is the fraction of the MXFP4 MFMA peak (10.1 PFLOP/s dense).
+            # The bf16 MFMA peak (2.5 PFLOP/s) is the ceiling of exact bf16 activations and is
+            # reported alongside, as is the two-term activation path's own ceiling.
+            achieved = ffn_flops / (ffn_ms * 1e-3) / 1e12
+            r = {"bound": "mfma", "achieved": round(achieved, 1), "peak": MXFP4_PEAK_TFLOPS, "unit": "TFLOP/s",
+                 "frac": round(achieved / MXFP4_PEAK_TFLOPS, 4), "traffic": stored_traffic(cfg.name, T),
+                 "frac_of_bf16_peak": round(achieved / BF16_PEAK_TFLOPS, 4),
+                 "path_ceiling": path_ceiling(self.args.path)}
+        r.update({"kernel": "moe_mxfp4_ffn (gate_up + down)", "ms_per_launch": round(ffn_ms, 5),
+                  "timed_calls": calls, "algorithmic_bytes": int(ffn_bytes), "algorithmic_flops": ffn_flops})
+        self.log(f"{cfg.name} T={T} ffn: {ffn_ms * 1e3:.1f} us over {calls} calls, {r['achieved']} {r['unit']} "
+                 f"({r['frac']:.1%})")
+        return r
+
+    def layer_bytes(self, b):
+        cfg = self.cfg
+        T, H, E, k = b["T"], cfg.H, cfg.E, cfg.k
+        return b["touched"] * self.expert_bytes + E * H * 4 + E * 4 + T * H * 4 + T * k * 8
+
+    def free(self):
+        self.layers = []
+        self.torch.cuda.synchronize()
+        self.torch.cuda.empty_cache()
+
+
+def path_ceiling(path):
+    """The MFMA ceiling of the prefill kernel family, in algorithmic flops."""
+    if path in (0, 3):
+        return {"tflops": 2500.0, "basis": "FP8xFP4 scaled MFMA 5.0 PFLOP/s / 2 (two exact E4M3 terms per bf16 "
+                                           "activation)"}
+    return {"tflops": BF16_PEAK_TFLOPS, "basis": "bf16 MFMA 2.5 PFLOP/s"}
+
+
 def main():
     args = parse()
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -175,160 +353,50 @@ def main():
     if args.workload == "attn_decode":
         attn_main(args, torch, synth, moe, dev)
         return
-    cfg = synth.get_config(args.workload)
-    T = args.T or cfg.T_list[-1]
-    L = args.layers or (24 if cfg.E <= 32 else 36)
-    H, I, E, k = cfg.H, cfg.I, cfg.E, cfg.k
 
     def log(msg):
         print(f"[bench] {msg}", file=sys.stderr, flush=True)
 
-    t0 = time.time()
-    inp = synth.make_inputs(cfg, T)
-    log(f"generated {cfg.name} T={T} in {time.time() - t0:.1f}s")
-
-    def u8(a):
-        return torch.from_numpy(np.ascontiguousarray(a)).to(dev)
-
-    def bf16(a):
-        return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).to(dev).view(torch.bfloat16)
-
-    base_w1 = moe.MXFP4Weight(u8(inp.w1_codes), u8(inp.w1_scales), bf16(inp.w1_bias))
-    base_w2 = moe.MXFP4Weight(u8(inp.w2_codes), u8(inp.w2_scales), bf16(inp.w2_bias))
-    if args.layout == "tiled":  # one-time load-time conversion, outside the timed region
-        base_w1, base_w2 = moe.moe_mxfp4_pack(base_w1), moe.moe_mxfp4_pack(base_w2)
-    base_rt = moe.Router(torch.from_numpy(inp.router_w).to(dev), torch.from_numpy(inp.router_b).to(dev))
-    layers = [(base_rt, base_w1, base_w2)]
-    def clone(w):
-        return moe.MXFP4Weight(w.codes.clone(), w.scales.clone(), w.bias.clone(), w.layout, w.shape_nk)
-
-    for _ in range(L - 1):  # device-side copies at distinct addresses
-        layers.append((moe.Router(base_rt.weight.clone(), base_rt.bias.clone()), clone(base_w1), clone(base_w2)))
-    x = bf16(inp.x)
+    cfg = synth.get_config(args.workload)
+    T = args.T or cfg.T_list[-1]
+    H, I, E, k = cfg.H, cfg.I, cfg.E, cfg.k
+    lb = LayerBench(args, torch, synth, moe, dev, cfg, T, log)
+    inp = lb.inp
+    norm_scale_np = None
     if args.block:  # the block's input: the residual stream, normalised inside the timed step
-        x = bf16(synth.make_block_x(cfg, T))
         inp.x = synth.make_block_x(cfg, T)
         norm_scale_np = synth.make_norm_scale(cfg)
-        norm_scale = torch.from_numpy(norm_scale_np).to(dev)
-    opts = moe.Options(path=args.path)
-    ws = moe.workspace(T, E, k, H, I, args.path, device=dev)
-    out = torch.empty((T, H), dtype=torch.bfloat16, device=dev)
-    torch.cuda.synchronize()
-    log(f"{L} layer copies resident ({L * (base_w1.codes.numel() + base_w1.scales.numel() + base_w2.codes.numel() + base_w2.scales.numel()) / 1e9:.1f} GB)")
-
-    # realised routing of this batch (same for every copy); the block routes the normalised rows
-    x_layer = moe.moe_rmsnorm(x, norm_scale, NORM_EPS) if args.block else x
-    idx, _ = moe.moe_route(x_layer, base_rt, k)
-    counts = np.bincount(idx.cpu().numpy().ravel(), minlength=E)
-    touched = int((counts > 0).sum())
-
-    def step(i):
-        rt, w1, w2 = layers[i % L]
-        if args.block:
-            moe.moe_block_forward_ex(x, norm_scale, NORM_EPS, rt, w1, w2, k, opts, out=out, ws=ws)
-        else:
-            moe.moe_forward_ex(x, rt, w1, w2, k, opts, out=out, ws=ws)
-
-    def timed_steps(n, warm):
-        for i in range(warm):
-            step(i)
-        torch.cuda.synchronize()
-        ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        ev0.record()
-        for i in range(n):
-            step(i)
-        ev1.record()
-        torch.cuda.synchronize()
-        return ev0.elapsed_time(ev1) / n  # ms per step
-
-    ms = timed_steps(args.steps, args.warmup)
-    tok_s = T / (ms * 1e-3)
-    log(f"T={T}: {ms * 1e3:.1f} us/step, {tok_s:.0f} tok/s, touched {touched}/{E}")
-
-    # ---- dominant step: the expert FFN (gate_up + down), timed with events on its stream. The
-    # routing is the same for every weight copy (same router, same x), so it is computed once
-    # and n_ffn FFN calls run back to back between two events (no event or routing kernel
-    # between the timed calls).
-    offsets = torch.empty(E + 1, dtype=torch.int32, device=dev)
-    sorted_slot = torch.empty(T * k, dtype=torch.int32, device=dev)
-    slot_row = torch.empty(T * k, dtype=torch.int32, device=dev)
-    y = torch.empty((T * k, H), dtype=torch.float32, device=dev)
-    tw = torch.empty((T, k), dtype=torch.float32, device=dev)
-    ti = torch.empty((T, k), dtype=torch.int32, device=dev)
-    moe.moe_route(x_layer, base_rt, k, topk_idx=ti, topk_w=tw, ws=ws)
-    moe.moe_permute(ti, E, out=(offsets, sorted_slot, slot_row))
-    n_ffn = max(20, min(args.steps, 200))
-    ev_a, ev_b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    for rep in range(2):  # first pass warms up
-        torch.cuda.synchronize()
-        if rep:
-            ev_a.record()
-        for i in range(n_ffn):
-            _, w1, w2 = layers[i % L]
-            moe.moe_mxfp4_ffn(x_layer, k, E, offsets, sorted_slot, w1, w2, opts, y=y, ws=ws)
-        if rep:
-            ev_b.record()
-        torch.cuda.synchronize()
-    ffn_ms = ev_a.elapsed_time(ev_b) / n_ffn
-
-    expert_bytes = 2 * I * EXPERT_BYTES_PER_ROW(H) + H * EXPERT_BYTES_PER_ROW(I)
-    ffn_bytes = touched * expert_bytes + T * H * 2
-    ffn_flops = 2.0 * T * k * (2 * I * H + H * I)
-    decode_like = cfg.name.startswith("decode")
-    if decode_like:
-        achieved = ffn_bytes / (ffn_ms * 1e-3) / 1e9
-        roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                    "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": stored_traffic(cfg.name, T)}
+        b = lb.batch(T, inp.x, block=True, norm_scale=torch.from_numpy(norm_scale_np).to(dev))
     else:
-        # Both grouped-GEMM paths do the algorithmic flops at a 2.5 PFLOP/s ceiling: the bf16 one
-        # on the bf16 MFMA; the block-scaled one on the FP8xFP4 scaled MFMA (5.0 PFLOP/s) with two
-        # E4M3 terms per bf16 activation, i.e. two instruction flops per algorithmic flop.
-        mx = args.path in (0, 3)
-        basis = ("FP8xFP4 scaled MFMA 5.0 PFLOP/s / 2 (two E4M3 terms per bf16 activation)" if mx
-                 else "bf16 MFMA 2.5 PFLOP/s")
-        achieved = ffn_flops / (ffn_ms * 1e-3) / 1e12
-        roofline = {"bound": "mfma", "achieved": round(achieved, 1), "peak": BF16_PEAK_TFLOPS,
-                    "unit": "TFLOP/s", "frac": round(achieved / BF16_PEAK_TFLOPS, 4),
-                    "traffic": stored_traffic(cfg.name, T), "peak_basis": basis,
-                    "frac_of_mxfp4_peak": round(achieved / MXFP4_PEAK_TFLOPS, 4)}
-    roofline.update({"kernel": "moe_mxfp4_ffn (gate_up + down)", "ms_per_launch": round(ffn_ms, 5),
-                     "algorithmic_bytes": int(ffn_bytes), "algorithmic_flops": ffn_flops})
-    log(f"ffn: {ffn_ms * 1e3:.1f} us, {roofline['achieved']} {roofline['unit']} ({roofline['frac']:.1%})")
+        b = lb.batch(T, inp.x)
+    ms = lb.time_steps(b, args.steps, args.warmup)
+    tok_s = T / (ms * 1e-3)
+    log(f"T={T}: {ms * 1e3:.1f} us/step, {tok_s:.0f} tok/s, touched {b['touched']}/{E}")
+    roofline = lb.ffn_roofline(b)
+    decode_like = cfg.name.startswith("decode")
 
     sweep = []
     if not args.no_sweep and decode_like and not args.block:
         for Ts in cfg.T_list:
             if Ts == T:
                 continue
-            xs = bf16(synth.make_x(cfg, Ts))
-            wss = moe.workspace(Ts, E, k, H, I, args.path, device=dev)
-            outs = torch.empty((Ts, H), dtype=torch.bfloat16, device=dev)
-            ids, _ = moe.moe_route(xs, base_rt, k)
-            tch = int((np.bincount(ids.cpu().numpy().ravel(), minlength=E) > 0).sum())
-
-            def step_s(i):
-                rt, w1, w2 = layers[i % L]
-                moe.moe_forward_ex(xs, rt, w1, w2, k, opts, out=outs, ws=wss)
-            for i in range(args.warmup):
-                step_s(i)
-            torch.cuda.synchronize()
-            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-            a.record()
-            for i in range(args.steps):
-                step_s(i)
-            b.record()
-            torch.cuda.synchronize()
-            ms_s = a.elapsed_time(b) / args.steps
-            layer_bytes = tch * expert_bytes + E * H * 4 + E * 4 + Ts * H * 4 + Ts * k * 8
+            bs = lb.batch(Ts)
+            ms_s = lb.time_steps(bs, args.steps, args.warmup)
+            gbps = lb.layer_bytes(bs) / (ms_s * 1e-3) / 1e9
+            rs = lb.ffn_roofline(bs)
             sweep.append({"T": Ts, "ms_per_step": round(ms_s, 5), "tokens_per_s": round(Ts / (ms_s * 1e-3), 1),
-                          "touched_experts": tch, "layer_GBps": round(layer_bytes / (ms_s * 1e-3) / 1e9, 1)})
-            log(f"sweep T={Ts}: {ms_s * 1e3:.1f} us/step, touched {tch}")
+                          "touched_experts": bs["touched"], "layer_GBps": round(gbps, 1),
+                          "layer_frac_of_hbm_peak": round(gbps / HBM_PEAK_GBS, 4),
+                          "ffn_ms_per_launch": rs["ms_per_launch"], "ffn_GBps": rs["achieved"],
+                          "ffn_frac_of_hbm_peak": rs["frac"]})
+            log(f"sweep T={Ts}: {ms_s * 1e3:.1f} us/step, touched {bs['touched']}, layer {gbps:.0f} GB/s")
 
     cpu = None
     if not args.no_cpu_baseline:
-        cpu = cpu_baseline(cfg, inp, T, log, norm_scale_np if args.block else None)
+        cpu = cpu_baseline(cfg, inp, T, log, norm_scale_np)
 
-    layer_bytes = touched * expert_bytes + E * H * 4 + E * 4 + T * H * 4 + T * k * 8
+    layer_bytes = lb.layer_bytes(b)
+    counts = b["counts"]
     line = {
         "metric": METRIC,
         "value": round(tok_s, 1),
@@ -344,8 +412,8 @@ def main():
         "data": "synthetic",
         "config": {"workload": cfg.name, "T": T, "E": E, "k": k, "hidden": H, "expert_width": I,
                    "weights": "MXFP4 (E2M1 + E8M0 per 32)", "weight_layout": args.layout,
-                   "layers_rotated": L, "path": args.path,
-                   "touched_experts": touched, "per_expert_slots_min_max": [int(counts.min()), int(counts.max())],
+                   "layers_rotated": lb.L, "path": args.path,
+                   "touched_experts": b["touched"], "per_expert_slots_min_max": [int(counts.min()), int(counts.max())],
                    "layer_GBps": round(layer_bytes / (ms * 1e-3) / 1e9, 1)},
         "roofline": roofline,
         "cpu_baseline": cpu,
@@ -354,6 +422,22 @@ def main():
         line["config"]["block"] = f"x + layer(RMSNorm(x)), eps {NORM_EPS:g}"
     if sweep:
         line["sweep"] = sweep
+    # the metric's other half: the 4096-token prefill of the 20b-shaped layer, % of the MXFP4 peak
+    if not args.no_prefill and decode_like and not args.block:
+        lb.free()
+        del lb, b
+        pcfg = synth.get_config("prefill20b")
+        pT = pcfg.T_list[-1]
+        plb = LayerBench(args, torch, synth, moe, dev, pcfg, pT, log)
+        pb = plb.batch(pT, plb.inp.x)
+        pms = plb.time_steps(pb, args.steps, args.warmup)
+        log(f"prefill20b T={pT}: {pms * 1e3:.1f} us/step, {pT / (pms * 1e-3):.0f} tok/s")
+        pc = pb["counts"]
+        line["prefill"] = {"workload": pcfg.name, "T": pT, "E": pcfg.E, "k": pcfg.k, "path": args.path,
+                           "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(pms, 5),
+                           "tokens_per_s": round(pT / (pms * 1e-3), 1), "layers_rotated": plb.L,
+                           "per_expert_slots_min_max": [int(pc.min()), int(pc.max())],
+                           "roofline": plb.ffn_roofline(pb)}
     print(json.dumps(line), flush=True)
 
 
@@ -422,8 +506,9 @@ def attn_main(args, torch, synth, moe, dev):
             dt += time.perf_counter() - t1
             reps += 1
         log(f"oracle: {reps} x {n} sequences in {dt:.1f}s")
+        model, blas = host_description()
         cpu = {"value": round(reps * n / dt, 3), "unit": "tokens/s", "cores": threads, "kind": "oracle",
-               "sample": f"first {n} of the {B} sequences, {reps} repetitions, fp64 numpy decode attention; {dt:.1f} s"}
+               "cpu_model": model, "blas": blas, "sample": f"first {n} of the {B} sequences, {reps} repetitions, fp64 numpy decode attention; {dt:.1f} s"}
     line = {
         "metric": "decode attention tokens/s (one new token per sequence)",
         "value": round(B / (ms * 1e-3), 1), "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
@@ -456,7 +541,9 @@ def cpu_baseline(cfg, inp, T, log, norm_scale=None, min_seconds=10.0, max_reps=1
         dt += time.perf_counter() - t0
         reps += 1
     log(f"oracle: {reps} x {n} tokens in {dt:.1f}s on {threads} threads")
+    model, blas = host_description()
     return {"value": round(reps * n / dt, 3), "unit": "tokens/s", "cores": threads, "kind": "oracle",
+            "cpu_model": model, "blas": blas,
             "sample": f"first {n} of the {T} tokens, {reps} repetitions, full {'block' if norm_scale is not None else 'layer'} in fp64 numpy (router, "
                       f"top-{cfg.k}, per-expert MXFP4 decode, FFN, combine); {dt:.1f} s"}
 

@@ -212,10 +212,12 @@ int moe_combine(const float *y, const int32_t *slot_row, const float *topk_w, in
 
 /*
  * The whole layer: route, permute, expert FFNs, combine; out bf16 [T][H].
- * Uses a workspace owned by the library, one per device, grown on demand and kept until
- * moe_release_workspace() or process exit; growing it synchronises `stream` and calls
- * hipMalloc. Calls that share a device and run concurrently from several host threads
- * must use moe_forward_ex with their own workspaces instead.
+ * Uses a workspace owned by the library, one per (device, stream), grown on demand and kept
+ * until moe_release_workspace() or process exit; growing it synchronises `stream` and calls
+ * hipMalloc. Calls on different streams use different workspaces; calls on one stream are
+ * ordered by that stream. Concurrent calls from several host threads are safe (a mutex guards
+ * the table of workspaces), but callers that cannot afford the first call's allocation, or
+ * that capture the call in a HIP graph, use moe_forward_ex with their own workspace.
  */
 int moe_forward(const uint16_t *x, const moe_router_t *router, const moe_mxfp4_weight_t *w_gate_up,
                 const moe_mxfp4_weight_t *w_down, int64_t T, int32_t E, int32_t k, uint16_t *out,
@@ -289,7 +291,8 @@ int moe_attn_decode(const uint16_t *q, const uint16_t *k_cache, const uint16_t *
                     int64_t max_len, int32_t window, void *out, int32_t out_dtype, void *ws, size_t ws_bytes,
                     moe_stream_t stream);
 
-/* Free moe_forward's workspace on the current device (synchronises the device). */
+/* Free moe_forward's workspaces (every stream's) on the current device (synchronises the
+ * device first). */
 int moe_release_workspace(void);
 
 #ifdef __cplusplus

@@ -17,8 +17,8 @@ What it computes, and where each step comes from:
   - [OCP-MX] OCP Microscaling Formats (MX) Specification v1.0 -- the public definition of
     the MXFP4 element (E2M1) and scale (E8M0) encodings; the pages only name the format.
 * Every floating-point step runs in float64 on exact inputs (bf16 and fp32 inputs widen
-  exactly). The one place floating point decides an integer -- which experts a token
-  picks -- is decided on logits rounded to float32, the precision the GPU router works in.
+  exactly), including the one place floating point decides an integer: which experts a
+  token picks is decided on the float64 logits.
 """
 from __future__ import annotations
 
@@ -104,10 +104,10 @@ def topk_select(logits: np.ndarray, k: int) -> np.ndarray:
 
     The pages do not say how ties break or in which order the k experts are listed. Reading
     taken: ties go to the lower expert id, and the list is in descending score order. The
-    choice is made on the scores rounded to float32 (the GPU router's precision).
+    ranking is the plain one of the float64 scores.
     """
-    l32 = np.asarray(logits).astype(np.float32)
-    order = np.argsort(-l32, axis=-1, kind="stable")  # stable: equal scores keep id order
+    lg = np.asarray(logits, np.float64)
+    order = np.argsort(-lg, axis=-1, kind="stable")  # stable: equal scores keep id order
     return order[..., :k].astype(np.int32)
 
 

@@ -5,7 +5,8 @@
 #include <cmath>
 #include <mutex>
 #include <new>
-#include <unordered_map>
+#include <map>
+#include <utility>
 
 #include "kernels.h"
 #include "moe_mxfp4.h"
@@ -256,8 +257,10 @@ struct OwnedWorkspace {
   void *ptr = nullptr;
   size_t bytes = 0;
 };
+// moe_forward's workspaces, one per (device, stream): calls on different streams never share
+// one, so they do not race; calls on one stream are ordered by the stream itself.
 std::mutex g_ws_mutex;
-std::unordered_map<int, OwnedWorkspace> g_ws;
+std::map<std::pair<int, uintptr_t>, OwnedWorkspace> g_ws;
 
 }  // namespace
 
@@ -525,7 +528,7 @@ int moe_forward(const uint16_t *x, const moe_router_t *router, const moe_mxfp4_w
   void *ws = nullptr;
   {
     std::lock_guard<std::mutex> lock(g_ws_mutex);
-    OwnedWorkspace &w = g_ws[dev];
+    OwnedWorkspace &w = g_ws[{dev, reinterpret_cast<uintptr_t>(s)}];
     if (w.bytes < L.total) {
       if (w.ptr != nullptr) {
         if (hipStreamSynchronize(s) != hipSuccess) return MOE_ERR_HIP;
@@ -551,11 +554,22 @@ int moe_release_workspace(void) {
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess) return MOE_ERR_HIP;
   std::lock_guard<std::mutex> lock(g_ws_mutex);
-  auto it = g_ws.find(dev);
-  if (it == g_ws.end() || it->second.ptr == nullptr) return MOE_OK;
-  if (hipDeviceSynchronize() != hipSuccess) return MOE_ERR_HIP;
-  const hipError_t err = hipFree(it->second.ptr);
-  g_ws.erase(it);
+  bool synced = false;
+  hipError_t err = hipSuccess;
+  for (auto it = g_ws.begin(); it != g_ws.end();) {
+    if (it->first.first != dev) {
+      ++it;
+      continue;
+    }
+    if (it->second.ptr != nullptr) {
+      if (!synced) {
+        if (hipDeviceSynchronize() != hipSuccess) return MOE_ERR_HIP;
+        synced = true;
+      }
+      if (hipFree(it->second.ptr) != hipSuccess) err = hipErrorInvalidValue;
+    }
+    it = g_ws.erase(it);
+  }
   return err == hipSuccess ? MOE_OK : MOE_ERR_HIP;
   MOE_GUARD_END
 }

@@ -76,6 +76,17 @@ def _stream(stream: Optional[torch.cuda.Stream]) -> int:
     return s.cuda_stream
 
 
+def _empty(shape, dtype, device, stream: Optional[torch.cuda.Stream]) -> torch.Tensor:
+    """A new device tensor allocated on the stream the library will launch on. torch's caching
+    allocator ties a block to the stream it was allocated on: a temporary allocated on another
+    stream and freed when the call returns could be handed to that stream's next work while the
+    library's kernels, queued on `stream`, still use it."""
+    if stream is None:
+        return torch.empty(shape, dtype=dtype, device=device)
+    with torch.cuda.stream(stream):
+        return torch.empty(shape, dtype=dtype, device=device)
+
+
 def abi_version() -> int:
     return int(L.lib().moe_abi_version())
 
@@ -85,13 +96,13 @@ def moe_workspace_size(T: int, E: int, k: int, H: int, I: int, path: int = L.MOE
 
 
 def workspace(T: int, E: int, k: int, H: int, I: int, path: int = L.MOE_PATH_AUTO,
-              device=None) -> torch.Tensor:
+              device=None, stream=None) -> torch.Tensor:
     """A caller-owned workspace tensor of the size the library asks for (torch's allocator
-    returns 256-byte aligned blocks)."""
+    returns 256-byte aligned blocks), allocated on `stream` (None: the current stream)."""
     n = moe_workspace_size(T, E, k, H, I, path)
     if n == 0:
         raise ValueError("invalid sizes for a workspace")
-    return torch.empty(n, dtype=torch.uint8, device=device or "cuda")
+    return _empty(n, torch.uint8, device or "cuda", stream)
 
 
 def moe_mxfp4_tiled_bytes(E: int, n: int, k: int) -> Tuple[int, int]:
@@ -104,8 +115,8 @@ def moe_mxfp4_pack(w: MXFP4Weight, stream=None) -> MXFP4Weight:
     """A tiled copy of a row-major weight (new device buffers; the bias tensor is shared)."""
     E = int(w.codes.shape[0])
     cb, sb = moe_mxfp4_tiled_bytes(E, w.n, w.k)
-    codes = torch.empty(cb, dtype=torch.uint8, device=w.codes.device)
-    scales = torch.empty(sb, dtype=torch.uint8, device=w.codes.device)
+    codes = _empty(cb, torch.uint8, w.codes.device, stream)
+    scales = _empty(sb, torch.uint8, w.codes.device, stream)
     d = w.desc()
     L.check("moe_mxfp4_pack", L.lib().moe_mxfp4_pack(ctypes.byref(d), E, _ptr(codes), _ptr(scales),
                                                         _stream(stream)))
@@ -116,7 +127,7 @@ def moe_mxfp4_dequant(codes: torch.Tensor, scales: torch.Tensor, out: Optional[t
                       stream=None) -> torch.Tensor:
     n = codes.numel() * 2
     if out is None:
-        out = torch.empty(n, dtype=torch.float32, device=codes.device)
+        out = _empty(n, torch.float32, codes.device, stream)
     L.check("moe_mxfp4_dequant", L.lib().moe_mxfp4_dequant(_ptr(codes), _ptr(scales), n, _ptr(out),
                                                               _stream(stream)))
     return out
@@ -127,11 +138,11 @@ def moe_route(x: torch.Tensor, router: Router, k: int, topk_idx=None, topk_w=Non
     T, H = x.shape
     E = int(router.weight.shape[0])
     if topk_idx is None:
-        topk_idx = torch.empty((T, k), dtype=torch.int32, device=x.device)
+        topk_idx = _empty((T, k), torch.int32, x.device, stream)
     if topk_w is None:
-        topk_w = torch.empty((T, k), dtype=torch.float32, device=x.device)
+        topk_w = _empty((T, k), torch.float32, x.device, stream)
     if ws is None:
-        ws = workspace(T, E, k, H, H, device=x.device)
+        ws = workspace(T, E, k, H, H, device=x.device, stream=stream)
     r = router.desc()
     L.check("moe_route", L.lib().moe_route(_ptr(x), T, H, ctypes.byref(r), E, k, _ptr(topk_idx),
                                               _ptr(topk_w), _ptr(ws), ws.numel(), _stream(stream)))
@@ -145,9 +156,8 @@ def moe_permute(topk_idx: torch.Tensor, E: int, out=None, ws=None, stream=None
     T, k = topk_idx.shape
     dev = topk_idx.device
     if out is None:
-        out = (torch.empty(E + 1, dtype=torch.int32, device=dev),
-               torch.empty(T * k, dtype=torch.int32, device=dev),
-               torch.empty(T * k, dtype=torch.int32, device=dev))
+        out = (_empty(E + 1, torch.int32, dev, stream), _empty(T * k, torch.int32, dev, stream),
+               _empty(T * k, torch.int32, dev, stream))
     offsets, sorted_slot, slot_row = out
     L.check("moe_permute", L.lib().moe_permute(_ptr(topk_idx), T, E, k, _ptr(offsets), _ptr(sorted_slot),
                                                   _ptr(slot_row), _ptr(ws), 0 if ws is None else ws.numel(),
@@ -163,9 +173,9 @@ def moe_mxfp4_ffn(x: torch.Tensor, k: int, E: int, expert_offsets: torch.Tensor,
     o = opts or Options()
     width = {L.MOE_FLAG_EMIT_PREACT: 2 * I, L.MOE_FLAG_EMIT_ACT: I}.get(o.flags, H)
     if y is None:
-        y = torch.empty((T * k, width), dtype=torch.float32, device=x.device)
+        y = _empty((T * k, width), torch.float32, x.device, stream)
     if ws is None:
-        ws = workspace(T, E, k, H, I, o.path, device=x.device)
+        ws = workspace(T, E, k, H, I, o.path, device=x.device, stream=stream)
     g, d, od = gate_up.desc(), down.desc(), o.desc()
     L.check("moe_mxfp4_ffn", L.lib().moe_mxfp4_ffn(
         _ptr(x), T, k, E, _ptr(expert_offsets), _ptr(sorted_slot), ctypes.byref(g), ctypes.byref(d),
@@ -180,7 +190,7 @@ def moe_combine(y: torch.Tensor, slot_row: torch.Tensor, topk_w: torch.Tensor,
     H = int(y.shape[1])
     if out is None:
         dt = torch.bfloat16 if out_dtype == L.MOE_DTYPE_BF16 else torch.float32
-        out = torch.empty((T, H), dtype=dt, device=y.device)
+        out = _empty((T, H), dt, y.device, stream)
     L.check("moe_combine", L.lib().moe_combine(_ptr(y), _ptr(slot_row), _ptr(topk_w), T, k, H, _ptr(out),
                                                   out_dtype, _stream(stream)))
     return out
@@ -191,7 +201,7 @@ def moe_forward(x: torch.Tensor, router: Router, w_gate_up: MXFP4Weight, w_down:
     T, H = x.shape
     E = int(router.weight.shape[0])
     if out is None:
-        out = torch.empty((T, H), dtype=torch.bfloat16, device=x.device)
+        out = _empty((T, H), torch.bfloat16, x.device, stream)
     r, g, d = router.desc(), w_gate_up.desc(), w_down.desc()
     L.check("moe_forward", L.lib().moe_forward(_ptr(x), ctypes.byref(r), ctypes.byref(g), ctypes.byref(d),
                                                   T, E, k, _ptr(out), _stream(stream)))
@@ -206,9 +216,9 @@ def moe_forward_ex(x: torch.Tensor, router: Router, w_gate_up: MXFP4Weight, w_do
     o = opts or Options()
     if out is None:
         dt = torch.bfloat16 if o.out_dtype == L.MOE_DTYPE_BF16 else torch.float32
-        out = torch.empty((T, H), dtype=dt, device=x.device)
+        out = _empty((T, H), dt, x.device, stream)
     if ws is None:
-        ws = workspace(T, E, k, H, w_down.k, o.path, device=x.device)
+        ws = workspace(T, E, k, H, w_down.k, o.path, device=x.device, stream=stream)
     r, g, d, od = router.desc(), w_gate_up.desc(), w_down.desc(), o.desc()
     L.check("moe_forward_ex", L.lib().moe_forward_ex(
         _ptr(x), ctypes.byref(r), ctypes.byref(g), ctypes.byref(d), T, E, k, ctypes.byref(od), _ptr(out),
@@ -221,7 +231,7 @@ def moe_rmsnorm(x: torch.Tensor, scale: torch.Tensor, eps: float = 1e-5, out: Op
     """bf16(x / sqrt(mean(x^2) + eps) * scale) per row; x bf16 [T][H], scale fp32 [H]."""
     T, H = x.shape
     if out is None:
-        out = torch.empty((T, H), dtype=torch.bfloat16, device=x.device)
+        out = _empty((T, H), torch.bfloat16, x.device, stream)
     L.check("moe_rmsnorm", L.lib().moe_rmsnorm(_ptr(x), T, H, _ptr(scale), float(eps), _ptr(out),
                                                   _stream(stream)))
     return out
@@ -236,9 +246,9 @@ def moe_block_forward_ex(x: torch.Tensor, norm_scale: torch.Tensor, norm_eps: fl
     o = opts or Options()
     if out is None:
         dt = torch.bfloat16 if o.out_dtype == L.MOE_DTYPE_BF16 else torch.float32
-        out = torch.empty((T, H), dtype=dt, device=x.device)
+        out = _empty((T, H), dt, x.device, stream)
     if ws is None:
-        ws = workspace(T, E, k, H, w_down.k, o.path, device=x.device)
+        ws = workspace(T, E, k, H, w_down.k, o.path, device=x.device, stream=stream)
     r, g, d, od = router.desc(), w_gate_up.desc(), w_down.desc(), o.desc()
     L.check("moe_block_forward_ex", L.lib().moe_block_forward_ex(
         _ptr(x), _ptr(norm_scale), float(norm_eps), ctypes.byref(r), ctypes.byref(g), ctypes.byref(d), T, E, k,
@@ -256,10 +266,9 @@ def moe_attn_decode(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tenso
     Hkv, Lmax = int(k_cache.shape[1]), int(k_cache.shape[2])
     if out is None:
         dt = torch.bfloat16 if out_dtype == L.MOE_DTYPE_BF16 else torch.float32
-        out = torch.empty((B, Hq, D), dtype=dt, device=q.device)
+        out = _empty((B, Hq, D), dt, q.device, stream)
     if ws is None:
-        ws = torch.empty(int(L.lib().moe_attn_workspace_size(B, Hkv, Lmax, window)), dtype=torch.uint8,
-                         device=q.device)
+        ws = _empty(int(L.lib().moe_attn_workspace_size(B, Hkv, Lmax, window)), torch.uint8, q.device, stream)
     L.check("moe_attn_decode", L.lib().moe_attn_decode(
         _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(lens), _ptr(sinks), B, Hq, Hkv, D, Lmax, window, _ptr(out),
         out_dtype, _ptr(ws), ws.numel(), _stream(stream)))

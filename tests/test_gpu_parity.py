@@ -5,7 +5,9 @@ k-th and (k+1)-th fp64 logits differ by < 1e-3 (those must still be a valid choi
 routing weights within 1e-5; layer outputs within 2e-2 x RMS of the oracle output (plus half
 a bf16 ulp of the oracle value when the output is bf16).
 """
+import os
 import sys
+import time
 
 import numpy as np
 import pytest
@@ -234,19 +236,23 @@ def _gpu_idx(dev):
     return idx.cpu().numpy()
 
 
-def _check_layer(inp, tokens=None, path=0, tiled=True):
-    dev = gu.device_layer(inp, tiled=tiled)
-    gidx = _gpu_idx(dev)
-    ref = gu.oracle_forward(inp, gidx, tokens=tokens)
+def _check_layer(inp, tokens=None, path=0, tiled=True, act_rounded=False, dev=None, ref=None):
+    """The layer on AUTO or a forced kernel family against the oracle, fp32 and bf16 outputs,
+    at max|err| <= 2e-2 x RMS (+ half a bf16 ulp for bf16). act_rounded (degenerate shapes
+    only: one expert, I <= 64) grades against the oracle's layer with its activation rounded
+    to bf16 instead (act_rounded_layer). dev / ref: a device layer and an oracle result
+    already made for these inputs (ref for `tokens`, with the GPU's picks at near-ties)."""
+    dev = dev if dev is not None else gu.device_layer(inp, tiled=tiled)
+    if ref is None:
+        ref = gu.oracle_forward(inp, _gpu_idx(dev), tokens=tokens, keep_intermediates=act_rounded)
     tok = ref.tokens
-    # the activation-rounding allowance, computed only if the 2e-2 x RMS bar fails
-    act_bound = lambda: gu.act_rounding_bound(inp, gu.oracle_forward(inp, gidx, tokens=tok, keep_intermediates=True))
+    want = gu.act_rounded_layer(inp, ref) if act_rounded else ref.out
     out32 = _run_forward(dev, moe.MOE_DTYPE_F32, path).cpu().numpy()
     assert np.isfinite(out32).all()
-    rel32 = gu.check_output(out32[tok], ref.out, bf16=False, act_bound=act_bound)
+    rel32 = gu.check_output(out32[tok], want, bf16=False)
     out16 = gu.bf16_bits(_run_forward(dev, moe.MOE_DTYPE_BF16, path))
     o16 = synth.f32_from_bf16_bits(out16)
-    rel16 = gu.check_output(o16[tok], ref.out, bf16=True, act_bound=act_bound)
+    rel16 = gu.check_output(o16[tok], want, bf16=True)
     # both dtypes sum the same fp32 values: the bf16 output is the fp32 one rounded to nearest
     # even, bit for bit (checks the hardware conversion against the definition)
     assert np.array_equal(out16, synth.bf16_bits_from_f32(out32))
@@ -323,19 +329,70 @@ def test_layer_decode120b_zipf(T):
     _check_layer(synth.make_inputs(cfg, T))
 
 
+_FULL = {}
+
+
+def _full_layer(name):
+    """Inputs, device layer and the oracle over ALL tokens of a prefill workload (near-tied
+    tokens with the GPU's picks). Cached for the tests of one workload at a time: the fp64
+    pass over 4096 or 8192 tokens takes tens of seconds on the host."""
+    if name not in _FULL:
+        _FULL.clear()
+        cfg = synth.get_config(name)
+        inp = synth.make_inputs(cfg)
+        dev = gu.device_layer(inp, tiled=True)
+        gidx = _gpu_idx(dev)
+        t0 = time.perf_counter()
+        ref = gu.oracle_forward(inp, gidx)
+        dt = time.perf_counter() - t0
+        threads = len(os.sched_getaffinity(0)) if hasattr(os, "sched_getaffinity") else os.cpu_count()
+        sys.__stderr__.write(f"[oracle] {name}: all {inp.x.shape[0]} tokens in {dt:.1f} s on {threads} threads\n")
+        sys.__stderr__.flush()
+        _FULL[name] = (inp, dev, gidx, ref)
+    return _FULL[name]
+
+
 @pytest.mark.parametrize("path", [0, 1, 2])
-def test_layer_prefill20b_sampled(path):
-    cfg = synth.get_config("prefill20b")
-    inp = synth.make_inputs(cfg)
-    tokens = np.sort(np.random.default_rng(20).choice(cfg.T_list[-1], 48, replace=False))
-    _check_layer(inp, tokens, path=path)
+def test_layer_prefill20b_full(path):
+    """Every one of the 4096 tokens' outputs (fp32 and bf16) element by element: every m-tile,
+    n-tile and tail tile of the grouped GEMM is compared (path 0 = AUTO, the block-scaled GEMM)."""
+    inp, dev, _, ref = _full_layer("prefill20b")
+    _check_layer(inp, path=path, dev=dev, ref=ref)
 
 
-def test_layer_prefill120b_sampled():
-    cfg = synth.get_config("prefill120b")
-    inp = synth.make_inputs(cfg)
-    tokens = np.sort(np.random.default_rng(120).choice(cfg.T_list[-1], 20, replace=False))
-    _check_layer(inp, tokens)
+@pytest.mark.parametrize("path", [0, 2])
+def test_layer_prefill120b_full(path):
+    inp, dev, _, ref = _full_layer("prefill120b")
+    _check_layer(inp, path=path, dev=dev, ref=ref)
+
+
+@pytest.mark.parametrize("path", [0, 2])
+def test_prefill20b_steps_on_subset(path):
+    """Per-step checks at the full 4096-token launch, graded on a seeded 256-token subset: the
+    pre-activations h = W1 x + b1, the bf16 activation and the down output y of each of the
+    subset's slots, read from the sorted rows the kernels wrote."""
+    inp, dev, gidx, _ = _full_layer("prefill20b")
+    k, E = dev.k, dev.E
+    tokens = np.sort(np.random.default_rng(2560).choice(inp.x.shape[0], 256, replace=False))
+    sub = gu.oracle_forward(inp, gidx, tokens=tokens, keep_intermediates=True)
+    idx, _ = moe.moe_route(dev.x, dev.router, k)
+    off, ss, sr = moe.moe_permute(idx, E)
+    rows = sr.cpu().numpy().reshape(-1, k)[tokens]  # [256][k] sorted row of each slot
+
+    def ffn(flags):
+        return moe.moe_mxfp4_ffn(dev.x, k, E, off, ss, dev.w1, dev.w2,
+                                 moe.Options(flags=flags, path=path)).cpu().numpy()[rows]
+    h = ffn(moe.MOE_FLAG_EMIT_PREACT)
+    # exact products summed in fp32 (the block-scaled MFMA sums a block's products in reduced
+    # internal precision: measured 4.6e-5 of the RMS on these inputs)
+    rms_h = np.sqrt(np.mean(sub.h ** 2))
+    assert np.abs(h - sub.h).max() <= 2e-4 * rms_h, np.abs(h - sub.h).max() / rms_h
+    act = ffn(moe.MOE_FLAG_EMIT_ACT)
+    rms_a = np.sqrt(np.mean(sub.act ** 2))
+    assert (np.abs(act - sub.act) <= 1e-2 * rms_a + gu.bf16_half_ulp(sub.act)).all()
+    y = ffn(0)
+    rms_y = np.sqrt(np.mean(sub.y ** 2))
+    assert np.abs(y - sub.y).max() <= gu.OUT_TOL * rms_y, np.abs(y - sub.y).max() / rms_y
 
 
 # ------------------------------------------------------------------ edge cases
@@ -349,7 +406,11 @@ def _small_cfg(E, k, H=128, I=96, T=24, seed=31, scales=(119, 123)):
                                        (4, 2, 288, 160, 300), (8, 4, 256, 128, 100), (256, 8, 64, 64, 50),
                                        (32, 8, 2880, 2880, 40), (1, 1, 64, 96, 10), (1, 1, 128, 64, 600)])
 def test_layer_shapes(E, k, H, I, T, tiled, path):
-    _check_layer(synth.make_inputs(_small_cfg(E, k, H, I, T)), tiled=tiled, path=path)
+    # one expert with a down projection of at most 64 terms: an output at several times the
+    # RMS whose terms share one sign moves by ~2% of the RMS from the activation's bf16
+    # rounding alone, so that rounding is applied to the reference there (and only there)
+    degenerate = E == 1 and I <= 64
+    _check_layer(synth.make_inputs(_small_cfg(E, k, H, I, T)), tiled=tiled, path=path, act_rounded=degenerate)
 
 
 @pytest.mark.parametrize("tiled,path", [(False, 0), (True, 1), (True, 2), (True, 3)])

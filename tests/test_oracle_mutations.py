@@ -89,12 +89,12 @@ def _swiglu_alpha_ignored(h, limit=7.0, alpha=1.0):
 
 
 def _topk_ascending(logits, k):
-    l32 = np.asarray(logits).astype(np.float32)
+    l32 = np.asarray(logits, np.float64)
     return np.argsort(l32, axis=-1, kind="stable")[..., :k].astype(np.int32)
 
 
 def _topk_high_id_ties(logits, k):
-    l32 = np.asarray(logits).astype(np.float32)
+    l32 = np.asarray(logits, np.float64)
     E = l32.shape[-1]
     order = np.argsort(-l32[..., ::-1], axis=-1, kind="stable")
     return (E - 1 - order[..., :k]).astype(np.int32)

@@ -63,6 +63,12 @@ def parse():
     p.add_argument("--no-sweep", action="store_true")
     p.add_argument("--no-prefill", action="store_true",
                    help="decode workloads: skip the 4096-token prefill20b record added to the line")
+    p.add_argument("--chain", type=int, default=0, metavar="L",
+                   help="multi-layer decode: a step is L chained blocks x <- x + layer_l(RMSNorm_l(x)) over L "
+                        "distinct layers, each router reading the previous block's output")
+    p.add_argument("--prefetch-hot", type=int, default=0, metavar="N",
+                   help="with --chain: at the start of each block, read the layer's N most popular experts' "
+                        "weights (by the previous step's routing) on a side stream while the block routes")
     p.add_argument("--pmc-summary", nargs=4, metavar=("COPY_FETCH", "COPY_WRITE", "FETCH", "WRITE"),
                    help="only print the traffic line for --workload/--T from four rocprofv3 --pmc csv "
                         "output folders (FETCH_SIZE and WRITE_SIZE of --copy-calibration 1024, then of "
@@ -361,6 +367,9 @@ def main():
     T = args.T or cfg.T_list[-1]
     H, I, E, k = cfg.H, cfg.I, cfg.E, cfg.k
     lb = LayerBench(args, torch, synth, moe, dev, cfg, T, log)
+    if args.chain:
+        chain_main(args, torch, synth, moe, dev, cfg, T, lb, log)
+        return
     inp = lb.inp
     norm_scale_np = None
     if args.block:  # the block's input: the residual stream, normalised inside the timed step
@@ -438,6 +447,86 @@ def main():
                            "tokens_per_s": round(pT / (pms * 1e-3), 1), "layers_rotated": plb.L,
                            "per_expert_slots_min_max": [int(pc.min()), int(pc.max())],
                            "roofline": plb.ffn_roofline(pb)}
+    print(json.dumps(line), flush=True)
+
+
+def chain_main(args, torch, synth, moe, dev, cfg, T, lb, log):
+    """L chained blocks per step: x_{l+1} = x_l + layer_l(bf16(RMSNorm_l(x_l))) (moe_block_forward_ex)
+    over L distinct layer copies, so each layer's router reads the previous layer's output and
+    its experts are streamed from HBM (L copies exceed the last-level cache). With
+    --prefetch-hot N, each block first records an event; a side stream waits for it and reads
+    that layer's N most popular experts (counts of the previous step through the same layer)
+    while the block routes, as a test of warming the last-level cache for the expert stream."""
+    L, H, E, k = args.chain, cfg.H, cfg.E, cfg.k
+    if L > lb.L:
+        raise SystemExit(f"--chain {L} needs --layers >= {L}")
+    x0 = lb.bf16(synth.make_block_x(cfg, T))
+    norms = [torch.from_numpy(synth.make_norm_scale(cfg)).to(dev) for _ in range(L)]
+    ws = moe.workspace(T, E, k, H, cfg.I, args.path, device=dev)
+    bufs = [torch.empty_like(x0), torch.empty_like(x0)]
+    opts = moe.Options(path=args.path)
+    side = torch.cuda.Stream()
+    nb = len(lb.layers)
+
+    # the routing each layer sees in the chain (same every step: same inputs), for the hot sets
+    hot, touched = [], []
+    x = x0
+    for l in range(L):
+        rt, w1, w2 = lb.layers[l % nb]
+        xn = moe.moe_rmsnorm(x, norms[l], NORM_EPS)
+        idx, _ = moe.moe_route(xn, rt, k)
+        counts = np.bincount(idx.cpu().numpy().ravel(), minlength=E)
+        touched.append(int((counts > 0).sum()))
+        hot.append([int(e) for e in np.argsort(-counts, kind="stable")[:args.prefetch_hot] if counts[e] > 0])
+        x = moe.moe_block_forward_ex(x, norms[l], NORM_EPS, rt, w1, w2, k, opts, ws=ws)
+    per_e1 = lb.layers[0][1].codes.numel() // E  # tiled gate_up codes per expert (contiguous)
+    per_e2 = lb.layers[0][2].codes.numel() // E
+    sink = torch.zeros(1, dtype=torch.int64, device=dev)
+
+    def prefetch(l):
+        _, w1, w2 = lb.layers[l % nb]
+        with torch.cuda.stream(side):
+            for e in hot[l]:
+                sink.add_(w1.codes[e * per_e1:(e + 1) * per_e1].view(torch.int32).sum(dtype=torch.int64))
+                sink.add_(w2.codes[e * per_e2:(e + 1) * per_e2].view(torch.int32).sum(dtype=torch.int64))
+
+    def step(_):
+        x = x0
+        for l in range(L):
+            rt, w1, w2 = lb.layers[l % nb]
+            if args.prefetch_hot:
+                ev = torch.cuda.Event()
+                ev.record()
+                side.wait_event(ev)
+                prefetch(l)
+            out = bufs[l % 2]
+            moe.moe_block_forward_ex(x, norms[l], NORM_EPS, rt, w1, w2, k, opts, out=out, ws=ws)
+            x = out
+        if args.prefetch_hot:
+            torch.cuda.current_stream().wait_stream(side)
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record()
+    for i in range(args.steps):
+        step(i)
+    b.record()
+    torch.cuda.synchronize()
+    ms = a.elapsed_time(b) / args.steps
+    per_layer = ms / L
+    log(f"chain of {L} blocks, T={T}, prefetch {args.prefetch_hot}: {ms * 1e3:.1f} us/step, "
+        f"{per_layer * 1e3:.1f} us per layer")
+    line = {"metric": "chained MoE blocks tokens/s (one decode step through L layers)",
+            "value": round(T / (ms * 1e-3), 1), "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
+            "warmup": args.warmup, "ms_per_step": round(ms, 5), "higher_is_better": True, "scaling": "weak",
+            "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+            "config": {"workload": cfg.name, "T": T, "E": E, "k": k, "chain_layers": L, "path": args.path,
+                       "prefetch_hot_experts": args.prefetch_hot, "ms_per_layer": round(per_layer, 5),
+                       "layer_tokens_per_s": round(T / (per_layer * 1e-3), 1),
+                       "touched_per_layer": touched},
+            "roofline": None, "cpu_baseline": None}
     print(json.dumps(line), flush=True)
 
 

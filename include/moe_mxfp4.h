@@ -53,17 +53,28 @@ extern "C" {
 #define MOE_DTYPE_BF16 0
 #define MOE_DTYPE_F32 1
 
-/* expert-FFN kernel family */
-#define MOE_PATH_AUTO 0    /* chosen from T*k and E on the host */
-#define MOE_PATH_STREAM 1  /* weight-streaming kernels for decode-sized batches */
-#define MOE_PATH_GEMM 2    /* LDS-tiled grouped GEMM for prefill-sized batches, bf16 activations
-                              times MXFP4 weights decoded to bf16 in registers; needs
-                              MOE_LAYOUT_TILED weights (else MOE_ERR_UNSUPPORTED). */
-#define MOE_PATH_GEMM_MX 3 /* the same grouped GEMM on gfx950's block-scaled MFMA: the MXFP4
-                              weights are an operand as stored, each bf16 activation is split
-                              exactly into two MXFP8 (E4M3) terms with E8M0 block scales. Needs
-                              MOE_LAYOUT_TILED weights. AUTO picks it for tiled weights when
-                              T*k >= 32*E. */
+/* expert-FFN kernel family (moe_options_t.path) */
+#define MOE_PATH_AUTO 0  /* chosen from T*k and E on the host */
+#define MOE_PATH_DECODE 1 /* weight-streaming kernels for decode-sized batches */
+#define MOE_PATH_PREFILL_BF16 2 /* LDS-tiled grouped GEMM for prefill-sized batches, bf16
+                                   activations times MXFP4 weights decoded to bf16 in registers;
+                                   needs MOE_LAYOUT_TILED weights (else MOE_ERR_UNSUPPORTED). */
+#define MOE_PATH_PREFILL_MX8SPLIT 3 /* the same grouped GEMM on gfx950's block-scaled MFMA: the
+                                   MXFP4 weights are an operand as stored, each bf16 activation is
+                                   split exactly into two MXFP8 (E4M3) terms with E8M0 block
+                                   scales. Needs MOE_LAYOUT_TILED weights. AUTO picks it for
+                                   tiled weights when T*k >= 32*E. */
+#define MOE_PATH_PREFILL_MX6SPLIT 4 /* gate_up as MX8SPLIT; the down projection's input (the
+                                   bf16-rounded activation) as two MXFP6 (E2M3) terms with E8M0
+                                   block scales, on the FP6 x FP4 scaled MFMA, which issues faster
+                                   than FP8 x FP4. That split is exact for activations within 2^3
+                                   of their 32-element block's maximum, else off by less than 2^-9
+                                   of that maximum (so not bit-equal to the bf16 GEMM). Needs
+                                   MOE_LAYOUT_TILED weights. */
+/* earlier names of the same paths */
+#define MOE_PATH_STREAM MOE_PATH_DECODE
+#define MOE_PATH_GEMM MOE_PATH_PREFILL_BF16
+#define MOE_PATH_GEMM_MX MOE_PATH_PREFILL_MX8SPLIT
 
 /* moe_mxfp4_weight_t.layout */
 #define MOE_LAYOUT_ROWMAJOR 0 /* codes [E][n][k/2], scales [E][n][k/32] as described below */

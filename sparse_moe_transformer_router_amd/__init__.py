@@ -12,8 +12,12 @@ from ._lib import (  # noqa: F401
     MOE_LAYOUT_ROWMAJOR,
     MOE_LAYOUT_TILED,
     MOE_PATH_AUTO,
+    MOE_PATH_DECODE,
     MOE_PATH_GEMM,
     MOE_PATH_GEMM_MX,
+    MOE_PATH_PREFILL_BF16,
+    MOE_PATH_PREFILL_MX6SPLIT,
+    MOE_PATH_PREFILL_MX8SPLIT,
     MOE_PATH_STREAM,
     MoeError,
     lib,

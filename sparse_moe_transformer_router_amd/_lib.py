@@ -25,9 +25,14 @@ MOE_DTYPE_BF16 = 0
 MOE_DTYPE_F32 = 1
 
 MOE_PATH_AUTO = 0
-MOE_PATH_STREAM = 1
-MOE_PATH_GEMM = 2
-MOE_PATH_GEMM_MX = 3
+MOE_PATH_DECODE = 1
+MOE_PATH_PREFILL_BF16 = 2
+MOE_PATH_PREFILL_MX8SPLIT = 3
+MOE_PATH_PREFILL_MX6SPLIT = 4
+# earlier names of the same paths
+MOE_PATH_STREAM = MOE_PATH_DECODE
+MOE_PATH_GEMM = MOE_PATH_PREFILL_BF16
+MOE_PATH_GEMM_MX = MOE_PATH_PREFILL_MX8SPLIT
 
 MOE_LAYOUT_ROWMAJOR = 0
 MOE_LAYOUT_TILED = 1

@@ -70,21 +70,29 @@ constexpr int kGBiasAreas = 3;    // tile j's bias lives in area j % 3 (the DMA 
 constexpr int kGGroupM = 4;       // m-tiles per group of the XCD-local tile order
 constexpr int kXcds = 8;
 constexpr int kGMaxExperts = 256;
-// RGW = 32-row weight tiles per wave: a tile is 64 RGW weight rows x 128 slots. MX adds the
-// activation terms' scales (128 slots x 2 dwords) after the activation rows.
-template <int RGW, bool MX>
+// RGW = 32-row weight tiles per wave: a tile is 64 RGW weight rows x 128 slots. The block-scaled
+// forms add the activation terms' scales (128 slots x 2 dwords) after the activation rows. An
+// MXFP6 stage holds 128 rows x 192 bytes: the records' 16-byte parts as 128-byte rows (kM6A),
+// then their 8-byte parts as 64-byte rows (kM6B).
+template <int RGW, int AF>
 struct GShape {
+  static constexpr bool kMx = AF != kActBf16;
   static constexpr int kRows = 64 * RGW;
-  static constexpr int kAScBytes = MX ? kGCols * 8 : 0;
-  static constexpr int kWOff = kGActBytes + kAScBytes;  // weight codes, then scales, then bias
+  static constexpr int kActBytes = AF == kActMx6 ? kGCols * kMx6RecBytes : kGActBytes;
+  static constexpr int kAScBytes = kMx ? kGCols * 8 : 0;
+  static constexpr int kWOff = kActBytes + kAScBytes;  // weight codes, then scales, then bias
   static constexpr int kWBytes = 2 * RGW * 2048;       // codes of the 2 RGW weight tiles
   static constexpr int kStageBytes = kWOff + kWBytes + kGSBytes;
   static constexpr int kBiasOff = kGStages * kStageBytes;  // 3 tile-bias areas after the ring
-  static constexpr int kDma = 8 + RGW + 2 + (MX ? 1 : 0);  // DMAs per wave per stage
+  static constexpr int kActDma = AF == kActMx6 ? 6 : 8;    // activation DMAs per wave per stage
+  static constexpr int kDma = kActDma + RGW + 2 + (kMx ? 1 : 0);  // DMAs per wave per stage
   // the expert offsets, then (block-scaled) each wave's 256-byte area for row-map entries
   static constexpr int kMapOff = kBiasOff + kGBiasAreas * kGBBytes + (kGMaxExperts + 4) * 4;
-  static constexpr size_t kLds = (size_t)kMapOff + (MX ? 4 * 256 : 0);
+  static constexpr size_t kLds = (size_t)kMapOff + (kMx ? 4 * 256 : 0);
 };
+constexpr int kM6A = kMx6BPart;             // bytes of a row's 16-byte parts in an MXFP6 stage
+constexpr int kM6B = kMx6RecBytes - kMx6BPart;  // bytes of its 8-byte parts
+constexpr int kM6BOff = kGCols * kM6A;     // the 8-byte parts' area in an MXFP6 stage
 
 __device__ __forceinline__ int g_off(int row, int col16) { return row * kGRowBytes + ((col16 ^ (row & 15)) << 4); }
 
@@ -164,7 +172,7 @@ __device__ GTile g_tile(int L, const int32_t *off, int E, int mt_total, int ntn,
 
 // One workgroup per CU (the LDS ring takes most of it): the compiler is told so, and schedules
 // for one wave per SIMD instead of saving registers for more.
-template <int EPI, int RGW, bool MX>
+template <int EPI, int RGW, int AF>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) void ffn_gemm_kernel(const void *__restrict__ a_src, const uint8_t *__restrict__ a_scales,
                                                        const int32_t *__restrict__ a_rows, int a_div,
                                                        const int32_t *__restrict__ offsets, int E,
@@ -173,10 +181,13 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
                                                        const uint16_t *__restrict__ bias, int N, int K, int ntn,
                                                        void *__restrict__ out, uint8_t *__restrict__ out_scales,
                                                        float limit, float alpha) {
-  using SH = GShape<RGW, MX>;
+  using SH = GShape<RGW, AF>;
+  constexpr bool MX = AF != kActBf16, M6 = AF == kActMx6;
   constexpr int kGRows = SH::kRows, kGWBytes = SH::kWBytes, kGStageBytes = SH::kStageBytes, kGDma = SH::kDma;
-  constexpr int kWOff = SH::kWOff;
-  static_assert(EPI != kEpiMxAct || (MX && RGW == 4), "two-term output: one 128-element record per n-tile");
+  constexpr int kWOff = SH::kWOff, kActDma = SH::kActDma;
+  static_assert((EPI != kEpiMxAct && EPI != kEpiMx6Act) || (AF == kActMx8 && RGW == 4),
+                "two-term output: one 128-element record per n-tile, from the MXFP8 gate_up");
+  static_assert(!M6 || EPI == kEpiLinearF32, "MXFP6 input: the down projection");
   static_assert(EPI != kEpiSwigluBf16 || !MX, "bf16 activation output belongs to the bf16 path");
   extern __shared__ __attribute__((aligned(16))) unsigned char lds[];
   int32_t *off = reinterpret_cast<int32_t *>(lds + SH::kBiasOff + kGBiasAreas * kGBBytes);
@@ -212,7 +223,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
   int ji = 0, ci = 0;
   GTile ti = g_tile(first, off, E, mt_total, ntn, lane);
   // bytes per activation row: K bf16, or nchunk two-term records
-  const int64_t arow = MX ? (int64_t)nchunk * kMxRecBytes : (int64_t)K * 2;
+  const int64_t arow = M6 ? (int64_t)nchunk * kMx6RecBytes : MX ? (int64_t)nchunk * kMxRecBytes : (int64_t)K * 2;
   // DMA i (0 .. kDma - 1) of the issue-side chunk into ring slot `slot`:
   //   0..7            activation rows 32 wave + 4 i .. + 3 (bf16 elements, or a two-term record);
   //   8..8+RGW-1      1 KB of weight codes: tile m / 2, half m % 2, m = RGW wave + i - 8;
@@ -253,8 +264,10 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
       srcv = ti.row0 + ((32 * wave + (lane & 31)) < ti.mcount ? 32 * wave + (lane & 31) : 0);
     }
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const int src = __builtin_amdgcn_ds_bpermute((4 * i + lane / 16) * 4, srcv);
+    for (int i = 0; i < kActDma; ++i) {
+      // tile row (within the wave's 32) of the lane's piece of activation DMA i
+      const int rw = M6 ? (i < 4 ? 8 * i + lane / 8 : 16 * (i - 4) + lane / 4) : 4 * i + lane / 16;
+      const int src = __builtin_amdgcn_ds_bpermute(rw * 4, srcv);
       aptr[i] = static_cast<const uint8_t *>(a_src) + (int64_t)src * arow;
     }
     const int gt0 = ti.nt * 2 * RGW;
@@ -281,8 +294,12 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
       sptr = a_scales + (int64_t)src * nchunk * kMxScBytes + (lane & 1) * 4;
     }
   };
+  // (MXFP6: a 16-byte part's row holds 8 units, swizzled by row & 7; an 8-byte part's row 4 units
+  // of two pieces, swizzled by (row >> 1) & 3)
 #pragma unroll
-  for (int i = 0; i < 8; ++i) lcol[i] = ((lane % 16) ^ ((32 * wave + 4 * i + lane / 16) & 15)) * 16;
+  for (int i = 0; i < 8; ++i)
+    lcol[i] = M6 ? (i < 4 ? ((lane % 8) ^ (lane / 8)) * 16 : kM6A + ((lane % 4) ^ ((lane / 8) & 3)) * 16)
+                 : ((lane % 16) ^ ((32 * wave + 4 * i + lane / 16) & 15)) * 16;
   if (mapped) {
     dma_map(ti);
     __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));  // this wave's map entries are in its area
@@ -316,29 +333,35 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
   };
   auto dma = [&](int i, int slot) {
     unsigned char *st = lds + slot * kGStageBytes;
-    if (i < 8) {
-      const uint8_t *src;
-      if constexpr (MX) {
-        src = aptr[i] + ci * kMxRecBytes + lcol[i];
+    if (i < kActDma) {
+      if constexpr (M6) {
+        // 16-byte parts: 8 rows x 128 bytes per DMA; 8-byte parts: 16 rows x 64 bytes
+        unsigned char *dst = i < 4 ? st + (32 * wave + 8 * i) * kM6A : st + kM6BOff + (32 * wave + 16 * (i - 4)) * kM6B;
+        __builtin_amdgcn_global_load_lds(aptr[i] + ci * kMx6RecBytes + lcol[i], dst, 16, 0, 0);
       } else {
-        int kk = ci * 128 + lcol[i] / 2;
-        kk = kk < K ? kk : 0;  // past K: any in-bounds element (its weight is an exact zero)
-        src = aptr[i] + 2 * (int64_t)kk;
+        const uint8_t *src;
+        if constexpr (MX) {
+          src = aptr[i] + ci * kMxRecBytes + lcol[i];
+        } else {
+          int kk = ci * 128 + lcol[i] / 2;
+          kk = kk < K ? kk : 0;  // past K: any in-bounds element (its weight is an exact zero)
+          src = aptr[i] + 2 * (int64_t)kk;
+        }
+        __builtin_amdgcn_global_load_lds(src, st + (32 * wave + 4 * i) * kGRowBytes, 16, 0, 0);
       }
-      __builtin_amdgcn_global_load_lds(src, st + (32 * wave + 4 * i) * kGRowBytes, 16, 0, 0);
-    } else if (i < 8 + RGW) {
-      const int m = i - 8;
+    } else if (i < kActDma + RGW) {
+      const int m = i - kActDma;
       // (the offset goes through a local: with the array reads inside the builtin's argument
       // the host compilation silently drops the kernel's launch stub)
       const int64_t wo = woff[m] + ci * wstr[m];
       __builtin_amdgcn_global_load_lds(pcodes + wo, st + kWOff + (RGW * wave + m) * 1024, 16, 0, 0);
-    } else if (i == 8 + RGW) {
+    } else if (i == kActDma + RGW) {
       __builtin_amdgcn_global_load_lds(pscales + soff + ci * sstr, st + kWOff + kGWBytes + 256 * wave, 4, 0, 0);
-    } else if (i == 8 + RGW + 1) {
+    } else if (i == kActDma + RGW + 1) {
       const uint8_t *src = boff >= 0 ? reinterpret_cast<const uint8_t *>(bias) + boff : pscales;  // else a dummy
       __builtin_amdgcn_global_load_lds(src, lds + SH::kBiasOff + (ji % kGBiasAreas) * kGBBytes + 256 * wave, 4, 0, 0);
     } else {
-      __builtin_amdgcn_global_load_lds(sptr + ci * kMxScBytes, st + kGActBytes + 256 * wave, 4, 0, 0);
+      __builtin_amdgcn_global_load_lds(sptr + ci * kMxScBytes, st + SH::kActBytes + 256 * wave, 4, 0, 0);
     }
   };
 
@@ -550,6 +573,87 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
     }
   };
 
+  // MXFP6 form of the fp32 staging above: the wave's own 16-byte-part rows of ring slot fs are
+  // 4 KB (32 rows x 128 bytes), so a round is 32 slots x one 32-row tile (XOR-swizzled 16-byte
+  // units), and each store writes 8 slots x 128 contiguous bytes.
+  auto epilogue_staged6 = [&](int fs) {
+    unsigned char *stg = lds + fs * kGStageBytes + wave * 32 * kM6A;
+    float *outp = static_cast<float *>(out);
+    const int nb_live = tc.mcount > 64 ? 2 : 1;
+#pragma unroll
+    for (int b = 0; b < 2; ++b) {
+      if (b >= nb_live) break;
+#pragma unroll
+      for (int g = 0; g < RGW; ++g) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int u = 2 * i + kh;
+          *reinterpret_cast<f32x4_t *>(stg + r32 * kM6A + ((u ^ (r32 & 7)) << 4)) =
+              f32x4_t{acc[g][b][4 * i], acc[g][b][4 * i + 1], acc[g][b][4 * i + 2], acc[g][b][4 * i + 3]};
+        }
+        f32x4_t v[4];  // all reads before the first (conditional) store
+        const int u = lane % 8;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const int sl = 8 * j + lane / 8;
+          v[j] = *reinterpret_cast<const f32x4_t *>(stg + sl * kM6A + ((u ^ (sl & 7)) << 4));
+        }
+        const int n = tc.nt * kGRows + nloc0 + 32 * g + 4 * u;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const int col = 32 * (wx + 2 * b) + 8 * j + lane / 8;
+          if (n < N && col < tc.mcount) *reinterpret_cast<f32x4_t *>(outp + (int64_t)(tc.row0 + col) * N + n) = v[j];
+        }
+      }
+    }
+  };
+  // Two-term MXFP6 activation output (gate_up, 256-row tiles): as epilogue_mx, the n-tile's 128
+  // activations are record nt of each slot row and this wave's 64 are blocks 2 wy, 2 wy + 1. A
+  // lane holds 16 of each block's 32 values (elements 16 gg + 4 i + 2 kh + {0, 1} of block j from
+  // tile 2 j + gg); one permlane32_swap per bf16 pair gives lane kh all 32 of block 2 wy + kh,
+  // which it splits and stores alone (no cross-lane maximum).
+  auto epilogue_mx6 = [&]() {
+    uint8_t *orec = static_cast<uint8_t *>(out);
+#pragma unroll
+    for (int b = 0; b < 2; ++b) {
+      const int col = scol(b);
+      const bool live = col < tc.mcount;  // same for the lane pair; the swaps run on every lane
+      const int64_t r = tc.row0 + (live ? col : 0);
+      uint32_t pk[2][2][4];  // [block j][tile gg][i]: elements 16 gg + 4 i + 2 kh + {0, 1}
+#pragma unroll
+      for (int g = 0; g < RGW; ++g)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int n = tc.nt * kGRows + nloc0 + 32 * g + 8 * i + 4 * kh;
+          const uint32_t a0 = f32_to_bf16_rne(swiglu_unit(acc[g][b][4 * i], acc[g][b][4 * i + 1], limit, alpha));
+          const uint32_t a1 = f32_to_bf16_rne(swiglu_unit(acc[g][b][4 * i + 2], acc[g][b][4 * i + 3], limit, alpha));
+          pk[g / 2][g % 2][i] = n < N ? (a0 | (a1 << 16)) : 0u;
+        }
+      float v[32];
+#pragma unroll
+      for (int gg = 0; gg < 2; ++gg)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          // [own j = 0 | the low lanes' j = 1] and [the high lanes' j = 0 | own j = 1]: lane kh
+          // now has elements 16 gg + 4 i + 2 kk + {0, 1} of its block from swap result kk
+          const auto rr = __builtin_amdgcn_permlane32_swap(pk[0][gg][i], pk[1][gg][i], false, false);
+#pragma unroll
+          for (int kk = 0; kk < 2; ++kk) {
+            v[16 * gg + 4 * i + 2 * kk] = __uint_as_float((uint32_t)rr[kk] << 16);
+            v[16 * gg + 4 * i + 2 * kk + 1] = __uint_as_float((uint32_t)rr[kk] & 0xffff0000u);
+          }
+        }
+      uint32_t hi[6], lo[6], sh, sl;
+      mx6_split_block(v, hi, lo, sh, sl);
+      const int blk = 2 * wy + kh;
+      if (live) {
+        mx6_store_block(orec + (r * ntn + tc.nt) * kMx6RecBytes, blk, hi, lo);
+        out_scales[(r * ntn + tc.nt) * kMxScBytes + blk] = (uint8_t)sh;
+        out_scales[(r * ntn + tc.nt) * kMxScBytes + 4 + blk] = (uint8_t)sl;
+      }
+    }
+  };
+
   // prologue: stages 0 and 1
 #pragma unroll
   for (int s = 0; s < 2; ++s) {
@@ -567,17 +671,40 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
   // declared here. Lane group kh of the FP8 operand holds elements 16 kh .. 16 kh + 15 and
   // 32 + 16 kh .. of a 64-element half, i.e. 16-byte columns 4p + kh and 4p + 2 + kh of the
   // term's 128 bytes.
-  i32x8_t bv[2][2];
+  // MXFP6: the lane's block 2p + kh of term t is its record's 16-byte unit (t, 2p + kh) in the
+  // 16-byte-part rows and half p of unit (t, kh) in the 8-byte-part rows (both swizzled); the
+  // operand's dwords 6 and 7 are unused (zero).
+  i32x8_t bv[2][2] = {};
   u32x4_t wv[2][RGW];
   uint32_t swd[RGW], ash[2][2];
+  // half h of the FP8 operand (16-byte columns 4p + kh, 4p + 2 + kh of term t), or the MXFP6
+  // operand's part h (h = 0: dwords 0-3, h = 1: dwords 4-5), of slot row `row` into b8
+  auto act_read = [&](const unsigned char *abuf, int row, int p, int t, int h, i32x8_t &b8) {
+    if constexpr (M6) {
+      if (h == 0) {
+        const u32x4_t u = *reinterpret_cast<const u32x4_t *>(abuf + row * kM6A + (((4 * t + 2 * p + kh) ^ (row & 7)) << 4));
+#pragma unroll
+        for (int i = 0; i < 4; ++i) b8[i] = (int)u[i];
+      } else {
+        // two dword reads, not one 8-byte read: read as 8 bytes, the compiler takes the piece
+        // for a possible target of the DMAs in flight and waits for all of them
+        const uint32_t *q = reinterpret_cast<const uint32_t *>(abuf + kM6BOff + row * kM6B +
+                                                               (((2 * t + kh) ^ ((row >> 1) & 3)) << 4) + 8 * p);
+        b8[4] = (int)q[0];
+        b8[5] = (int)q[1];
+      }
+    } else {
+      const u32x4_t u = *reinterpret_cast<const u32x4_t *>(abuf + g_off(row, 8 * t + 4 * p + 2 * h + kh));
+#pragma unroll
+      for (int i = 0; i < 4; ++i) b8[4 * h + i] = (int)u[i];
+    }
+  };
   auto bload = [&](const unsigned char *abuf, int p, int t, i32x8_t *b8, int nb) {
 #pragma unroll
     for (int b = 0; b < 2; ++b) {
       if (b >= nb) break;
-      const int row = scol(b);
-      const u32x4_t u0 = *reinterpret_cast<const u32x4_t *>(abuf + g_off(row, 8 * t + 4 * p + kh));
-      const u32x4_t u1 = *reinterpret_cast<const u32x4_t *>(abuf + g_off(row, 8 * t + 4 * p + 2 + kh));
-      b8[b] = i32x8_t{(int)u0[0], (int)u0[1], (int)u0[2], (int)u0[3], (int)u1[0], (int)u1[1], (int)u1[2], (int)u1[3]};
+      act_read(abuf, scol(b), p, t, 0, b8[b]);
+      act_read(abuf, scol(b), p, t, 1, b8[b]);
     }
   };
   auto wload = [&](const unsigned char *abuf, int p, u32x4_t *w4) {
@@ -597,8 +724,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
       swd[g] = *reinterpret_cast<const uint32_t *>(abuf + kWOff + kGWBytes + (wy * RGW + g) * 128 + r32 * 4);
 #pragma unroll
     for (int b = 0; b < 2; ++b) {
-      ash[b][0] = *reinterpret_cast<const uint32_t *>(abuf + kGActBytes + scol(b) * 8);
-      ash[b][1] = *reinterpret_cast<const uint32_t *>(abuf + kGActBytes + scol(b) * 8 + 4);
+      ash[b][0] = *reinterpret_cast<const uint32_t *>(abuf + SH::kActBytes + scol(b) * 8);
+      ash[b][1] = *reinterpret_cast<const uint32_t *>(abuf + SH::kActBytes + scol(b) * 8 + 4);
     }
   };
   // Wait for stage G + 1 while stage G + 2's DMAs of steps 0..2 (the youngest) may still fly.
@@ -657,9 +784,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
             wd[k] = *reinterpret_cast<const u32x4_t *>(buf + kWOff + (wy * RGW + k) * 2048 + pw * 1024 + lane * 16);
           } else {
             const int b = (k - nw) / 2, h = (k - nw) % 2;
-            const u32x4_t u = *reinterpret_cast<const u32x4_t *>(buf + g_off(scol(b), 8 * t + 4 * p + 2 * h + kh));
-#pragma unroll
-            for (int i = 0; i < 4; ++i) bd[b][4 * h + i] = (int)u[i];
+            act_read(buf, scol(b), p, t, h, bd[b]);
           }
         };
         auto step = [&](auto SC) {
@@ -674,8 +799,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
           auto mfma = [&](int g, int b) {
             const u32x4_t u = wv[p][g];
             const i32x8_t wa = i32x8_t{(int)u[0], (int)u[1], (int)u[2], (int)u[3], 0, 0, 0, 0};
+            // A: FP4 (format 4); B: FP8 E4M3 (0) or FP6 E2M3 (2)
             acc[g][b] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
-                wa, bv[s % 2][b], acc[g][b], 4, 0, 2 * p, (int)sw_c[g], 2 * p, (int)as_c[b][t]);
+                wa, bv[s % 2][b], acc[g][b], 4, M6 ? 2 : 0, 2 * p, (int)sw_c[g], 2 * p, (int)as_c[b][t]);
           };
           mfma(0, 0);
           if constexpr (s == 3) {
@@ -763,11 +889,16 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
       tile_chunks(std::integral_constant<int, 2>{});
     else
       tile_chunks(std::integral_constant<int, 1>{});
-    if constexpr (EPI == kEpiMxAct) {
+    if constexpr (EPI == kEpiMx6Act) {
+      epilogue_mx6();
+    } else if constexpr (EPI == kEpiMxAct) {
       epilogue_mx(jc);
     } else {
-      if constexpr (MX && EPI == kEpiLinearF32)
-        epilogue_staged((G + 2) % kGStages);  // the slot of the tile's last chunk, free until the next chunk's DMAs
+      // the slot of the tile's last chunk, free until the next chunk's DMAs
+      if constexpr (M6 && EPI == kEpiLinearF32)
+        epilogue_staged6((G + 2) % kGStages);
+      else if constexpr (MX && EPI == kEpiLinearF32)
+        epilogue_staged((G + 2) % kGStages);
       else
         epilogue(jc);
     }
@@ -796,16 +927,21 @@ int gemm_grid_cap() {
 // loads: 624 vs 674 us for the 5760-row gate_up at 16,384 slots) unless that pads more than
 // a tenth of the 32-row tiles; then 192 if it pads less. The two-term activation output
 // always uses 256 rows (one 128-element record per n-tile).
-hipError_t launch_ffn_gemm(const void *a, const uint8_t *a_scales, const int32_t *a_rows, int a_div, bool mx,
+hipError_t launch_ffn_gemm(const void *a, const uint8_t *a_scales, const int32_t *a_rows, int a_div, int af,
                            const int32_t *offsets, int E, int64_t S, const MxWeight &w, int epilogue, void *out,
                            uint8_t *out_scales, float limit, float alpha, hipStream_t stream) {
+  const bool mx = af != kActBf16;
+  if (af < kActBf16 || af > kActMx6) return hipErrorInvalidValue;
   if (a_rows != nullptr && (!mx || a_div < 1)) return hipErrorInvalidValue;
   if (E > kGMaxExperts) return hipErrorInvalidValue;
   if (epilogue == kEpiMxAct && !mx) return hipErrorInvalidValue;
   if (epilogue == kEpiSwigluBf16 && mx) return hipErrorInvalidValue;
   const int NG = w.N / 32;
   const int pad4 = (NG + 7) / 8 * 8 - NG, pad3 = (NG + 5) / 6 * 6 - NG;
-  const bool tall = epilogue == kEpiMxAct || pad4 * 10 <= NG || pad4 <= pad3;
+  const bool rec_out = epilogue == kEpiMxAct || epilogue == kEpiMx6Act;
+  if (rec_out && af != kActMx8) return hipErrorInvalidValue;
+  if (af == kActMx6 && epilogue != kEpiLinearF32) return hipErrorInvalidValue;
+  const bool tall = rec_out || pad4 * 10 <= NG || pad4 <= pad3;
   const int rows = tall ? 256 : 192;
   const int64_t busy = (S < E) ? S : E;
   const int64_t mtiles = (S + kGCols - 1) / kGCols + busy;  // bound on the real m-tile count
@@ -816,28 +952,34 @@ hipError_t launch_ffn_gemm(const void *a, const uint8_t *a_scales, const int32_t
 #define MOE_LAUNCH_GEMM(EPI, RG, M)                                                                          \
   hipLaunchKernelGGL((ffn_gemm_kernel<EPI, RG, M>), grid, dim3(256), (GShape<RG, M>::kLds), stream, a, a_scales, \
                      a_rows, a_div, offsets, E, w.codes, w.scales, w.bias, w.N, w.K, ntn, out, out_scales, limit, alpha)
-  if (mx) {
+  if (af == kActMx6) {  // the down projection on MXFP6 activation records
+    if (tall)
+      MOE_LAUNCH_GEMM(kEpiLinearF32, 4, kActMx6);
+    else
+      MOE_LAUNCH_GEMM(kEpiLinearF32, 3, kActMx6);
+  } else if (af == kActMx8) {
     if (tall) {
       switch (epilogue) {
-        case kEpiMxAct: MOE_LAUNCH_GEMM(kEpiMxAct, 4, true); break;
-        case kEpiPreactF32: MOE_LAUNCH_GEMM(kEpiPreactF32, 4, true); break;
-        case kEpiActF32: MOE_LAUNCH_GEMM(kEpiActF32, 4, true); break;
-        default: MOE_LAUNCH_GEMM(kEpiLinearF32, 4, true); break;
+        case kEpiMxAct: MOE_LAUNCH_GEMM(kEpiMxAct, 4, kActMx8); break;
+        case kEpiMx6Act: MOE_LAUNCH_GEMM(kEpiMx6Act, 4, kActMx8); break;
+        case kEpiPreactF32: MOE_LAUNCH_GEMM(kEpiPreactF32, 4, kActMx8); break;
+        case kEpiActF32: MOE_LAUNCH_GEMM(kEpiActF32, 4, kActMx8); break;
+        default: MOE_LAUNCH_GEMM(kEpiLinearF32, 4, kActMx8); break;
       }
     } else {
       switch (epilogue) {
-        case kEpiPreactF32: MOE_LAUNCH_GEMM(kEpiPreactF32, 3, true); break;
-        case kEpiActF32: MOE_LAUNCH_GEMM(kEpiActF32, 3, true); break;
-        default: MOE_LAUNCH_GEMM(kEpiLinearF32, 3, true); break;
+        case kEpiPreactF32: MOE_LAUNCH_GEMM(kEpiPreactF32, 3, kActMx8); break;
+        case kEpiActF32: MOE_LAUNCH_GEMM(kEpiActF32, 3, kActMx8); break;
+        default: MOE_LAUNCH_GEMM(kEpiLinearF32, 3, kActMx8); break;
       }
     }
   } else {
 #define MOE_LAUNCH_GEMM_EPI(RG)                                                  \
   switch (epilogue) {                                                            \
-    case kEpiSwigluBf16: MOE_LAUNCH_GEMM(kEpiSwigluBf16, RG, false); break;      \
-    case kEpiPreactF32: MOE_LAUNCH_GEMM(kEpiPreactF32, RG, false); break;        \
-    case kEpiActF32: MOE_LAUNCH_GEMM(kEpiActF32, RG, false); break;              \
-    default: MOE_LAUNCH_GEMM(kEpiLinearF32, RG, false); break;                   \
+    case kEpiSwigluBf16: MOE_LAUNCH_GEMM(kEpiSwigluBf16, RG, kActBf16); break;   \
+    case kEpiPreactF32: MOE_LAUNCH_GEMM(kEpiPreactF32, RG, kActBf16); break;     \
+    case kEpiActF32: MOE_LAUNCH_GEMM(kEpiActF32, RG, kActBf16); break;           \
+    default: MOE_LAUNCH_GEMM(kEpiLinearF32, RG, kActBf16); break;                \
   }
     if (tall) {
       MOE_LAUNCH_GEMM_EPI(4)

@@ -13,6 +13,7 @@ enum FfnEpilogue : int {
   kEpiActF32 = 2,      // gate_up: bf16-rounded SwiGLU(h) widened to fp32 [S][N/2]
   kEpiLinearF32 = 3,   // down: W a + b -> fp32 [S][N]
   kEpiMxAct = 4,       // gate_up: bf16-rounded SwiGLU(h) -> two-term MXFP8 records (mx_act.h)
+  kEpiMx6Act = 5,      // gate_up: bf16-rounded SwiGLU(h) -> two-term MXFP6 records (mx_act.h)
 };
 
 struct MxWeight {
@@ -60,13 +61,18 @@ hipError_t launch_ffn_stream(const uint16_t *a_src, bool a_by_token, const int32
                              int k, const int32_t *offsets, int E, int64_t S, const MxWeight &w,
                              int epilogue, void *out, float limit, float alpha, hipStream_t stream);
 
+// Activation forms of the grouped GEMM's input rows: bf16, or two-term block-scaled records
+// (MXFP8 or MXFP6 terms, mx_act.h).
+enum ActForm : int { kActBf16 = 0, kActMx8 = 1, kActMx6 = 2 };
+
 // One expert GEMM, persistent LDS-tiled grouped-GEMM family (tiled weights only): the
-// activations are expert-sorted rows (r = sorted row), either bf16 a[r * K] (mx false) or
-// two-term MXFP8 records with their scale array a_scales (mx true, layout in mx_act.h); with
-// a_rows (mx only), sorted row r reads record row a_rows[r] / a_div instead (a slot's token:
-// a_rows = sorted_slot, a_div = k). Output rows are sorted rows. kEpiMxAct (mx only) writes
-// records to out and their scales to out_scales. E at most 256.
-hipError_t launch_ffn_gemm(const void *a, const uint8_t *a_scales, const int32_t *a_rows, int a_div, bool mx,
+// activations are expert-sorted rows (r = sorted row), either bf16 a[r * K] (af kActBf16) or
+// two-term records with their scale array a_scales (kActMx8, kActMx6; layouts in mx_act.h);
+// with a_rows (records only), sorted row r reads record row a_rows[r] / a_div instead (a slot's
+// token: a_rows = sorted_slot, a_div = k). Output rows are sorted rows. kEpiMxAct / kEpiMx6Act
+// (MXFP8 input only) write MXFP8 / MXFP6 records to out and their scales to out_scales; an
+// MXFP6 input takes the linear epilogue only (the down projection). E at most 256.
+hipError_t launch_ffn_gemm(const void *a, const uint8_t *a_scales, const int32_t *a_rows, int a_div, int af,
                            const int32_t *offsets, int E, int64_t S, const MxWeight &w, int epilogue, void *out,
                            uint8_t *out_scales, float limit, float alpha, hipStream_t stream);
 

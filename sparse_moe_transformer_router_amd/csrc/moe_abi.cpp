@@ -96,7 +96,7 @@ moe_options_t default_options() {
 
 int check_options(const moe_options_t &o) {
   if (o.out_dtype != MOE_DTYPE_BF16 && o.out_dtype != MOE_DTYPE_F32) return MOE_ERR_INVALID_ARG;
-  if (o.path < MOE_PATH_AUTO || o.path > MOE_PATH_GEMM_MX) return MOE_ERR_INVALID_ARG;
+  if (o.path < MOE_PATH_AUTO || o.path > MOE_PATH_PREFILL_MX6SPLIT) return MOE_ERR_INVALID_ARG;
   if (!(o.swiglu_limit > 0.0f) || !(o.swiglu_alpha == o.swiglu_alpha)) return MOE_ERR_INVALID_ARG;
   if (o.flags & ~(MOE_FLAG_EMIT_PREACT | MOE_FLAG_EMIT_ACT)) return MOE_ERR_INVALID_ARG;
   if ((o.flags & MOE_FLAG_EMIT_PREACT) && (o.flags & MOE_FLAG_EMIT_ACT)) return MOE_ERR_INVALID_ARG;
@@ -105,17 +105,20 @@ int check_options(const moe_options_t &o) {
 
 // Which expert-GEMM family runs: a grouped GEMM (tiled weights only) when asked for, or on
 // AUTO when the batch averages at least kGemmSlotsPerExpert slots per expert; otherwise the
-// weight-streaming kernels. AUTO's grouped GEMM is the block-scaled one when kAutoMx is set.
+// weight-streaming kernels. AUTO's grouped GEMM is kAutoGemm.
 // Measured crossover (FFN time, stream vs block-scaled GEMM): E = 32 at 24 slots per expert
 // 105 vs 142 us, at 32: 150 vs 145 us; E = 128 at 16: 354 vs 467 us, at 32: 544 vs 485 us.
 constexpr int64_t kGemmSlotsPerExpert = 32;
-constexpr bool kAutoMx = true;
 
-enum class Family { kStream, kGemm, kGemmMx };
+enum class Family { kStream, kGemm, kGemmMx, kGemmMx6 };
+constexpr Family kAutoGemm = Family::kGemmMx;
+
+bool is_gemm_path(int path) {
+  return path == MOE_PATH_PREFILL_BF16 || path == MOE_PATH_PREFILL_MX8SPLIT || path == MOE_PATH_PREFILL_MX6SPLIT;
+}
 
 int check_path(const moe_options_t &o, const moe_mxfp4_weight_t &gu, const moe_mxfp4_weight_t &dn) {
-  if ((o.path == MOE_PATH_GEMM || o.path == MOE_PATH_GEMM_MX) &&
-      (gu.layout != MOE_LAYOUT_TILED || dn.layout != MOE_LAYOUT_TILED))
+  if (is_gemm_path(o.path) && (gu.layout != MOE_LAYOUT_TILED || dn.layout != MOE_LAYOUT_TILED))
     return MOE_ERR_UNSUPPORTED;
   return MOE_OK;
 }
@@ -123,18 +126,19 @@ int check_path(const moe_options_t &o, const moe_mxfp4_weight_t &gu, const moe_m
 Family family(const moe_options_t &o, const moe_mxfp4_weight_t &gu, const moe_mxfp4_weight_t &dn, int64_t S,
               int E) {
   const bool tiled = gu.layout == MOE_LAYOUT_TILED && dn.layout == MOE_LAYOUT_TILED;
-  if (o.path == MOE_PATH_GEMM) return Family::kGemm;
-  if (o.path == MOE_PATH_GEMM_MX) return Family::kGemmMx;
-  if (o.path == MOE_PATH_STREAM || !tiled || S < kGemmSlotsPerExpert * (int64_t)E) return Family::kStream;
-  return kAutoMx ? Family::kGemmMx : Family::kGemm;
+  if (o.path == MOE_PATH_PREFILL_BF16) return Family::kGemm;
+  if (o.path == MOE_PATH_PREFILL_MX8SPLIT) return Family::kGemmMx;
+  if (o.path == MOE_PATH_PREFILL_MX6SPLIT) return Family::kGemmMx6;
+  if (o.path == MOE_PATH_DECODE || !tiled || S < kGemmSlotsPerExpert * (int64_t)E) return Family::kStream;
+  return kAutoGemm;
 }
 
 // The expert GEMMs that follow the permutation. Arguments already validated. The GEMM
 // families read their gate_up activations from an expert-sorted copy of x in the xs region
 // (S x H bf16, or two-term records); the act region holds the activation between the
 // projections (bf16 or two-term records).
-// x_records_ready: the block-scaled family's per-token records of x are already in xs (the
-// block's normalisation writes them), so the gather is skipped.
+// x_records_ready: the block-scaled families' per-token MXFP8 records of x are already in xs
+// (the block's normalisation writes them), so the gather is skipped.
 int run_ffn(const uint16_t *x, int64_t T, int k, int E, const int32_t *offsets, const int32_t *sorted_slot,
             const moe_mxfp4_weight_t &gu, const moe_mxfp4_weight_t &dn, const moe_options_t &o, float *y,
             void *act, void *xs, hipStream_t stream, bool x_records_ready = false) {
@@ -156,11 +160,17 @@ int run_ffn(const uint16_t *x, int64_t T, int k, int E, const int32_t *offsets, 
     return launch(static_cast<uint16_t *>(act), false, w2, moe::kEpiLinearF32, y) == hipSuccess ? MOE_OK
                                                                                               : MOE_ERR_HIP;
   }
-  const bool mxp = f == Family::kGemmMx;
+  // block-scaled families: x's T rows become exact two-term MXFP8 records once, and gate_up reads
+  // each sorted row's token record (a_rows = sorted_slot, a_div = k); its epilogue writes the
+  // activation as MXFP8 records, or as MXFP6 records for the MXFP6 down GEMM. bf16: an
+  // expert-sorted copy of x. (The scale arrays sit at the same offset for both record forms:
+  // the regions are sized for the larger MXFP8 records.)
+  const bool mxp = f == Family::kGemmMx || f == Family::kGemmMx6;
+  const int af_x = mxp ? moe::kActMx8 : moe::kActBf16;
+  const int af_act = f == Family::kGemmMx6 ? moe::kActMx6 : af_x;
+  const int epi_act = f == Family::kGemmMx6 ? moe::kEpiMx6Act : mxp ? moe::kEpiMxAct : moe::kEpiSwigluBf16;
   uint8_t *xs_sc = mxp ? static_cast<uint8_t *>(xs) + mx_scales_offset((size_t)S, H) : nullptr;
   uint8_t *act_sc = mxp ? static_cast<uint8_t *>(act) + mx_scales_offset((size_t)S, I) : nullptr;
-  // block-scaled: x's T rows become two-term records once, and gate_up reads each sorted row's
-  // token record (a_rows = sorted_slot, a_div = k); bf16: an expert-sorted copy of x
   const hipError_t g =
       mxp ? (x_records_ready ? hipSuccess
                              : moe::launch_gather_rows_mx(x, nullptr, 1, T, H, static_cast<uint8_t *>(xs), xs_sc, stream))
@@ -168,15 +178,15 @@ int run_ffn(const uint16_t *x, int64_t T, int k, int E, const int32_t *offsets, 
   if (g != hipSuccess) return MOE_ERR_HIP;
   const int32_t *rows = mxp ? sorted_slot : nullptr;
   if (first_epi >= 0)
-    return moe::launch_ffn_gemm(xs, xs_sc, rows, k, mxp, offsets, E, S, w1, first_epi, y, nullptr, lim, alpha,
+    return moe::launch_ffn_gemm(xs, xs_sc, rows, k, af_x, offsets, E, S, w1, first_epi, y, nullptr, lim, alpha,
                                 stream) == hipSuccess
                ? MOE_OK
                : MOE_ERR_HIP;
-  if (moe::launch_ffn_gemm(xs, xs_sc, rows, k, mxp, offsets, E, S, w1, mxp ? moe::kEpiMxAct : moe::kEpiSwigluBf16,
-                           act, act_sc, lim, alpha, stream) != hipSuccess)
+  if (moe::launch_ffn_gemm(xs, xs_sc, rows, k, af_x, offsets, E, S, w1, epi_act, act, act_sc, lim, alpha, stream) !=
+      hipSuccess)
     return MOE_ERR_HIP;
-  return moe::launch_ffn_gemm(act, act_sc, nullptr, 1, mxp, offsets, E, S, w2, moe::kEpiLinearF32, y, nullptr, lim,
-                              alpha, stream) == hipSuccess
+  return moe::launch_ffn_gemm(act, act_sc, nullptr, 1, af_act, offsets, E, S, w2, moe::kEpiLinearF32, y, nullptr,
+                              lim, alpha, stream) == hipSuccess
              ? MOE_OK
              : MOE_ERR_HIP;
 }
@@ -213,8 +223,9 @@ int forward_impl(const uint16_t *x, const moe_router_t *router, const moe_mxfp4_
   const uint16_t *residual = nullptr;
   bool records_ready = false;
   if (norm_scale != nullptr) {
-    // the block-scaled family reads x as per-token records: the normalisation writes them
-    const bool mxp = family(o, *gu, *dn, S, E) == Family::kGemmMx;
+    // the block-scaled families read x as per-token records: the normalisation writes them
+    const Family f = family(o, *gu, *dn, S, E);
+    const bool mxp = f == Family::kGemmMx || f == Family::kGemmMx6;
     uint8_t *xs = at<uint8_t>(ws, L.xs);
     uint16_t *xn = at<uint16_t>(ws, L.xn);
     if (moe::launch_rmsnorm(x, T, H, norm_scale, norm_eps, xn, mxp ? xs : nullptr,
@@ -290,7 +301,7 @@ const char *moe_status_string(int status) {
 }
 
 size_t moe_workspace_size(int64_t T, int32_t E, int32_t k, int32_t H, int32_t I, int32_t path) {
-  if (path < MOE_PATH_AUTO || path > MOE_PATH_GEMM_MX) return 0;
+  if (path < MOE_PATH_AUTO || path > MOE_PATH_PREFILL_MX6SPLIT) return 0;
   if (check_common(T, E, k) != MOE_OK || check_dim(H) != MOE_OK || check_dim(I) != MOE_OK) return 0;
   WsLayout L;
   if (!ws_layout(T, E, k, H, I, &L)) return 0;

@@ -107,6 +107,8 @@ def test_ffn_and_forward_errors():
     assert lib.moe_mxfp4_ffn(*args(gr, d, o)) == L.MOE_ERR_INVALID_ARG
     assert lib.moe_mxfp4_ffn(*args(g, d, L.MoeOptions(7.0, 1.0, 3, 0, 0))) == L.MOE_ERR_INVALID_ARG
     assert lib.moe_mxfp4_ffn(*args(g, d, L.MoeOptions(7.0, 1.0, 0, 9, 0))) == L.MOE_ERR_INVALID_ARG
+    for path in (2, 3, 4):  # the grouped GEMMs need tiled weights
+        assert lib.moe_mxfp4_ffn(*args(g, d, L.MoeOptions(7.0, 1.0, 0, path, 0))) == L.MOE_ERR_UNSUPPORTED
     assert lib.moe_mxfp4_ffn(*args(g, d, L.MoeOptions(-1.0, 1.0, 0, 0, 0))) == L.MOE_ERR_INVALID_ARG
     assert lib.moe_mxfp4_ffn(*args(g, d, L.MoeOptions(7.0, 1.0, 0, 0, 3))) == L.MOE_ERR_INVALID_ARG
     assert lib.moe_mxfp4_ffn(*args(g, d, o, wsb=64)) == L.MOE_ERR_WORKSPACE

@@ -98,7 +98,8 @@ def _gpu_block(dev, scale_d, out_dtype, path=0):
 @pytest.mark.parametrize("name,T,path", [("tiny", 16, 0), ("tiny", 16, 1), ("tiny", 16, 2), ("tiny", 16, 3),
                                          ("decode20b", 64, 0), ("decode20b", 1024, 2), ("decode20b", 1024, 3),
                                          ("decode20b", 3, 3), ("prefill20b", 4096, 0), ("wide", 20, 0),
-                                         ("wide", 20, 3)])
+                                         ("wide", 20, 3), ("tiny", 16, 4), ("decode20b", 1024, 4),
+                                         ("wide", 20, 4)])  # (path 4 kernel against kernel: any shape)
 def test_block_equals_layer_on_normalised_rows(name, T, path):
     """Kernel against kernel: the block's fp32 output is the layer's fp32 output on
     moe_rmsnorm's rows plus x, bit for bit (so the records the normalisation writes for the
@@ -176,10 +177,11 @@ def test_block_decode120b_zipf():
     _check_block("decode120b_zipf", 256)
 
 
-def test_block_prefill20b_full():
+@pytest.mark.parametrize("path", [0, 4])
+def test_block_prefill20b_full(path):
     """All 4096 tokens of the block at the 20b prefill shape (AUTO: the normalisation writes
-    the block-scaled GEMM's records)."""
-    _check_block("prefill20b", 4096, 0)
+    the block-scaled GEMM's records; path 4 gathers MXFP6 records from the normalised rows)."""
+    _check_block("prefill20b", 4096, path)
 
 
 def test_block_in_place():

@@ -129,7 +129,7 @@ def _ffn_inputs(E, H, I, scale_lo, scale_hi, seed):
     return w1c, w1s, w2c, w2s
 
 
-@pytest.mark.parametrize("tiled,path", [(False, 1), (True, 1), (True, 2), (True, 3)])
+@pytest.mark.parametrize("tiled,path", [(False, 1), (True, 1), (True, 2), (True, 3), (True, 4)])
 @pytest.mark.parametrize("scale_lo,scale_hi", [(4, 252), (123, 127)])
 def test_ffn_preact_identity_decode(scale_lo, scale_hi, tiled, path):
     """One-hot activations and no bias: h = W1 x is one decoded weight column, exactly."""
@@ -154,7 +154,7 @@ def test_ffn_preact_identity_decode(scale_lo, scale_hi, tiled, path):
             assert np.array_equal(y[r], W1[:, t]), (e, t)
 
 
-@pytest.mark.parametrize("tiled,path", [(False, 1), (True, 1), (True, 2), (True, 3)])
+@pytest.mark.parametrize("tiled,path", [(False, 1), (True, 1), (True, 2), (True, 3), (True, 4)])
 def test_ffn_activation_step(tiled, path):
     """Stop after the SwiGLU: the bf16-rounded activation of every slot."""
     cfg = synth.get_config("tiny").with_(scale_bytes=(118, 122))
@@ -181,6 +181,68 @@ def _e4m3_values() -> np.ndarray:
     return (np.where(c & 0x80, -v, v)).astype(np.float32)
 
 
+def _preact_inputs(kind):
+    cfg = synth.get_config("tiny").with_(scale_bytes=(118, 122))
+    inp = synth.make_inputs(cfg)
+    rng = np.random.default_rng(77)
+    if kind == "narrow":
+        codes = rng.integers(0x38, 0x48, inp.x.shape) | (rng.integers(0, 2, inp.x.shape) << 7)
+        inp.x[...] = synth.bf16_bits_from_f32(_e4m3_values()[codes])
+    elif kind == "spread":
+        xf = synth.f32_from_bf16_bits(inp.x) * np.exp2(rng.integers(-12, 4, inp.x.shape)).astype(np.float32)
+        inp.x[...] = synth.bf16_bits_from_f32(xf)
+    return cfg, inp
+
+
+def _preacts(cfg, inp, paths):
+    dev = gu.device_layer(inp, tiled=True)
+    _, off, ss, _ = oracle.permute(gu.oracle_forward(inp, None, keep_intermediates=True).idx, cfg.E)
+    out = {}
+    for path in paths:
+        out[path] = moe.moe_mxfp4_ffn(dev.x, cfg.k, cfg.E, torch.from_numpy(off).cuda(), torch.from_numpy(ss).cuda(),
+                                      dev.w1, dev.w2, moe.Options(flags=moe.MOE_FLAG_EMIT_PREACT, path=path)
+                                      ).cpu().numpy()
+    return off, ss, out
+
+
+@pytest.mark.parametrize("scales", [(118, 122), (121, 124), (123, 127)])
+def test_mx6_down_error_bound(scales):
+    """The down projection on two-term MXFP6 activations (path 4) against the same projection on
+    the exact two-term MXFP8 split (path 3): both gate_ups round the same activation to bf16, so
+    the outputs differ by the MXFP6 split alone. Each activation's two E2M3 terms miss its bf16
+    value by at most 2^-9 of its 32-element block's maximum M_b (the hi term's scale puts M_b in
+    [2, 4), the residual is at most 1/8 there, and the lo term, 2^-5 below, rounds it to within
+    1/8 of its own unit), so |y4 - y3| <= 2^-9 sum_b M_b sum_{i in b} |W2[n, i]|, plus fp32
+    summation slack and the scaled MFMA's reduced-precision block sums (the allowance
+    test_mx_preact_matches_bf16_gemm holds the MXFP8 path to). The scale ranges give ~0%, ~50%
+    and ~93% clamped pre-activations."""
+    cfg = synth.get_config("tiny").with_(scale_bytes=scales)
+    inp = synth.make_inputs(cfg)
+    dev = gu.device_layer(inp, tiled=True)
+    _, off, ss, _ = oracle.permute(gu.oracle_forward(inp, None).idx, cfg.E)
+    offd, ssd = torch.from_numpy(off).cuda(), torch.from_numpy(ss).cuda()
+
+    def ffn(path, flags=0):
+        return moe.moe_mxfp4_ffn(dev.x, cfg.k, cfg.E, offd, ssd, dev.w1, dev.w2,
+                                 moe.Options(flags=flags, path=path)).cpu().numpy().astype(np.float64)
+    act = ffn(3, moe.MOE_FLAG_EMIT_ACT)
+    assert np.array_equal(act, ffn(4, moe.MOE_FLAG_EMIT_ACT))  # the same gate_up
+    y3, y4 = ffn(3), ffn(4)
+    S, I = act.shape
+    M = np.abs(act).reshape(S, I // 32, 32).max(-1)
+    hw = 2e-4 * np.sqrt(np.mean(y3 ** 2))
+    for e in range(cfg.E):
+        rows = np.arange(off[e], off[e + 1])
+        if rows.size == 0:
+            continue
+        W = np.abs(oracle.mxfp4_decode(inp.w2_codes[e], inp.w2_scales[e]))  # [H][I]
+        bound = 2.0 ** -9 * (M[rows] @ W.reshape(W.shape[0], I // 32, 32).sum(-1).T)
+        slack = 4e-6 * (np.abs(act[rows]) @ W.T) + hw
+        d = np.abs(y4[rows] - y3[rows])
+        assert (d <= bound + slack).all(), (e, float((d - bound - slack).max()))
+    assert np.abs(y4 - y3).max() > 0.0  # the split is not exact on these activations
+
+
 @pytest.mark.parametrize("kind,tol", [("narrow", 1e-6), ("plain", 2e-4), ("spread", 2e-3)])
 def test_mx_preact_matches_bf16_gemm(kind, tol):
     """Pre-activations of the block-scaled GEMM against the bf16 GEMM (exact products, fp32 sums).
@@ -192,22 +254,8 @@ def test_mx_preact_matches_bf16_gemm(kind, tol):
     is still exact, but the scaled MFMA sums a block's products in reduced internal precision
     when they span a wide range (measured: 4.6e-5 and 4.7e-4 of the RMS, against 3e-7 for the
     bf16 path); the bounds keep a 4x margin and stay far inside the layer's 2e-2 RMS tolerance."""
-    cfg = synth.get_config("tiny").with_(scale_bytes=(118, 122))
-    inp = synth.make_inputs(cfg)
-    rng = np.random.default_rng(77)
-    if kind == "narrow":
-        codes = rng.integers(0x38, 0x48, inp.x.shape) | (rng.integers(0, 2, inp.x.shape) << 7)
-        inp.x[...] = synth.bf16_bits_from_f32(_e4m3_values()[codes])
-    elif kind == "spread":
-        xf = synth.f32_from_bf16_bits(inp.x) * np.exp2(rng.integers(-12, 4, inp.x.shape)).astype(np.float32)
-        inp.x[...] = synth.bf16_bits_from_f32(xf)
-    dev = gu.device_layer(inp, tiled=True)
-    _, off, ss, _ = oracle.permute(gu.oracle_forward(inp, None, keep_intermediates=True).idx, cfg.E)
-    out = {}
-    for path in (2, 3):
-        out[path] = moe.moe_mxfp4_ffn(dev.x, cfg.k, cfg.E, torch.from_numpy(off).cuda(), torch.from_numpy(ss).cuda(),
-                                      dev.w1, dev.w2, moe.Options(flags=moe.MOE_FLAG_EMIT_PREACT, path=path)
-                                      ).cpu().numpy()
+    cfg, inp = _preact_inputs(kind)
+    _, _, out = _preacts(cfg, inp, (2, 3))
     scale = np.sqrt(np.mean(out[2] ** 2))
     assert np.abs(out[3] - out[2]).max() <= tol * scale, np.abs(out[3] - out[2]).max() / scale
 
@@ -269,7 +317,7 @@ def test_layer_tiny(tiled, path):
     _check_layer(synth.make_inputs(synth.get_config("tiny")), tiled=tiled, path=path)
 
 
-@pytest.mark.parametrize("path", [1, 2, 3])
+@pytest.mark.parametrize("path", [1, 2, 3, 4])
 def test_gemm_and_stream_agree(path):
     """Both kernel families on the same 1024-token batch: each against the oracle on samples."""
     cfg = synth.get_config("decode20b")
@@ -352,7 +400,7 @@ def _full_layer(name):
     return _FULL[name]
 
 
-@pytest.mark.parametrize("path", [0, 1, 2])
+@pytest.mark.parametrize("path", [0, 1, 2, 3, 4])
 def test_layer_prefill20b_full(path):
     """Every one of the 4096 tokens' outputs (fp32 and bf16) element by element: every m-tile,
     n-tile and tail tile of the grouped GEMM is compared (path 0 = AUTO, the block-scaled GEMM)."""
@@ -360,13 +408,13 @@ def test_layer_prefill20b_full(path):
     _check_layer(inp, path=path, dev=dev, ref=ref)
 
 
-@pytest.mark.parametrize("path", [0, 2])
+@pytest.mark.parametrize("path", [0, 2, 4])
 def test_layer_prefill120b_full(path):
     inp, dev, _, ref = _full_layer("prefill120b")
     _check_layer(inp, path=path, dev=dev, ref=ref)
 
 
-@pytest.mark.parametrize("path", [0, 2])
+@pytest.mark.parametrize("path", [0, 2, 4])
 def test_prefill20b_steps_on_subset(path):
     """Per-step checks at the full 4096-token launch, graded on a seeded 256-token subset: the
     pre-activations h = W1 x + b1, the bf16 activation and the down output y of each of the
@@ -413,6 +461,40 @@ def test_layer_shapes(E, k, H, I, T, tiled, path):
     _check_layer(synth.make_inputs(_small_cfg(E, k, H, I, T)), tiled=tiled, path=path, act_rounded=degenerate)
 
 
+@pytest.mark.parametrize("E,k,H,I,T", [(4, 4, 128, 96, 9), (16, 8, 96, 160, 21), (256, 4, 64, 32, 40),
+                                       (8, 4, 256, 128, 100), (4, 2, 288, 160, 300), (2, 1, 160, 96, 70),
+                                       (32, 8, 2880, 2880, 40), (4, 2, 256, 1024, 300)])
+def test_layer_shapes_mx6(E, k, H, I, T):
+    """The MXFP6 down path (opt-in, never AUTO) on small shapes, against the layer it must equal up
+    to its own split: path 3's output (exact two-term MXFP8 activations) plus at most the split's
+    proven bound per output (test_mx6_down_error_bound), and against the oracle within
+    2e-2 x RMS where the down projection is long (I >= 1024). A down projection of ~100 terms
+    averages few split errors: one of these shapes (E = 2, I = 96) sits at 2.04% of the RMS."""
+    inp = synth.make_inputs(_small_cfg(E, k, H, I, T))
+    dev = gu.device_layer(inp, tiled=True)
+    o3 = _run_forward(dev, moe.MOE_DTYPE_F32, 3).cpu().numpy().astype(np.float64)
+    o4 = _run_forward(dev, moe.MOE_DTYPE_F32, 4).cpu().numpy().astype(np.float64)
+    assert np.isfinite(o4).all()
+    # the bound of the split, weighted like the combine: sum_j w_j 2^-9 sum_b M_b sum_i |W2|, with
+    # the activations of path 3 (the same gate_up) and the GPU's routing
+    idx, w = moe.moe_route(dev.x, dev.router, dev.k)
+    idx, w = idx.cpu().numpy(), w.cpu().numpy().astype(np.float64)
+    _, off, ss, sr = oracle.permute(idx, E)
+    act = moe.moe_mxfp4_ffn(dev.x, k, E, torch.from_numpy(off).cuda(), torch.from_numpy(ss).cuda(), dev.w1, dev.w2,
+                            moe.Options(flags=moe.MOE_FLAG_EMIT_ACT, path=3)).cpu().numpy().astype(np.float64)
+    M = np.abs(act).reshape(act.shape[0], I // 32, 32).max(-1)  # [sorted row][block]
+    bound = np.zeros_like(o3)
+    for e in range(E):
+        W = np.abs(oracle.mxfp4_decode(inp.w2_codes[e], inp.w2_scales[e])).reshape(H, I // 32, 32).sum(-1)
+        for r in range(off[e], off[e + 1]):
+            s_ = ss[r]
+            bound[s_ // k] += w[s_ // k, s_ % k] * 2.0 ** -9 * (W @ M[r])
+    slack = 2e-4 * np.sqrt(np.mean(o3 ** 2))
+    assert (np.abs(o4 - o3) <= bound + slack).all()
+    if I >= 1024:
+        _check_layer(inp, path=4, dev=dev)
+
+
 @pytest.mark.parametrize("tiled,path", [(False, 0), (True, 1), (True, 2), (True, 3)])
 @pytest.mark.parametrize("E,k,H,I,T", [(2, 1, 16384, 256, 5), (2, 2, 256, 16384, 7)])
 def test_layer_largest_widths(E, k, H, I, T, tiled, path):
@@ -457,3 +539,25 @@ def test_determinism_and_guard_regions():
     assert np.array_equal(first, gu.bf16_bits(out)), "two runs differ"
     b = buf.cpu().numpy()
     assert (b[:pad] == 12345).all() and (b[pad + T * H:] == 12345).all(), "write outside the output"
+
+
+def test_side_streams():
+    """Calls on explicit side streams (the binding allocates its temporaries there) give the bits
+    of the current-stream call; moe_forward on two streams runs on two owned workspaces."""
+    cfg = synth.get_config("decode20b")
+    dev = gu.device_layer(synth.make_inputs(cfg, 64))
+    want = gu.bf16_bits(moe.moe_forward_ex(dev.x, dev.router, dev.w1, dev.w2, dev.k, moe.Options()))
+    s1, s2 = torch.cuda.Stream(), torch.cuda.Stream()
+    s1.wait_stream(torch.cuda.current_stream())
+    s2.wait_stream(torch.cuda.current_stream())
+    o1 = moe.moe_forward_ex(dev.x, dev.router, dev.w1, dev.w2, dev.k, moe.Options(), stream=s1)
+    o2 = moe.moe_forward(dev.x, dev.router, dev.w1, dev.w2, dev.k, stream=s2)
+    o3 = moe.moe_forward(dev.x, dev.router, dev.w1, dev.w2, dev.k, stream=s1)
+    idx, w = moe.moe_route(dev.x, dev.router, dev.k, stream=s2)
+    off, ss, sr = moe.moe_permute(idx, cfg.E, stream=s2)
+    y = moe.moe_mxfp4_ffn(dev.x, dev.k, cfg.E, off, ss, dev.w1, dev.w2, moe.Options(), stream=s2)
+    o4 = moe.moe_combine(y, sr, w, stream=s2)
+    s1.synchronize()
+    s2.synchronize()
+    for o in (o1, o2, o3, o4):
+        assert np.array_equal(gu.bf16_bits(o), want)

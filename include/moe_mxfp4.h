@@ -48,6 +48,7 @@ extern "C" {
 #define MOE_ERR_UNSUPPORTED (-2)  /* shape outside the limits above */
 #define MOE_ERR_WORKSPACE (-3)    /* caller workspace smaller than moe_workspace_size() */
 #define MOE_ERR_HIP (-4)          /* a HIP runtime call or kernel launch failed */
+#define MOE_ERR_SCRATCH (-5)      /* moe_forward_noalloc: the sizes need more than its fixed scratch */
 
 /* output element types */
 #define MOE_DTYPE_BF16 0
@@ -301,6 +302,24 @@ int moe_attn_decode(const uint16_t *q, const uint16_t *k_cache, const uint16_t *
                     const float *sinks, int64_t B, int32_t n_q_heads, int32_t n_kv_heads, int32_t head_dim,
                     int64_t max_len, int32_t window, void *out, int32_t out_dtype, void *ws, size_t ws_bytes,
                     moe_stream_t stream);
+
+/*
+ * moe_forward for callers that cannot allocate device memory (code under HIP graph capture,
+ * tight serving loops, harnesses that forbid hipMalloc): the same layer, the same kernels and
+ * the same result as moe_forward, with its workspace in a fixed device array of
+ * moe_noalloc_scratch_bytes() bytes (64 MiB) that each GPU the library runs on holds until the
+ * process ends. The call itself allocates nothing, never synchronises and records no memset.
+ * Sizes whose workspace (moe_workspace_size(T, E, k, H, I, MOE_PATH_AUTO)) exceeds the array are
+ * rejected with MOE_ERR_SCRATCH before anything is launched; at H = I = 2880, k = 4 that allows
+ * about 650 tokens. Every call on one GPU uses that GPU's one array, and the array keeps the last
+ * call's contents (each call zeroes, by a kernel of its own, what it needs zeroed): calls that
+ * overlap on one GPU (other streams, other host threads) race on it and must be serialised by
+ * the caller, e.g. issued on one stream.
+ */
+int moe_forward_noalloc(const uint16_t *x, const moe_router_t *router, const moe_mxfp4_weight_t *w_gate_up,
+                        const moe_mxfp4_weight_t *w_down, int64_t T, int32_t E, int32_t k, uint16_t *out,
+                        moe_stream_t stream);
+size_t moe_noalloc_scratch_bytes(void);
 
 /* Free moe_forward's workspaces (every stream's) on the current device (synchronises the
  * device first). */

@@ -32,6 +32,7 @@ from .ops import (  # noqa: F401
     moe_combine,
     moe_forward,
     moe_forward_ex,
+    moe_forward_noalloc,
     moe_mxfp4_dequant,
     moe_mxfp4_ffn,
     moe_mxfp4_pack,

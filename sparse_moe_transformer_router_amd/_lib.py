@@ -20,6 +20,7 @@ MOE_ERR_INVALID_ARG = -1
 MOE_ERR_UNSUPPORTED = -2
 MOE_ERR_WORKSPACE = -3
 MOE_ERR_HIP = -4
+MOE_ERR_SCRATCH = -5
 
 MOE_DTYPE_BF16 = 0
 MOE_DTYPE_F32 = 1
@@ -92,6 +93,10 @@ SIGNATURES = {
     "moe_attn_workspace_size": (c_size_t, [c_int64, c_int32, c_int64, c_int32]),
     "moe_attn_decode": (c_int32, [c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_int64, c_int32, c_int32,
                                   c_int32, c_int64, c_int32, c_void_p, c_int32, c_void_p, c_size_t, c_void_p]),
+    "moe_forward_noalloc": (c_int32, [c_void_p, ctypes.POINTER(MoeRouter), ctypes.POINTER(MoeMxfp4Weight),
+                                      ctypes.POINTER(MoeMxfp4Weight), c_int64, c_int32, c_int32, c_void_p,
+                                      c_void_p]),
+    "moe_noalloc_scratch_bytes": (c_size_t, []),
     "moe_release_workspace": (c_int32, []),
 }
 

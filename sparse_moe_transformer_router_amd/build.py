@@ -35,6 +35,7 @@ SOURCES = [
     "combine.hip",
     "norm.hip",
     "attn.hip",
+    "noalloc.hip",
 ]
 
 ARCH = "gfx950"

@@ -85,6 +85,11 @@ hipError_t launch_gather_rows(const uint16_t *x, const int32_t *sorted_slot, int
 hipError_t launch_gather_rows_mx(const uint16_t *x, const int32_t *sorted_slot, int k, int64_t S, int H,
                                  uint8_t *rec, uint8_t *scales, hipStream_t stream);
 
+// The fixed device array behind moe_forward_noalloc (noalloc.hip): its size, and this device's
+// address of it (looked up once per device, then kept).
+size_t scratch_bytes();
+hipError_t scratch_address(void **ptr);
+
 // residual (bf16 [T][H], nullable) is added to the weighted sum before the rounding.
 hipError_t launch_combine(const float *y, const int32_t *slot_row, const float *topk_w, int64_t T,
                           int k, int H, void *out, bool out_f32, hipStream_t stream,

@@ -296,6 +296,7 @@ const char *moe_status_string(int status) {
     case MOE_ERR_UNSUPPORTED: return "unsupported shape (k, E, H, I or T*k outside the limits)";
     case MOE_ERR_WORKSPACE: return "workspace too small";
     case MOE_ERR_HIP: return "HIP runtime or kernel launch error";
+    case MOE_ERR_SCRATCH: return "the call needs more workspace than moe_forward_noalloc's fixed scratch holds";
     default: return "unknown status";
   }
 }
@@ -559,6 +560,25 @@ int moe_forward(const uint16_t *x, const moe_router_t *router, const moe_mxfp4_w
   return forward_impl(x, router, w_gate_up, w_down, T, E, k, o, out, ws, L.total, s);
   MOE_GUARD_END
 }
+
+int moe_forward_noalloc(const uint16_t *x, const moe_router_t *router, const moe_mxfp4_weight_t *w_gate_up,
+                        const moe_mxfp4_weight_t *w_down, int64_t T, int32_t E, int32_t k, uint16_t *out,
+                        moe_stream_t stream) {
+  MOE_GUARD_BEGIN
+  int st = check_layer(x, router, w_gate_up, w_down, T, E, k, out);
+  if (st != MOE_OK) return st;
+  if (T == 0) return MOE_OK;
+  WsLayout L;
+  ws_layout(T, E, k, w_gate_up->k, w_down->k, &L);
+  if (L.total > moe::scratch_bytes()) return MOE_ERR_SCRATCH;
+  void *ws = nullptr;
+  if (moe::scratch_address(&ws) != hipSuccess) return MOE_ERR_HIP;
+  return forward_impl(x, router, w_gate_up, w_down, T, E, k, default_options(), out, ws, L.total,
+                      (hipStream_t)stream);
+  MOE_GUARD_END
+}
+
+size_t moe_noalloc_scratch_bytes(void) { return moe::scratch_bytes(); }
 
 int moe_release_workspace(void) {
   MOE_GUARD_BEGIN

@@ -208,6 +208,21 @@ def moe_forward(x: torch.Tensor, router: Router, w_gate_up: MXFP4Weight, w_down:
     return out
 
 
+def moe_forward_noalloc(x: torch.Tensor, router: Router, w_gate_up: MXFP4Weight, w_down: MXFP4Weight, k: int,
+                        out: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    """moe_forward with the library's fixed device scratch as its workspace (no allocation in the
+    library; `out` is allocated here only if it is not given)."""
+    T, H = x.shape
+    E = int(router.weight.shape[0])
+    if out is None:
+        out = _empty((T, H), torch.bfloat16, x.device, stream)
+    r, g, d = router.desc(), w_gate_up.desc(), w_down.desc()
+    L.check("moe_forward_noalloc", L.lib().moe_forward_noalloc(_ptr(x), ctypes.byref(r), ctypes.byref(g),
+                                                                  ctypes.byref(d), T, E, k, _ptr(out),
+                                                                  _stream(stream)))
+    return out
+
+
 def moe_forward_ex(x: torch.Tensor, router: Router, w_gate_up: MXFP4Weight, w_down: MXFP4Weight, k: int,
                    opts: Optional[Options] = None, out: Optional[torch.Tensor] = None, ws=None,
                    stream=None) -> torch.Tensor:

@@ -1,0 +1,48 @@
+"""The allocation-free entry point (moe_forward_noalloc), through the C ABI, against moe_forward:
+the same kernels on the same inputs, so the same bits; two calls in a row on the one fixed
+scratch array, the second with a smaller batch (the array keeps the first call's contents)."""
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import gpu_util as gu
+import synth
+
+pytestmark = pytest.mark.gpu
+
+moe = pytest.importorskip("sparse_moe_transformer_router_amd")
+
+
+@pytest.fixture(autouse=True)
+def _announce(request):
+    sys.__stderr__.write(f"\n[gpu case] {request.node.nodeid}\n")
+    sys.__stderr__.flush()
+    yield
+    torch.cuda.synchronize()
+
+
+@pytest.mark.parametrize("name,T1,T2", [("decode20b", 64, 8), ("decode120b_zipf", 256, 16), ("tiny", 16, 3)])
+def test_noalloc_matches_moe_forward(name, T1, T2):
+    cfg = synth.get_config(name)
+    for T in (T1, T2):  # the second call runs on what the first left in the scratch array
+        dev = gu.device_layer(synth.make_inputs(cfg, T), tiled=name != "tiny")
+        got = gu.bf16_bits(moe.moe_forward_noalloc(dev.x, dev.router, dev.w1, dev.w2, dev.k))
+        want = gu.bf16_bits(moe.moe_forward(dev.x, dev.router, dev.w1, dev.w2, dev.k))
+        assert np.array_equal(got, want), (name, T)
+
+
+def test_noalloc_rejects_sizes_beyond_the_scratch():
+    cfg = synth.get_config("decode20b")
+    lib = moe.lib()
+    cap = int(lib.moe_noalloc_scratch_bytes())
+    T = 1
+    while moe.moe_workspace_size(T, cfg.E, cfg.k, cfg.H, cfg.I) <= cap:
+        T *= 2
+    inp = synth.make_inputs(cfg, 1)
+    dev = gu.device_layer(inp, tiled=True)
+    x = torch.zeros((T, cfg.H), dtype=torch.bfloat16, device="cuda")
+    with pytest.raises(moe.MoeError) as err:
+        moe.moe_forward_noalloc(x, dev.router, dev.w1, dev.w2, dev.k)
+    assert err.value.status == -5  # MOE_ERR_SCRATCH: rejected before any launch

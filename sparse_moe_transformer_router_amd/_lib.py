@@ -13,7 +13,9 @@ import threading
 import torch  # noqa: F401  (must precede the library load: one HIP runtime per process)
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_PKG, "lib", "libmoe_mxfp4.so")
+# MOE_MXFP4_LIBRARY selects another build of the same library (the host-sanitizer build of the
+# C ABI's tests); by default the in-tree build.
+LIB_PATH = os.environ.get("MOE_MXFP4_LIBRARY") or os.path.join(_PKG, "lib", "libmoe_mxfp4.so")
 
 MOE_OK = 0
 MOE_ERR_INVALID_ARG = -1

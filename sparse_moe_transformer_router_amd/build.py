@@ -1,6 +1,6 @@
 """Compile the HIP library in-tree for gfx950: sparse_moe_transformer_router_amd/lib/libmoe_mxfp4.so.
 
-    python -m sparse_moe_transformer_router_amd.build [--verbose]
+    python -m sparse_moe_transformer_router_amd.build [--verbose] [--asan]
 
 Every source is compiled with hipcc (objects in parallel) and linked into one shared
 library; nothing is JIT-compiled at import time.
@@ -73,29 +73,48 @@ def _run(cmd, verbose):
     return r
 
 
-def build(verbose: bool = False, jobs: int = 0) -> str:
+# Host-side AddressSanitizer build of the same sources (the GPU code is built as always): the
+# C ABI's argument checks, workspace layout and host logic run instrumented on the CPU. Load it
+# with the sanitizer runtime preloaded (asan_runtime()) and MOE_MXFP4_LIBRARY pointing at it.
+ASAN_FLAGS = ["-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fno-omit-frame-pointer"]
+ASAN_LIB_PATH = os.path.join(LIB_DIR, "libmoe_mxfp4_asan.so")
+
+
+def asan_runtime() -> str:
+    """Path of the compiler's shared AddressSanitizer runtime (to preload into the host process)."""
+    clang = os.path.join(os.path.dirname(os.path.realpath(_hipcc())), "..", "llvm", "bin", "clang")
+    if not os.path.exists(clang):
+        clang = shutil.which("amdclang") or "/opt/rocm/llvm/bin/clang"
+    r = subprocess.run([clang, "-print-file-name=libclang_rt.asan-x86_64.so"], capture_output=True, text=True)
+    return r.stdout.strip()
+
+
+def build(verbose: bool = False, jobs: int = 0, asan: bool = False) -> str:
     """Compile every source and link the shared library; returns its path."""
     hipcc = _hipcc()
-    os.makedirs(OBJ_DIR, exist_ok=True)
+    obj_dir = OBJ_DIR + ("_asan" if asan else "")
+    lib_path = ASAN_LIB_PATH if asan else LIB_PATH
+    os.makedirs(obj_dir, exist_ok=True)
     os.makedirs(LIB_DIR, exist_ok=True)
     t0 = time.time()
     objs = []
     cmds = []
     for src in SOURCES:
-        obj = os.path.join(OBJ_DIR, os.path.splitext(src)[0] + ".o")
+        obj = os.path.join(obj_dir, os.path.splitext(src)[0] + ".o")
         objs.append(obj)
-        cmds.append([hipcc, *HIPCC_FLAGS, "-c", os.path.join(CSRC, src), "-o", obj])
+        cmds.append([hipcc, *HIPCC_FLAGS, *(ASAN_FLAGS if asan else []), "-c", os.path.join(CSRC, src), "-o", obj])
     jobs = jobs or min(len(cmds), max(1, min(8, os.cpu_count() or 1)))
     with concurrent.futures.ThreadPoolExecutor(jobs) as ex:
         for fut in [ex.submit(_run, c, verbose) for c in cmds]:
             fut.result()
-    tmp = LIB_PATH + ".tmp"
-    _run([hipcc, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, *objs], verbose)
-    os.replace(tmp, LIB_PATH)
+    tmp = lib_path + ".tmp"
+    _run([hipcc, f"--offload-arch={ARCH}", "-shared", "-fPIC", *(ASAN_FLAGS if asan else []), "-o", tmp, *objs],
+         verbose)
+    os.replace(tmp, lib_path)
     if verbose:
-        print(f"built {LIB_PATH} in {time.time() - t0:.1f}s", flush=True)
-    return LIB_PATH
+        print(f"built {lib_path} in {time.time() - t0:.1f}s", flush=True)
+    return lib_path
 
 
 if __name__ == "__main__":
-    build(verbose="--verbose" in sys.argv or "-v" in sys.argv)
+    build(verbose="--verbose" in sys.argv or "-v" in sys.argv, asan="--asan" in sys.argv)

@@ -208,6 +208,11 @@ int moe_permute(const int32_t *topk_idx, int64_t T, int32_t E, int32_t k, int32_
  * x bf16 [T][H]; gate_up->n = 2 * down->k, gate_up->k = down->n = H.
  * opts->flags may stop early (MOE_FLAG_EMIT_PREACT: y is [T*k][2I]; MOE_FLAG_EMIT_ACT:
  * y is [T*k][I]). ws: at least moe_workspace_size(T, E, k, H, I, opts->path) bytes.
+ * The routing must give each expert at most one slot per token (distinct experts in each
+ * token's k picks, as moe_route's top-k and moe_permute produce): on AUTO with tiled weights, one
+ * token, H <= 3072 and I <= 4096 the FFNs run fused per (expert, 32-activation block) with the
+ * token's row staged on chip, and an expert holding more than one slot there gives unspecified
+ * values for its slots (never an access outside the buffers).
  */
 int moe_mxfp4_ffn(const uint16_t *x, int64_t T, int32_t k, int32_t E, const int32_t *expert_offsets,
                   const int32_t *sorted_slot, const moe_mxfp4_weight_t *gate_up,

@@ -47,7 +47,8 @@ hipError_t launch_permute(const int32_t *topk_idx, int64_t S, int E, int32_t *of
 
 // Decode-sized batches (topk_permute_fits): the top-k step of launch_router on the partials of
 // launch_router_partial (token-major; counter zeroed by that launch), and the permutation of
-// launch_permute, in one launch. Same outputs as the two separate steps.
+// launch_permute, in one launch. Same outputs as the two separate steps. Up to 16 tokens one
+// workgroup does both (the counter is not used).
 bool topk_permute_fits(int64_t T, int E, int k);
 hipError_t launch_router_topk_permute(const float *partial, int nsplit, const float *bias, int64_t T, int E, int k,
                                       int32_t *topk_idx, float *topk_w, int *counter, int32_t *offsets,
@@ -76,6 +77,25 @@ hipError_t launch_ffn_gemm(const void *a, const uint8_t *a_scales, const int32_t
                            const int32_t *offsets, int E, int64_t S, const MxWeight &w, int epilogue, void *out,
                            uint8_t *out_scales, float limit, float alpha, hipStream_t stream);
 
+// Smallest decode batches (T <= kSmallMaxT, H <= 3072, I <= 32 kSmallMaxSlices, tiled weights):
+// gate_up, SwiGLU and the down projection in one launch (ffn_small.hip), one workgroup per
+// (expert, 32-activation block). Writes per-block partial outputs part[block][sorted row][H]
+// (small_partial_floats floats; b2 in block 0); the combine adds the blocks in order. Every
+// expert must hold at most kSmallMaxT slots (top-k routing picks distinct experts per token,
+// so T <= kSmallMaxT does). One token only: the kernel's VALU products grow with the slots,
+// and from two tokens on the two-kernel form on the matrix cores is faster.
+constexpr int kSmallMaxT = 1;
+constexpr int kSmallMaxSlices = 128;  // the sliced combine's limit
+bool small_ffn_fits(int64_t T, int H, int I);
+int small_slices(int I);
+size_t small_partial_floats(int64_t T, int k, int H, int I);
+hipError_t launch_ffn_small(const uint16_t *x, const int32_t *sorted_slot, int k, const int32_t *offsets, int E,
+                            int64_t S, const MxWeight &w1, const MxWeight &w2, float *part, float limit, float alpha,
+                            hipStream_t stream);
+// y[r][h] = the sum over s = 0 .. nslice-1 of part[s][r][h] (S rows of H), in the fixed order of
+// launch_combine_sliced.
+hipError_t launch_slice_sum(const float *part, int nslice, int64_t S, int H, float *y, hipStream_t stream);
+
 // xs[r] = x[sorted_slot[r] / k] for every sorted row r (rows of H bf16).
 hipError_t launch_gather_rows(const uint16_t *x, const int32_t *sorted_slot, int k, int64_t S, int H,
                               uint16_t *xs, hipStream_t stream);
@@ -94,6 +114,12 @@ hipError_t scratch_address(void **ptr);
 hipError_t launch_combine(const float *y, const int32_t *slot_row, const float *topk_w, int64_t T,
                           int k, int H, void *out, bool out_f32, hipStream_t stream,
                           const uint16_t *residual = nullptr);
+// The same combine when each picked expert's output row is the sum of nslice partial rows
+// (part + s * S * H, s = 0 .. nslice-1; the smallest-batch path), summed in the fixed order that
+// launch_slice_sum uses. nslice <= kSmallMaxSlices.
+hipError_t launch_combine_sliced(const float *part, int nslice, const int32_t *slot_row, const float *topk_w,
+                                 int64_t T, int k, int H, void *out, bool out_f32, hipStream_t stream,
+                                 const uint16_t *residual);
 
 // xn = bf16(x / sqrt(mean(x^2) + eps) * scale) per row of H; with rec non-null also the rows'
 // two-term MXFP8 records and scales (as launch_gather_rows_mx with sorted_slot null, of xn).

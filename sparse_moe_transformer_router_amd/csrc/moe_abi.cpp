@@ -24,7 +24,7 @@ size_t align_up(size_t v) { return (v + kWsAlign - 1) / kWsAlign * kWsAlign; }
 
 // One workspace layout serves every entry point (each uses a subset of the regions).
 struct WsLayout {
-  size_t logits, topk_idx, topk_w, offsets, counter, sorted_slot, slot_row, act, y, xs, xn, pscratch, total;
+  size_t logits, topk_idx, topk_w, offsets, counter, sorted_slot, slot_row, act, y, xs, xn, pscratch, ypart, total;
 };
 
 // Bytes of S activation rows of K elements: bf16, or the two-term records and their scales
@@ -52,6 +52,7 @@ bool ws_layout(int64_t T, int E, int k, int H, int I, WsLayout *L) {
   L->xs = off;          off = align_up(off + act_rows_bytes(S, H));  // sorted x (GEMM paths)
   L->xn = off;          off = align_up(off + (size_t)T * (size_t)H * sizeof(uint16_t));  // normalised x (block)
   L->pscratch = off;    off = align_up(off + (size_t)moe::permute_scratch_ints((int64_t)S, E) * sizeof(int32_t));
+  L->ypart = off;       off = align_up(off + moe::small_partial_floats(T, k, H, I) * sizeof(float));  // smallest batches
   L->total = off;
   return true;
 }
@@ -139,9 +140,15 @@ Family family(const moe_options_t &o, const moe_mxfp4_weight_t &gu, const moe_mx
 // projections (bf16 or two-term records).
 // x_records_ready: the block-scaled families' per-token MXFP8 records of x are already in xs
 // (the block's normalisation writes them), so the gather is skipped.
+// part / nslice_out: on AUTO with tiled weights and the smallest batches (small_ffn_fits; the
+// routing picks distinct experts per token, so an expert holds at most T slots), the expert
+// FFNs run as one launch (launch_ffn_small) writing per-block partial rows into part; then
+// *nslice_out = the block count (1 or more), and y is written (the blocks' in-order sum) only
+// if want_y. Otherwise y is written and *nslice_out = 0.
 int run_ffn(const uint16_t *x, int64_t T, int k, int E, const int32_t *offsets, const int32_t *sorted_slot,
             const moe_mxfp4_weight_t &gu, const moe_mxfp4_weight_t &dn, const moe_options_t &o, float *y,
-            void *act, void *xs, hipStream_t stream, bool x_records_ready = false) {
+            void *act, void *xs, float *part, bool want_y, int *nslice_out, hipStream_t stream,
+            bool x_records_ready = false) {
   const int64_t S = T * k;
   const int H = gu.k, I = dn.k;
   const moe::MxWeight w1 = mx(gu);
@@ -151,6 +158,15 @@ int run_ffn(const uint16_t *x, int64_t T, int k, int E, const int32_t *offsets, 
   const int first_epi = (o.flags & MOE_FLAG_EMIT_PREACT) ? moe::kEpiPreactF32
                         : (o.flags & MOE_FLAG_EMIT_ACT)  ? moe::kEpiActF32
                                                          : -1;
+  *nslice_out = 0;
+  if (f == Family::kStream && o.path == MOE_PATH_AUTO && first_epi < 0 && w1.tiled && w2.tiled &&
+      moe::small_ffn_fits(T, H, I)) {
+    if (moe::launch_ffn_small(x, sorted_slot, k, offsets, E, S, w1, w2, part, lim, alpha, stream) != hipSuccess)
+      return MOE_ERR_HIP;
+    *nslice_out = moe::small_slices(I);
+    if (want_y && moe::launch_slice_sum(part, *nslice_out, S, H, y, stream) != hipSuccess) return MOE_ERR_HIP;
+    return MOE_OK;
+  }
   if (f == Family::kStream) {
     auto launch = [&](const uint16_t *a, bool by_token, const moe::MxWeight &w, int epi, void *out) {
       return moe::launch_ffn_stream(a, by_token, sorted_slot, k, offsets, E, S, w, epi, out, lim, alpha, stream);
@@ -256,11 +272,17 @@ int forward_impl(const uint16_t *x, const moe_router_t *router, const moe_mxfp4_
         hipSuccess)
       return MOE_ERR_HIP;
   }
-  int st = run_ffn(x, T, k, E, offsets, sorted_slot, *gu, *dn, o, y, act, at<void>(ws, L.xs), stream, records_ready);
+  int nslice = 0;
+  float *part = at<float>(ws, L.ypart);
+  int st = run_ffn(x, T, k, E, offsets, sorted_slot, *gu, *dn, o, y, act, at<void>(ws, L.xs), part, false, &nslice,
+                   stream, records_ready);
   if (st != MOE_OK) return st;
-  if (moe::launch_combine(y, slot_row, wts, T, k, H, out, o.out_dtype == MOE_DTYPE_F32, stream, residual) !=
-      hipSuccess)
-    return MOE_ERR_HIP;
+  // the experts' outputs: y, or the per-slice partial rows of the smallest-batch path
+  const hipError_t ce =
+      nslice > 0 ? moe::launch_combine_sliced(part, nslice, slot_row, wts, T, k, H, out, o.out_dtype == MOE_DTYPE_F32,
+                                              stream, residual)
+                 : moe::launch_combine(y, slot_row, wts, T, k, H, out, o.out_dtype == MOE_DTYPE_F32, stream, residual);
+  if (ce != hipSuccess) return MOE_ERR_HIP;
   return MOE_OK;
 }
 
@@ -420,8 +442,9 @@ int moe_mxfp4_ffn(const uint16_t *x, int64_t T, int32_t k, int32_t E, const int3
   ws_layout(T, E, k, H, I, &L);
   if (ws == nullptr || ws_bytes < L.total) return MOE_ERR_WORKSPACE;
   if (!aligned(ws, kWsAlign)) return MOE_ERR_INVALID_ARG;
+  int nslice = 0;
   return run_ffn(x, T, k, E, expert_offsets, sorted_slot, *gate_up, *down, o, y, at<void>(ws, L.act),
-                 at<void>(ws, L.xs), (hipStream_t)stream);
+                 at<void>(ws, L.xs), at<float>(ws, L.ypart), true, &nslice, (hipStream_t)stream);
   MOE_GUARD_END
 }
 

@@ -208,6 +208,7 @@ __global__ __launch_bounds__(kPermThreads) void permute_scatter_kernel(const int
 // back at device scope. No workgroup waits for another. The counter is zeroed by
 // router_partial_kernel of the same call.
 constexpr int64_t kTopkPermMaxSlots = 2048;
+constexpr int64_t kTopkSmallMaxT = kPermWaves;  // one wave per token in one workgroup
 
 __global__ __launch_bounds__(256) void router_topk_permute_kernel(
     const float *__restrict__ partial, int nsplit, const float *__restrict__ bias, int64_t T, int E, int k,
@@ -238,6 +239,32 @@ __global__ __launch_bounds__(256) void router_topk_permute_kernel(
       T * k, E, offsets, sorted_slot, slot_row, hist, scan);
 }
 
+// Batches of at most kTopkSmallMaxT tokens: one workgroup of 16 waves; wave t picks token t's
+// experts (the same top-k and softmax as above) and leaves its picks in LDS, then the counting
+// sort runs on them there. No hand-off between workgroups, so no arrival counter and no
+// device-scope fences: at these sizes those round trips, not the work, set the kernel's time.
+__global__ __launch_bounds__(kPermThreads) void router_topk_permute_small_kernel(
+    const float *__restrict__ partial, int nsplit, const float *__restrict__ bias, int64_t T, int E, int k,
+    int32_t *__restrict__ topk_idx, float *__restrict__ topk_w, int32_t *__restrict__ offsets,
+    int32_t *__restrict__ sorted_slot, int32_t *__restrict__ slot_row) {
+  __shared__ int hist[kPermWaves][kMaxExperts];
+  __shared__ int scan[kMaxExperts + 1];
+  __shared__ int picks[kTopkSmallMaxT * 8];
+  const int lane = threadIdx.x % kWave, wave = threadIdx.x / kWave;
+  if (wave < T) {  // wave-uniform
+    float v[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int e = lane + i * kWave;
+      v[i] = (e < E) ? router_logit_tm(partial, nsplit, (nsplit + 3) / 4 * 4, bias, wave, e, E) : 0.f;
+    }
+    topk_softmax_wave(v, E, k, lane, topk_idx + (int64_t)wave * k, topk_w + (int64_t)wave * k, picks + wave * k);
+  }
+  __syncthreads();
+  permute_block<kPermWaves>([&](int64_t s) { return picks[s]; }, T * k, E, offsets, sorted_slot, slot_row, hist,
+                            scan);
+}
+
 bool topk_permute_fits(int64_t T, int E, int k) {
   return T * k <= kTopkPermMaxSlots && T < 1024 && E <= kMaxExperts && k <= 8;
 }
@@ -246,6 +273,11 @@ hipError_t launch_router_topk_permute(const float *partial, int nsplit, const fl
                                       int32_t *topk_idx, float *topk_w, int *counter, int32_t *offsets,
                                       int32_t *sorted_slot, int32_t *slot_row, hipStream_t stream) {
   if (T <= 0) return hipSuccess;
+  if (T <= kTopkSmallMaxT) {
+    hipLaunchKernelGGL(router_topk_permute_small_kernel, dim3(1), dim3(kPermThreads), 0, stream, partial, nsplit, bias,
+                       T, E, k, topk_idx, topk_w, offsets, sorted_slot, slot_row);
+    return hipGetLastError();
+  }
   hipLaunchKernelGGL(router_topk_permute_kernel, dim3((unsigned)((T + 3) / 4)), dim3(256), 0, stream, partial, nsplit,
                      bias, T, E, k, topk_idx, topk_w, counter, offsets, sorted_slot, slot_row);
   return hipGetLastError();

@@ -363,10 +363,11 @@ def test_forward_matches_composed_steps(name, T):
     cfg = synth.get_config(name)
     dev = gu.device_layer(synth.make_inputs(cfg, T), tiled=True)
     E = int(dev.router.weight.shape[0])
-    out_fw = gu.bf16_bits(moe.moe_forward_ex(dev.x, dev.router, dev.w1, dev.w2, dev.k, moe.Options()))
+    opts = moe.Options()
+    out_fw = gu.bf16_bits(moe.moe_forward_ex(dev.x, dev.router, dev.w1, dev.w2, dev.k, opts))
     idx, w = moe.moe_route(dev.x, dev.router, dev.k)
     off, ss, sr = moe.moe_permute(idx, E)
-    y = moe.moe_mxfp4_ffn(dev.x, dev.k, E, off, ss, dev.w1, dev.w2, moe.Options())
+    y = moe.moe_mxfp4_ffn(dev.x, dev.k, E, off, ss, dev.w1, dev.w2, opts)
     out = gu.bf16_bits(moe.moe_combine(y, sr, w))
     assert np.array_equal(out_fw, out)
 
@@ -493,6 +494,31 @@ def test_layer_shapes_mx6(E, k, H, I, T):
     assert (np.abs(o4 - o3) <= bound + slack).all()
     if I >= 1024:
         _check_layer(inp, path=4, dev=dev)
+
+
+@pytest.mark.parametrize("E,k,H,I,T", [(32, 4, 2880, 2880, 1), (128, 4, 2880, 2880, 1), (8, 2, 32, 32, 1),
+                                       (4, 4, 128, 96, 1), (16, 8, 96, 160, 1), (256, 8, 64, 64, 1),
+                                       (2, 2, 3072, 256, 1), (2, 2, 3104, 256, 1), (2, 2, 256, 4096, 1),
+                                       (2, 2, 256, 4128, 1), (1, 1, 64, 96, 1), (32, 4, 2880, 2880, 2),
+                                       (32, 4, 2880, 2880, 5)])
+def test_small_batch_path(E, k, H, I, T):
+    """One token with tiled weights: AUTO runs gate_up, SwiGLU and down in one launch per
+    (expert, 32-activation block), summing the blocks' partial outputs in the combine; against
+    the oracle, and the two-kernel stream path (path 1) at the same bar. Shapes cover one chunk
+    of input (H = 32: three of the four chunk quarters empty), one block (I = 32), blocks in
+    every place of W2's tiles (I = 96, 160), k = 8, E = 256, the largest H and I it takes (3072,
+    4096 = 128 blocks) and the next sizes past them (3104, 4128: the two-kernel path), and two
+    and five tokens (the two-kernel path on AUTO)."""
+    inp = synth.make_inputs(_small_cfg(E, k, H, I, T))
+    _check_layer(inp, path=0)
+    _check_layer(inp, path=1)
+
+
+def test_small_batch_path_hot_expert():
+    cfg = _small_cfg(32, 4, T=8)
+    bias = np.zeros(32, np.float32)
+    bias[[3, 9, 17, 30]] = 50.0  # every token picks these four: four experts with 8 slots each
+    _check_layer(synth.make_inputs(cfg, router_bias=bias), path=0)
 
 
 @pytest.mark.parametrize("tiled,path", [(False, 0), (True, 1), (True, 2), (True, 3)])

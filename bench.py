@@ -84,11 +84,11 @@ CALIBRATION_MIB = 1024
 FFN_KERNELS = ("ffn_", "gather_rows")  # kernels one moe_mxfp4_ffn call launches, once each
 
 
-# the sources of what one moe_mxfp4_ffn call runs at decode (the weight-streaming kernels) and
-# at prefill (the gather and the grouped GEMM): kernels, their headers and the host code that
-# picks and launches them
+# the sources of what one moe_mxfp4_ffn call runs at decode (the weight-streaming kernels, or for
+# one token the one-launch FFN and its per-block sum) and at prefill (the gather and the grouped
+# GEMM): kernels, their headers and the host code that picks and launches them
 FFN_SOURCES = {
-    "stream": ("ffn_stream.hip", "common.h", "kernels.h", "moe_abi.cpp"),
+    "stream": ("ffn_stream.hip", "ffn_small.hip", "combine.hip", "common.h", "kernels.h", "moe_abi.cpp"),
     "gemm": ("ffn_gemm.hip", "gather.hip", "common.h", "mx_act.h", "kernels.h", "moe_abi.cpp"),
 }
 

@@ -327,6 +327,12 @@ def path_ceiling(path):
     if path in (0, 3):
         return {"tflops": 2500.0, "basis": "FP8xFP4 scaled MFMA 5.0 PFLOP/s / 2 (two exact E4M3 terms per bf16 "
                                            "activation)"}
+    if path == 4:
+        # gate_up (2/3 of the flops) on FP8xFP4 at 2.5 PFLOP/s algorithmic, down (1/3) on FP6xFP4 at
+        # 10.1 / 2 PFLOP/s: the harmonic combination
+        return {"tflops": round(1.0 / ((2.0 / 3.0) / 2500.0 + (1.0 / 3.0) / 5050.0), 1),
+                "basis": "gate_up FP8xFP4 5.0 PFLOP/s / 2, down FP6xFP4 10.1 PFLOP/s / 2 (two E2M3 terms), "
+                         "weighted 2:1 by their flops"}
     return {"tflops": BF16_PEAK_TFLOPS, "basis": "bf16 MFMA 2.5 PFLOP/s"}
 
 

@@ -304,7 +304,7 @@ class LayerBench:
             r = {"bound": "mfma", "achieved": round(achieved, 1), "peak": MXFP4_PEAK_TFLOPS, "unit": "TFLOP/s",
                  "frac": round(achieved / MXFP4_PEAK_TFLOPS, 4), "traffic": stored_traffic(cfg.name, T),
                  "frac_of_bf16_peak": round(achieved / BF16_PEAK_TFLOPS, 4),
-                 "path_ceiling": path_ceiling(self.args.path)}
+                 "path_ceiling": path_ceiling(self.args.path, I)}
         r.update({"kernel": "moe_mxfp4_ffn (gate_up + down)", "ms_per_launch": round(ffn_ms, 5),
                   "timed_calls": calls, "algorithmic_bytes": int(ffn_bytes), "algorithmic_flops": ffn_flops})
         self.log(f"{cfg.name} T={T} ffn: {ffn_ms * 1e3:.1f} us over {calls} calls, {r['achieved']} {r['unit']} "
@@ -322,9 +322,12 @@ class LayerBench:
         self.torch.cuda.empty_cache()
 
 
-def path_ceiling(path):
-    """The MFMA ceiling of the prefill kernel family, in algorithmic flops."""
-    if path in (0, 3):
+def path_ceiling(path, I):
+    """The MFMA ceiling of the prefill kernel family, in algorithmic flops (AUTO's grouped GEMM
+    takes the MXFP6 down input from 1024 activations on)."""
+    if path == 0:
+        path = 4 if I >= 1024 else 3
+    if path == 3:
         return {"tflops": 2500.0, "basis": "FP8xFP4 scaled MFMA 5.0 PFLOP/s / 2 (two exact E4M3 terms per bf16 "
                                            "activation)"}
     if path == 4:

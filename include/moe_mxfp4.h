@@ -64,14 +64,15 @@ extern "C" {
                                    MXFP4 weights are an operand as stored, each bf16 activation is
                                    split exactly into two MXFP8 (E4M3) terms with E8M0 block
                                    scales. Needs MOE_LAYOUT_TILED weights. AUTO picks it for
-                                   tiled weights when T*k >= 32*E. */
+                                   tiled weights when T*k >= 32*E and I < 1024. */
 #define MOE_PATH_PREFILL_MX6SPLIT 4 /* gate_up as MX8SPLIT; the down projection's input (the
                                    bf16-rounded activation) as two MXFP6 (E2M3) terms with E8M0
                                    block scales, on the FP6 x FP4 scaled MFMA, which issues faster
                                    than FP8 x FP4. That split is exact for activations within 2^3
                                    of their 32-element block's maximum, else off by less than 2^-9
                                    of that maximum (so not bit-equal to the bf16 GEMM). Needs
-                                   MOE_LAYOUT_TILED weights. */
+                                   MOE_LAYOUT_TILED weights. AUTO picks it for tiled weights
+                                   when T*k >= 32*E and I >= 1024 (the gpt-oss widths). */
 /* earlier names of the same paths */
 #define MOE_PATH_STREAM MOE_PATH_DECODE
 #define MOE_PATH_GEMM MOE_PATH_PREFILL_BF16

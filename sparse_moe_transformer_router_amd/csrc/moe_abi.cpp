@@ -106,13 +106,19 @@ int check_options(const moe_options_t &o) {
 
 // Which expert-GEMM family runs: a grouped GEMM (tiled weights only) when asked for, or on
 // AUTO when the batch averages at least kGemmSlotsPerExpert slots per expert; otherwise the
-// weight-streaming kernels. AUTO's grouped GEMM is kAutoGemm.
+// weight-streaming kernels. AUTO's grouped GEMM takes the exact two-term MXFP8 activation for
+// gate_up, and for down the two-term MXFP6 one from kMx6MinI activations on: its error (below
+// 2^-9 of each 32-element block's maximum, the order of the activation's own bf16 rounding)
+// averages over many blocks there (measured max |err| / RMS against the fp64 layer: 7.7e-3
+// against 6.4e-3 at 4096 tokens of the 2880-wide layer, 1.1e-2 against 9.5e-3 at I = 1024,
+// under the 2e-2 bar; three blocks, I = 96, reach 2.04e-2), and the down GEMM runs ~12% faster
+// (FFN 703 against 742 us at 4096 tokens, 1536 against 1603 us at 8192 x 128 experts).
 // Measured crossover (FFN time, stream vs block-scaled GEMM): E = 32 at 24 slots per expert
 // 105 vs 142 us, at 32: 150 vs 145 us; E = 128 at 16: 354 vs 467 us, at 32: 544 vs 485 us.
 constexpr int64_t kGemmSlotsPerExpert = 32;
+constexpr int kMx6MinI = 1024;
 
 enum class Family { kStream, kGemm, kGemmMx, kGemmMx6 };
-constexpr Family kAutoGemm = Family::kGemmMx;
 
 bool is_gemm_path(int path) {
   return path == MOE_PATH_PREFILL_BF16 || path == MOE_PATH_PREFILL_MX8SPLIT || path == MOE_PATH_PREFILL_MX6SPLIT;
@@ -131,7 +137,7 @@ Family family(const moe_options_t &o, const moe_mxfp4_weight_t &gu, const moe_mx
   if (o.path == MOE_PATH_PREFILL_MX8SPLIT) return Family::kGemmMx;
   if (o.path == MOE_PATH_PREFILL_MX6SPLIT) return Family::kGemmMx6;
   if (o.path == MOE_PATH_DECODE || !tiled || S < kGemmSlotsPerExpert * (int64_t)E) return Family::kStream;
-  return kAutoGemm;
+  return dn.k >= kMx6MinI ? Family::kGemmMx6 : Family::kGemmMx;
 }
 
 // The expert GEMMs that follow the permutation. Arguments already validated. The GEMM

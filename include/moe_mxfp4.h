@@ -231,9 +231,10 @@ int moe_combine(const float *y, const int32_t *slot_row, const float *topk_w, in
 /*
  * The whole layer: route, permute, expert FFNs, combine; out bf16 [T][H].
  * Uses a workspace owned by the library, one per (device, stream), grown on demand and kept
- * until moe_release_workspace() or process exit; growing it synchronises `stream` and calls
- * hipMalloc. Calls on different streams use different workspaces; calls on one stream are
- * ordered by that stream. Concurrent calls from several host threads are safe (a mutex guards
+ * until moe_release_workspace() or process exit; growing it is stream-ordered (hipFreeAsync of
+ * the old buffer and hipMallocAsync of the new one on `stream`, no host synchronisation). Calls
+ * on different streams use different workspaces; calls on one stream are ordered by that
+ * stream. Concurrent calls from several host threads are safe (a mutex guards
  * the table of workspaces), but callers that cannot afford the first call's allocation, or
  * that capture the call in a HIP graph, use moe_forward_ex with their own workspace.
  */

@@ -571,13 +571,14 @@ int moe_forward(const uint16_t *x, const moe_router_t *router, const moe_mxfp4_w
     std::lock_guard<std::mutex> lock(g_ws_mutex);
     OwnedWorkspace &w = g_ws[{dev, reinterpret_cast<uintptr_t>(s)}];
     if (w.bytes < L.total) {
+      // stream-ordered: the old buffer is released after the work already queued on s, the new
+      // one is ready for the work queued next; no host synchronisation
       if (w.ptr != nullptr) {
-        if (hipStreamSynchronize(s) != hipSuccess) return MOE_ERR_HIP;
-        if (hipFree(w.ptr) != hipSuccess) return MOE_ERR_HIP;
+        if (hipFreeAsync(w.ptr, s) != hipSuccess) return MOE_ERR_HIP;
         w.ptr = nullptr;
         w.bytes = 0;
       }
-      if (hipMalloc(&w.ptr, L.total) != hipSuccess) {
+      if (hipMallocAsync(&w.ptr, L.total, s) != hipSuccess) {
         w.ptr = nullptr;
         return MOE_ERR_HIP;
       }
@@ -626,10 +627,13 @@ int moe_release_workspace(void) {
         if (hipDeviceSynchronize() != hipSuccess) return MOE_ERR_HIP;
         synced = true;
       }
-      if (hipFree(it->second.ptr) != hipSuccess) err = hipErrorInvalidValue;
+      // stream-ordered memory goes back the same way (its stream may no longer exist; after the
+      // device synchronisation the null stream orders the release)
+      if (hipFreeAsync(it->second.ptr, nullptr) != hipSuccess) err = hipErrorInvalidValue;
     }
     it = g_ws.erase(it);
   }
+  if (synced && hipStreamSynchronize(nullptr) != hipSuccess) err = hipErrorInvalidValue;
   return err == hipSuccess ? MOE_OK : MOE_ERR_HIP;
   MOE_GUARD_END
 }

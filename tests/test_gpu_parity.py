@@ -154,6 +154,44 @@ def test_ffn_preact_identity_decode(scale_lo, scale_hi, tiled, path):
             assert np.array_equal(y[r], W1[:, t]), (e, t)
 
 
+@pytest.mark.parametrize("tiled,path,tokens", [(False, 1, None), (True, 1, None), (True, 2, None), (True, 3, None),
+                                               (True, 4, None), (True, 0, [37])])
+def test_ffn_down_identity(tiled, path, tokens):
+    """One-hot activations of exactly 1.0: y = W2 a is one decoded weight column, exactly, on
+    every kernel family, including the two-term MXFP6 down input (1.0 and 0 are exact in E2M3)
+    and the one-launch kernel of a one-token batch (path 0, T = 1). W1's gate row 2i holds 2.0
+    at input i (zero elsewhere), its linear rows are zero with bias -0.431640625, so token e_t
+    gets gate 2.0 at unit t only: a_t = 2 sigma(2) (1 - 0.431640625) = 1.0012, which rounds to
+    1.0 in bf16, and every other unit has gate 0, so a = 0 there."""
+    E, H, I, k = 3, 128, 96, 1
+    rng = np.random.default_rng(12)
+    w1c = np.zeros((E, 2 * I, H // 2), np.uint8)
+    for i in range(I):  # E2M1 code 4 = 2.0, low nibble = even element
+        w1c[:, 2 * i, i // 2] = 4 if i % 2 == 0 else 4 << 4
+    w1s = np.full((E, 2 * I, H // 32), 127, np.uint8)
+    b1 = np.zeros((E, 2 * I), np.uint16)
+    b1[:, 1::2] = 0xBEDD  # bf16 -0.431640625
+    w2c = rng.integers(0, 256, (E, H, I // 2), dtype=np.uint8)
+    w2s = rng.integers(118, 128, (E, H, I // 32), dtype=np.uint8)
+    toks = np.arange(I) if tokens is None else np.asarray(tokens)
+    T = len(toks)
+    x = np.zeros((T, H), np.uint16)
+    x[np.arange(T), toks] = 0x3F80
+    idx = (toks % E).astype(np.int32).reshape(T, 1)
+    _, off, ss, sr = oracle.permute(idx, E)
+    w1 = moe.MXFP4Weight(gu.to_dev_u8(w1c), gu.to_dev_u8(w1s), gu.to_dev_bf16(b1))
+    w2 = moe.MXFP4Weight(gu.to_dev_u8(w2c), gu.to_dev_u8(w2s), None)
+    if tiled:
+        w1, w2 = moe.moe_mxfp4_pack(w1), moe.moe_mxfp4_pack(w2)
+    y = moe.moe_mxfp4_ffn(gu.to_dev_bf16(x), k, E, torch.from_numpy(off).cuda(), torch.from_numpy(ss).cuda(),
+                          w1, w2, moe.Options(path=path)).cpu().numpy()
+    for e in range(E):
+        W2 = oracle.mxfp4_decode(w2c[e], w2s[e]).astype(np.float32)
+        for r in range(off[e], off[e + 1]):
+            t = toks[ss[r]]  # k = 1: slot id = batch row
+            assert np.array_equal(y[r], W2[:, t] + np.float32(0.0)), (e, t)
+
+
 @pytest.mark.parametrize("tiled,path", [(False, 1), (True, 1), (True, 2), (True, 3), (True, 4)])
 def test_ffn_activation_step(tiled, path):
     """Stop after the SwiGLU: the bf16-rounded activation of every slot."""
@@ -565,6 +603,29 @@ def test_determinism_and_guard_regions():
     assert np.array_equal(first, gu.bf16_bits(out)), "two runs differ"
     b = buf.cpu().numpy()
     assert (b[:pad] == 12345).all() and (b[pad + T * H:] == 12345).all(), "write outside the output"
+
+
+def test_forward_owned_workspace_grows_and_releases():
+    """moe_forward's own workspace grows stream-ordered (freed and reallocated on the call's
+    stream, no host synchronisation) as the batch grows, on the current stream and on a side
+    stream, and is allocated again after moe_release_workspace: every call gives the bits of
+    moe_forward_ex with a caller workspace."""
+    cfg = synth.get_config("decode20b")
+    dev = gu.device_layer(synth.make_inputs(cfg, 64))
+    want = {T: gu.bf16_bits(moe.moe_forward_ex(dev.x[:T], dev.router, dev.w1, dev.w2, dev.k, moe.Options()))
+            for T in (1, 8, 64)}
+    moe.moe_release_workspace()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    for stream in (None, side):
+        outs = [(T, moe.moe_forward(dev.x[:T], dev.router, dev.w1, dev.w2, dev.k, stream=stream))
+                for T in (1, 8, 64, 8)]  # grows twice without waiting, then reuses
+        torch.cuda.synchronize()
+        for T, o in outs:
+            assert np.array_equal(gu.bf16_bits(o), want[T]), (stream, T)
+    moe.moe_release_workspace()
+    o = moe.moe_forward(dev.x[:8], dev.router, dev.w1, dev.w2, dev.k)
+    assert np.array_equal(gu.bf16_bits(o), want[8])
 
 
 def test_side_streams():

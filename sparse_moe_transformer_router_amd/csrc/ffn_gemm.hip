@@ -77,8 +77,12 @@ constexpr int kXcds = 8;
 constexpr int kGMaxExperts = 256;
 // RGW = 32-row weight tiles per wave: a tile is 64 RGW weight rows x 128 slots. The block-scaled
 // forms add the activation terms' scales (128 slots x 2 dwords) after the activation rows. An
-// MXFP6 stage holds 128 rows x 192 bytes: the records' 16-byte parts as 128-byte rows (kM6A),
-// then their 8-byte parts as 64-byte rows (kM6B).
+// MXFP6 stage holds 128 rows x 192 bytes: the records' 16-byte parts as 128-byte rows (kM6A,
+// the 8 units of a row XOR-swizzled by (row >> 1) & 7), then their 8-byte parts (kM6B bytes per
+// row) as, per 32-row group, four planes (t, g) of 32 16-byte units (unit (t, g) of the record:
+// half 0's and half 1's 8-byte pieces of lane group g, term t). A wave's operand reads then hit
+// distinct banks: 16 lanes of a 16-byte read cover 16 rows = 256 distinct bytes (with the rows'
+// former swizzle by row & 7, or 8-byte pieces in 64-byte rows, 2 and 4 lanes shared a bank).
 template <int RGW, int AF>
 struct GShape {
   static constexpr bool kMx = AF != kActBf16;
@@ -271,7 +275,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
 #pragma unroll
     for (int i = 0; i < kActDma; ++i) {
       // tile row (within the wave's 32) of the lane's piece of activation DMA i
-      const int rw = M6 ? (i < 4 ? 8 * i + lane / 8 : 16 * (i - 4) + lane / 4) : 4 * i + lane / 16;
+      const int rw = M6 ? (i < 4 ? 8 * i + lane / 8 : lane % 32) : 4 * i + lane / 16;
       const int src = __builtin_amdgcn_ds_bpermute(rw * 4, srcv);
       aptr[i] = static_cast<const uint8_t *>(a_src) + (int64_t)src * arow;
     }
@@ -299,11 +303,12 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
       sptr = a_scales + (int64_t)src * nchunk * kMxScBytes + (lane & 1) * 4;
     }
   };
-  // (MXFP6: a 16-byte part's row holds 8 units, swizzled by row & 7; an 8-byte part's row 4 units
-  // of two pieces, swizzled by (row >> 1) & 3)
+  // (MXFP6: a 16-byte part's row holds 8 units, swizzled by (row >> 1) & 7; the 8-byte parts go
+  // to planes (t, g) of 16-byte units, DMA 4 + j bringing planes 2j and 2j + 1 of the wave's 32
+  // rows, lane l plane 2j + l / 32, row l % 32)
 #pragma unroll
   for (int i = 0; i < 8; ++i)
-    lcol[i] = M6 ? (i < 4 ? ((lane % 8) ^ (lane / 8)) * 16 : kM6A + ((lane % 4) ^ ((lane / 8) & 3)) * 16)
+    lcol[i] = M6 ? (i < 4 ? ((lane % 8) ^ (((8 * i + lane / 8) >> 1) & 7)) * 16 : kM6A + (2 * (i - 4) + lane / 32) * 16)
                  : ((lane % 16) ^ ((32 * wave + 4 * i + lane / 16) & 15)) * 16;
   if (mapped) {
     dma_map(ti);
@@ -340,8 +345,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
     unsigned char *st = lds + slot * kGStageBytes;
     if (i < kActDma) {
       if constexpr (M6) {
-        // 16-byte parts: 8 rows x 128 bytes per DMA; 8-byte parts: 16 rows x 64 bytes
-        unsigned char *dst = i < 4 ? st + (32 * wave + 8 * i) * kM6A : st + kM6BOff + (32 * wave + 16 * (i - 4)) * kM6B;
+        // 16-byte parts: 8 rows x 128 bytes per DMA; 8-byte parts: two planes of the wave's 32 rows
+        unsigned char *dst = i < 4 ? st + (32 * wave + 8 * i) * kM6A : st + kM6BOff + wave * (32 * kM6B) + (i - 4) * 1024;
         __builtin_amdgcn_global_load_lds(aptr[i] + ci * kMx6RecBytes + lcol[i], dst, 16, 0, 0);
       } else {
         const uint8_t *src;
@@ -677,26 +682,32 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
   // 32 + 16 kh .. of a 64-element half, i.e. 16-byte columns 4p + kh and 4p + 2 + kh of the
   // term's 128 bytes.
   // MXFP6: the lane's block 2p + kh of term t is its record's 16-byte unit (t, 2p + kh) in the
-  // 16-byte-part rows and half p of unit (t, kh) in the 8-byte-part rows (both swizzled); the
-  // operand's dwords 6 and 7 are unused (zero).
+  // 16-byte-part rows and half p of unit (t, kh) in the 8-byte-part planes (read whole at half
+  // 0, half 1's piece kept for the step of half 1); the operand's dwords 6 and 7 are unused.
   i32x8_t bv[2][2] = {};
+  uint32_t m6h1[2][2][2] = {};  // MXFP6: half 1's 8-byte piece of column group b, term t (read with half 0's)
   u32x4_t wv[2][RGW];
   uint32_t swd[RGW], ash[2][2];
   // half h of the FP8 operand (16-byte columns 4p + kh, 4p + 2 + kh of term t), or the MXFP6
   // operand's part h (h = 0: dwords 0-3, h = 1: dwords 4-5), of slot row `row` into b8
-  auto act_read = [&](const unsigned char *abuf, int row, int p, int t, int h, i32x8_t &b8) {
+  auto act_read = [&](const unsigned char *abuf, int row, int p, int t, int h, int b, i32x8_t &b8) {
     if constexpr (M6) {
       if (h == 0) {
-        const u32x4_t u = *reinterpret_cast<const u32x4_t *>(abuf + row * kM6A + (((4 * t + 2 * p + kh) ^ (row & 7)) << 4));
+        const u32x4_t u =
+            *reinterpret_cast<const u32x4_t *>(abuf + row * kM6A + (((4 * t + 2 * p + kh) ^ ((row >> 1) & 7)) << 4));
 #pragma unroll
         for (int i = 0; i < 4; ++i) b8[i] = (int)u[i];
+      } else if (p == 0) {
+        // the 16-byte unit (t, kh) of the row in its plane: half 0's piece now, half 1's kept
+        const u32x4_t u = *reinterpret_cast<const u32x4_t *>(abuf + kM6BOff + (row >> 5) * (32 * kM6B) +
+                                                             (2 * t + kh) * 512 + (row & 31) * 16);
+        b8[4] = (int)u[0];
+        b8[5] = (int)u[1];
+        m6h1[b][t][0] = u[2];
+        m6h1[b][t][1] = u[3];
       } else {
-        // two dword reads, not one 8-byte read: read as 8 bytes, the compiler takes the piece
-        // for a possible target of the DMAs in flight and waits for all of them
-        const uint32_t *q = reinterpret_cast<const uint32_t *>(abuf + kM6BOff + row * kM6B +
-                                                               (((2 * t + kh) ^ ((row >> 1) & 3)) << 4) + 8 * p);
-        b8[4] = (int)q[0];
-        b8[5] = (int)q[1];
+        b8[4] = (int)m6h1[b][t][0];
+        b8[5] = (int)m6h1[b][t][1];
       }
     } else {
       const u32x4_t u = *reinterpret_cast<const u32x4_t *>(abuf + g_off(row, 8 * t + 4 * p + 2 * h + kh));
@@ -708,8 +719,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
 #pragma unroll
     for (int b = 0; b < 2; ++b) {
       if (b >= nb) break;
-      act_read(abuf, scol(b), p, t, 0, b8[b]);
-      act_read(abuf, scol(b), p, t, 1, b8[b]);
+      act_read(abuf, scol(b), p, t, 0, b, b8[b]);
+      act_read(abuf, scol(b), p, t, 1, b, b8[b]);
     }
   };
   auto wload = [&](const unsigned char *abuf, int p, u32x4_t *w4) {
@@ -789,7 +800,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
             wd[k] = *reinterpret_cast<const u32x4_t *>(buf + kWOff + (wy * RGW + k) * 2048 + pw * 1024 + lane * 16);
           } else {
             const int b = (k - nw) / 2, h = (k - nw) % 2;
-            act_read(buf, scol(b), p, t, h, bd[b]);
+            act_read(buf, scol(b), p, t, h, b, bd[b]);
           }
         };
         auto step = [&](auto SC) {

@@ -44,7 +44,7 @@ def _replays_match(run, eager_out, graph_out, other):
         torch.cuda.synchronize()
 
 
-@pytest.mark.parametrize("name,T", [("decode20b", 64), ("prefill20b", 4096)])
+@pytest.mark.parametrize("name,T", [("decode20b", 64), ("decode20b", 1), ("prefill20b", 4096)])
 def test_layer_and_block_replay(name, T):
     cfg = synth.get_config(name)
     inp = synth.make_inputs(cfg, T)

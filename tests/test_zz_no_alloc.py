@@ -23,7 +23,8 @@ def _announce(request):
     torch.cuda.synchronize()
 
 
-@pytest.mark.parametrize("name,T1,T2", [("decode20b", 64, 8), ("decode120b_zipf", 256, 16), ("tiny", 16, 3)])
+@pytest.mark.parametrize("name,T1,T2", [("decode20b", 64, 8), ("decode20b", 8, 1), ("decode120b_zipf", 256, 16),
+                                        ("tiny", 16, 3)])
 def test_noalloc_matches_moe_forward(name, T1, T2):
     cfg = synth.get_config(name)
     for T in (T1, T2):  # the second call runs on what the first left in the scratch array

@@ -53,7 +53,9 @@ def parse():
     p.add_argument("--window", type=int, default=0, help="attn_decode: 0 dense, else the band (gpt-oss: 128)")
     p.add_argument("--T", type=int, default=0, help="batch size (default: the workload's largest)")
     p.add_argument("--layers", type=int, default=0, help="rotated weight copies (default 24 / 36)")
-    p.add_argument("--path", type=int, default=0, help="0 auto, 1 stream, 2 gemm (bf16), 3 gemm (block-scaled)")
+    p.add_argument("--path", type=int, default=0,
+                   help="0 auto, 1 decode (weight streaming), 2 prefill bf16 GEMM, 3 prefill two-term MXFP8 GEMM, "
+                        "4 prefill with MXFP6 down input, 5 decode with one token in one launch")
     p.add_argument("--layout", default="tiled", choices=["tiled", "rowmajor"],
                    help="weights prepacked once (untimed) into the kernel layout, or row-major")
     p.add_argument("--block", action="store_true",

@@ -73,6 +73,13 @@ extern "C" {
                                    of that maximum (so not bit-equal to the bf16 GEMM). Needs
                                    MOE_LAYOUT_TILED weights. AUTO picks it for tiled weights
                                    when T*k >= 32*E and I >= 1024 (the gpt-oss widths). */
+#define MOE_PATH_DECODE_FUSED 5 /* a batch of one token (H <= 3072, I <= 4096, tiled weights):
+                                   gate_up, SwiGLU and down in one launch, one workgroup per
+                                   (picked expert, 32-activation block), each writing its block's
+                                   share of the expert's output, the shares added in a fixed
+                                   order by the combine; other batches run as MOE_PATH_DECODE.
+                                   Opt-in: on MI355X the two-kernel form of MOE_PATH_DECODE is
+                                   faster at one token. Needs MOE_LAYOUT_TILED weights. */
 /* earlier names of the same paths */
 #define MOE_PATH_STREAM MOE_PATH_DECODE
 #define MOE_PATH_GEMM MOE_PATH_PREFILL_BF16
@@ -210,10 +217,10 @@ int moe_permute(const int32_t *topk_idx, int64_t T, int32_t E, int32_t k, int32_
  * opts->flags may stop early (MOE_FLAG_EMIT_PREACT: y is [T*k][2I]; MOE_FLAG_EMIT_ACT:
  * y is [T*k][I]). ws: at least moe_workspace_size(T, E, k, H, I, opts->path) bytes.
  * The routing must give each expert at most one slot per token (distinct experts in each
- * token's k picks, as moe_route's top-k and moe_permute produce): on AUTO with tiled weights, one
- * token, H <= 3072 and I <= 4096 the FFNs run fused per (expert, 32-activation block) with the
- * token's row staged on chip, and an expert holding more than one slot there gives unspecified
- * values for its slots (never an access outside the buffers).
+ * token's k picks, as moe_route's top-k and moe_permute produce): on MOE_PATH_DECODE_FUSED with
+ * one token the FFNs run fused per (expert, 32-activation block) with the token's row staged on
+ * chip, and an expert holding more than one slot there gives unspecified values for its slots
+ * (never an access outside the buffers).
  */
 int moe_mxfp4_ffn(const uint16_t *x, int64_t T, int32_t k, int32_t E, const int32_t *expert_offsets,
                   const int32_t *sorted_slot, const moe_mxfp4_weight_t *gate_up,

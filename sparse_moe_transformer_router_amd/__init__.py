@@ -13,6 +13,7 @@ from ._lib import (  # noqa: F401
     MOE_LAYOUT_TILED,
     MOE_PATH_AUTO,
     MOE_PATH_DECODE,
+    MOE_PATH_DECODE_FUSED,
     MOE_PATH_GEMM,
     MOE_PATH_GEMM_MX,
     MOE_PATH_PREFILL_BF16,

@@ -32,6 +32,7 @@ MOE_PATH_DECODE = 1
 MOE_PATH_PREFILL_BF16 = 2
 MOE_PATH_PREFILL_MX8SPLIT = 3
 MOE_PATH_PREFILL_MX6SPLIT = 4
+MOE_PATH_DECODE_FUSED = 5
 # earlier names of the same paths
 MOE_PATH_STREAM = MOE_PATH_DECODE
 MOE_PATH_GEMM = MOE_PATH_PREFILL_BF16

@@ -182,6 +182,7 @@ __global__ __launch_bounds__(kSWaves *kWave) void ffn_stream_kernel(
 // k-assignment (64 contiguous bytes per lane and block). PF = chunks of register prefetch.
 constexpr int kTRows = 64;   // weight rows per workgroup (two 32-row tiles)
 constexpr int kTCols = 32;   // slots per m-tile
+constexpr int kTiledPrefetch = 2;  // chunks in flight per wave
 
 template <int EPI, int PF>
 __global__ __launch_bounds__(kSWaves *kWave) void ffn_stream_tiled_kernel(
@@ -233,59 +234,69 @@ __global__ __launch_bounds__(kSWaves *kWave) void ffn_stream_tiled_kernel(
   const int NG = N / 32;
   const uint8_t *cbase = pcodes + (int64_t)e * NG * nchunk * 2048 + lane * 16;
   const uint8_t *sbase = pscales + (int64_t)e * NG * nchunk * 128 + r32 * 4;
-  const uint16_t *ap = arow + kh * 32;  // + (4c + 2p) * 32 elements: this lane's block
 
   f32x16_t acc[RG];
 #pragma unroll
   for (int g = 0; g < RG; ++g)
 #pragma unroll
     for (int i = 0; i < 16; ++i) acc[g][i] = 0.f;
+  // this wave's chunks c = wave + kSWaves i, i < nmine, PF of them in flight. Every load is
+  // issued unconditionally from a clamped in-bounds address (a tile past N reads tile 0 and is
+  // never stored; a block past K reads block 0 and is zeroed at its use; a chunk past the
+  // wave's last re-reads that last one, from cache), and the loop body has no path that skips
+  // its loads: with a load under a branch the compiler waits for every load in flight at the
+  // top of each iteration, which serialises the prefetch.
+  const int nmine = wave < nchunk ? (nchunk - wave + kSWaves - 1) / kSWaves : 0;
   u32x4_t cw[PF][RG][2];
   uint32_t sw[PF][RG];
   u32x4_t av[PF][2][4];
-  auto load = [&](int c, int s) {
-    const bool cvalid = c < nchunk;
+  auto load = [&](int i, int s) {
+    const int c = nmine > 0 ? wave + kSWaves * (i < nmine ? i : nmine - 1) : 0;
 #pragma unroll
     for (int g = 0; g < RG; ++g) {
-      const bool ok = cvalid && (g0 + g) < NG;
-      const int64_t t = (int64_t)(g0 + g) * nchunk + c;
+      const int gg = (g0 + g) < NG ? g0 + g : 0;
+      const int64_t t = (int64_t)gg * nchunk + c;
 #pragma unroll
       for (int p = 0; p < 2; ++p)
-        cw[s][g][p] = ok ? __builtin_nontemporal_load(reinterpret_cast<const u32x4_t *>(cbase + t * 2048 + p * 1024))
-                         : u32x4_t{0u, 0u, 0u, 0u};
-      sw[s][g] = ok ? __builtin_nontemporal_load(reinterpret_cast<const uint32_t *>(sbase + t * 128)) : 0x7f7f7f7fu;
+        cw[s][g][p] = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t *>(cbase + t * 2048 + p * 1024));
+      sw[s][g] = __builtin_nontemporal_load(reinterpret_cast<const uint32_t *>(sbase + t * 128));
     }
 #pragma unroll
     for (int p = 0; p < 2; ++p) {
-      const bool ok = cvalid && col_ok && (4 * c + 2 * p + kh) < KB;
-      const u32x4_t *a4 = reinterpret_cast<const u32x4_t *>(ap + (4 * c + 2 * p) * 32);
+      const int blk = 4 * c + 2 * p + kh;  // this lane's MX block of half p
+      const u32x4_t *a4 = reinterpret_cast<const u32x4_t *>(arow + (blk < KB ? blk : 0) * 32);
 #pragma unroll
-      for (int j = 0; j < 4; ++j) av[s][p][j] = ok ? a4[j] : u32x4_t{0u, 0u, 0u, 0u};
+      for (int j = 0; j < 4; ++j) av[s][p][j] = a4[j];
     }
   };
+  auto body = [&](int i, int s) {
+    const int c = wave + kSWaves * i;
 #pragma unroll
-  for (int s = 0; s < PF; ++s) load(wave + s * kSWaves, s);
-  for (int c = wave; c < nchunk; c += PF * kSWaves) {
+    for (int p = 0; p < 2; ++p) {
+      const bool ok = col_ok && (4 * c + 2 * p + kh) < KB;
 #pragma unroll
-    for (int s = 0; s < PF; ++s) {
-      const int cc = c + s * kSWaves;
-      if (cc < nchunk) {
+      for (int g = 0; g < RG; ++g) {
+        const float sc = e8m0_to_f32((sw[s][g] >> (8 * (2 * p + kh))) & 0xffu);
 #pragma unroll
-        for (int g = 0; g < RG; ++g) {
-#pragma unroll
-          for (int p = 0; p < 2; ++p) {
-            const float sc = e8m0_to_f32((sw[s][g] >> (8 * (2 * p + kh))) & 0xffu);
-#pragma unroll
-            for (int j = 0; j < 4; ++j) {
-              const bf16x8_t wa = fp4x8_to_bf16x8(cw[s][g][p][j], sc);
-              acc[g] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wa, as_bf16x8(av[s][p][j]), acc[g], 0, 0, 0);
-            }
-          }
+        for (int j = 0; j < 4; ++j) {
+          const bf16x8_t wa = fp4x8_to_bf16x8(cw[s][g][p][j], sc);
+          const u32x4_t a = ok ? av[s][p][j] : u32x4_t{0u, 0u, 0u, 0u};
+          acc[g] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wa, as_bf16x8(a), acc[g], 0, 0, 0);
         }
-        load(cc + PF * kSWaves, s);
       }
     }
+    load(i + PF, s);
+  };
+#pragma unroll
+  for (int s = 0; s < PF; ++s) load(s, s);
+  int i = 0;
+  for (; i + PF <= nmine; i += PF) {
+#pragma unroll
+    for (int s = 0; s < PF; ++s) body(i + s, s);
   }
+#pragma unroll
+  for (int s = 0; s < PF - 1; ++s)
+    if (i + s < nmine) body(i + s, s);
 
   // 32x32 output: lane holds slot column lane%32, rows 8i + 4*(lane/32) + j (i, j = 0..3)
 #pragma unroll
@@ -565,22 +576,14 @@ hipError_t launch_ffn_stream(const uint16_t *a_src, bool a_by_token, const int32
     return hipGetLastError();
   }
   if (w.tiled) {
-    // m-tile-major 1-D grid; a deeper register prefetch when few slots make few workgroups
+    // m-tile-major 1-D grid; each wave keeps kTiledPrefetch of its chunks in flight
     const int64_t mt32 = (S + kTCols - 1) / kTCols + busy;
     const int ntn = (w.N + kTRows - 1) / kTRows;
     dim3 g1((unsigned)(mt32 * ntn));
-    const bool deep = S <= 64;
-#define MOE_LAUNCH_TILED(EPI)                                                                        \
-  do {                                                                                               \
-    if (deep)                                                                                        \
-      hipLaunchKernelGGL((ffn_stream_tiled_kernel<EPI, 2>), g1, block, 0, stream, a_src,            \
-                         a_by_token ? 1 : 0, sorted_slot, k, offsets, E, w.codes, w.scales, w.bias, \
-                         w.N, w.K, ntn, out, limit, alpha);                                         \
-    else                                                                                             \
-      hipLaunchKernelGGL((ffn_stream_tiled_kernel<EPI, 1>), g1, block, 0, stream, a_src,            \
-                         a_by_token ? 1 : 0, sorted_slot, k, offsets, E, w.codes, w.scales, w.bias, \
-                         w.N, w.K, ntn, out, limit, alpha);                                         \
-  } while (0)
+#define MOE_LAUNCH_TILED(EPI)                                                                       \
+  hipLaunchKernelGGL((ffn_stream_tiled_kernel<EPI, kTiledPrefetch>), g1, block, 0, stream, a_src,   \
+                     a_by_token ? 1 : 0, sorted_slot, k, offsets, E, w.codes, w.scales, w.bias, w.N, \
+                     w.K, ntn, out, limit, alpha)
     switch (epilogue) {
       case kEpiSwigluBf16: MOE_LAUNCH_TILED(kEpiSwigluBf16); break;
       case kEpiPreactF32: MOE_LAUNCH_TILED(kEpiPreactF32); break;

@@ -82,8 +82,8 @@ hipError_t launch_ffn_gemm(const void *a, const uint8_t *a_scales, const int32_t
 // (expert, 32-activation block). Writes per-block partial outputs part[block][sorted row][H]
 // (small_partial_floats floats; b2 in block 0); the combine adds the blocks in order. Every
 // expert must hold at most kSmallMaxT slots (top-k routing picks distinct experts per token,
-// so T <= kSmallMaxT does). One token only: the kernel's VALU products grow with the slots,
-// and from two tokens on the two-kernel form on the matrix cores is faster.
+// so T <= kSmallMaxT does). One token only: the kernel's VALU products grow with the slots.
+// Opt-in (MOE_PATH_DECODE_FUSED): the two-kernel form is faster on this part even at one token.
 constexpr int kSmallMaxT = 1;
 constexpr int kSmallMaxSlices = 128;  // the sliced combine's limit
 bool small_ffn_fits(int64_t T, int H, int I);

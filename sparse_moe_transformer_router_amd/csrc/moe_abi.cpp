@@ -97,7 +97,7 @@ moe_options_t default_options() {
 
 int check_options(const moe_options_t &o) {
   if (o.out_dtype != MOE_DTYPE_BF16 && o.out_dtype != MOE_DTYPE_F32) return MOE_ERR_INVALID_ARG;
-  if (o.path < MOE_PATH_AUTO || o.path > MOE_PATH_PREFILL_MX6SPLIT) return MOE_ERR_INVALID_ARG;
+  if (o.path < MOE_PATH_AUTO || o.path > MOE_PATH_DECODE_FUSED) return MOE_ERR_INVALID_ARG;
   if (!(o.swiglu_limit > 0.0f) || !(o.swiglu_alpha == o.swiglu_alpha)) return MOE_ERR_INVALID_ARG;
   if (o.flags & ~(MOE_FLAG_EMIT_PREACT | MOE_FLAG_EMIT_ACT)) return MOE_ERR_INVALID_ARG;
   if ((o.flags & MOE_FLAG_EMIT_PREACT) && (o.flags & MOE_FLAG_EMIT_ACT)) return MOE_ERR_INVALID_ARG;
@@ -123,9 +123,10 @@ enum class Family { kStream, kGemm, kGemmMx, kGemmMx6 };
 bool is_gemm_path(int path) {
   return path == MOE_PATH_PREFILL_BF16 || path == MOE_PATH_PREFILL_MX8SPLIT || path == MOE_PATH_PREFILL_MX6SPLIT;
 }
+bool needs_tiled(int path) { return is_gemm_path(path) || path == MOE_PATH_DECODE_FUSED; }
 
 int check_path(const moe_options_t &o, const moe_mxfp4_weight_t &gu, const moe_mxfp4_weight_t &dn) {
-  if (is_gemm_path(o.path) && (gu.layout != MOE_LAYOUT_TILED || dn.layout != MOE_LAYOUT_TILED))
+  if (needs_tiled(o.path) && (gu.layout != MOE_LAYOUT_TILED || dn.layout != MOE_LAYOUT_TILED))
     return MOE_ERR_UNSUPPORTED;
   return MOE_OK;
 }
@@ -136,7 +137,8 @@ Family family(const moe_options_t &o, const moe_mxfp4_weight_t &gu, const moe_mx
   if (o.path == MOE_PATH_PREFILL_BF16) return Family::kGemm;
   if (o.path == MOE_PATH_PREFILL_MX8SPLIT) return Family::kGemmMx;
   if (o.path == MOE_PATH_PREFILL_MX6SPLIT) return Family::kGemmMx6;
-  if (o.path == MOE_PATH_DECODE || !tiled || S < kGemmSlotsPerExpert * (int64_t)E) return Family::kStream;
+  if (o.path == MOE_PATH_DECODE || o.path == MOE_PATH_DECODE_FUSED || !tiled || S < kGemmSlotsPerExpert * (int64_t)E)
+    return Family::kStream;
   return dn.k >= kMx6MinI ? Family::kGemmMx6 : Family::kGemmMx;
 }
 
@@ -146,11 +148,11 @@ Family family(const moe_options_t &o, const moe_mxfp4_weight_t &gu, const moe_mx
 // projections (bf16 or two-term records).
 // x_records_ready: the block-scaled families' per-token MXFP8 records of x are already in xs
 // (the block's normalisation writes them), so the gather is skipped.
-// part / nslice_out: on AUTO with tiled weights and the smallest batches (small_ffn_fits; the
-// routing picks distinct experts per token, so an expert holds at most T slots), the expert
-// FFNs run as one launch (launch_ffn_small) writing per-block partial rows into part; then
-// *nslice_out = the block count (1 or more), and y is written (the blocks' in-order sum) only
-// if want_y. Otherwise y is written and *nslice_out = 0.
+// part / nslice_out: on MOE_PATH_DECODE_FUSED with tiled weights and the smallest batches
+// (small_ffn_fits; the routing picks distinct experts per token, so an expert holds at most T
+// slots), the expert FFNs run as one launch (launch_ffn_small) writing per-block partial rows
+// into part; then *nslice_out = the block count (1 or more), and y is written (the blocks'
+// in-order sum) only if want_y. Otherwise y is written and *nslice_out = 0.
 int run_ffn(const uint16_t *x, int64_t T, int k, int E, const int32_t *offsets, const int32_t *sorted_slot,
             const moe_mxfp4_weight_t &gu, const moe_mxfp4_weight_t &dn, const moe_options_t &o, float *y,
             void *act, void *xs, float *part, bool want_y, int *nslice_out, hipStream_t stream,
@@ -165,7 +167,7 @@ int run_ffn(const uint16_t *x, int64_t T, int k, int E, const int32_t *offsets, 
                         : (o.flags & MOE_FLAG_EMIT_ACT)  ? moe::kEpiActF32
                                                          : -1;
   *nslice_out = 0;
-  if (f == Family::kStream && o.path == MOE_PATH_AUTO && first_epi < 0 && w1.tiled && w2.tiled &&
+  if (f == Family::kStream && o.path == MOE_PATH_DECODE_FUSED && first_epi < 0 && w1.tiled && w2.tiled &&
       moe::small_ffn_fits(T, H, I)) {
     if (moe::launch_ffn_small(x, sorted_slot, k, offsets, E, S, w1, w2, part, lim, alpha, stream) != hipSuccess)
       return MOE_ERR_HIP;
@@ -330,7 +332,7 @@ const char *moe_status_string(int status) {
 }
 
 size_t moe_workspace_size(int64_t T, int32_t E, int32_t k, int32_t H, int32_t I, int32_t path) {
-  if (path < MOE_PATH_AUTO || path > MOE_PATH_PREFILL_MX6SPLIT) return 0;
+  if (path < MOE_PATH_AUTO || path > MOE_PATH_DECODE_FUSED) return 0;
   if (check_common(T, E, k) != MOE_OK || check_dim(H) != MOE_OK || check_dim(I) != MOE_OK) return 0;
   WsLayout L;
   if (!ws_layout(T, E, k, H, I, &L)) return 0;

@@ -48,7 +48,7 @@ def test_workspace_size():
     assert lib.moe_workspace_size(64, 3, 4, 2880, 2880, 0) == 0      # k > E
     assert lib.moe_workspace_size(64, 32, 4, 2880 + 16, 2880, 0) == 0  # H % 32
     assert lib.moe_workspace_size(-1, 32, 4, 2880, 2880, 0) == 0
-    assert lib.moe_workspace_size(64, 32, 4, 2880, 2880, 5) == 0     # bad path
+    assert lib.moe_workspace_size(64, 32, 4, 2880, 2880, 6) == 0     # bad path
     assert lib.moe_workspace_size(0, 32, 4, 2880, 2880, 0) > 0
 
 
@@ -107,7 +107,7 @@ def test_ffn_and_forward_errors():
     assert lib.moe_mxfp4_ffn(*args(gr, d, o)) == L.MOE_ERR_INVALID_ARG
     assert lib.moe_mxfp4_ffn(*args(g, d, L.MoeOptions(7.0, 1.0, 3, 0, 0))) == L.MOE_ERR_INVALID_ARG
     assert lib.moe_mxfp4_ffn(*args(g, d, L.MoeOptions(7.0, 1.0, 0, 9, 0))) == L.MOE_ERR_INVALID_ARG
-    for path in (2, 3, 4):  # the grouped GEMMs need tiled weights
+    for path in (2, 3, 4, 5):  # the grouped GEMMs and the one-launch decode need tiled weights
         assert lib.moe_mxfp4_ffn(*args(g, d, L.MoeOptions(7.0, 1.0, 0, path, 0))) == L.MOE_ERR_UNSUPPORTED
     assert lib.moe_mxfp4_ffn(*args(g, d, L.MoeOptions(-1.0, 1.0, 0, 0, 0))) == L.MOE_ERR_INVALID_ARG
     assert lib.moe_mxfp4_ffn(*args(g, d, L.MoeOptions(7.0, 1.0, 0, 0, 3))) == L.MOE_ERR_INVALID_ARG

@@ -99,7 +99,8 @@ def _gpu_block(dev, scale_d, out_dtype, path=0):
                                          ("decode20b", 64, 0), ("decode20b", 1024, 2), ("decode20b", 1024, 3),
                                          ("decode20b", 3, 3), ("prefill20b", 4096, 0), ("wide", 20, 0),
                                          ("wide", 20, 3), ("tiny", 16, 4), ("decode20b", 1024, 4),
-                                         ("wide", 20, 4), ("decode20b", 1, 0)])  # (path 4 kernel against kernel: any shape)
+                                         ("wide", 20, 4), ("decode20b", 1, 0), ("decode20b", 1, 5)])
+# (paths 4 and 5: kernel against kernel, any shape)
 def test_block_equals_layer_on_normalised_rows(name, T, path):
     """Kernel against kernel: the block's fp32 output is the layer's fp32 output on
     moe_rmsnorm's rows plus x, bit for bit (so the records the normalisation writes for the

@@ -44,13 +44,14 @@ def _replays_match(run, eager_out, graph_out, other):
         torch.cuda.synchronize()
 
 
-@pytest.mark.parametrize("name,T", [("decode20b", 64), ("decode20b", 1), ("prefill20b", 4096)])
-def test_layer_and_block_replay(name, T):
+@pytest.mark.parametrize("name,T,path", [("decode20b", 64, 0), ("decode20b", 1, 0), ("decode20b", 1, 5),
+                                         ("prefill20b", 4096, 0)])
+def test_layer_and_block_replay(name, T, path):
     cfg = synth.get_config(name)
     inp = synth.make_inputs(cfg, T)
     dev = gu.device_layer(inp, tiled=True)
     E, H, I, k = cfg.E, cfg.H, cfg.I, cfg.k
-    opts = moe.Options(out_dtype=moe.MOE_DTYPE_F32)
+    opts = moe.Options(out_dtype=moe.MOE_DTYPE_F32, path=path)
     ws_e, ws_g = moe.workspace(T, E, k, H, I), moe.workspace(T, E, k, H, I)
     out_e = torch.empty((T, H), dtype=torch.float32, device="cuda")
     out_g = torch.empty_like(out_e)

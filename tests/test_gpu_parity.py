@@ -155,11 +155,11 @@ def test_ffn_preact_identity_decode(scale_lo, scale_hi, tiled, path):
 
 
 @pytest.mark.parametrize("tiled,path,tokens", [(False, 1, None), (True, 1, None), (True, 2, None), (True, 3, None),
-                                               (True, 4, None), (True, 0, [37])])
+                                               (True, 4, None), (True, 5, [37])])
 def test_ffn_down_identity(tiled, path, tokens):
     """One-hot activations of exactly 1.0: y = W2 a is one decoded weight column, exactly, on
     every kernel family, including the two-term MXFP6 down input (1.0 and 0 are exact in E2M3)
-    and the one-launch kernel of a one-token batch (path 0, T = 1). W1's gate row 2i holds 2.0
+    and the one-launch kernel of a one-token batch (path 5, T = 1). W1's gate row 2i holds 2.0
     at input i (zero elsewhere), its linear rows are zero with bias -0.431640625, so token e_t
     gets gate 2.0 at unit t only: a_t = 2 sigma(2) (1 - 0.431640625) = 1.0012, which rounds to
     1.0 in bf16, and every other unit has gate 0, so a = 0 there."""
@@ -390,10 +390,10 @@ def test_layer_decode20b(T, tiled):
     _check_layer(synth.make_inputs(cfg, T), tiled=tiled)
 
 
-@pytest.mark.parametrize("name,T", [("decode20b", 1), ("decode20b", 64), ("decode20b", 256),
-                                    ("decode20b", 512), ("decode20b", 513), ("decode20b", 1023),
-                                    ("decode120b_zipf", 64), ("tiny", 16)])
-def test_forward_matches_composed_steps(name, T):
+@pytest.mark.parametrize("name,T,path", [("decode20b", 1, 0), ("decode20b", 1, 5), ("decode20b", 64, 0),
+                                         ("decode20b", 256, 0), ("decode20b", 512, 0), ("decode20b", 513, 0),
+                                         ("decode20b", 1023, 0), ("decode120b_zipf", 64, 0), ("tiny", 16, 0)])
+def test_forward_matches_composed_steps(name, T, path):
     """moe_forward_ex gives the same bits as the four steps called one by one through the C ABI
     (route, permute, expert FFN, combine) with their own workspaces. Up to 2048 slots the
     layer picks and sorts in one launch (the last workgroup to finish the top-k sorts), above
@@ -401,7 +401,7 @@ def test_forward_matches_composed_steps(name, T):
     cfg = synth.get_config(name)
     dev = gu.device_layer(synth.make_inputs(cfg, T), tiled=True)
     E = int(dev.router.weight.shape[0])
-    opts = moe.Options()
+    opts = moe.Options(path=path)
     out_fw = gu.bf16_bits(moe.moe_forward_ex(dev.x, dev.router, dev.w1, dev.w2, dev.k, opts))
     idx, w = moe.moe_route(dev.x, dev.router, dev.k)
     off, ss, sr = moe.moe_permute(idx, E)
@@ -540,16 +540,18 @@ def test_layer_shapes_mx6(E, k, H, I, T):
                                        (2, 2, 256, 4128, 1), (1, 1, 64, 96, 1), (32, 4, 2880, 2880, 2),
                                        (32, 4, 2880, 2880, 5)])
 def test_small_batch_path(E, k, H, I, T):
-    """One token with tiled weights: AUTO runs gate_up, SwiGLU and down in one launch per
-    (expert, 32-activation block), summing the blocks' partial outputs in the combine; against
-    the oracle, and the two-kernel stream path (path 1) at the same bar. Shapes cover one chunk
-    of input (H = 32: three of the four chunk quarters empty), one block (I = 32), blocks in
-    every place of W2's tiles (I = 96, 160), k = 8, E = 256, the largest H and I it takes (3072,
-    4096 = 128 blocks) and the next sizes past them (3104, 4128: the two-kernel path), and two
-    and five tokens (the two-kernel path on AUTO)."""
+    """Path 5 with one token and tiled weights runs gate_up, SwiGLU and down in one launch per
+    (expert, 32-activation block), summing the blocks' partial outputs in the combine; graded
+    against the oracle, as are AUTO and the two-kernel stream path (path 1) on the same inputs.
+    Shapes cover one chunk of input (H = 32: three of the four chunk quarters empty), one block
+    (I = 32), blocks in every place of W2's tiles (I = 96, 160), k = 8, E = 256, the largest H
+    and I it takes (3072, 4096 = 128 blocks) and the next sizes past them (3104, 4128: path 5
+    falls back to the two-kernel form), and two and five tokens (likewise)."""
     inp = synth.make_inputs(_small_cfg(E, k, H, I, T))
-    _check_layer(inp, path=0)
-    _check_layer(inp, path=1)
+    dev = gu.device_layer(inp, tiled=True)
+    ref = gu.oracle_forward(inp, _gpu_idx(dev))
+    for path in (5, 0, 1):
+        _check_layer(inp, path=path, dev=dev, ref=ref)
 
 
 def test_small_batch_path_hot_expert():

@@ -388,7 +388,9 @@ __device__ __forceinline__ void ring_tail(F &&body, int c, int nchunk, std::inte
 
 constexpr int kRWaves = 4;
 constexpr int kRCols = 32;            // slots per m-tile
-constexpr int kRowSplitMinSlots = 16; // below this the K-split form keeps more waves busy
+// below this many slots the K-split form keeps more waves busy (FFN, decode20b: 16 slots 45.0
+// against 47.5 us for the row-split form; 24 slots 52.9 against 51.4, 32 slots 74.1 against 70.7)
+constexpr int kRowSplitMinSlots = 20;
 
 template <int EPI, int D>
 __global__ __launch_bounds__(kRWaves *kWave) void ffn_stream_rows_kernel(

@@ -538,7 +538,7 @@ def test_layer_shapes_mx6(E, k, H, I, T):
                                        (4, 4, 128, 96, 1), (16, 8, 96, 160, 1), (256, 8, 64, 64, 1),
                                        (2, 2, 3072, 256, 1), (2, 2, 3104, 256, 1), (2, 2, 256, 4096, 1),
                                        (2, 2, 256, 4128, 1), (1, 1, 64, 96, 1), (32, 4, 2880, 2880, 2),
-                                       (32, 4, 2880, 2880, 5)])
+                                       (32, 4, 2880, 2880, 4), (32, 4, 2880, 2880, 5)])
 def test_small_batch_path(E, k, H, I, T):
     """Path 5 with one token and tiled weights runs gate_up, SwiGLU and down in one launch per
     (expert, 32-activation block), summing the blocks' partial outputs in the combine; graded
@@ -546,7 +546,8 @@ def test_small_batch_path(E, k, H, I, T):
     Shapes cover one chunk of input (H = 32: three of the four chunk quarters empty), one block
     (I = 32), blocks in every place of W2's tiles (I = 96, 160), k = 8, E = 256, the largest H
     and I it takes (3072, 4096 = 128 blocks) and the next sizes past them (3104, 4128: path 5
-    falls back to the two-kernel form), and two and five tokens (likewise)."""
+    falls back to the two-kernel form), and two, four and five tokens (likewise; 16 slots run
+    the K-split kernel, 20 the row-split one)."""
     inp = synth.make_inputs(_small_cfg(E, k, H, I, T))
     dev = gu.device_layer(inp, tiled=True)
     ref = gu.oracle_forward(inp, _gpu_idx(dev))

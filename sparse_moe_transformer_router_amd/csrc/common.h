@@ -75,6 +75,19 @@ __device__ __forceinline__ int wave_inclusive_scan(int v) {
   return v;
 }
 
+// Minimum over the wave's 64 lanes (the same DPP pattern as wave_max_f32), read from lane 63.
+__device__ __forceinline__ int wave_min_i32(int x) {
+#define MOE_DPP_MIN(CTRL, ROWS) x = min(x, __builtin_amdgcn_update_dpp(x, x, CTRL, ROWS, 0xF, false))
+  MOE_DPP_MIN(0xB1, 0xF);   // quad_perm [1, 0, 3, 2]
+  MOE_DPP_MIN(0x4E, 0xF);   // quad_perm [2, 3, 0, 1]
+  MOE_DPP_MIN(0x141, 0xF);  // row_half_mirror
+  MOE_DPP_MIN(0x140, 0xF);  // row_mirror
+  MOE_DPP_MIN(0x142, 0xA);  // row_bcast15 into rows 1 and 3
+  MOE_DPP_MIN(0x143, 0xC);  // row_bcast31 into rows 2 and 3
+#undef MOE_DPP_MIN
+  return __builtin_amdgcn_readlane(x, 63);
+}
+
 // Value of lane `l` (wave-uniform) for every lane.
 __device__ __forceinline__ int wave_read(int v, int l) { return __builtin_amdgcn_readlane(v, l); }
 

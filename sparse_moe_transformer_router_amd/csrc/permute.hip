@@ -221,11 +221,7 @@ __global__ __launch_bounds__(256) void router_topk_permute_kernel(
   const int64_t t = (int64_t)blockIdx.x * 4 + threadIdx.x / kWave;
   if (t < T) {
     float v[4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int e = lane + i * kWave;
-      v[i] = (e < E) ? router_logit_tm(partial, nsplit, (nsplit + 3) / 4 * 4, bias, t, e, E) : 0.f;
-    }
+    router_logits_wave<false>(partial, nsplit, bias, t, T, E, lane, v);
     topk_softmax_wave(v, E, k, lane, topk_idx + t * k, topk_w + t * k);
   }
   __threadfence();
@@ -253,11 +249,7 @@ __global__ __launch_bounds__(kPermThreads) void router_topk_permute_small_kernel
   const int lane = threadIdx.x % kWave, wave = threadIdx.x / kWave;
   if (wave < T) {  // wave-uniform
     float v[4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int e = lane + i * kWave;
-      v[i] = (e < E) ? router_logit_tm(partial, nsplit, (nsplit + 3) / 4 * 4, bias, wave, e, E) : 0.f;
-    }
+    router_logits_wave<false>(partial, nsplit, bias, wave, T, E, lane, v);
     topk_softmax_wave(v, E, k, lane, topk_idx + (int64_t)wave * k, topk_w + (int64_t)wave * k, picks + wave * k);
   }
   __syncthreads();

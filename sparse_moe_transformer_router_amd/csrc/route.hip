@@ -142,14 +142,7 @@ __global__ __launch_bounds__(256) void router_topk_kernel(const float *__restric
   const int64_t t = (int64_t)blockIdx.x * (blockDim.x / kWave) + threadIdx.x / kWave;
   if (t >= T) return;
   float v[4];
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int e = lane + i * kWave;
-    if constexpr (SM)
-      v[i] = (e < E) ? router_logit_sm(partial, nsplit, bias, t, e, T, E) : 0.f;
-    else
-      v[i] = (e < E) ? router_logit_tm(partial, nsplit, (nsplit + 3) / 4 * 4, bias, t, e, E) : 0.f;
-  }
+  router_logits_wave<SM>(partial, nsplit, bias, t, T, E, lane, v);
   topk_softmax_wave(v, E, k, lane, topk_idx + t * k, topk_w + t * k);
 }
 

@@ -390,14 +390,15 @@ def test_layer_decode20b(T, tiled):
     _check_layer(synth.make_inputs(cfg, T), tiled=tiled)
 
 
-@pytest.mark.parametrize("name,T,path", [("decode20b", 1, 0), ("decode20b", 1, 5), ("decode20b", 64, 0),
-                                         ("decode20b", 256, 0), ("decode20b", 512, 0), ("decode20b", 513, 0),
-                                         ("decode20b", 1023, 0), ("decode120b_zipf", 64, 0), ("tiny", 16, 0)])
+@pytest.mark.parametrize("name,T,path", [("decode20b", 1, 0), ("decode20b", 1, 5), ("decode20b", 16, 0),
+                                         ("decode20b", 17, 0), ("decode20b", 64, 0), ("decode20b", 256, 0),
+                                         ("decode20b", 512, 0), ("decode20b", 513, 0), ("decode20b", 1023, 0), ("decode120b_zipf", 64, 0), ("tiny", 16, 0)])
 def test_forward_matches_composed_steps(name, T, path):
     """moe_forward_ex gives the same bits as the four steps called one by one through the C ABI
     (route, permute, expert FFN, combine) with their own workspaces. Up to 2048 slots the
-    layer picks and sorts in one launch (the last workgroup to finish the top-k sorts), above
-    that in two; 512 / 513 tokens sit on either side of that switch."""
+    layer picks and sorts in one launch, above that in two (512 / 513 tokens sit on either side
+    of that switch); up to 16 tokens that launch is one workgroup, above that the last
+    workgroup to finish the top-k sorts (16 / 17 tokens)."""
     cfg = synth.get_config(name)
     dev = gu.device_layer(synth.make_inputs(cfg, T), tiled=True)
     E = int(dev.router.weight.shape[0])

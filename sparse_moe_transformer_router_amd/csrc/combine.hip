@@ -9,39 +9,44 @@
 
 namespace moe {
 
+// Every load is issued unconditionally from an in-bounds address and the unused values are
+// dropped at their use (a pick outside [0, S) reads row 0 and is skipped; without a residual
+// the residual load reads y's first bytes and is ignored): with loads under branches the
+// compiler waited for the rows two at a time, one memory round trip per pair. K = k.
+template <int K>
 __global__ __launch_bounds__(256) void combine_kernel(const float *__restrict__ y,
                                                       const int32_t *__restrict__ slot_row,
-                                                      const float *__restrict__ topk_w, int64_t T,
-                                                      int k, int H, const uint16_t *__restrict__ residual,
+                                                      const float *__restrict__ topk_w, int64_t T, int H,
+                                                      const uint16_t *__restrict__ residual,
                                                       void *__restrict__ out, int out_f32) {
   const int chunks = (H / 4 + blockDim.x - 1) / blockDim.x;
   const int64_t t = blockIdx.x / chunks;
   const int h = ((blockIdx.x % chunks) * blockDim.x + threadIdx.x) * 4;
   if (h >= H) return;
-  const int64_t S = T * k;
-  // all index/weight loads first, then all row loads, then the sum in rank order
-  int32_t r[8];
-  float w[8];
+  const int64_t S = T * K;
+  int32_t r[K];
+  float w[K];
+  bool ok[K];
 #pragma unroll
-  for (int j = 0; j < 8; ++j) {
-    r[j] = (j < k) ? slot_row[t * k + j] : -1;
-    w[j] = (j < k) ? topk_w[t * k + j] : 0.f;
+  for (int j = 0; j < K; ++j) {
+    r[j] = slot_row[t * K + j];
+    w[j] = topk_w[t * K + j];
+    ok[j] = (uint32_t)r[j] < (uint64_t)S;
   }
-  f32x4_t v[8];
+  f32x4_t v[K];
 #pragma unroll
-  for (int j = 0; j < 8; ++j)
-    v[j] = ((uint32_t)r[j] < (uint64_t)S) ? *reinterpret_cast<const f32x4_t *>(y + (int64_t)r[j] * H + h)
-                                          : f32x4_t{0.f, 0.f, 0.f, 0.f};
-  uint2 res = {0u, 0u};
-  if (residual != nullptr) res = *reinterpret_cast<const uint2 *>(residual + t * H + h);
+  for (int j = 0; j < K; ++j) v[j] = *reinterpret_cast<const f32x4_t *>(y + (int64_t)(ok[j] ? r[j] : 0) * H + h);
+  // y holds S >= T rows of H floats, so its first T H halves cover the dummy residual read
+  const uint2 res = *reinterpret_cast<const uint2 *>(
+      (residual != nullptr ? residual : reinterpret_cast<const uint16_t *>(y)) + t * H + h);
+  // the residual's value is taken here, with the rows' (else the compiler sinks its load into
+  // the residual branch, a second round trip after the rows)
+  asm volatile("" ::"v"(res.x), "v"(res.y));
   f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-  for (int j = 0; j < 8; ++j) {
-    if (j < k && (uint32_t)r[j] < (uint64_t)S) {
+  for (int j = 0; j < K; ++j)
 #pragma unroll
-      for (int i = 0; i < 4; ++i) acc[i] = fmaf(w[j], v[j][i], acc[i]);
-    }
-  }
+    for (int i = 0; i < 4; ++i) acc[i] = ok[j] ? fmaf(w[j], v[j][i], acc[i]) : acc[i];
   if (residual != nullptr) {
     acc[0] += __uint_as_float(res.x << 16);
     acc[1] += __uint_as_float(res.x & 0xffff0000u);
@@ -64,8 +69,21 @@ hipError_t launch_combine(const float *y, const int32_t *slot_row, const float *
   const int threads = 256;
   const int64_t chunks = (H / 4 + threads - 1) / threads;
   dim3 grid((unsigned)(T * chunks));
-  hipLaunchKernelGGL(combine_kernel, grid, dim3(threads), 0, stream, y, slot_row, topk_w, T, k, H,
-                     residual, out, out_f32 ? 1 : 0);
+#define MOE_COMBINE(K)                                                                                    \
+  hipLaunchKernelGGL(combine_kernel<K>, grid, dim3(threads), 0, stream, y, slot_row, topk_w, T, H, residual, \
+                     out, out_f32 ? 1 : 0)
+  switch (k) {
+    case 1: MOE_COMBINE(1); break;
+    case 2: MOE_COMBINE(2); break;
+    case 3: MOE_COMBINE(3); break;
+    case 4: MOE_COMBINE(4); break;
+    case 5: MOE_COMBINE(5); break;
+    case 6: MOE_COMBINE(6); break;
+    case 7: MOE_COMBINE(7); break;
+    case 8: MOE_COMBINE(8); break;
+    default: return hipErrorInvalidValue;
+  }
+#undef MOE_COMBINE
   return hipGetLastError();
 }
 
@@ -88,17 +106,19 @@ template <typename Rows>
 __device__ __forceinline__ void sliced_rows_sum(const float *__restrict__ part, int nslice, int64_t stride, int H,
                                                 Rows rows, int nrows, int h, bool h_ok, int q, int g,
                                                 f32x4_t (*red)[kSlRows][kSlQuads]) {
+  // every load is issued from an in-bounds address (unused ones read part[0] and are zeroed at
+  // their use), so all of them are in flight together
   f32x4_t u[kSlRows][2];
 #pragma unroll
   for (int j = 0; j < kSlRows; ++j) {
-    if (j >= nrows) break;
-    const int64_t r = rows(j);
-    const bool ok = h_ok && r >= 0;
+    const int64_t r = rows(j < nrows ? j : 0);
+    const bool ok = j < nrows && h_ok && r >= 0;
 #pragma unroll
     for (int i = 0; i < 2; ++i) {
       const int sl = g + kSlGroups * i;
       const bool use = ok && sl < nslice;
-      u[j][i] = use ? *reinterpret_cast<const f32x4_t *>(part + sl * stride + r * H + h) : f32x4_t{0.f, 0.f, 0.f, 0.f};
+      const f32x4_t x = *reinterpret_cast<const f32x4_t *>(part + (use ? sl * stride + r * H + h : 0));
+      u[j][i] = use ? x : f32x4_t{0.f, 0.f, 0.f, 0.f};
     }
   }
 #pragma unroll

@@ -329,7 +329,9 @@ def attention_decode(q: np.ndarray, k_cache: np.ndarray, v_cache: np.ndarray, le
 
     Readings taken: query head h reads key/value head h // (Hq / Hkv) (consecutive query heads
     share one); the score is q.k / sqrt(D); the sink is one more logit in the softmax whose
-    value vector is zero, so the weights of the real keys sum to less than one.
+    value vector is zero, so the weights of the real keys sum to less than one. A sequence with
+    no visible position (lens[b] = 0) gives 0: with a sink every real key's weight is 0, and
+    without one the weighted sum has no terms (the pages do not reach this case).
     Returns float64 [B][Hq][D].
     """
     q = np.asarray(q, np.float64)
@@ -342,6 +344,8 @@ def attention_decode(q: np.ndarray, k_cache: np.ndarray, v_cache: np.ndarray, le
     for b in range(B):
         n = int(lens[b])
         lo = 0 if window <= 0 else max(0, n - window)
+        if n <= lo:
+            continue  # nothing visible: the output row stays 0
         for h in range(Hq):
             g = h // group
             keys = kc[b, g, lo:n]      # [n - lo][D]

@@ -509,6 +509,21 @@ def pin_attention_closed_forms():
     assert np.allclose(out[0, 0], want, rtol=1e-14, atol=1e-15)
 
 
+def pin_attention_empty_sequence():
+    """No visible position (lens = 0): the output row is 0, with a sink (every real key's weight
+    is 0) and without one (an empty weighted sum); the other sequence is unaffected."""
+    rng = np.random.default_rng(43)
+    q = rng.standard_normal((2, 4, 64))
+    k = rng.standard_normal((2, 2, 3, 64))
+    v = rng.standard_normal((2, 2, 3, 64))
+    lens = np.array([0, 3])
+    for sinks in (None, np.array([0.5, -1.0, 2.0, 0.0])):
+        out = om.attention_decode(q, k, v, lens, sinks, 0)
+        assert np.all(out[0] == 0.0)
+        alone = om.attention_decode(q[1:], k[1:], v[1:], lens[1:], sinks, 0)
+        assert np.array_equal(out[1], alone[0])
+
+
 # --------------------------------------------------------------------------- shapes vs pages
 GIB = 2.0 ** 30
 
@@ -558,5 +573,5 @@ ALL_PINS = [
     pin_single_expert_reduction, pin_dense_masked_bruteforce, pin_token_subset,
     pin_shapes_against_pages, pin_rms_norm_closed_forms, pin_rms_norm_invariants,
     pin_bf16_rounding, pin_block_reductions, pin_attention_library_reductions,
-    pin_attention_closed_forms,
+    pin_attention_closed_forms, pin_attention_empty_sequence,
 ]

@@ -95,13 +95,20 @@ def test_attn_invisible_positions_are_never_read_into_the_result():
     _check(inp, 128)
 
 
-def test_attn_zero_length_and_determinism():
+@pytest.mark.parametrize("with_sink", [True, False])
+@pytest.mark.parametrize("window", [0, 128])
+def test_attn_zero_length_and_determinism(with_sink, window):
+    """A sequence with no visible position gives 0 (with or without sinks, as the oracle does);
+    the others match the oracle; a second call gives the same bits."""
     inp = synth.make_attn_inputs(3, 64, seed=5)
+    inp.lens[1] = 0
     q, k, v, lens, sinks = _dev(inp)
-    lens[1] = 0
-    out = moe.moe_attn_decode(q, k, v, lens, sinks, 0, out_dtype=moe.MOE_DTYPE_F32).cpu().numpy()
+    out = moe.moe_attn_decode(q, k, v, lens, sinks if with_sink else None, window,
+                              out_dtype=moe.MOE_DTYPE_F32).cpu().numpy()
     assert np.all(out[1] == 0.0)
-    again = moe.moe_attn_decode(q, k, v, lens, sinks, 0, out_dtype=moe.MOE_DTYPE_F32).cpu().numpy()
+    _check(inp, window, with_sink=with_sink)
+    again = moe.moe_attn_decode(q, k, v, lens, sinks if with_sink else None, window,
+                                out_dtype=moe.MOE_DTYPE_F32).cpu().numpy()
     assert np.array_equal(out, again)
 
 

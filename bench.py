@@ -345,7 +345,7 @@ def main():
     args = parse()
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
-        print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1"}), flush=True)
+        print(json.dumps({"error": "one GPU only: the layer runs on a single device, so --gpus must be 1"}), flush=True)
         sys.exit(2)
 
     import torch

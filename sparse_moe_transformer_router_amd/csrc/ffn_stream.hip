@@ -26,6 +26,7 @@
 
 #include "common.h"
 #include "kernels.h"
+#include "topk.h"
 
 namespace moe {
 
@@ -184,12 +185,46 @@ constexpr int kTRows = 64;   // weight rows per workgroup (two 32-row tiles)
 constexpr int kTCols = 32;   // slots per m-tile
 constexpr int kTiledPrefetch = 2;  // chunks in flight per wave
 
-template <int EPI, int PF>
+// One token's routing inside the gate_up launch (R1 = k, its pick count; 0: off): the slots
+// are the token's k picks, and m-tile j is pick j alone. Every wave sums the router's split-K
+// partials and picks the experts exactly as the router's top-k kernels do (the same helpers,
+// so the same picks and weights), and workgroup 0's first wave publishes the routing (picks,
+// weights, offsets, the stable sort of the k slots) for the down projection and the combine.
+// No workgroup reads what another writes.
+template <int R1>
+__device__ __forceinline__ int route1_rank(const int (&pe)[R1], int e) {
+  int rank = 0;
+#pragma unroll
+  for (int j = 0; j < R1; ++j) rank += (pe[j] >= 0 && pe[j] < e) ? 1 : 0;
+  return rank;
+}
+
+template <int R1>
+__device__ __forceinline__ void route1_publish(const int (&pe)[R1], const float (&pw)[R1], int E, int lane,
+                                               const Route1 &r1) {
+  int ej = -1;
+  float wj = 0.f;
+#pragma unroll
+  for (int j = 0; j < R1; ++j) {
+    ej = lane == j ? pe[j] : ej;
+    wj = lane == j ? pw[j] : wj;
+  }
+  if (lane < R1) {
+    const int rank = route1_rank<R1>(pe, ej);
+    r1.topk_idx[lane] = ej;
+    r1.topk_w[lane] = wj;
+    r1.slot_row[lane] = ej >= 0 ? rank : -1;  // a pick with no expert (NaN logits) gets no row
+    if (ej >= 0) r1.sorted_slot[rank] = lane;
+  }
+  for (int x = lane; x <= E; x += kWave) r1.offsets[x] = route1_rank<R1>(pe, x);
+}
+
+template <int EPI, int PF, int R1 = 0>
 __global__ __launch_bounds__(kSWaves *kWave) void ffn_stream_tiled_kernel(
     const uint16_t *__restrict__ a_src, int a_by_token, const int32_t *__restrict__ sorted_slot, int k,
     const int32_t *__restrict__ offsets, int E, const uint8_t *__restrict__ pcodes,
     const uint8_t *__restrict__ pscales, const uint16_t *__restrict__ bias, int N, int K, int ntiles_n,
-    void *__restrict__ out, float limit, float alpha) {
+    void *__restrict__ out, float limit, float alpha, Route1 r1) {
   constexpr int RG = kTRows / 32;
   __shared__ float red[kSWaves][kTRows][kTCols + 1];
   const int wave = threadIdx.x / kWave, lane = threadIdx.x % kWave;
@@ -198,7 +233,22 @@ __global__ __launch_bounds__(kSWaves *kWave) void ffn_stream_tiled_kernel(
   const int n0 = nt * kTRows;
 
   int e = -1, m0 = 0, rbase = 0, mcount = 0;
-  {
+  if constexpr (R1 > 0) {
+    float v[4];
+    router_logits_wave<false>(r1.partial, r1.nsplit, r1.bias, 0, 1, E, lane, v);
+    int pe[R1];
+    float pw[R1];
+    topk_picks_wave_k<R1>(v, E, lane, pe, pw);
+    if (blockIdx.x == 0 && wave == 0) route1_publish<R1>(pe, pw, E, lane, r1);
+    int sel = -1;
+#pragma unroll
+    for (int j = 0; j < R1; ++j) sel = j == mt ? pe[j] : sel;
+    if (sel >= 0) {
+      e = sel;
+      rbase = route1_rank<R1>(pe, sel);
+      mcount = 1;
+    }
+  } else {
     int carry = 0;
     for (int eb = 0; eb < E; eb += kWave) {
       const int ex = eb + lane;
@@ -224,8 +274,8 @@ __global__ __launch_bounds__(kSWaves *kWave) void ffn_stream_tiled_kernel(
 
   const int r32 = lane % 32, kh = lane / 32;
   const bool col_ok = r32 < mcount;
-  const uint16_t *arow = a_src;
-  if (col_ok) {
+  const uint16_t *arow = a_src;  // R1: the one token's row
+  if (R1 == 0 && col_ok) {
     const int r = rbase + m0 + r32;
     arow = a_src + (a_by_token ? (int64_t)(sorted_slot[r] / k) : (int64_t)r) * K;
   }
@@ -585,7 +635,7 @@ hipError_t launch_ffn_stream(const uint16_t *a_src, bool a_by_token, const int32
 #define MOE_LAUNCH_TILED(EPI)                                                                       \
   hipLaunchKernelGGL((ffn_stream_tiled_kernel<EPI, kTiledPrefetch>), g1, block, 0, stream, a_src,   \
                      a_by_token ? 1 : 0, sorted_slot, k, offsets, E, w.codes, w.scales, w.bias, w.N, \
-                     w.K, ntn, out, limit, alpha)
+                     w.K, ntn, out, limit, alpha, Route1{})
     switch (epilogue) {
       case kEpiSwigluBf16: MOE_LAUNCH_TILED(kEpiSwigluBf16); break;
       case kEpiPreactF32: MOE_LAUNCH_TILED(kEpiPreactF32); break;
@@ -602,6 +652,33 @@ hipError_t launch_ffn_stream(const uint16_t *a_src, bool a_by_token, const int32
     default: MOE_LAUNCH_STREAM(kEpiLinearF32); break;
   }
 #undef MOE_LAUNCH_STREAM
+  return hipGetLastError();
+}
+
+bool ffn_route1_fits(int64_t T, int E, int k, const MxWeight &w) {
+  return T == 1 && w.tiled && k >= 1 && k <= 8 && E >= k && E <= 256 && (int64_t)k < kRowSplitMinSlots;
+}
+
+hipError_t launch_ffn_stream_route1(const uint16_t *x, int k, int E, const MxWeight &w, void *act, float limit,
+                                    float alpha, const Route1 &r1, hipStream_t stream) {
+  // one m-tile per pick, the weight rows of gate_up in 64-row tiles
+  const int ntn = (w.N + kTRows - 1) / kTRows;
+  const dim3 grid((unsigned)(k * ntn)), block(kSWaves * kWave);
+#define MOE_LAUNCH_ROUTE1(K1)                                                                                      \
+  hipLaunchKernelGGL((ffn_stream_tiled_kernel<kEpiSwigluBf16, kTiledPrefetch, K1>), grid, block, 0, stream, x, 0, \
+                     nullptr, k, nullptr, E, w.codes, w.scales, w.bias, w.N, w.K, ntn, act, limit, alpha, r1)
+  switch (k) {
+    case 1: MOE_LAUNCH_ROUTE1(1); break;
+    case 2: MOE_LAUNCH_ROUTE1(2); break;
+    case 3: MOE_LAUNCH_ROUTE1(3); break;
+    case 4: MOE_LAUNCH_ROUTE1(4); break;
+    case 5: MOE_LAUNCH_ROUTE1(5); break;
+    case 6: MOE_LAUNCH_ROUTE1(6); break;
+    case 7: MOE_LAUNCH_ROUTE1(7); break;
+    case 8: MOE_LAUNCH_ROUTE1(8); break;
+    default: return hipErrorInvalidValue;
+  }
+#undef MOE_LAUNCH_ROUTE1
   return hipGetLastError();
 }
 

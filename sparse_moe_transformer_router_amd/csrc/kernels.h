@@ -62,6 +62,26 @@ hipError_t launch_ffn_stream(const uint16_t *a_src, bool a_by_token, const int32
                              int k, const int32_t *offsets, int E, int64_t S, const MxWeight &w,
                              int epilogue, void *out, float limit, float alpha, hipStream_t stream);
 
+// One token (ffn_route1_fits: T = 1, tiled weights, k <= 8, E <= 256): the gate_up launch of
+// launch_ffn_stream (SwiGLU bf16 epilogue, act rows in sorted order) that also does the top-k of
+// launch_router_topk_permute on the router's partials (launch_router_partial, token-major) and
+// writes its outputs (topk_idx, topk_w, offsets, sorted_slot, slot_row; a pick without an
+// expert gets slot_row -1), so the routing needs no launch of its own. The down launch and the
+// combine then run as usual on those outputs.
+struct Route1 {
+  const float *partial;
+  int nsplit;
+  const float *bias;
+  int32_t *topk_idx;
+  float *topk_w;
+  int32_t *offsets;
+  int32_t *sorted_slot;
+  int32_t *slot_row;
+};
+bool ffn_route1_fits(int64_t T, int E, int k, const MxWeight &w);
+hipError_t launch_ffn_stream_route1(const uint16_t *x, int k, int E, const MxWeight &w, void *act, float limit,
+                                    float alpha, const Route1 &r1, hipStream_t stream);
+
 // Activation forms of the grouped GEMM's input rows: bf16, or two-term block-scaled records
 // (MXFP8 or MXFP6 terms, mx_act.h).
 enum ActForm : int { kActBf16 = 0, kActMx8 = 1, kActMx6 = 2 };

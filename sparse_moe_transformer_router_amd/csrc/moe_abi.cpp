@@ -267,6 +267,20 @@ int forward_impl(const uint16_t *x, const moe_router_t *router, const moe_mxfp4_
   int32_t *slot_row = at<int32_t>(ws, L.slot_row);
   void *act = at<void>(ws, L.act);
   float *y = at<float>(ws, L.y);
+  const moe::MxWeight w1 = mx(*gu);
+  if (o.path != MOE_PATH_DECODE_FUSED && o.flags == 0 && family(o, *gu, *dn, S, E) == Family::kStream &&
+      moe::ffn_route1_fits(T, E, k, w1)) {
+    // one token: the top-k and the permutation of its k slots run inside the gate_up launch
+    const moe::Route1 r1{logits, moe::router_splits(T, E, H), router->bias, idx, wts, offsets, sorted_slot, slot_row};
+    if (moe::launch_router_partial(x, T, H, router->weight, E, logits, stream) != hipSuccess ||
+        moe::launch_ffn_stream_route1(x, k, E, w1, act, o.swiglu_limit, o.swiglu_alpha, r1, stream) != hipSuccess ||
+        moe::launch_ffn_stream(static_cast<uint16_t *>(act), false, sorted_slot, k, offsets, E, S, mx(*dn),
+                               moe::kEpiLinearF32, y, o.swiglu_limit, o.swiglu_alpha, stream) != hipSuccess ||
+        moe::launch_combine(y, slot_row, wts, T, k, H, out, o.out_dtype == MOE_DTYPE_F32, stream, residual) !=
+            hipSuccess)
+      return MOE_ERR_HIP;
+    return MOE_OK;
+  }
   if (moe::topk_permute_fits(T, E, k)) {  // decode batches: top-k and permutation in one launch
     int *counter = at<int>(ws, L.counter);
     if (moe::launch_router_partial(x, T, H, router->weight, E, logits, stream, counter) != hipSuccess ||

@@ -49,7 +49,11 @@ __device__ __forceinline__ void router_logit_tm_issue(const float *__restrict__ 
                                                       const float *__restrict__ bias, int64_t t, int e, int E,
                                                       TmLogitLoads &l) {
   const f32x4_t *p = reinterpret_cast<const f32x4_t *>(partial + (t * E + e) * nsp);
-  const int nv = nsp / 4;
+  // opaque to the compiler: otherwise it computes the clamped offsets (and, below, the split
+  // predicates) once for all of a wave's logits and keeps them in scalar registers, dozens of
+  // them, which spill where a kernel has few to spare
+  int nv = nsp / 4;
+  asm volatile("" : "+s"(nv));
   l.bv = *(bias != nullptr ? bias + e : partial);
 #pragma unroll
   for (int c = 0; c < kMaxSplitVec; ++c) l.pv[c] = p[c < nv ? c : nv - 1];
@@ -57,6 +61,7 @@ __device__ __forceinline__ void router_logit_tm_issue(const float *__restrict__ 
 
 __device__ __forceinline__ float router_logit_tm_add(const TmLogitLoads &l, int nsplit,
                                                      const float *__restrict__ bias) {
+  asm volatile("" : "+s"(nsplit));
   float s = 0.f;
 #pragma unroll
   for (int c = 0; c < kMaxSplitVec; ++c)
@@ -109,17 +114,15 @@ __device__ __forceinline__ void router_logits_wave(const float *__restrict__ par
 // larger logit wins, equal logits go to the lower expert id): the maximum of the experts not
 // yet picked by DPP moves, then the lowest id holding it by a DPP minimum over the lanes'
 // candidate ids. Then softmax over the K picked logits (in pick order, relative to the
-// largest); lane j < K writes pick j's id and weight (and, if lds_idx is given, the id there
-// too). Branch-free per round: the picks are wave-uniform values. A logit that equals no
-// maximum (all remaining NaN) gives id -1.
+// largest). Branch-free per round; the picks and weights come out wave-uniform. A logit that
+// equals no maximum (all remaining NaN) gives id -1.
 template <int K>
-__device__ __forceinline__ void topk_softmax_wave_k(const float (&v)[4], int E, int lane, int32_t *__restrict__ idx_out,
-                                                    float *__restrict__ w_out, int *lds_idx) {
+__device__ __forceinline__ void topk_picks_wave_k(const float (&v)[4], int E, int lane, int (&sel_e)[K],
+                                                  float (&wt)[K]) {
   bool tk[4];
 #pragma unroll
   for (int i = 0; i < 4; ++i) tk[i] = lane + i * kWave >= E;
   float sel_v[K];
-  int sel_e[K];
 #pragma unroll
   for (int j = 0; j < K; ++j) {
     float lm = -INFINITY;
@@ -142,12 +145,24 @@ __device__ __forceinline__ void topk_softmax_wave_k(const float (&v)[4], int E, 
     sum += z[j];
   }
   const float inv = 1.0f / sum;
+#pragma unroll
+  for (int j = 0; j < K; ++j) wt[j] = z[j] * inv;
+}
+
+// The picks above, then lane j < K writes pick j's id and weight (and, if lds_idx is given,
+// the id there too).
+template <int K>
+__device__ __forceinline__ void topk_softmax_wave_k(const float (&v)[4], int E, int lane, int32_t *__restrict__ idx_out,
+                                                    float *__restrict__ w_out, int *lds_idx) {
+  int sel_e[K];
+  float wt[K];
+  topk_picks_wave_k<K>(v, E, lane, sel_e, wt);
   int my_e = 0;
   float my_w = 0.f;
 #pragma unroll
   for (int j = 0; j < K; ++j) {
     my_e = lane == j ? sel_e[j] : my_e;
-    my_w = lane == j ? z[j] * inv : my_w;
+    my_w = lane == j ? wt[j] : my_w;
   }
   if (lane < K) {
     idx_out[lane] = my_e;

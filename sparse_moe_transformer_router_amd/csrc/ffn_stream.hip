@@ -606,7 +606,10 @@ hipError_t launch_ffn_stream(const uint16_t *a_src, bool a_by_token, const int32
     const int64_t mt32 = (S + kRCols - 1) / kRCols + busy;
     const int ntn = (w.N / 32 + kRWaves - 1) / kRWaves;
     dim3 g1((unsigned)(mt32 * ntn));
-    const bool deep = S >= 128;  // a 4-chunk weight ring once the grid is large
+    // a 4-chunk weight ring from 80 slots (FFN, decode20b: 20 tokens 77.6 against 81.3 us, 28 tokens 81.7
+    // against 85.1; at 16 tokens and fewer the 2-chunk ring, with a wave more per SIMD, is faster: 73.0
+    // against 75.8 us at 16, 69.0 against 71.1 at 8)
+    const bool deep = S >= 80;
 #define MOE_LAUNCH_ROWS(EPI)                                                                           \
   do {                                                                                                 \
     if (deep)                                                                                          \

@@ -411,6 +411,32 @@ def test_forward_matches_composed_steps(name, T, path):
     assert np.array_equal(out_fw, out)
 
 
+@pytest.mark.parametrize("E,k,H,I", [(1, 1, 64, 96), (2, 2, 128, 64), (7, 3, 96, 160), (8, 8, 256, 128),
+                                     (64, 4, 128, 96), (65, 4, 64, 64), (130, 5, 96, 96), (256, 8, 64, 32),
+                                     (32, 4, 2880, 2880)])
+@pytest.mark.parametrize("tiled,router_bias,out_dtype", [(True, True, "bf16"), (True, False, "f32"),
+                                                         (False, True, "f32")])
+def test_one_token_forward_matches_steps(E, k, H, I, tiled, router_bias, out_dtype):
+    """One token: with tiled gate_up weights the layer picks and sorts the token's k slots inside
+    the gate_up launch (no launch of their own); the output must be the same bits as route,
+    permute, expert FFN and combine called one by one, over expert counts on both sides of 64
+    and 128 (one to three logits per lane), k from 1 to 8, a router without bias and row-major
+    weights (the separate launches)."""
+    inp = synth.make_inputs(_small_cfg(E, k, H, I, T=1, seed=53 + E + k))
+    dev = gu.device_layer(inp, tiled=tiled)
+    router = dev.router if router_bias else moe.Router(dev.router.weight, None)
+    od = moe.MOE_DTYPE_BF16 if out_dtype == "bf16" else moe.MOE_DTYPE_F32
+    out_fw = moe.moe_forward_ex(dev.x, router, dev.w1, dev.w2, k, moe.Options(out_dtype=od))
+    idx, w = moe.moe_route(dev.x, router, k)
+    off, ss, sr = moe.moe_permute(idx, E)
+    y = moe.moe_mxfp4_ffn(dev.x, k, E, off, ss, dev.w1, dev.w2, moe.Options())
+    out = moe.moe_combine(y, sr, w, out_dtype=od)
+    a, b = out_fw.cpu(), out.cpu()
+    assert torch.isfinite(a.float()).all()
+    assert torch.equal(a.view(torch.int16) if od == moe.MOE_DTYPE_BF16 else a.view(torch.int32),
+                       b.view(torch.int16) if od == moe.MOE_DTYPE_BF16 else b.view(torch.int32))
+
+
 @pytest.mark.parametrize("T", [1, 16, 64, 256])
 def test_layer_decode120b_zipf(T):
     cfg = synth.get_config("decode120b_zipf")

@@ -384,7 +384,7 @@ def test_layer_tiny_alpha_limit():
 
 
 @pytest.mark.parametrize("tiled", [False, True])
-@pytest.mark.parametrize("T", [1, 8, 32, 64])
+@pytest.mark.parametrize("T", [1, 8, 20, 32, 64])  # 20 tokens: the 4-chunk weight ring's smallest batch
 def test_layer_decode20b(T, tiled):
     cfg = synth.get_config("decode20b")
     _check_layer(synth.make_inputs(cfg, T), tiled=tiled)

@@ -84,6 +84,9 @@ def parse():
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "pmc_traffic.md")
 CALIBRATION_MIB = 1024
 FFN_KERNELS = ("ffn_", "gather_rows")  # kernels one moe_mxfp4_ffn call launches, once each
+# instances that only the layer steps launch (the down projection writing y in slot order, epilogue
+# 6), not the expert-FFN calls the traffic line is per
+LAYER_ONLY_KERNELS = ("_kernel<6,",)
 
 
 # the sources of what one moe_mxfp4_ffn call runs at decode (the weight-streaming kernels, or for
@@ -132,7 +135,8 @@ def pmc_summary(args, T):
     write_scale = cal / cw[copy[0]]
     f = pmc_means(args.pmc_summary[2], "FETCH_SIZE")
     w = pmc_means(args.pmc_summary[3], "WRITE_SIZE")
-    names = sorted(k for k in f if any(t in k for t in FFN_KERNELS))
+    names = sorted(k for k in f if any(t in k for t in FFN_KERNELS)
+                   and not any(t in k.replace(" ", "") for t in LAYER_ONLY_KERNELS))
     fk = sum(f[k] for k in names)
     wk = sum(w.get(k, 0.0) for k in names)
     nbytes = int(round((fk * fetch_scale + wk * write_scale) * 1024))

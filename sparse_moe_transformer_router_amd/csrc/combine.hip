@@ -13,7 +13,7 @@ namespace moe {
 // dropped at their use (a pick outside [0, S) reads row 0 and is skipped; without a residual
 // the residual load reads y's first bytes and is ignored): with loads under branches the
 // compiler waited for the rows two at a time, one memory round trip per pair. K = k.
-template <int K>
+template <int K, bool BY_SLOT>
 __global__ __launch_bounds__(256) void combine_kernel(const float *__restrict__ y,
                                                       const int32_t *__restrict__ slot_row,
                                                       const float *__restrict__ topk_w, int64_t T, int H,
@@ -35,7 +35,11 @@ __global__ __launch_bounds__(256) void combine_kernel(const float *__restrict__ 
   }
   f32x4_t v[K];
 #pragma unroll
-  for (int j = 0; j < K; ++j) v[j] = *reinterpret_cast<const f32x4_t *>(y + (int64_t)(ok[j] ? r[j] : 0) * H + h);
+  for (int j = 0; j < K; ++j) {
+    // slot order: the row is the slot itself, so this load does not wait for slot_row's
+    const int64_t row = BY_SLOT ? t * K + j : (int64_t)(ok[j] ? r[j] : 0);
+    v[j] = *reinterpret_cast<const f32x4_t *>(y + row * H + h);
+  }
   // y holds S >= T rows of H floats, so its first T H halves cover the dummy residual read
   const uint2 res = *reinterpret_cast<const uint2 *>(
       (residual != nullptr ? residual : reinterpret_cast<const uint16_t *>(y)) + t * H + h);
@@ -65,13 +69,20 @@ __global__ __launch_bounds__(256) void combine_kernel(const float *__restrict__ 
 }
 
 hipError_t launch_combine(const float *y, const int32_t *slot_row, const float *topk_w, int64_t T,
-                          int k, int H, void *out, bool out_f32, hipStream_t stream, const uint16_t *residual) {
+                          int k, int H, void *out, bool out_f32, hipStream_t stream, const uint16_t *residual,
+                          bool by_slot) {
   const int threads = 256;
   const int64_t chunks = (H / 4 + threads - 1) / threads;
   dim3 grid((unsigned)(T * chunks));
-#define MOE_COMBINE(K)                                                                                    \
-  hipLaunchKernelGGL(combine_kernel<K>, grid, dim3(threads), 0, stream, y, slot_row, topk_w, T, H, residual, \
-                     out, out_f32 ? 1 : 0)
+#define MOE_COMBINE(K)                                                                                          \
+  do {                                                                                                          \
+    if (by_slot)                                                                                                \
+      hipLaunchKernelGGL((combine_kernel<K, true>), grid, dim3(threads), 0, stream, y, slot_row, topk_w, T, H,  \
+                         residual, out, out_f32 ? 1 : 0);                                                       \
+    else                                                                                                        \
+      hipLaunchKernelGGL((combine_kernel<K, false>), grid, dim3(threads), 0, stream, y, slot_row, topk_w, T, H, \
+                         residual, out, out_f32 ? 1 : 0);                                                       \
+  } while (0)
   switch (k) {
     case 1: MOE_COMBINE(1); break;
     case 2: MOE_COMBINE(2); break;

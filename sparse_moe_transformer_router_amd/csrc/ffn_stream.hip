@@ -274,6 +274,9 @@ __global__ __launch_bounds__(kSWaves *kWave) void ffn_stream_tiled_kernel(
 
   const int r32 = lane % 32, kh = lane / 32;
   const bool col_ok = r32 < mcount;
+  // slot-order output: the epilogue thread's slot row, looked up now, not after the loop
+  const int ycol = threadIdx.x % kTCols;
+  const int yrow = EPI == kEpiLinearSlotF32 ? sorted_slot[rbase + m0 + (ycol < mcount ? ycol : 0)] : 0;
   const uint16_t *arow = a_src;  // R1: the one token's row
   if (R1 == 0 && col_ok) {
     const int r = rbase + m0 + r32;
@@ -360,7 +363,7 @@ __global__ __launch_bounds__(kSWaves *kWave) void ffn_stream_tiled_kernel(
   const int col = threadIdx.x % kTCols;
   const int rq = (threadIdx.x / kTCols) * 8;  // 8 consecutive rows of the 64
   if (col >= mcount) return;
-  const int64_t r = rbase + m0 + col;
+  const int64_t r = EPI == kEpiLinearSlotF32 ? (int64_t)yrow : rbase + m0 + col;
   uint2 bq[2] = {uint2{0u, 0u}, uint2{0u, 0u}};  // bias of the 8 rows (rows past N: row 0)
   if (bias != nullptr) {
 #pragma unroll
@@ -478,6 +481,8 @@ __global__ __launch_bounds__(kRWaves *kWave) void ffn_stream_rows_kernel(
   }
   if (e < 0) return;
   const int r32 = lane % 32, kh = lane / 32;
+  // slot-order output: this lane's row goes to its slot's row, looked up now, not after the loop
+  const int yrow = EPI == kEpiLinearSlotF32 ? sorted_slot[rbase + m0 + (r32 < mcount ? r32 : 0)] : 0;
   const int KB = K / 32;
   const int nchunk = (KB + 3) / 4;
   const int NG = N / 32;
@@ -563,7 +568,7 @@ __global__ __launch_bounds__(kRWaves *kWave) void ffn_stream_rows_kernel(
 
   // epilogue: lane holds slot lane % 32 and rows 32 g + 8 i + 4 kh + jj of the output
   if (g >= NG || r32 >= mcount) return;
-  const int64_t r = rbase + m0 + r32;
+  const int64_t r = EPI == kEpiLinearSlotF32 ? (int64_t)yrow : rbase + m0 + r32;
   uint2 bq[4];
 #pragma unroll
   for (int i = 0; i < 4; ++i)
@@ -625,6 +630,7 @@ hipError_t launch_ffn_stream(const uint16_t *a_src, bool a_by_token, const int32
       case kEpiSwigluBf16: MOE_LAUNCH_ROWS(kEpiSwigluBf16); break;
       case kEpiPreactF32: MOE_LAUNCH_ROWS(kEpiPreactF32); break;
       case kEpiActF32: MOE_LAUNCH_ROWS(kEpiActF32); break;
+      case kEpiLinearSlotF32: MOE_LAUNCH_ROWS(kEpiLinearSlotF32); break;
       default: MOE_LAUNCH_ROWS(kEpiLinearF32); break;
     }
 #undef MOE_LAUNCH_ROWS
@@ -643,11 +649,13 @@ hipError_t launch_ffn_stream(const uint16_t *a_src, bool a_by_token, const int32
       case kEpiSwigluBf16: MOE_LAUNCH_TILED(kEpiSwigluBf16); break;
       case kEpiPreactF32: MOE_LAUNCH_TILED(kEpiPreactF32); break;
       case kEpiActF32: MOE_LAUNCH_TILED(kEpiActF32); break;
+      case kEpiLinearSlotF32: MOE_LAUNCH_TILED(kEpiLinearSlotF32); break;
       default: MOE_LAUNCH_TILED(kEpiLinearF32); break;
     }
 #undef MOE_LAUNCH_TILED
     return hipGetLastError();
   }
+  if (epilogue == kEpiLinearSlotF32) return hipErrorInvalidValue;  // tiled weights only
   switch (epilogue) {
     case kEpiSwigluBf16: MOE_LAUNCH_STREAM(kEpiSwigluBf16); break;
     case kEpiPreactF32: MOE_LAUNCH_STREAM(kEpiPreactF32); break;

@@ -14,6 +14,8 @@ enum FfnEpilogue : int {
   kEpiLinearF32 = 3,   // down: W a + b -> fp32 [S][N]
   kEpiMxAct = 4,       // gate_up: bf16-rounded SwiGLU(h) -> two-term MXFP8 records (mx_act.h)
   kEpiMx6Act = 5,      // gate_up: bf16-rounded SwiGLU(h) -> two-term MXFP6 records (mx_act.h)
+  kEpiLinearSlotF32 = 6,  // down, tiled weights: W a + b -> fp32 [S][N] in slot order (sorted row r
+                          // goes to row sorted_slot[r]), for launch_combine's by_slot form
 };
 
 struct MxWeight {
@@ -131,9 +133,11 @@ size_t scratch_bytes();
 hipError_t scratch_address(void **ptr);
 
 // residual (bf16 [T][H], nullable) is added to the weighted sum before the rounding.
+// by_slot: y's rows are in slot order (y[t * k + j], kEpiLinearSlotF32), so no row is looked up
+// before its load; slot_row still marks the picks that have a row.
 hipError_t launch_combine(const float *y, const int32_t *slot_row, const float *topk_w, int64_t T,
                           int k, int H, void *out, bool out_f32, hipStream_t stream,
-                          const uint16_t *residual = nullptr);
+                          const uint16_t *residual = nullptr, bool by_slot = false);
 // The same combine when each picked expert's output row is the sum of nslice partial rows
 // (part + s * S * H, s = 0 .. nslice-1; the smallest-batch path), summed in the fixed order that
 // launch_slice_sum uses. nslice <= kSmallMaxSlices.

@@ -153,10 +153,14 @@ Family family(const moe_options_t &o, const moe_mxfp4_weight_t &gu, const moe_mx
 // slots), the expert FFNs run as one launch (launch_ffn_small) writing per-block partial rows
 // into part; then *nslice_out = the block count (1 or more), and y is written (the blocks'
 // in-order sum) only if want_y. Otherwise y is written and *nslice_out = 0.
+// y_slot: non-null when the caller takes y in slot order (row t * k + j, for launch_combine's
+// by_slot form); *y_slot then says whether y was written that way (the weight-streaming family
+// with tiled down weights) or in sorted order.
 int run_ffn(const uint16_t *x, int64_t T, int k, int E, const int32_t *offsets, const int32_t *sorted_slot,
             const moe_mxfp4_weight_t &gu, const moe_mxfp4_weight_t &dn, const moe_options_t &o, float *y,
             void *act, void *xs, float *part, bool want_y, int *nslice_out, hipStream_t stream,
-            bool x_records_ready = false) {
+            bool x_records_ready = false, bool *y_slot = nullptr) {
+  if (y_slot != nullptr) *y_slot = false;
   const int64_t S = T * k;
   const int H = gu.k, I = dn.k;
   const moe::MxWeight w1 = mx(gu);
@@ -181,8 +185,12 @@ int run_ffn(const uint16_t *x, int64_t T, int k, int E, const int32_t *offsets, 
     };
     if (first_epi >= 0) return launch(x, true, w1, first_epi, y) == hipSuccess ? MOE_OK : MOE_ERR_HIP;
     if (launch(x, true, w1, moe::kEpiSwigluBf16, act) != hipSuccess) return MOE_ERR_HIP;
-    return launch(static_cast<uint16_t *>(act), false, w2, moe::kEpiLinearF32, y) == hipSuccess ? MOE_OK
-                                                                                              : MOE_ERR_HIP;
+    const bool slot = y_slot != nullptr && w2.tiled;
+    if (launch(static_cast<uint16_t *>(act), false, w2, slot ? moe::kEpiLinearSlotF32 : moe::kEpiLinearF32, y) !=
+        hipSuccess)
+      return MOE_ERR_HIP;
+    if (slot) *y_slot = true;
+    return MOE_OK;
   }
   // block-scaled families: x's T rows become exact two-term MXFP8 records once, and gate_up reads
   // each sorted row's token record (a_rows = sorted_slot, a_div = k); its epilogue writes the
@@ -272,12 +280,14 @@ int forward_impl(const uint16_t *x, const moe_router_t *router, const moe_mxfp4_
       moe::ffn_route1_fits(T, E, k, w1)) {
     // one token: the top-k and the permutation of its k slots run inside the gate_up launch
     const moe::Route1 r1{logits, moe::router_splits(T, E, H), router->bias, idx, wts, offsets, sorted_slot, slot_row};
+    const moe::MxWeight w2 = mx(*dn);
     if (moe::launch_router_partial(x, T, H, router->weight, E, logits, stream) != hipSuccess ||
         moe::launch_ffn_stream_route1(x, k, E, w1, act, o.swiglu_limit, o.swiglu_alpha, r1, stream) != hipSuccess ||
-        moe::launch_ffn_stream(static_cast<uint16_t *>(act), false, sorted_slot, k, offsets, E, S, mx(*dn),
-                               moe::kEpiLinearF32, y, o.swiglu_limit, o.swiglu_alpha, stream) != hipSuccess ||
-        moe::launch_combine(y, slot_row, wts, T, k, H, out, o.out_dtype == MOE_DTYPE_F32, stream, residual) !=
-            hipSuccess)
+        moe::launch_ffn_stream(static_cast<uint16_t *>(act), false, sorted_slot, k, offsets, E, S, w2,
+                               w2.tiled ? moe::kEpiLinearSlotF32 : moe::kEpiLinearF32, y, o.swiglu_limit,
+                               o.swiglu_alpha, stream) != hipSuccess ||
+        moe::launch_combine(y, slot_row, wts, T, k, H, out, o.out_dtype == MOE_DTYPE_F32, stream, residual,
+                            w2.tiled) != hipSuccess)
       return MOE_ERR_HIP;
     return MOE_OK;
   }
@@ -296,14 +306,16 @@ int forward_impl(const uint16_t *x, const moe_router_t *router, const moe_mxfp4_
   }
   int nslice = 0;
   float *part = at<float>(ws, L.ypart);
+  bool y_slot = false;
   int st = run_ffn(x, T, k, E, offsets, sorted_slot, *gu, *dn, o, y, act, at<void>(ws, L.xs), part, false, &nslice,
-                   stream, records_ready);
+                   stream, records_ready, &y_slot);
   if (st != MOE_OK) return st;
   // the experts' outputs: y, or the per-slice partial rows of the smallest-batch path
   const hipError_t ce =
       nslice > 0 ? moe::launch_combine_sliced(part, nslice, slot_row, wts, T, k, H, out, o.out_dtype == MOE_DTYPE_F32,
                                               stream, residual)
-                 : moe::launch_combine(y, slot_row, wts, T, k, H, out, o.out_dtype == MOE_DTYPE_F32, stream, residual);
+                 : moe::launch_combine(y, slot_row, wts, T, k, H, out, o.out_dtype == MOE_DTYPE_F32, stream, residual,
+                                       y_slot);
   if (ce != hipSuccess) return MOE_ERR_HIP;
   return MOE_OK;
 }
